@@ -1,0 +1,149 @@
+"""Pins for the oracle's activation quantiser and forward contraction
+(BitNet b1.58 2B4T article §一 and §四: 8-bit activations times ternary
+weights, no bias).  The quantiser is checked against exact Fractions with
+Python's ties-to-even round(); the contraction against numpy's integer
+matmul; the epilogue against exact rational evaluation."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_linear_layers_group_amd import synth
+
+
+def vals(B):
+    return synth.bf16_bits_to_f32(B).astype(np.float64)
+
+
+def exact_act_quant(X):
+    v = vals(X)
+    xq = np.zeros(v.shape, np.int64)
+    sc = []
+    for t in range(v.shape[0]):
+        a = max(abs(Fraction(float(x))) for x in v[t])
+        sc.append(a / 127)
+        for c in range(v.shape[1]):
+            if a == 0:
+                continue
+            q = round(127 * Fraction(float(v[t, c])) / a)  # ties to even
+            xq[t, c] = max(-128, min(127, q))
+    return xq, sc
+
+
+def test_act_quant_matches_exact_rationals():
+    X = synth.activations(12, 384, seed=21)
+    xq, sc = oracle.act_quant(X)
+    exq, esc = exact_act_quant(X)
+    assert np.array_equal(xq.astype(np.int64), exq)
+    for t in range(12):
+        assert sc[t] == float(esc[t])
+
+
+def test_act_quant_crafted_half_way_values():
+    # a = 127 makes 127*x/a = x: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, -2.5 -> -2
+    row = np.zeros(128, np.float32)
+    row[:6] = [127, 0.5, 1.5, 2.5, -2.5, -127]
+    xq, sc = oracle.act_quant(synth.f32_to_bf16_bits(row[None, :]))
+    assert list(xq[0, :6]) == [127, 0, 2, 2, -2, -127]
+    assert sc[0] == 1.0
+
+
+def test_act_quant_absmax_maps_to_127_and_zero_rows():
+    X = synth.activations(8, 256, seed=22)
+    X[3] = 0
+    xq, sc = oracle.act_quant(X)
+    v = vals(X)
+    for t in range(8):
+        if t == 3:
+            assert sc[t] == 0.0 and not xq[t].any()
+            continue
+        j = int(np.argmax(np.abs(v[t])))
+        assert abs(int(xq[t, j])) == 127 and np.sign(xq[t, j]) == np.sign(v[t, j])
+        assert np.max(np.abs(xq[t].astype(int))) == 127
+
+
+def test_act_quant_rounding_mode_is_exercised_by_workload_data():
+    """N(0,1) bf16 rows produce exact half-way quotients, where ties-to-even
+    and ties-away differ; the exact check above therefore pins the mode."""
+    X = synth.activations(256, 2048, seed=0)
+    v = vals(X)
+    a = np.max(np.abs(v), axis=1, keepdims=True)
+    q = 127.0 * v / a
+    frac = np.abs(q - np.trunc(q))
+    ties = np.count_nonzero(frac == 0.5)
+    assert ties > 100
+
+
+def small_problem(n, m, tokens=5, k=256, n_out=48, seed=30):
+    W = synth.weights(n_out, k, seed=seed)
+    X = synth.activations(tokens, k, seed=seed)
+    return oracle.forward_all(W, X, n, m)
+
+
+@pytest.mark.parametrize("n,m", [(8, 8), (6, 8), (4, 8), (2, 4)])
+def test_acc_matches_integer_matmul(n, m):
+    r = small_problem(n, m)
+    ref = r["xq"].astype(np.int64) @ r["T"].astype(np.int64).T
+    assert np.array_equal(r["acc"].astype(np.int64), ref)
+
+
+def test_epilogue_matches_exact_rationals():
+    r = small_problem(6, 8, tokens=3, n_out=16)
+    g = Fraction(r["gamma"])
+    for t in range(3):
+        s = Fraction(r["scale"][t])
+        for j in range(16):
+            exact = int(r["acc"][t, j]) * g * s
+            y = r["Y"][t, j]
+            assert abs(Fraction(y) - exact) <= abs(exact) * Fraction(1, 2 ** 50)
+
+
+def test_forward_equals_dequantised_float_product():
+    """Y = (x_q * s) @ (T * gamma)^T evaluated directly in binary64."""
+    r = small_problem(6, 8, tokens=4, n_out=32)
+    ref = (r["xq"] * r["scale"][:, None]) @ (r["T"].astype(np.float64) * r["gamma"]).T
+    assert np.allclose(r["Y"], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_dense_pattern_is_dense_bitnet_product():
+    W = synth.weights(32, 256, seed=31)
+    X = synth.activations(4, 256, seed=31)
+    r = oracle.forward_all(W, X, 8, 8)
+    v = vals(W)
+    dense = np.where(2 * np.abs(v) > r["gamma"], np.sign(v), 0)
+    assert np.array_equal(r["acc"], (r["xq"].astype(np.int64) @ dense.astype(np.int64).T))
+
+
+def test_single_token_rows_equal_batched_rows():
+    W = synth.weights(32, 256, seed=32)
+    X = synth.activations(6, 256, seed=32)
+    full = oracle.forward_all(W, X, 6, 8)
+    for t in range(6):
+        one = oracle.forward_all(W, X[t:t + 1], 6, 8)
+        assert np.array_equal(one["acc"][0], full["acc"][t])
+        assert np.array_equal(one["Y"][0], full["Y"][t])
+
+
+def test_pairs_and_threads_agree_with_full():
+    r = small_problem(6, 8, tokens=7, n_out=40)
+    acc4, y4 = oracle.fwd(r["xq"], r["scale"], r["T"], r["gamma"], threads=4)
+    assert np.array_equal(acc4, r["acc"]) and np.array_equal(y4, r["Y"])
+    ti = np.array([0, 6, 3, 2])
+    ni = np.array([39, 0, 17, 5])
+    a, y = oracle.fwd_pairs(r["xq"], r["scale"], r["T"], r["gamma"], ti, ni)
+    assert np.array_equal(a, r["acc"][ti, ni]) and np.array_equal(y, r["Y"][ti, ni])
+
+
+def test_forward_is_not_transposed():
+    """Non-square shapes: each output row depends on its own token only and
+    each column on its own weight row only."""
+    r = small_problem(6, 8, tokens=3, k=128, n_out=80)
+    assert r["acc"].shape == (3, 80)
+    W = synth.weights(80, 128, seed=30)
+    X = synth.activations(3, 128, seed=30)
+    X2 = X.copy()
+    X2[1] = synth.activations(1, 128, seed=99)[0]
+    r2 = oracle.forward_all(W, X2, 6, 8)
+    assert np.array_equal(r2["acc"][0], r["acc"][0]) and np.array_equal(r2["acc"][2], r["acc"][2])
+    assert not np.array_equal(r2["acc"][1], r["acc"][1])

@@ -1,0 +1,120 @@
+"""Pins for the oracle's N:M mask (Sparse-BitNet article, §三 dynamic mask,
+§五 per-group threshold keeping 6 of 8, §六 mask from full-precision
+weights).  Each check is independent of the oracle's ranking loop."""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_linear_layers_group_amd import synth
+
+PATTERNS = [(8, 8), (6, 8), (4, 8), (2, 4)]
+
+
+def bits_of(mask_bytes, k):
+    """uint8 [rows, k/8] -> 0/1 [rows, k] (bit k%8 of byte k/8)."""
+    m = np.unpackbits(mask_bytes, axis=1, bitorder="little")
+    return m[:, :k].astype(np.int64)
+
+
+def mag(W):
+    return np.abs(synth.bf16_bits_to_f32(W).astype(np.float64))
+
+
+def brute_force_mask(W, n, m):
+    """Enumerate every N-subset of each group and keep the one whose entries,
+    listed by (|W| descending, index ascending), is lexicographically
+    greatest -- a search, not a ranking."""
+    a = mag(W)
+    rows, k = a.shape
+    out = np.zeros((rows, k), dtype=np.int64)
+    for r in range(rows):
+        for g0 in range(0, k, m):
+            best = None
+            for sub in itertools.combinations(range(m), n):
+                key = sorted(((a[r, g0 + j], -j) for j in sub), reverse=True)
+                if best is None or key > best[0]:
+                    best = (key, sub)
+            for j in best[1]:
+                out[r, g0 + j] = 1
+    return out
+
+
+@pytest.mark.parametrize("n,m", PATTERNS)
+def test_exactly_n_kept_per_group(n, m):
+    W = synth.weights(64, 512, seed=11)
+    b = bits_of(oracle.mask(W, n, m), 512)
+    per_group = b.reshape(64, 512 // m, m).sum(axis=2)
+    assert np.all(per_group == n)
+
+
+@pytest.mark.parametrize("n,m", PATTERNS)
+def test_matches_subset_search(n, m):
+    # few distinct magnitudes -> many ties at the keep/drop boundary
+    rng = np.random.default_rng(5)
+    vals = rng.choice(np.array([0.0, -0.0, 0.25, -0.25, 0.5, -1.0, 1.0], np.float32), size=(6, 64))
+    W = synth.f32_to_bf16_bits(vals)
+    assert np.array_equal(bits_of(oracle.mask(W, n, m), 64), brute_force_mask(W, n, m))
+    W2 = synth.weights(6, 64, seed=3)
+    assert np.array_equal(bits_of(oracle.mask(W2, n, m), 64), brute_force_mask(W2, n, m))
+
+
+@pytest.mark.parametrize("n,m", PATTERNS)
+def test_pairwise_keep_drop_order(n, m):
+    """Every kept entry beats every dropped one in its group: larger |W|,
+    or equal |W| and a lower index."""
+    W = synth.weights(32, 256, seed=7)
+    a = mag(W)
+    b = bits_of(oracle.mask(W, n, m), 256)
+    for r in range(32):
+        for g0 in range(0, 256, m):
+            kept = [j for j in range(m) if b[r, g0 + j]]
+            dropped = [j for j in range(m) if not b[r, g0 + j]]
+            for i in kept:
+                for j in dropped:
+                    ai, aj = a[r, g0 + i], a[r, g0 + j]
+                    assert ai > aj or (ai == aj and i < j)
+
+
+def test_dense_pattern_keeps_everything():
+    W = synth.weights(16, 256, seed=1)
+    assert np.all(oracle.mask(W, 8, 8) == 0xFF)
+
+
+def test_all_equal_keeps_lowest_indices():
+    W = synth.f32_to_bf16_bits(np.full((3, 128), -0.5, np.float32))
+    b = bits_of(oracle.mask(W, 6, 8), 128)
+    assert np.all(b.reshape(3, 16, 8) == np.array([1, 1, 1, 1, 1, 1, 0, 0]))
+    b24 = bits_of(oracle.mask(W, 2, 4), 128)
+    assert np.all(b24.reshape(3, 32, 4) == np.array([1, 1, 0, 0]))
+
+
+def test_signed_zeros_tie():
+    # +0 and -0 have equal magnitude: the lower index wins
+    row = np.array([0.0, -0.0, 1, 1, 1, 1, 1, 1], np.float32)
+    W = synth.f32_to_bf16_bits(np.tile(row, (1, 16)))
+    b = bits_of(oracle.mask(W, 6, 8), 128)
+    assert list(b[0, :8]) == [0, 0, 1, 1, 1, 1, 1, 1]
+    row2 = np.array([-0.0, 0.0, 0.0, 1, 1, 1, 1, 1], np.float32)
+    W2 = synth.f32_to_bf16_bits(np.tile(row2, (1, 16)))
+    assert list(bits_of(oracle.mask(W2, 6, 8), 128)[0, :8]) == [1, 0, 0, 1, 1, 1, 1, 1]
+
+
+def test_sign_and_scale_invariance():
+    W = synth.weights(16, 256, seed=2)
+    neg = W ^ np.uint16(0x8000)
+    assert np.array_equal(oracle.mask(W, 6, 8), oracle.mask(neg, 6, 8))
+    # doubling every entry (exact in bf16 away from overflow) keeps the order
+    f = synth.bf16_bits_to_f32(W) * np.float32(2.0)
+    assert np.array_equal(oracle.mask(W, 6, 8), oracle.mask(synth.f32_to_bf16_bits(f), 6, 8))
+
+
+def test_tie_rule_is_exercised_by_the_workload_data():
+    """bf16 N(0, 0.02) weights produce magnitude ties at the keep/drop
+    boundary often enough that the index rule decides real groups."""
+    W = synth.weights(512, 2048, seed=0)
+    a = mag(W).reshape(512, 256, 8)
+    s = np.sort(a, axis=2)
+    boundary_ties = np.count_nonzero(s[:, :, 1] == s[:, :, 2])  # 6:8 drop boundary
+    assert boundary_ties > 100
