@@ -1,0 +1,166 @@
+/*
+ * bitlinear.h -- C ABI of the Sparse-BitNet BitLinear hot path on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * A BitLinear layer replaces a linear layer and has no bias (BitNet b1.58
+ * 2B4T article, §一).  Its weight path, per Sparse-BitNet (explainer
+ * article §三-§六; paper abstract), recomputes an N:M mask from the latent
+ * full-precision weights every step, quantises to absmean ternary codes
+ * (quantise first, then sparsify), multiplies with per-token int8
+ * activations, and trains through both non-differentiable steps with a
+ * straight-through estimator that still sends gradient to masked weights.
+ *
+ * Conventions shared by every call
+ *   - Pointers named as device pointers must be device memory of the
+ *     current HIP device, 16-byte aligned (gamma: 8-byte; x_scale: 4-byte).
+ *     The caller allocates and frees every buffer; the library keeps no
+ *     device memory and no global state between calls.
+ *   - bf16 tensors are passed as uint16_t bit patterns.  W is [n_out x k],
+ *     X is [tokens x k], dY is [tokens x n_out]; all row-major, contiguous.
+ *   - Supported patterns (n, m): 8:8 (dense), 6:8, 4:8, 2:4.  k must be a
+ *     positive multiple of 128; n_out >= 1; n_out*k, tokens*k and
+ *     tokens*n_out below 2^31.
+ *   - Outputs must not alias inputs or each other.
+ *   - Every compute call only enqueues work on `stream` (a hipStream_t; NULL
+ *     = the default stream) and returns without synchronising.  Arguments
+ *     are validated on the host before anything is enqueued; on a non-zero
+ *     status nothing was enqueued, except BL_EHIP, which reports a failed
+ *     launch (work enqueued earlier in the same call may have run).  Faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - NaN or infinite inputs are outside the contract (not checked).
+ *   - Calls are reentrant; the last-error text is per host thread.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define BL_OK            0
+#define BL_EINVAL        1  /* null or misaligned pointer, bad enum value  */
+#define BL_ESHAPE        2  /* sizes outside the supported range           */
+#define BL_EUNSUPPORTED  3  /* N:M pattern not supported                    */
+#define BL_EWORKSPACE    4  /* workspace missing or smaller than required   */
+#define BL_EHIP          5  /* a HIP runtime call or kernel launch failed   */
+
+/* Which entries the absmean scale averages over (gamma_over). */
+#define BL_GAMMA_DENSE   0  /* all n_out*k latent entries: quantise first
+                               (Sparse-BitNet article §六, the order the
+                               pages report as better)                    */
+#define BL_GAMMA_MASKED  1  /* ablation: sum over kept entries only, still
+                               divided by n_out*k (sparsify first)        */
+
+/* Bytes of the packed ternary weights for an [n_out x k] layer under
+ * pattern n:m, or 0 if the shape or pattern is unsupported.  The packed
+ * layout stores each row's codes per 8-group as a nonzero bitmap plus one
+ * sign bit per nonzero (S = 8, 6, 4, 4 sign slots for 8:8, 6:8, 4:8, 2:4),
+ * 16 groups per 128-wide k block, rows in tiles of 16:
+ *   ceil(n_out/16) * 16 * (k/128) * 2*(8+S) bytes.
+ * The 2-bit-per-weight storage of BitNet b1.58 (2B4T article §四) is the
+ * 8:8 size of this format. */
+size_t bitlinear_packed_bytes(int64_t n_out, int64_t k, int n, int m);
+
+/* Workspace bytes bitlinear_quantize_mask needs (exact-sum accumulators and
+ * a completion counter).  Host function; never fails for valid shapes. */
+size_t bitlinear_workspace_bytes(int64_t n_out, int64_t k);
+
+/* Workspace bytes bitlinear_fwd needs for `tokens` tokens (split-k partial
+ * sums of the decode kernel); 0 means ws may be NULL. */
+size_t bitlinear_fwd_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out);
+
+/* Steps 1-2 (and optionally 3): mask and absmean scale.
+ * Sparse-BitNet article §三 (mask recomputed every step), §五 (keep N of
+ * every M by a per-group threshold), §六 (rank by the latent
+ * full-precision weights); BitNet b1.58 2B4T article §一 (absmean).
+ *   W      device, bf16 [n_out x k], read only.
+ *   mask   device, uint8 [n_out x k/8], written: bit (c % 8) of byte
+ *          (r, c/8) is 1 where W[r, c] is kept.  In each group of m
+ *          consecutive entries along k the n largest |W| are kept; equal
+ *          magnitudes keep the lower index (+0 and -0 are equal).
+ *   wq     device, int8 [n_out x k] or NULL; if given, the masked ternary
+ *          codes are also written (see bitlinear_pack).
+ *   gamma  device, one double, written: the exact sum of |W| (over all
+ *          entries, or kept entries for BL_GAMMA_MASKED) rounded once to
+ *          binary64, divided by n_out*k in binary64.  Bit-reproducible.
+ *   ws     device workspace of at least bitlinear_workspace_bytes(); its
+ *          contents need not be initialised and are clobbered.
+ */
+int bitlinear_quantize_mask(const uint16_t *W, int64_t n_out, int64_t k,
+                            int n, int m, int gamma_over, uint8_t *mask,
+                            int8_t *wq, double *gamma, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/* Step 3-4: masked ternary codes, packed.  BitNet b1.58 2B4T article §一
+ * (ternary codes) and §四 (packed low-bit storage streamed from HBM).
+ * The code of W[r, c] is sign(W) where the mask keeps it and 2|W| > gamma
+ * (the exact form of clip(round_half_even(W/gamma), -1, 1) != 0), else 0.
+ *   W, mask, gamma  device inputs as produced above.
+ *   packed          device output of packed_bytes bytes (must equal
+ *                   bitlinear_packed_bytes(n_out, k, n, m)).
+ */
+int bitlinear_pack(const uint16_t *W, const uint8_t *mask,
+                   const double *gamma, int64_t n_out, int64_t k, int n,
+                   int m, void *packed, size_t packed_bytes, void *stream);
+
+/* Steps 5-7: per-token int8 activations, int32 contraction, epilogue.
+ * BitNet b1.58 2B4T article §一 (8-bit activations, no bias) and §四
+ * (ternary times int8 kernel).  For each token t:
+ *   a_t = max_c |X[t, c]|,  x_q = clip(round_half_even(127 X / a_t),
+ *   -128, 127) (exact quotient),  s_t = a_t / 127 (binary32, correctly
+ *   rounded); a_t = 0 gives x_q = 0, s_t = 0.
+ *   acc[t, r] = sum_c x_q[t, c] * code[r, c]  (int32, exact)
+ *   Y[t, r]   = acc[t, r] * gamma * s_t      (binary32)
+ *   X        device bf16 [tokens x k].
+ *   packed   device, from bitlinear_pack with the same n_out, k, n, m.
+ *   gamma    device double from bitlinear_quantize_mask.
+ *   Y        device float [tokens x n_out], written.
+ *   xq       device int8 [tokens x k], written (kept for the backward).
+ *   x_scale  device float [tokens], written (s_t).
+ *   acc      device int32 [tokens x n_out] or NULL (debug output).
+ *   ws       device workspace of bitlinear_fwd_workspace_bytes(), or NULL
+ *            when that is 0; clobbered.
+ * tokens <= 16 runs the decode kernel, larger counts the prefill kernel;
+ * both give identical results.  tokens == 0 is a no-op.
+ */
+int bitlinear_fwd(const uint16_t *X, int64_t tokens, int64_t k,
+                  const void *packed, int64_t n_out, int n, int m,
+                  const double *gamma, float *Y, int8_t *xq, float *x_scale,
+                  int32_t *acc, void *ws, size_t ws_bytes, void *stream);
+
+/* Step 8-9: dual straight-through backward.  Sparse-BitNet article §三 and
+ * §六: gradients pass straight through the ternary rounding and the
+ * sparsification, and masked weights still receive their gradient.
+ *   dX[t, c] = gamma * sum_r dY[t, r] * code[r, c]          (binary32)
+ *   dW[r, c] = sum_t dY[t, r] * s_t * x_q[t, c]   for all (r, c), masked
+ *              entries included                               (binary32)
+ * computed on bf16 matrix cores with binary32 accumulation (dY*s_t is
+ * rounded to bf16; codes and x_q are exact in bf16).
+ *   dY       device bf16 [tokens x n_out].
+ *   xq, x_scale  device, as written by bitlinear_fwd.
+ *   packed, gamma  device, as for bitlinear_fwd.
+ *   dX       device float [tokens x k] or NULL (skip).
+ *   dW       device float [n_out x k] or NULL (skip).
+ *   ws, ws_bytes  reserved; pass NULL, 0.
+ */
+int bitlinear_bwd(const uint16_t *dY, const int8_t *xq, const float *x_scale,
+                  const void *packed, const double *gamma, int64_t tokens,
+                  int64_t k, int64_t n_out, int n, int m, float *dX,
+                  float *dW, void *ws, size_t ws_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *bitlinear_status_string(int status);
+
+/* Detail of the last non-zero status returned on this host thread ("" if
+ * none).  The pointer stays valid until the next call on this thread. */
+const char *bitlinear_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,171 @@
+"""Thin Python binding of libbitlinear.so (C ABI in include/bitlinear.h).
+
+Argument marshalling only: each function has the C entry point's name and
+argument order, takes torch tensors where the C call takes device pointers,
+checks dtype / device / contiguity / size, and passes raw pointers and the
+caller's HIP stream (default: torch's current stream).  Every step of the
+computation runs in the HIP library; if the library is not built, loading
+fails with an error -- there is no fallback path.
+"""
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "bitlinear.h")
+
+BL_OK, BL_EINVAL, BL_ESHAPE, BL_EUNSUPPORTED, BL_EWORKSPACE, BL_EHIP = range(6)
+BL_GAMMA_DENSE, BL_GAMMA_MASKED = 0, 1
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status, where, detail):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+_lib = None
+_i64, _int, _sz, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGS = {
+    "bitlinear_packed_bytes": (_sz, [_i64, _i64, _int, _int]),
+    "bitlinear_workspace_bytes": (_sz, [_i64, _i64]),
+    "bitlinear_fwd_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "bitlinear_quantize_mask": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "bitlinear_pack": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _sz, _vp]),
+    "bitlinear_fwd": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "bitlinear_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _sz, _vp]),
+    "bitlinear_status_string": (ctypes.c_char_p, [_int]),
+    "bitlinear_last_error": (ctypes.c_char_p, []),
+}
+
+
+def header_functions():
+    """Names of the functions include/bitlinear.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_\w+)\s*\(", text)))
+
+
+def lib():
+    """Load libbitlinear.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "or python -m sparse_linear_layers_group_amd.build")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _ptr(t, dtypes, numel, name, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+def _check(status, where):
+    if status != BL_OK:
+        detail = lib().bitlinear_last_error().decode() or lib().bitlinear_status_string(status).decode()
+        raise BitLinearError(status, where, detail)
+
+
+def bitlinear_status_string(status):
+    return lib().bitlinear_status_string(int(status)).decode()
+
+
+def bitlinear_last_error():
+    return lib().bitlinear_last_error().decode()
+
+
+def bitlinear_packed_bytes(n_out, k, n, m):
+    return int(lib().bitlinear_packed_bytes(int(n_out), int(k), int(n), int(m)))
+
+
+def bitlinear_workspace_bytes(n_out, k):
+    return int(lib().bitlinear_workspace_bytes(int(n_out), int(k)))
+
+
+def bitlinear_fwd_workspace_bytes(tokens, k, n_out):
+    return int(lib().bitlinear_fwd_workspace_bytes(int(tokens), int(k), int(n_out)))
+
+
+def bitlinear_quantize_mask(W, n_out, k, n, m, gamma_over, mask, wq, gamma, ws, ws_bytes=None,
+                            stream=None):
+    st = lib().bitlinear_quantize_mask(
+        _ptr(W, _BF16, n_out * k, "W"), n_out, k, n, m, gamma_over,
+        _ptr(mask, (torch.uint8,), n_out * (k // 8), "mask"),
+        _ptr(wq, (torch.int8,), n_out * k, "wq", optional=True),
+        _ptr(gamma, (torch.float64,), 1, "gamma"),
+        _ptr(ws, (torch.uint8,), None, "ws"),
+        ws.numel() if ws_bytes is None else int(ws_bytes), _stream(stream))
+    _check(st, "bitlinear_quantize_mask")
+
+
+def bitlinear_pack(W, mask, gamma, n_out, k, n, m, packed, packed_bytes=None, stream=None):
+    st = lib().bitlinear_pack(
+        _ptr(W, _BF16, n_out * k, "W"), _ptr(mask, (torch.uint8,), n_out * (k // 8), "mask"),
+        _ptr(gamma, (torch.float64,), 1, "gamma"), n_out, k, n, m,
+        _ptr(packed, (torch.uint8,), None, "packed"),
+        packed.numel() if packed_bytes is None else int(packed_bytes), _stream(stream))
+    _check(st, "bitlinear_pack")
+
+
+def bitlinear_fwd(X, tokens, k, packed, n_out, n, m, gamma, Y, xq, x_scale, acc=None, ws=None,
+                  ws_bytes=None, stream=None):
+    st = lib().bitlinear_fwd(
+        _ptr(X, _BF16, tokens * k, "X"), tokens, k, _ptr(packed, (torch.uint8,), None, "packed"),
+        n_out, n, m, _ptr(gamma, (torch.float64,), 1, "gamma"),
+        _ptr(Y, (torch.float32,), tokens * n_out, "Y"), _ptr(xq, (torch.int8,), tokens * k, "xq"),
+        _ptr(x_scale, (torch.float32,), tokens, "x_scale"),
+        _ptr(acc, (torch.int32,), tokens * n_out, "acc", optional=True),
+        _ptr(ws, (torch.uint8,), None, "ws", optional=True),
+        (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes),
+        _stream(stream))
+    _check(st, "bitlinear_fwd")
+
+
+def bitlinear_bwd(dY, xq, x_scale, packed, gamma, tokens, k, n_out, n, m, dX, dW, ws=None,
+                  ws_bytes=None, stream=None):
+    st = lib().bitlinear_bwd(
+        _ptr(dY, _BF16, tokens * n_out, "dY"), _ptr(xq, (torch.int8,), tokens * k, "xq", optional=True),
+        _ptr(x_scale, (torch.float32,), tokens, "x_scale", optional=True),
+        _ptr(packed, (torch.uint8,), None, "packed", optional=True),
+        _ptr(gamma, (torch.float64,), 1, "gamma", optional=True), tokens, k, n_out, n, m,
+        _ptr(dX, (torch.float32,), tokens * k, "dX", optional=True),
+        _ptr(dW, (torch.float32,), n_out * k, "dW", optional=True),
+        _ptr(ws, (torch.uint8,), None, "ws", optional=True),
+        (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes),
+        _stream(stream))
+    _check(st, "bitlinear_bwd")

@@ -1,0 +1,230 @@
+// abi.hip -- the C ABI declared in include/bitlinear.h: host-side argument
+// validation, then kernel launches on the caller's stream.  No exception
+// leaves this file; no device memory is allocated.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/bitlinear.h"
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return BL_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kLimit = (int64_t)1 << 31;
+
+int check_nm(int n, int m) {
+  if (bl::s_of(n, m) < 0)
+    return fail(BL_EUNSUPPORTED, "N:M pattern %d:%d unsupported (use 8:8, 6:8, 4:8 or 2:4)", n, m);
+  return BL_OK;
+}
+
+int check_layer(int64_t n_out, int64_t k) {
+  if (n_out < 1) return fail(BL_ESHAPE, "n_out must be >= 1 (got %lld)", (long long)n_out);
+  if (k < 128 || k % 128 != 0)
+    return fail(BL_ESHAPE, "k must be a positive multiple of 128 (got %lld)", (long long)k);
+  if (n_out >= kLimit || k >= kLimit || n_out * k >= kLimit)
+    return fail(BL_ESHAPE, "n_out*k must stay below 2^31");
+  return BL_OK;
+}
+
+int check_ptr(const void* p, size_t align, const char* name) {
+  if (!p) return fail(BL_EINVAL, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(BL_EINVAL, "%s is not %zu-byte aligned", name, align);
+  return BL_OK;
+}
+
+int check_opt_ptr(const void* p, size_t align, const char* name) {
+  if (p && !aligned(p, align)) return fail(BL_EINVAL, "%s is not %zu-byte aligned", name, align);
+  return BL_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(BL_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+#define TRY(expr)            \
+  do {                       \
+    int _st = (expr);        \
+    if (_st != BL_OK) return _st; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t bitlinear_packed_bytes(int64_t n_out, int64_t k, int n, int m) {
+  const int S = bl::s_of(n, m);
+  if (S < 0 || n_out < 1 || k < 128 || k % 128 != 0 || n_out >= kLimit || k >= kLimit ||
+      n_out * k >= kLimit)
+    return 0;
+  const int64_t tiles = (n_out + 15) / 16;
+  return (size_t)(tiles * 16 * (k / 128) * bl::block_bytes(S));
+}
+
+size_t bitlinear_workspace_bytes(int64_t n_out, int64_t k) {
+  (void)n_out;
+  (void)k;
+  return bl::kGammaWsBytes;
+}
+
+size_t bitlinear_fwd_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out) {
+  if (tokens < 1 || tokens > 16 || n_out < 1 || k < 128) return 0;
+  return bl::gemv_ws_bytes_max(tokens, k, n_out);
+}
+
+int bitlinear_quantize_mask(const uint16_t* W, int64_t n_out, int64_t k, int n, int m,
+                            int gamma_over, uint8_t* mask, int8_t* wq, double* gamma, void* ws,
+                            size_t ws_bytes, void* stream) {
+  TRY(check_nm(n, m));
+  TRY(check_layer(n_out, k));
+  TRY(check_ptr(W, 16, "W"));
+  TRY(check_ptr(mask, 16, "mask"));
+  TRY(check_opt_ptr(wq, 16, "wq"));
+  TRY(check_ptr(gamma, 8, "gamma"));
+  if (gamma_over != BL_GAMMA_DENSE && gamma_over != BL_GAMMA_MASKED)
+    return fail(BL_EINVAL, "gamma_over must be BL_GAMMA_DENSE or BL_GAMMA_MASKED (got %d)", gamma_over);
+  if (!ws || ws_bytes < bl::kGammaWsBytes)
+    return fail(BL_EWORKSPACE, "workspace needs %zu bytes (got %zu)", bl::kGammaWsBytes,
+                ws ? ws_bytes : (size_t)0);
+  TRY(check_ptr(ws, 16, "ws"));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = bl::launch_mask_gamma(W, n_out, k, n, m, gamma_over, mask, gamma, ws, s);
+  if (e != hipSuccess) return hip_status(e, "mask/gamma launch");
+  if (wq) {
+    e = bl::launch_ternary_pack(W, mask, gamma, n_out, k, bl::s_of(n, m), nullptr, wq, s);
+    if (e != hipSuccess) return hip_status(e, "ternary launch");
+  }
+  return ok();
+}
+
+int bitlinear_pack(const uint16_t* W, const uint8_t* mask, const double* gamma, int64_t n_out,
+                   int64_t k, int n, int m, void* packed, size_t packed_bytes, void* stream) {
+  TRY(check_nm(n, m));
+  TRY(check_layer(n_out, k));
+  TRY(check_ptr(W, 16, "W"));
+  TRY(check_ptr(mask, 16, "mask"));
+  TRY(check_ptr(gamma, 8, "gamma"));
+  TRY(check_ptr(packed, 16, "packed"));
+  const size_t need = bitlinear_packed_bytes(n_out, k, n, m);
+  if (packed_bytes != need)
+    return fail(BL_ESHAPE, "packed_bytes must be %zu for this layer (got %zu)", need, packed_bytes);
+  hipError_t e = bl::launch_ternary_pack(W, mask, gamma, n_out, k, bl::s_of(n, m), packed, nullptr,
+                                         reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "pack launch");
+}
+
+int bitlinear_fwd(const uint16_t* X, int64_t tokens, int64_t k, const void* packed, int64_t n_out,
+                  int n, int m, const double* gamma, float* Y, int8_t* xq, float* x_scale,
+                  int32_t* acc, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_nm(n, m));
+  TRY(check_layer(n_out, k));
+  if (tokens < 0) return fail(BL_ESHAPE, "tokens must be >= 0 (got %lld)", (long long)tokens);
+  if (tokens >= kLimit || tokens * k >= kLimit || tokens * n_out >= kLimit)
+    return fail(BL_ESHAPE, "tokens*k and tokens*n_out must stay below 2^31");
+  if (tokens == 0) return ok();
+  TRY(check_ptr(X, 16, "X"));
+  TRY(check_ptr(packed, 16, "packed"));
+  TRY(check_ptr(gamma, 8, "gamma"));
+  TRY(check_ptr(Y, 16, "Y"));
+  TRY(check_ptr(xq, 16, "xq"));
+  TRY(check_ptr(x_scale, 4, "x_scale"));
+  TRY(check_opt_ptr(acc, 16, "acc"));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int S = bl::s_of(n, m);
+  if (tokens <= 16) {
+    const size_t need = bl::gemv_ws_bytes_max(tokens, k, n_out);
+    if (need && (!ws || ws_bytes < need))
+      return fail(BL_EWORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
+                  ws ? ws_bytes : (size_t)0);
+    if (need) TRY(check_ptr(ws, 16, "ws"));
+    hipError_t e = bl::launch_act_quant(X, tokens, k, xq, x_scale, need ? ws : nullptr,
+                                        (int64_t)need, s);
+    if (e != hipSuccess) return hip_status(e, "activation quant launch");
+    e = bl::launch_gemv(packed, xq, x_scale, gamma, Y, acc, ws, (int)tokens, k, n_out, S, s);
+    return hip_status(e, "decode launch");
+  }
+  hipError_t e = bl::launch_act_quant(X, tokens, k, xq, x_scale, nullptr, 0, s);
+  if (e != hipSuccess) return hip_status(e, "activation quant launch");
+  e = bl::launch_gemm(packed, xq, x_scale, gamma, Y, acc, tokens, k, n_out, S, s);
+  return hip_status(e, "prefill launch");
+}
+
+int bitlinear_bwd(const uint16_t* dY, const int8_t* xq, const float* x_scale, const void* packed,
+                  const double* gamma, int64_t tokens, int64_t k, int64_t n_out, int n, int m,
+                  float* dX, float* dW, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  TRY(check_nm(n, m));
+  TRY(check_layer(n_out, k));
+  if (n_out % 16 != 0)
+    return fail(BL_ESHAPE, "the backward needs n_out to be a multiple of 16 (got %lld)", (long long)n_out);
+  if (tokens < 0) return fail(BL_ESHAPE, "tokens must be >= 0 (got %lld)", (long long)tokens);
+  if (tokens >= kLimit || tokens * k >= kLimit || tokens * n_out >= kLimit)
+    return fail(BL_ESHAPE, "tokens*k and tokens*n_out must stay below 2^31");
+  TRY(check_opt_ptr(dX, 16, "dX"));
+  TRY(check_opt_ptr(dW, 16, "dW"));
+  if (!dX && !dW) return ok();
+  if (tokens == 0) {
+    // no tokens: dX is empty and dW is all zeros (the dW kernel's token
+    // loop is empty, so it reads nothing and stores zeros)
+    if (dW) {
+      hipError_t e = bl::launch_bwd_dw(nullptr, nullptr, nullptr, dW, 0, k, n_out,
+                                       reinterpret_cast<hipStream_t>(stream));
+      return hip_status(e, "dW clear");
+    }
+    return ok();
+  }
+  TRY(check_ptr(dY, 16, "dY"));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dX) {
+    TRY(check_ptr(packed, 16, "packed"));
+    TRY(check_ptr(gamma, 8, "gamma"));
+    hipError_t e = bl::launch_bwd_dx(dY, packed, gamma, dX, tokens, k, n_out, bl::s_of(n, m), s);
+    if (e != hipSuccess) return hip_status(e, "dX launch");
+  }
+  if (dW) {
+    TRY(check_ptr(xq, 16, "xq"));
+    TRY(check_ptr(x_scale, 4, "x_scale"));
+    hipError_t e = bl::launch_bwd_dw(dY, xq, x_scale, dW, tokens, k, n_out, s);
+    if (e != hipSuccess) return hip_status(e, "dW launch");
+  }
+  return ok();
+}
+
+const char* bitlinear_status_string(int status) {
+  switch (status) {
+    case BL_OK: return "ok";
+    case BL_EINVAL: return "invalid argument (null or misaligned pointer, bad enum)";
+    case BL_ESHAPE: return "unsupported shape";
+    case BL_EUNSUPPORTED: return "unsupported N:M pattern";
+    case BL_EWORKSPACE: return "workspace missing or too small";
+    case BL_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* bitlinear_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// common.h -- device-side helpers shared by the gfx950 kernels of the
+// BitLinear library.  Host code includes it only for the format constants.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+// ---------------------------------------------------------------------
+// Packed ternary format ("code plus index"), per 8-group of one row:
+//   bits [0,4)      nonzero bitmap of positions 0..3
+//   bits [4,4+S)    sign bits (1 = negative); the i-th nonzero of the low
+//                   half at 4+i, the i-th nonzero of the high half at
+//                   4+S-1-i
+//   bits [4+S,8+S)  nonzero bitmap of positions 4..7
+// so the low half decodes from field bits [0,8) and the high half from
+// field bits [S, S+8), each an 8-bit key of (bitmap, 4 sign bits).
+// A block holds the 16 fields of one row and one 128-wide k block, field
+// g at bit g*(8+S), 2*(8+S) bytes.  Blocks are stored by slot
+//   ((row/16) * (k/128) + kb) * 16 + row%16
+// so the 64 blocks a wavefront reads for 16 rows x 512 k are contiguous.
+// ---------------------------------------------------------------------
+constexpr int kBlockK = 128;
+constexpr int kTileRows = 16;
+
+__host__ __device__ constexpr int block_bytes(int S) { return 2 * (8 + S); }
+
+// sign slots per 8-group for a supported n:m, else -1
+__host__ __device__ constexpr int s_of(int n, int m) {
+  return (m == 8 && n == 8) ? 8 : (m == 8 && n == 6) ? 6 : (m == 8 && n == 4) ? 4
+       : (m == 4 && n == 2) ? 4 : -1;
+}
+
+// bf16 helpers ---------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// MFMA operand types ---------------------------------------------------
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// wave-level reductions ------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// funnel shift: bits [sh, sh+32) of the 64-bit value (hi:lo)
+__device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t sh) {
+  return __builtin_amdgcn_alignbit(hi, lo, sh);
+}
+
+// int8x4 codes of one half-group from its 8-bit key.
+// half 0: key = bitmap(4) | signs(4) << 4, i-th nonzero's sign at bit 4+i
+// half 1: key = signs(4) | bitmap(4) << 4, i-th nonzero's sign at bit 3-i
+__device__ inline uint32_t half_codes(uint32_t key, uint32_t half) {
+  const uint32_t bm = half ? (key >> 4) : (key & 15u);
+  const uint32_t sg = half ? (key & 15u) : (key >> 4);
+  uint32_t out = 0, rank = 0;
+  for (int p = 0; p < 4; ++p) {
+    if ((bm >> p) & 1u) {
+      const uint32_t bit = half ? (3u - rank) : rank;
+      out |= (((sg >> bit) & 1u) ? 0xffu : 0x01u) << (8 * p);
+      ++rank;
+    }
+  }
+  return out;
+}
+
+
+// Decode groups [G0, G0+NG) of one packed block held in registers w[0..kW]
+// (w[kW] = 0): emit(g, lo, hi) receives the int8x4 codes of positions 0..3
+// and 4..7 of group g.  lut[key] is the low-half table, lut[256+key] the
+// high-half table.  Offsets are compile-time, so w stays in registers.
+template <int S, int G0, int NG, class Lut, class Emit>
+__device__ __forceinline__ void decode_groups(const uint32_t* w, Lut lut, Emit emit) {
+#pragma unroll
+  for (int gg = 0; gg < NG; ++gg) {
+    constexpr int kField = 8 + S;
+    const int off = (G0 + gg) * kField, offh = off + S;
+    const uint32_t klo = funnel(w[(off >> 5) + 1], w[off >> 5], off & 31) & 0xffu;
+    const uint32_t khi = funnel(w[(offh >> 5) + 1], w[offh >> 5], offh & 31) & 0xffu;
+    emit(G0 + gg, lut(klo, 0), lut(khi, 1));
+  }
+}
+
+}  // namespace bl

@@ -1,0 +1,436 @@
+// quant.hip -- weight and activation quantisation kernels (gfx950).
+//
+//  mask_gamma_kernel  : N:M mask from latent |W| plus the exact |W| sum;
+//                       the last block to finish rounds the sum to binary64
+//                       and writes gamma.
+//  ternary_pack_kernel: masked ternary codes -> packed bitmap+sign blocks
+//                       (and/or plain int8 codes).
+//  act_quant_kernel   : per-token absmax int8 activations.
+//
+// Sparse-BitNet explainer article §三/§五/§六 (dynamic N:M mask from the
+// full-precision weights, quantise before sparsifying); BitNet b1.58 2B4T
+// article §一 (absmean ternary weights, 8-bit activations).
+#include "common.h"
+#include "launch.h"
+
+namespace bl {
+
+// ---------------------------------------------------------------------
+// Exact sum of |W|.  A finite bf16 magnitude is sig * 2^(max(E,1) - 134)
+// with E the 8-bit exponent field and sig = (E ? 128 : 0) + fraction.
+// Magnitudes with E in [kWinLo, kWinLo + kWin) (|W| in [2^-20, 2)) add
+// sig << (E - kWinLo) into a per-thread 64-bit integer; every other
+// nonzero magnitude (rare for weight-scale data) adds sig into hist[E]
+// with a 64-bit integer atomic.  Integer addition is associative, so the
+// result does not depend on scheduling.
+// ---------------------------------------------------------------------
+constexpr int kWinLo = 107;
+constexpr int kWin = 21;  // sig << 20 < 2^28: eight of them fit in 32 bits
+
+struct GammaWS {
+  unsigned long long main;       // in units of 2^(kWinLo - 134)
+  unsigned long long hist[256];  // sig sums per exponent field
+  unsigned int ticket;
+  unsigned int pad;
+};
+static_assert(sizeof(GammaWS) <= kGammaWsBytes, "gamma workspace");
+
+__global__ void gamma_ws_clear_kernel(GammaWS* ws) {
+  unsigned long long* p = reinterpret_cast<unsigned long long*>(ws);
+  for (int i = threadIdx.x; i < (int)(sizeof(GammaWS) / 8); i += blockDim.x) p[i] = 0ull;
+}
+
+// keys: |h| (15 bits) above a 3-bit code that ranks a lower index higher;
+// all keys of a group are distinct and a larger key ranks first.
+__device__ __forceinline__ uint32_t rank_key(uint32_t h, int j) {
+  return ((h & 0x7fffu) << 3) | (uint32_t)(7 - j);
+}
+
+__device__ __forceinline__ void cswap(uint32_t& a, uint32_t& b) {
+  uint32_t lo = min(a, b), hi = max(a, b);
+  a = lo;
+  b = hi;
+}
+
+// mask bits of one 8-group (w = 8 bf16, element j in bits 16j..16j+15 of
+// the four words) for the pattern N:M
+template <int N, int M>
+__device__ __forceinline__ uint32_t group_mask(const uint32_t w[4]) {
+  if (N == M) return 0xffu;
+  uint32_t key[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) key[j] = rank_key((w[j >> 1] >> (16 * (j & 1))) & 0xffffu, j);
+  uint32_t tau_lo, tau_hi;  // a key is kept iff it exceeds its half's / group's tau
+  if (M == 4) {
+    // 2:4 -- per half of four, drop the two smallest keys
+    uint32_t t[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t p0 = min(key[4 * h], key[4 * h + 1]), P0 = max(key[4 * h], key[4 * h + 1]);
+      uint32_t p1 = min(key[4 * h + 2], key[4 * h + 3]), P1 = max(key[4 * h + 2], key[4 * h + 3]);
+      t[h] = min(max(p0, p1), min(P0, P1));  // second smallest of four
+    }
+    tau_lo = t[0];
+    tau_hi = t[1];
+  } else if (N == 6) {
+    // 6:8 -- tau = second smallest of eight
+    uint32_t p[4], P[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = min(key[2 * i], key[2 * i + 1]);
+      P[i] = max(key[2 * i], key[2 * i + 1]);
+    }
+    uint32_t q1 = min(p[0], p[1]), q2 = min(max(p[0], p[1]), min(P[0], P[1]));
+    uint32_t r1 = min(p[2], p[3]), r2 = min(max(p[2], p[3]), min(P[2], P[3]));
+    tau_lo = tau_hi = min(max(q1, r1), min(q2, r2));
+  } else {
+    // general N of 8: sort (Batcher odd-even merge network, 19 swaps),
+    // tau = (8-N)-th smallest
+    uint32_t s[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] = key[j];
+    cswap(s[0], s[1]); cswap(s[2], s[3]); cswap(s[4], s[5]); cswap(s[6], s[7]);
+    cswap(s[0], s[2]); cswap(s[1], s[3]); cswap(s[4], s[6]); cswap(s[5], s[7]);
+    cswap(s[1], s[2]); cswap(s[5], s[6]);
+    cswap(s[0], s[4]); cswap(s[1], s[5]); cswap(s[2], s[6]); cswap(s[3], s[7]);
+    cswap(s[2], s[4]); cswap(s[3], s[5]);
+    cswap(s[1], s[2]); cswap(s[3], s[4]); cswap(s[5], s[6]);
+    tau_lo = tau_hi = s[7 - N];
+  }
+  uint32_t bits = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t tau = (j < 4) ? tau_lo : tau_hi;
+    bits |= ((tau - key[j]) >> 31) << j;  // key > tau (keys < 2^18)
+  }
+  return bits;
+}
+
+// exact |W| accumulation of one 8-group; returns the in-window sum
+template <bool MASKED>
+__device__ __forceinline__ uint32_t group_abs_sum(const uint32_t w[4], uint32_t keep,
+                                                 GammaWS* ws) {
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t a = (w[j >> 1] >> (16 * (j & 1))) & 0x7fffu;
+    if (MASKED && !((keep >> j) & 1u)) a = 0;
+    uint32_t e = a >> 7;
+    uint32_t sig = (a & 0x7fu) | (e ? 0x80u : 0u);
+    uint32_t sh = e - (uint32_t)kWinLo;
+    bool in = sh < (uint32_t)kWin;
+    sum += in ? (sig << sh) : 0u;
+    if (!in && a != 0u) atomicAdd(&ws->hist[e], (unsigned long long)sig);
+  }
+  return sum;
+}
+
+// 320-bit unsigned integer in 32-bit limbs, units of 2^-133
+struct Big {
+  uint32_t limb[10];
+};
+
+__device__ void big_add(Big& b, unsigned long long v, int shift) {
+  // b += v * 2^shift
+  // v * 2^bo spans three 32-bit limbs starting at limb li
+  int li = shift >> 5, bo = shift & 31;
+  unsigned long long carry = 0;
+  uint32_t parts[3];
+  parts[0] = (uint32_t)(v << bo);
+  parts[1] = bo ? (uint32_t)(v >> (32 - bo)) : (uint32_t)(v >> 32);
+  parts[2] = bo ? (uint32_t)(v >> (64 - bo)) : 0u;
+  for (int i = li; i < 10; ++i) {
+    unsigned long long add = (i - li < 3) ? parts[i - li] : 0u;
+    unsigned long long s = (unsigned long long)b.limb[i] + add + carry;
+    b.limb[i] = (uint32_t)s;
+    carry = s >> 32;
+    if (i - li >= 2 && carry == 0) break;
+  }
+}
+
+__device__ int big_bit(const Big& b, int pos) { return (b.limb[pos >> 5] >> (pos & 31)) & 1; }
+
+// nearest binary64 (ties to even) of b * 2^-133
+__device__ double big_round(const Big& b) {
+  int top = -1;
+  for (int i = 9; i >= 0 && top < 0; --i)
+    if (b.limb[i]) top = 32 * i + 31 - __clz(b.limb[i]);
+  if (top < 0) return 0.0;
+  unsigned long long sig = 0;
+  int low = top > 52 ? top - 52 : 0;
+  for (int pos = top; pos >= low; --pos) sig = (sig << 1) | (unsigned long long)big_bit(b, pos);
+  if (low > 0) {
+    int half = big_bit(b, low - 1);
+    int sticky = 0;
+    for (int pos = low - 2; pos >= 0 && !sticky; --pos) sticky = big_bit(b, pos);
+    if (half && (sticky || (sig & 1ull))) sig += 1;
+  }
+  return ldexp((double)sig, low - 133);
+}
+
+template <int N, int M, bool MASKED>
+__global__ __launch_bounds__(256) void mask_gamma_kernel(const uint4* __restrict__ W,
+                                                        int64_t nchunks,  // 4-group chunks
+                                                        uint32_t* __restrict__ mask_words,
+                                                        GammaWS* __restrict__ ws,
+                                                        double* __restrict__ gamma,
+                                                        double count) {
+  unsigned long long acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) v[g] = W[c * 4 + g];
+    uint32_t mword = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t w[4] = {v[g].x, v[g].y, v[g].z, v[g].w};
+      uint32_t keep = group_mask<N, M>(w);
+      mword |= keep << (8 * g);
+      acc += group_abs_sum<MASKED>(w, keep, ws);
+    }
+    mask_words[c] = mword;
+  }
+  // block reduction of the in-window sums, one 64-bit atomic per block
+  __shared__ unsigned long long part[8];
+  __shared__ int last;
+  acc = wave_sum_u64(acc);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) part[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long s = 0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += part[i];
+    if (s) atomicAdd(&ws->main, s);
+    __threadfence();
+    unsigned int t = atomicAdd(&ws->ticket, 1u);
+    last = (t == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!last || threadIdx.x != 0) return;
+  // last block: every other block's atomics were made visible before its
+  // ticket increment; read the accumulators from L2 with atomics.
+  __threadfence();
+  Big b;
+  for (int i = 0; i < 10; ++i) b.limb[i] = 0;
+  big_add(b, atomicAdd(&ws->main, 0ull), kWinLo - 1);
+  for (int e = 0; e < 256; ++e) {
+    unsigned long long h = atomicAdd(&ws->hist[e], 0ull);
+    if (h) big_add(b, h, e > 0 ? e - 1 : 0);
+  }
+  *gamma = big_round(b) / count;
+}
+
+// ---------------------------------------------------------------------
+// Ternary codes and packing.  The code of W is sign(W) where the mask
+// keeps it and 2|W| > gamma.  Since bf16 magnitudes are ordered like their
+// 15-bit patterns, that test is |h| >= thr for the smallest pattern thr
+// whose value v has 2v > gamma (found by bisection in binary64; exact).
+// ---------------------------------------------------------------------
+__device__ uint32_t code_threshold(double g) {
+  if (!(g > 0.0)) return 0x10000u;  // no entry qualifies
+  uint32_t lo = 0, hi = 0x7f80u;    // 0x7f80 = inf: always qualifies
+  while (lo < hi) {
+    uint32_t mid = (lo + hi) >> 1;
+    double v = (double)__uint_as_float(mid << 16);
+    if (2.0 * v > g) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+template <int S, bool PACKED, bool WQ>
+__global__ __launch_bounds__(256) void ternary_pack_kernel(const uint16_t* __restrict__ W,
+                                                          const uint8_t* __restrict__ mask,
+                                                          const double* __restrict__ gamma,
+                                                          int64_t n_out, int64_t k,
+                                                          uint32_t* __restrict__ packed,
+                                                          int8_t* __restrict__ wq) {
+  constexpr int kWords = block_bytes(S) / 4;
+  constexpr int kField = 8 + S;
+  const int64_t nkb = k / kBlockK;
+  const int64_t tiles = (n_out + kTileRows - 1) / kTileRows;
+  const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (slot >= tiles * kTileRows * nkb) return;
+  const int64_t tile = slot / (kTileRows * nkb);
+  const int64_t rem = slot - tile * kTileRows * nkb;
+  const int64_t kb = rem / kTileRows;
+  const int64_t row = tile * kTileRows + (rem % kTileRows);
+
+  uint32_t out[kWords];
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) out[i] = 0;
+
+  if (row < n_out) {
+    const uint32_t thr = code_threshold(*gamma);
+    const uint4* wrow = reinterpret_cast<const uint4*>(W + row * k + kb * kBlockK);
+    const uint4 mk = *reinterpret_cast<const uint4*>(mask + row * (k / 8) + kb * 16);
+    const uint32_t mw[4] = {mk.x, mk.y, mk.z, mk.w};
+    uint4 codes_out[8];
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const uint4 v = wrow[g];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t keep = (mw[g >> 2] >> (8 * (g & 3))) & 0xffu;
+      uint32_t nz = 0, neg = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t h = (w[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+        uint32_t on = ((keep >> j) & 1u) & ((h & 0x7fffu) >= thr ? 1u : 0u);
+        nz |= on << j;
+        neg |= (on & (h >> 15)) << j;
+      }
+      // field: low bitmap, signs (low half from the bottom, high half
+      // from the top), high bitmap
+      uint32_t sign = 0;
+      int nlo = 0, nhi = 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if ((nz >> p) & 1u) { sign |= ((neg >> p) & 1u) << nlo; ++nlo; }
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if ((nz >> (4 + p)) & 1u) { sign |= ((neg >> (4 + p)) & 1u) << (S - 1 - nhi); ++nhi; }
+      }
+      const uint32_t field = (nz & 0xfu) | (sign << 4) | ((nz >> 4) << (4 + S));
+      const int off = g * kField;
+      out[off >> 5] |= field << (off & 31);
+      if ((off & 31) + kField > 32) out[(off >> 5) + 1] |= field >> (32 - (off & 31));
+      if (WQ) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t cl = ((nz >> j) & 1u) ? (((neg >> j) & 1u) ? 0xffu : 0x01u) : 0u;
+          uint32_t ch = ((nz >> (4 + j)) & 1u) ? (((neg >> (4 + j)) & 1u) ? 0xffu : 0x01u) : 0u;
+          lo |= cl << (8 * j);
+          hi |= ch << (8 * j);
+        }
+        if (g & 1) { codes_out[g >> 1].z = lo; codes_out[g >> 1].w = hi; }
+        else { codes_out[g >> 1].x = lo; codes_out[g >> 1].y = hi; }
+      }
+    }
+    if (WQ) {
+      uint4* dst = reinterpret_cast<uint4*>(wq + row * k + kb * kBlockK);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[i] = codes_out[i];
+    }
+  }
+  if (PACKED) {
+    uint32_t* dst = packed + slot * kWords;
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) dst[i] = out[i];
+  }
+}
+
+// ---------------------------------------------------------------------
+// Per-token absmax int8 activations.  One block per token.
+// x_q = rint(127 x / a) with a correctly rounded binary32 division: 127 x
+// is exact in binary32, and a quotient of two 8-bit-significand values that
+// is not a half-integer sits at least ~2^-16 (relative) away from one, far
+// beyond binary32 rounding, so rint(ties to even) of the rounded quotient
+// equals round-half-even of the exact quotient.  |x_q| <= 127, so the clip
+// to [-128, 127] never binds.  Optionally zeroes a workspace range.
+// ---------------------------------------------------------------------
+__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ X, int64_t k,
+                                                       int8_t* __restrict__ xq,
+                                                       float* __restrict__ scale,
+                                                       uint32_t* __restrict__ zero_ws,
+                                                       int64_t zero_words) {
+  const int64_t t = blockIdx.x;
+  const uint4* row = reinterpret_cast<const uint4*>(X + t * k);
+  const int64_t nvec = k / 8;
+  float a = 0.f;
+  for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) {
+    uint4 v = row[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a = fmaxf(a, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
+  }
+  __shared__ float red[8];
+  a = wave_max(a);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) a = fmaxf(a, red[i]);
+  if (threadIdx.x == 0) scale[t] = a / 127.0f;
+  uint2* out = reinterpret_cast<uint2*>(xq + t * k);
+  for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) {
+    uint4 v = row[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t q[2] = {0, 0};
+    if (a > 0.f) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float x = (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
+        int qi = (int)rintf((127.0f * x) / a);
+        q[j >> 2] |= ((uint32_t)qi & 0xffu) << (8 * (j & 3));
+      }
+    }
+    out[i] = make_uint2(q[0], q[1]);
+  }
+  if (zero_ws) {
+    for (int64_t i = t * blockDim.x + threadIdx.x; i < zero_words; i += (int64_t)gridDim.x * blockDim.x)
+      zero_ws[i] = 0u;
+  }
+}
+
+// ------------------------------------------------------------- launchers
+template <int N, int M>
+static hipError_t launch_mask(const uint16_t* W, int64_t n_out, int64_t k, int gamma_over,
+                              uint8_t* mask, double* gamma, void* ws, hipStream_t s) {
+  GammaWS* g = reinterpret_cast<GammaWS*>(ws);
+  gamma_ws_clear_kernel<<<1, 256, 0, s>>>(g);
+  const int64_t nchunks = n_out * k / 32;
+  int64_t blocks = (nchunks + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  if (gamma_over == 0)
+    mask_gamma_kernel<N, M, false><<<(unsigned)blocks, 256, 0, s>>>(
+        reinterpret_cast<const uint4*>(W), nchunks, reinterpret_cast<uint32_t*>(mask), g, gamma,
+        (double)(n_out * k));
+  else
+    mask_gamma_kernel<N, M, true><<<(unsigned)blocks, 256, 0, s>>>(
+        reinterpret_cast<const uint4*>(W), nchunks, reinterpret_cast<uint32_t*>(mask), g, gamma,
+        (double)(n_out * k));
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_gamma(const uint16_t* W, int64_t n_out, int64_t k, int n, int m,
+                             int gamma_over, uint8_t* mask, double* gamma, void* ws,
+                             hipStream_t s) {
+  if (m == 8 && n == 8) return launch_mask<8, 8>(W, n_out, k, gamma_over, mask, gamma, ws, s);
+  if (m == 8 && n == 6) return launch_mask<6, 8>(W, n_out, k, gamma_over, mask, gamma, ws, s);
+  if (m == 8 && n == 4) return launch_mask<4, 8>(W, n_out, k, gamma_over, mask, gamma, ws, s);
+  return launch_mask<2, 4>(W, n_out, k, gamma_over, mask, gamma, ws, s);
+}
+
+template <int S>
+static hipError_t launch_tp(const uint16_t* W, const uint8_t* mask, const double* gamma,
+                            int64_t n_out, int64_t k, void* packed, int8_t* wq, hipStream_t s) {
+  const int64_t slots = ((n_out + 15) / 16) * 16 * (k / kBlockK);
+  const unsigned blocks = (unsigned)((slots + 255) / 256);
+  uint32_t* p = reinterpret_cast<uint32_t*>(packed);
+  if (packed && wq)
+    ternary_pack_kernel<S, true, true><<<blocks, 256, 0, s>>>(W, mask, gamma, n_out, k, p, wq);
+  else if (packed)
+    ternary_pack_kernel<S, true, false><<<blocks, 256, 0, s>>>(W, mask, gamma, n_out, k, p, wq);
+  else
+    ternary_pack_kernel<S, false, true><<<blocks, 256, 0, s>>>(W, mask, gamma, n_out, k, p, wq);
+  return hipGetLastError();
+}
+
+hipError_t launch_ternary_pack(const uint16_t* W, const uint8_t* mask, const double* gamma,
+                               int64_t n_out, int64_t k, int S, void* packed, int8_t* wq,
+                               hipStream_t s) {
+  if (S == 8) return launch_tp<8>(W, mask, gamma, n_out, k, packed, wq, s);
+  if (S == 6) return launch_tp<6>(W, mask, gamma, n_out, k, packed, wq, s);
+  return launch_tp<4>(W, mask, gamma, n_out, k, packed, wq, s);
+}
+
+hipError_t launch_act_quant(const uint16_t* X, int64_t tokens, int64_t k, int8_t* xq,
+                            float* scale, void* zero_ws, int64_t zero_bytes, hipStream_t s) {
+  act_quant_kernel<<<(unsigned)tokens, 256, 0, s>>>(X, k, xq, scale,
+                                                    reinterpret_cast<uint32_t*>(zero_ws),
+                                                    zero_ws ? zero_bytes / 4 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace bl

@@ -1,0 +1,67 @@
+"""Device-buffer plumbing around the C ABI for one BitLinear weight.
+
+`BitLinearWeight` owns the device buffers of one layer (mask, packed codes,
+gamma, workspaces) and calls the library's entry points in the order the
+method runs them: quantize_mask + pack once per training step (the mask is
+recomputed every step) or once at load time for inference, then fwd / bwd
+per batch.  torch is used for device memory and the stream only.
+"""
+import numpy as np
+import torch
+
+from . import bitlinear as bl
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """uint16 bf16 bit patterns (numpy) -> torch.bfloat16 device tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class BitLinearWeight:
+    def __init__(self, n_out, k, n=6, m=8, gamma_over=bl.BL_GAMMA_DENSE, device="cuda"):
+        self.n_out, self.k, self.n, self.m = int(n_out), int(k), int(n), int(m)
+        self.gamma_over = gamma_over
+        nbytes = bl.bitlinear_packed_bytes(n_out, k, n, m)
+        if nbytes == 0:
+            raise ValueError(f"unsupported layer {n_out}x{k} {n}:{m}")
+        self.mask = torch.empty(n_out * (k // 8), dtype=torch.uint8, device=device)
+        self.packed = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.gamma = torch.empty(1, dtype=torch.float64, device=device)
+        self.ws = torch.empty(bl.bitlinear_workspace_bytes(n_out, k), dtype=torch.uint8, device=device)
+        self.device = device
+
+    def quantize(self, W, wq=None, stream=None):
+        """Mask + gamma (+ optional int8 codes), then pack."""
+        bl.bitlinear_quantize_mask(W, self.n_out, self.k, self.n, self.m, self.gamma_over, self.mask,
+                                   wq, self.gamma, self.ws, stream=stream)
+        bl.bitlinear_pack(W, self.mask, self.gamma, self.n_out, self.k, self.n, self.m, self.packed,
+                          stream=stream)
+
+    def fwd_buffers(self, tokens):
+        d = self.device
+        ws_n = bl.bitlinear_fwd_workspace_bytes(tokens, self.k, self.n_out)
+        return {
+            "Y": torch.empty(tokens * self.n_out, dtype=torch.float32, device=d),
+            "xq": torch.empty(tokens * self.k, dtype=torch.int8, device=d),
+            "x_scale": torch.empty(max(tokens, 1), dtype=torch.float32, device=d)[:tokens],
+            "ws": torch.empty(ws_n, dtype=torch.uint8, device=d) if ws_n else None,
+        }
+
+    def fwd(self, X, tokens, bufs=None, acc=None, stream=None):
+        b = bufs if bufs is not None else self.fwd_buffers(tokens)
+        bl.bitlinear_fwd(X, tokens, self.k, self.packed, self.n_out, self.n, self.m, self.gamma,
+                         b["Y"], b["xq"], b["x_scale"], acc=acc, ws=b["ws"], stream=stream)
+        return b
+
+    def bwd(self, dY, xq, x_scale, tokens, dX=True, dW=True, stream=None):
+        d = self.device
+        gx = torch.empty(tokens * self.k, dtype=torch.float32, device=d) if dX else None
+        gw = torch.empty(self.n_out * self.k, dtype=torch.float32, device=d) if dW else None
+        bl.bitlinear_bwd(dY, xq, x_scale, self.packed, self.gamma, tokens, self.k, self.n_out,
+                         self.n, self.m, gx, gw, stream=stream)
+        return gx, gw

@@ -1,0 +1,86 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+and the oracle on the same seeded inputs, and compare."""
+import numpy as np
+import torch
+
+import oracle
+from sparse_linear_layers_group_amd import bitlinear as bl
+from sparse_linear_layers_group_amd.layer import BitLinearWeight, bf16_tensor
+
+S_OF = {(8, 8): 8, (6, 8): 6, (4, 8): 4, (2, 4): 4}
+
+
+def ensure_built():
+    import os
+    if not os.path.exists(bl.LIB_PATH):
+        from sparse_linear_layers_group_amd import build
+        build.build()
+    bl.lib()
+
+
+def f64_bits(x):
+    return np.float64(x).view(np.uint64)
+
+
+def quantize_on_gpu(Wbits, n, m, gamma_over=0, want_wq=True):
+    n_out, k = Wbits.shape
+    lw = BitLinearWeight(n_out, k, n, m, gamma_over)
+    W = bf16_tensor(Wbits)
+    wq = torch.empty(n_out * k, dtype=torch.int8, device="cuda") if want_wq else None
+    lw.quantize(W, wq=wq)
+    torch.cuda.synchronize()
+    return lw, W, wq
+
+
+def check_weight_path(Wbits, n, m, gamma_over=0):
+    """Mask, gamma, codes and packed bytes: bit-exact against the oracle."""
+    n_out, k = Wbits.shape
+    lw, W, wq = quantize_on_gpu(Wbits, n, m, gamma_over)
+    mb = oracle.mask(Wbits, n, m)
+    got_mask = lw.mask.cpu().numpy().reshape(mb.shape)
+    assert np.array_equal(got_mask, mb), f"mask mismatch at {np.argwhere(got_mask != mb)[:5]}"
+    g = oracle.gamma(Wbits, gamma_over == bl.BL_GAMMA_MASKED, mb)
+    got_g = lw.gamma.cpu().numpy()[0]
+    assert f64_bits(got_g) == f64_bits(g), f"gamma {got_g!r} != oracle {g!r}"
+    T = oracle.ternary(Wbits, mb, g)
+    got_T = wq.cpu().numpy().reshape(T.shape)
+    assert np.array_equal(got_T, T), f"codes mismatch at {np.argwhere(got_T != T)[:5]}"
+    P = oracle.pack(T, S_OF[(n, m)])
+    got_P = lw.packed.cpu().numpy()
+    assert got_P.size == P.size
+    assert np.array_equal(got_P, P), f"packed bytes differ at {np.flatnonzero(got_P != P)[:8]}"
+    return lw, T, g
+
+
+def check_forward(lw, T, g, Xbits, check_acc=True):
+    """x_q, s_t, acc bit-exact; Y within 1e-5 relative."""
+    tokens, k = Xbits.shape
+    acc_t = torch.empty(tokens * lw.n_out, dtype=torch.int32, device="cuda") if check_acc else None
+    bufs = lw.fwd(bf16_tensor(Xbits), tokens, acc=acc_t)
+    torch.cuda.synchronize()
+    xq, sc = oracle.act_quant(Xbits)
+    assert np.array_equal(bufs["xq"].cpu().numpy().reshape(xq.shape), xq)
+    assert np.array_equal(bufs["x_scale"].cpu().numpy(), sc.astype(np.float32))
+    acc_ref, Y_ref = oracle.fwd(xq, sc, T, g)
+    if check_acc:
+        got = acc_t.cpu().numpy().reshape(acc_ref.shape)
+        assert np.array_equal(got, acc_ref), f"acc differs at {np.argwhere(got != acc_ref)[:5]}"
+    Y = bufs["Y"].cpu().numpy().reshape(Y_ref.shape).astype(np.float64)
+    assert_y_close(Y, Y_ref, acc_ref)
+    return bufs, xq, sc
+
+
+def assert_y_close(Y, Y_ref, acc_ref=None):
+    err = np.abs(Y - Y_ref)
+    assert np.all(err <= 1e-5 * np.abs(Y_ref)), f"max rel err {np.max(err / np.maximum(np.abs(Y_ref), 1e-300))}"
+    if acc_ref is not None:
+        assert np.all(Y[acc_ref == 0] == 0.0)
+
+
+def assert_grad_close(G, R, abs_prod):
+    """Backward tolerance for bf16 matrix products with binary32
+    accumulation: elementwise error within 1e-2 of the sum of absolute
+    products, and Frobenius error within 1e-2 of the reference norm."""
+    err = np.abs(G - R)
+    assert np.all(err <= 1e-2 * abs_prod + 1e-30), f"max err/absprod {np.max(err / np.maximum(abs_prod, 1e-30))}"
+    assert np.linalg.norm(G - R) <= 1e-2 * np.linalg.norm(R) + 1e-30
