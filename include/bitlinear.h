@@ -132,6 +132,48 @@ int bitlinear_fwd(const uint16_t *X, int64_t tokens, int64_t k,
                   const double *gamma, float *Y, int8_t *xq, float *x_scale,
                   int32_t *acc, void *ws, size_t ws_bytes, void *stream);
 
+/* The two halves of bitlinear_fwd, for callers that quantise activations
+ * once and contract them against several weights, or that time the steps
+ * separately.  Same arguments and results as bitlinear_fwd.
+ * bitlinear_contract's ws (bitlinear_fwd_workspace_bytes, may be NULL when
+ * that is 0) must hold zeros on entry; every call leaves it zeroed
+ * (bitlinear_fwd zero-fills it itself). */
+int bitlinear_act_quant(const uint16_t *X, int64_t tokens, int64_t k, int8_t *xq,
+                        float *x_scale, void *stream);
+int bitlinear_contract(const int8_t *xq, const float *x_scale, int64_t tokens,
+                       int64_t k, const void *packed, int64_t n_out, int n,
+                       int m, const double *gamma, float *Y, int32_t *acc,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Grouped decode: many BitLinear forwards with the same token count (1..16)
+ * and N:M pattern in two launches (all activations, then all contractions),
+ * e.g. the projections of several layers or of independent streams.  The
+ * per-item results are those of bitlinear_fwd.
+ *   items  host array of `count` (<= 65535) item descriptors; every
+ *          pointer is a device pointer as in bitlinear_fwd.
+ *   plan   device buffer of bitlinear_fwd_group_plan_bytes() bytes, written
+ *          by bitlinear_fwd_group_plan (which synchronises `stream` once);
+ *          it must stay allocated and unchanged while the plan is used.
+ *   stages 1 = activation quantisation only, 2 = contraction only (x_q and
+ *          x_scale already written), 3 = both.
+ * n, m passed to bitlinear_fwd_group must be those the plan was made with. */
+typedef struct bitlinear_fwd_item {
+    const uint16_t *X;      /* bf16 [tokens x k]      */
+    const void *packed;     /* packed codes           */
+    const double *gamma;    /* absmean scale          */
+    float *Y;               /* float [tokens x n_out] */
+    int8_t *xq;             /* int8 [tokens x k]      */
+    float *x_scale;         /* float [tokens]         */
+    int64_t k, n_out;
+} bitlinear_fwd_item;
+
+size_t bitlinear_fwd_group_plan_bytes(const bitlinear_fwd_item *items, int count,
+                                      int64_t tokens);
+int bitlinear_fwd_group_plan(const bitlinear_fwd_item *items, int count,
+                             int64_t tokens, int n, int m, void *plan,
+                             size_t plan_bytes, void *stream);
+int bitlinear_fwd_group(const void *plan, int n, int m, int stages, void *stream);
+
 /* Step 8-9: dual straight-through backward.  Sparse-BitNet article §三 and
  * §六: gradients pass straight through the ternary rounding and the
  * sparsification, and masked weights still receive their gradient.

@@ -38,6 +38,11 @@ _SIGS = {
     "bitlinear_pack": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _sz, _vp]),
     "bitlinear_fwd": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _sz, _vp]),
+    "bitlinear_act_quant": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "bitlinear_contract": (_int, [_vp, _vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "bitlinear_fwd_group_plan_bytes": (_sz, [_vp, _int, _i64]),
+    "bitlinear_fwd_group_plan": (_int, [_vp, _int, _i64, _int, _int, _vp, _sz, _vp]),
+    "bitlinear_fwd_group": (_int, [_vp, _int, _int, _int, _vp]),
     "bitlinear_status_string": (ctypes.c_char_p, [_int]),
     "bitlinear_last_error": (ctypes.c_char_p, []),
 }
@@ -169,3 +174,59 @@ def bitlinear_bwd(dY, xq, x_scale, packed, gamma, tokens, k, n_out, n, m, dX, dW
         (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes),
         _stream(stream))
     _check(st, "bitlinear_bwd")
+
+
+def bitlinear_act_quant(X, tokens, k, xq, x_scale, stream=None):
+    st = lib().bitlinear_act_quant(_ptr(X, _BF16, tokens * k, "X"), tokens, k,
+                                   _ptr(xq, (torch.int8,), tokens * k, "xq"),
+                                   _ptr(x_scale, (torch.float32,), tokens, "x_scale"), _stream(stream))
+    _check(st, "bitlinear_act_quant")
+
+
+def bitlinear_contract(xq, x_scale, tokens, k, packed, n_out, n, m, gamma, Y, acc=None, ws=None,
+                       ws_bytes=None, stream=None):
+    st = lib().bitlinear_contract(
+        _ptr(xq, (torch.int8,), tokens * k, "xq"), _ptr(x_scale, (torch.float32,), tokens, "x_scale"),
+        tokens, k, _ptr(packed, (torch.uint8,), None, "packed"), n_out, n, m,
+        _ptr(gamma, (torch.float64,), 1, "gamma"), _ptr(Y, (torch.float32,), tokens * n_out, "Y"),
+        _ptr(acc, (torch.int32,), tokens * n_out, "acc", optional=True),
+        _ptr(ws, (torch.uint8,), None, "ws", optional=True),
+        (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes), _stream(stream))
+    _check(st, "bitlinear_contract")
+
+
+class bitlinear_fwd_item(ctypes.Structure):
+    """Mirror of the C struct bitlinear_fwd_item (device pointers as ints)."""
+    _fields_ = [("X", _vp), ("packed", _vp), ("gamma", _vp), ("Y", _vp), ("xq", _vp),
+                ("x_scale", _vp), ("k", _i64), ("n_out", _i64)]
+
+
+def make_fwd_items(entries, tokens):
+    """entries: dicts with tensors X, packed, gamma, Y, xq, x_scale and ints k, n_out."""
+    arr = (bitlinear_fwd_item * len(entries))()
+    for i, e in enumerate(entries):
+        k, n_out = int(e["k"]), int(e["n_out"])
+        arr[i] = bitlinear_fwd_item(
+            _ptr(e["X"], _BF16, tokens * k, "X"), _ptr(e["packed"], (torch.uint8,), None, "packed"),
+            _ptr(e["gamma"], (torch.float64,), 1, "gamma"),
+            _ptr(e["Y"], (torch.float32,), tokens * n_out, "Y"), _ptr(e["xq"], (torch.int8,), tokens * k, "xq"),
+            _ptr(e["x_scale"], (torch.float32,), tokens, "x_scale"), k, n_out)
+    return arr
+
+
+def bitlinear_fwd_group_plan_bytes(items, count, tokens):
+    return int(lib().bitlinear_fwd_group_plan_bytes(items, int(count), int(tokens)))
+
+
+def bitlinear_fwd_group_plan(items, count, tokens, n, m, plan, plan_bytes=None, stream=None):
+    st = lib().bitlinear_fwd_group_plan(items, int(count), int(tokens), n, m,
+                                        _ptr(plan, (torch.uint8,), None, "plan"),
+                                        plan.numel() if plan_bytes is None else int(plan_bytes),
+                                        _stream(stream))
+    _check(st, "bitlinear_fwd_group_plan")
+
+
+def bitlinear_fwd_group(plan, n, m, stages=3, stream=None):
+    st = lib().bitlinear_fwd_group(_ptr(plan, (torch.uint8,), None, "plan"), n, m, int(stages),
+                                   _stream(stream))
+    _check(st, "bitlinear_fwd_group")

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <string>
+#include <vector>
 
 #include "../../include/bitlinear.h"
 #include "common.h"
@@ -169,6 +170,137 @@ int bitlinear_fwd(const uint16_t* X, int64_t tokens, int64_t k, const void* pack
   if (e != hipSuccess) return hip_status(e, "activation quant launch");
   e = bl::launch_gemm(packed, xq, x_scale, gamma, Y, acc, tokens, k, n_out, S, s);
   return hip_status(e, "prefill launch");
+}
+
+int bitlinear_act_quant(const uint16_t* X, int64_t tokens, int64_t k, int8_t* xq, float* x_scale,
+                        void* stream) {
+  if (k < 128 || k % 128 != 0)
+    return fail(BL_ESHAPE, "k must be a positive multiple of 128 (got %lld)", (long long)k);
+  if (tokens < 0 || tokens >= kLimit || tokens * k >= kLimit)
+    return fail(BL_ESHAPE, "tokens must be >= 0 with tokens*k below 2^31");
+  if (tokens == 0) return ok();
+  TRY(check_ptr(X, 16, "X"));
+  TRY(check_ptr(xq, 16, "xq"));
+  TRY(check_ptr(x_scale, 4, "x_scale"));
+  hipError_t e = bl::launch_act_quant(X, tokens, k, xq, x_scale, nullptr, 0,
+                                      reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "activation quant launch");
+}
+
+int bitlinear_contract(const int8_t* xq, const float* x_scale, int64_t tokens, int64_t k,
+                       const void* packed, int64_t n_out, int n, int m, const double* gamma,
+                       float* Y, int32_t* acc, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_nm(n, m));
+  TRY(check_layer(n_out, k));
+  if (tokens < 0 || tokens >= kLimit || tokens * k >= kLimit || tokens * n_out >= kLimit)
+    return fail(BL_ESHAPE, "tokens must be >= 0 with tokens*k and tokens*n_out below 2^31");
+  if (tokens == 0) return ok();
+  TRY(check_ptr(xq, 16, "xq"));
+  TRY(check_ptr(x_scale, 4, "x_scale"));
+  TRY(check_ptr(packed, 16, "packed"));
+  TRY(check_ptr(gamma, 8, "gamma"));
+  TRY(check_ptr(Y, 16, "Y"));
+  TRY(check_opt_ptr(acc, 16, "acc"));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int S = bl::s_of(n, m);
+  hipError_t e;
+  if (tokens <= 16) {
+    const size_t need = bl::gemv_ws_bytes_max(tokens, k, n_out);
+    if (need && (!ws || ws_bytes < need))
+      return fail(BL_EWORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
+                  ws ? ws_bytes : (size_t)0);
+    if (need) TRY(check_ptr(ws, 16, "ws"));
+    e = bl::launch_gemv(packed, xq, x_scale, gamma, Y, acc, ws, (int)tokens, k, n_out, S, s);
+  } else {
+    e = bl::launch_gemm(packed, xq, x_scale, gamma, Y, acc, tokens, k, n_out, S, s);
+  }
+  return hip_status(e, "contraction launch");
+}
+
+namespace {
+int group_shape(const bitlinear_fwd_item* items, int count, int64_t tokens, int64_t* units) {
+  if (!items) return fail(BL_EINVAL, "items is NULL");
+  if (count < 1 || count > 65535) return fail(BL_ESHAPE, "count must be in 1..65535 (got %d)", count);
+  if (tokens < 1 || tokens > 16) return fail(BL_ESHAPE, "grouped decode takes 1..16 tokens (got %lld)", (long long)tokens);
+  int64_t u = 0;
+  for (int i = 0; i < count; ++i) {
+    const bitlinear_fwd_item& it = items[i];
+    int st = check_layer(it.n_out, it.k);
+    if (st != BL_OK) return fail(st, "item %d: %s", i, g_last_error.c_str());
+    if (tokens * it.k >= kLimit || tokens * it.n_out >= kLimit)
+      return fail(BL_ESHAPE, "item %d: tokens*k and tokens*n_out must stay below 2^31", i);
+    const int64_t tiles = (it.n_out + 15) / 16;
+    if (tiles > 65536) return fail(BL_ESHAPE, "item %d: n_out above 2^20 rows", i);
+    u += tiles;
+  }
+  *units = u;
+  return BL_OK;
+}
+}  // namespace
+
+size_t bitlinear_fwd_group_plan_bytes(const bitlinear_fwd_item* items, int count, int64_t tokens) {
+  int64_t units = 0;
+  if (group_shape(items, count, tokens, &units) != BL_OK) return 0;
+  return bl::group_plan_bytes(count, count * tokens, units);
+}
+
+int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t tokens, int n,
+                             int m, void* plan, size_t plan_bytes, void* stream) {
+  TRY(check_nm(n, m));
+  int64_t units = 0;
+  TRY(group_shape(items, count, tokens, &units));
+  for (int i = 0; i < count; ++i) {
+    const bitlinear_fwd_item& it = items[i];
+    TRY(check_ptr(it.X, 16, "item X"));
+    TRY(check_ptr(it.packed, 16, "item packed"));
+    TRY(check_ptr(it.gamma, 8, "item gamma"));
+    TRY(check_ptr(it.Y, 16, "item Y"));
+    TRY(check_ptr(it.xq, 16, "item xq"));
+    TRY(check_ptr(it.x_scale, 4, "item x_scale"));
+  }
+  const size_t need = bl::group_plan_bytes(count, count * tokens, units);
+  TRY(check_ptr(plan, 16, "plan"));
+  if (plan_bytes < need) return fail(BL_EWORKSPACE, "plan needs %zu bytes (got %zu)", need, plan_bytes);
+  std::vector<char> img(need);
+  bl::GroupHeader* h = reinterpret_cast<bl::GroupHeader*>(img.data());
+  h->count = count;
+  h->tokens = (int32_t)tokens;
+  h->S = bl::s_of(n, m);
+  h->pad = 0;
+  h->rows = count * tokens;
+  h->units = units;
+  bl::GroupItem* gi = reinterpret_cast<bl::GroupItem*>(img.data() + sizeof(bl::GroupHeader));
+  uint32_t* rows = reinterpret_cast<uint32_t*>(gi + count);
+  uint32_t* utab = rows + count * tokens;
+  int64_t r = 0, u = 0;
+  for (int i = 0; i < count; ++i) {
+    const bitlinear_fwd_item& it = items[i];
+    gi[i] = bl::GroupItem{it.X, reinterpret_cast<const uint32_t*>(it.packed), it.gamma, it.Y,
+                          it.xq, it.x_scale, it.k, it.n_out};
+    for (int64_t t = 0; t < tokens; ++t) rows[r++] = ((uint32_t)i << 4) | (uint32_t)t;
+    const int64_t tiles = (it.n_out + 15) / 16;
+    for (int64_t tl = 0; tl < tiles; ++tl) utab[u++] = ((uint32_t)i << 16) | (uint32_t)tl;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(plan, img.data(), need, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return hip_status(e, "plan upload");
+}
+
+int bitlinear_fwd_group(const void* plan, int n, int m, int stages, void* stream) {
+  TRY(check_nm(n, m));
+  TRY(check_ptr(plan, 16, "plan"));
+  if (stages < 1 || stages > 3) return fail(BL_EINVAL, "stages must be 1, 2 or 3 (got %d)", stages);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (stages & 1) {
+    hipError_t e = bl::launch_act_quant_group(plan, s);
+    if (e != hipSuccess) return hip_status(e, "grouped activation launch");
+  }
+  if (stages & 2) {
+    hipError_t e = bl::launch_gemv_group(plan, bl::s_of(n, m), s);
+    if (e != hipSuccess) return hip_status(e, "grouped decode launch");
+  }
+  return ok();
 }
 
 int bitlinear_bwd(const uint16_t* dY, const int8_t* xq, const float* x_scale, const void* packed,

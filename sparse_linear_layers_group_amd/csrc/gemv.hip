@@ -24,14 +24,89 @@
 //    ranges; partial sums meet in an int32 workspace by integer atomics
 //    (order independent, hence bit-reproducible), and the last range to
 //    finish a tile writes its outputs.
+//  * The grouped kernel runs many such GEMVs (same token count and pattern)
+//    from one device-resident plan in a single launch.
 #include "common.h"
 #include "launch.h"
 
 namespace bl {
 
 constexpr int kGemvThreads = 512;  // 8 wavefronts
+constexpr int kGemvWaves = kGemvThreads / 64;
 constexpr int kLutCopies = 32;
-constexpr int64_t kResidentWaves = 256 * 2 * 8;  // 256 CUs x 2 blocks x 8 waves
+constexpr int64_t kResidentWaves = 256 * 2 * kGemvWaves;  // 256 CUs x 2 blocks
+
+__device__ __forceinline__ void fill_lut(uint32_t* lut) {
+  for (int idx = threadIdx.x; idx < 512; idx += blockDim.x) {
+    const uint32_t key = idx & 255, half = idx >> 8;
+    const uint32_t v = half_codes(key, half);
+    uint4* dst = reinterpret_cast<uint4*>(&lut[(key * 2 + half) * kLutCopies]);
+#pragma unroll
+    for (int c = 0; c < kLutCopies / 4; ++c) dst[c] = make_uint4(v, v, v, v);
+  }
+}
+
+// partial dot products of one 16-row tile over super-tiles [st0, st1):
+// returns acc of rows tile*16 + 4*(lane/16) + i for token lane%16
+template <int S>
+__device__ __forceinline__ v4i tile_dot(const uint32_t* __restrict__ packed,
+                                        const int8_t* __restrict__ xq, int64_t tile, int64_t nkb,
+                                        int64_t st0, int64_t st1, int64_t k, bool tok_ok,
+                                        const uint32_t* lut_lane, int lane) {
+  constexpr int kW = block_bytes(S) / 4;
+  constexpr int kField = 8 + S;
+  const int r16 = lane & 15, grp = lane >> 4;
+  v4i c = {0, 0, 0, 0};
+  for (int64_t st = st0; st < st1; ++st) {
+    const int64_t kb = st * 4 + grp;
+    const bool blk_ok = kb < nkb;
+    uint32_t w[kW + 1];
+#pragma unroll
+    for (int i = 0; i <= kW; ++i) w[i] = 0;
+    if (blk_ok) {
+      const uint32_t* src = packed + ((tile * nkb + kb) * kTileRows + r16) * kW;
+#pragma unroll
+      for (int i = 0; i < kW; ++i) w[i] = src[i];
+    }
+    v4i b[8];
+    if (blk_ok && tok_ok) {
+      const v4i* xs = reinterpret_cast<const v4i*>(xq + (int64_t)r16 * k + kb * kBlockK);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) b[m] = xs[m];
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) b[m] = v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      v4i a;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int off = (2 * m + q) * kField;
+        const int offh = off + S;
+        const uint32_t klo = funnel(w[(off >> 5) + 1], w[off >> 5], off & 31) & 0xffu;
+        const uint32_t khi = funnel(w[(offh >> 5) + 1], w[offh >> 5], offh & 31) & 0xffu;
+        a[2 * q] = (int)lut_lane[(klo * 2 + 0) * kLutCopies];
+        a[2 * q + 1] = (int)lut_lane[(khi * 2 + 1) * kLutCopies];
+      }
+      c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[m], c, 0, 0, 0);
+    }
+  }
+  return c;
+}
+
+__device__ __forceinline__ void store_tile(float* __restrict__ Y, int32_t* __restrict__ acc_out,
+                                           const v4i& c, int64_t row0, int64_t n_out, int token,
+                                           double g, double st) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row0 + i;
+    if (row < n_out) {
+      Y[(int64_t)token * n_out + row] = (float)((double)c[i] * g * st);
+      if (acc_out) acc_out[(int64_t)token * n_out + row] = c[i];
+    }
+  }
+}
 
 template <int S>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
@@ -39,17 +114,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const float* __restrict__ scale, const double* __restrict__ gamma, float* __restrict__ Y,
     int32_t* __restrict__ acc_out, int32_t* __restrict__ partial, uint32_t* __restrict__ tickets,
     int tokens, int64_t k, int64_t n_out, int ksplit, int st_per_unit, int64_t units) {
-  constexpr int kW = block_bytes(S) / 4;
-  constexpr int kField = 8 + S;
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 2 * kLutCopies];
-
-  for (int idx = threadIdx.x; idx < 512; idx += kGemvThreads) {
-    const uint32_t key = idx & 255, half = idx >> 8;
-    const uint32_t v = half_codes(key, half);
-    uint4* dst = reinterpret_cast<uint4*>(&lut[(key * 2 + half) * kLutCopies]);
-#pragma unroll
-    for (int c = 0; c < kLutCopies / 4; ++c) dst[c] = make_uint4(v, v, v, v);
-  }
+  fill_lut(lut);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -60,63 +126,18 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
   const int64_t nst = (nkb + 3) / 4;
   const double g = *gamma;
   const bool tok_ok = r16 < tokens;
+  const double st = tok_ok ? (double)scale[r16] : 0.0;
 
-  for (int64_t u = (int64_t)blockIdx.x * (kGemvThreads / 64) + (threadIdx.x >> 6); u < units;
-       u += (int64_t)gridDim.x * (kGemvThreads / 64)) {
+  for (int64_t u = (int64_t)blockIdx.x * kGemvWaves + (threadIdx.x >> 6); u < units;
+       u += (int64_t)gridDim.x * kGemvWaves) {
     const int64_t tile = u / ksplit;
     const int part = (int)(u - tile * ksplit);
     const int64_t st0 = (int64_t)part * st_per_unit;
     const int64_t st1 = min(st0 + st_per_unit, nst);
-    v4i c = {0, 0, 0, 0};
-    for (int64_t st = st0; st < st1; ++st) {
-      const int64_t kb = st * 4 + grp;
-      const bool blk_ok = kb < nkb;
-      uint32_t w[kW + 1];
-#pragma unroll
-      for (int i = 0; i <= kW; ++i) w[i] = 0;
-      if (blk_ok) {
-        const uint32_t* src = packed + ((tile * nkb + kb) * kTileRows + r16) * kW;
-#pragma unroll
-        for (int i = 0; i < kW; ++i) w[i] = src[i];
-      }
-      v4i b[8];
-      if (blk_ok && tok_ok) {
-        const v4i* xs = reinterpret_cast<const v4i*>(xq + (int64_t)r16 * k + kb * kBlockK);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) b[m] = xs[m];
-      } else {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) b[m] = v4i{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        v4i a;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int off = (2 * m + q) * kField;
-          const int offh = off + S;
-          const uint32_t klo = funnel(w[(off >> 5) + 1], w[off >> 5], off & 31) & 0xffu;
-          const uint32_t khi = funnel(w[(offh >> 5) + 1], w[offh >> 5], offh & 31) & 0xffu;
-          a[2 * q] = (int)lut_lane[(klo * 2 + 0) * kLutCopies];
-          a[2 * q + 1] = (int)lut_lane[(khi * 2 + 1) * kLutCopies];
-        }
-        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[m], c, 0, 0, 0);
-      }
-    }
-    // c[i] = partial acc of row tile*16 + 4*grp + i for token r16
+    const v4i c = tile_dot<S>(packed, xq, tile, nkb, st0, st1, k, tok_ok, lut_lane, lane);
     const int64_t row0 = tile * kTileRows + 4 * grp;
     if (ksplit == 1) {
-      if (tok_ok) {
-        const double st = (double)scale[r16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t row = row0 + i;
-          if (row < n_out) {
-            Y[(int64_t)r16 * n_out + row] = (float)((double)c[i] * g * st);
-            if (acc_out) acc_out[(int64_t)r16 * n_out + row] = c[i];
-          }
-        }
-      }
+      if (tok_ok) store_tile(Y, acc_out, c, row0, n_out, r16, g, st);
       continue;
     }
     if (tok_ok) {
@@ -131,19 +152,47 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     if (lane == 0) t = atomicAdd(&tickets[tile], 1u);
     t = __shfl(t, 0, 64);
     if (t != (uint32_t)(ksplit - 1)) continue;
+    // last range of this tile: collect the sums and leave the workspace
+    // zeroed for the next call (no memset needed)
     __threadfence();
     if (tok_ok) {
-      const double st = (double)scale[r16];
+      v4i tot;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t row = row0 + i;
-        if (row < n_out) {
-          const int32_t v = atomicAdd(&partial[(int64_t)r16 * n_out + row], 0);
-          Y[(int64_t)r16 * n_out + row] = (float)((double)v * g * st);
-          if (acc_out) acc_out[(int64_t)r16 * n_out + row] = v;
-        }
+        tot[i] = row < n_out ? atomicExch(&partial[(int64_t)r16 * n_out + row], 0) : 0;
       }
+      store_tile(Y, acc_out, tot, row0, n_out, r16, g, st);
     }
+    if (lane == 0) atomicExch(&tickets[tile], 0u);
+  }
+}
+
+template <int S>
+__global__ __launch_bounds__(kGemvThreads) void gemv_group_kernel(const char* __restrict__ plan) {
+  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 2 * kLutCopies];
+  fill_lut(lut);
+  __syncthreads();
+  const GroupHeader* hdr = reinterpret_cast<const GroupHeader*>(plan);
+  const GroupItem* items = reinterpret_cast<const GroupItem*>(plan + sizeof(GroupHeader));
+  const uint32_t* units_tab =
+      reinterpret_cast<const uint32_t*>(items + hdr->count) + hdr->rows;
+  const int tokens = hdr->tokens;
+  const int64_t units = hdr->units;
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const bool tok_ok = r16 < tokens;
+  const uint32_t* lut_lane = lut + (lane & (kLutCopies - 1));
+  for (int64_t u = (int64_t)blockIdx.x * kGemvWaves + (threadIdx.x >> 6); u < units;
+       u += (int64_t)gridDim.x * kGemvWaves) {
+    const uint32_t e = units_tab[u];
+    const GroupItem it = items[e >> 16];
+    const int64_t tile = e & 0xffffu;
+    const int64_t nkb = it.k / kBlockK;
+    const v4i c = tile_dot<S>(it.packed, it.xq, tile, nkb, 0, (nkb + 3) / 4, it.k, tok_ok, lut_lane, lane);
+    if (tok_ok)
+      store_tile(it.Y, nullptr, c, tile * kTileRows + 4 * grp, it.n_out, r16, *it.gamma,
+                 (double)it.scale[r16]);
   }
 }
 
@@ -182,7 +231,7 @@ static hipError_t launch_gemv_s(const void* packed, const int8_t* xq, const floa
     tickets = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) +
                                           align256((size_t)tokens * n_out * 4));
   }
-  int64_t blocks = (p.units + 7) / 8;
+  int64_t blocks = (p.units + kGemvWaves - 1) / kGemvWaves;
   if (blocks > 512) blocks = 512;
   gemv_kernel<S><<<(unsigned)blocks, kGemvThreads, 0, s>>>(
       reinterpret_cast<const uint32_t*>(packed), xq, scale, gamma, Y, acc, partial, tickets,
@@ -196,6 +245,14 @@ hipError_t launch_gemv(const void* packed, const int8_t* xq, const float* scale,
   if (S == 8) return launch_gemv_s<8>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
   if (S == 6) return launch_gemv_s<6>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
   return launch_gemv_s<4>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
+}
+
+hipError_t launch_gemv_group(const void* plan, int S, hipStream_t s) {
+  const char* p = reinterpret_cast<const char*>(plan);
+  if (S == 8) gemv_group_kernel<8><<<512, kGemvThreads, 0, s>>>(p);
+  else if (S == 6) gemv_group_kernel<6><<<512, kGemvThreads, 0, s>>>(p);
+  else gemv_group_kernel<4><<<512, kGemvThreads, 0, s>>>(p);
+  return hipGetLastError();
 }
 
 }  // namespace bl

@@ -38,6 +38,31 @@ hipError_t launch_gemv(const void* packed, const int8_t* xq, const float* scale,
                        const double* gamma, float* Y, int32_t* acc, void* ws, int tokens,
                        int64_t k, int64_t n_out, int S, hipStream_t s);
 
+// grouped decode: one plan in device memory describes many GEMVs that share
+// the token count and N:M pattern; kernels read it, so a run needs only the
+// plan pointer.
+struct GroupHeader {
+  int32_t count, tokens, S, pad;
+  int64_t rows;   // activation rows = count * tokens
+  int64_t units;  // 16-row tiles over all items
+};
+struct GroupItem {
+  const uint16_t* X;
+  const uint32_t* packed;
+  const double* gamma;
+  float* Y;
+  int8_t* xq;
+  float* scale;
+  int64_t k, n_out;
+};
+// plan image: header | items[count] | row table[rows] | unit table[units]
+// row entry = item << 4 | token;  unit entry = item << 16 | tile
+inline size_t group_plan_bytes(int64_t count, int64_t rows, int64_t units) {
+  return sizeof(GroupHeader) + (size_t)count * sizeof(GroupItem) + (size_t)(rows + units) * 4;
+}
+hipError_t launch_act_quant_group(const void* plan, hipStream_t s);
+hipError_t launch_gemv_group(const void* plan, int S, hipStream_t s);
+
 // prefill-shaped contraction (any token count)
 hipError_t launch_gemm(const void* packed, const int8_t* xq, const float* scale,
                        const double* gamma, float* Y, int32_t* acc, int64_t tokens, int64_t k,

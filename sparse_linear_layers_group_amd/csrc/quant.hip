@@ -330,13 +330,10 @@ __global__ __launch_bounds__(256) void ternary_pack_kernel(const uint16_t* __res
 // equals round-half-even of the exact quotient.  |x_q| <= 127, so the clip
 // to [-128, 127] never binds.  Optionally zeroes a workspace range.
 // ---------------------------------------------------------------------
-__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ X, int64_t k,
-                                                       int8_t* __restrict__ xq,
-                                                       float* __restrict__ scale,
-                                                       uint32_t* __restrict__ zero_ws,
-                                                       int64_t zero_words) {
-  const int64_t t = blockIdx.x;
-  const uint4* row = reinterpret_cast<const uint4*>(X + t * k);
+__device__ __forceinline__ void quant_row(const uint16_t* __restrict__ X, int64_t k,
+                                          int8_t* __restrict__ xq, float* __restrict__ scale,
+                                          float* red) {
+  const uint4* row = reinterpret_cast<const uint4*>(X);
   const int64_t nvec = k / 8;
   float a = 0.f;
   for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) {
@@ -345,14 +342,14 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) a = fmaxf(a, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
   }
-  __shared__ float red[8];
   a = wave_max(a);
+  __syncthreads();  // red[] free from a previous row
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
   __syncthreads();
   a = red[0];
   for (int i = 1; i < (int)(blockDim.x >> 6); ++i) a = fmaxf(a, red[i]);
-  if (threadIdx.x == 0) scale[t] = a / 127.0f;
-  uint2* out = reinterpret_cast<uint2*>(xq + t * k);
+  if (threadIdx.x == 0) *scale = a / 127.0f;
+  uint2* out = reinterpret_cast<uint2*>(xq);
   for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) {
     uint4 v = row[i];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -367,9 +364,33 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
     }
     out[i] = make_uint2(q[0], q[1]);
   }
+}
+
+__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ X, int64_t k,
+                                                       int8_t* __restrict__ xq,
+                                                       float* __restrict__ scale,
+                                                       uint32_t* __restrict__ zero_ws,
+                                                       int64_t zero_words) {
+  __shared__ float red[8];
+  const int64_t t = blockIdx.x;
+  quant_row(X + t * k, k, xq + t * k, scale + t, red);
   if (zero_ws) {
     for (int64_t i = t * blockDim.x + threadIdx.x; i < zero_words; i += (int64_t)gridDim.x * blockDim.x)
       zero_ws[i] = 0u;
+  }
+}
+
+// grouped: every (item, token) row of a decode plan, grid-stride
+__global__ __launch_bounds__(256) void act_quant_group_kernel(const char* __restrict__ plan) {
+  __shared__ float red[8];
+  const GroupHeader* hdr = reinterpret_cast<const GroupHeader*>(plan);
+  const GroupItem* items = reinterpret_cast<const GroupItem*>(plan + sizeof(GroupHeader));
+  const uint32_t* rows = reinterpret_cast<const uint32_t*>(items + hdr->count);
+  for (int64_t r = blockIdx.x; r < hdr->rows; r += gridDim.x) {
+    const uint32_t e = rows[r];
+    const GroupItem it = items[e >> 4];
+    const int64_t t = e & 15u;
+    quant_row(it.X + t * it.k, it.k, it.xq + t * it.k, it.scale + t, red);
   }
 }
 
@@ -423,6 +444,11 @@ hipError_t launch_ternary_pack(const uint16_t* W, const uint8_t* mask, const dou
   if (S == 8) return launch_tp<8>(W, mask, gamma, n_out, k, packed, wq, s);
   if (S == 6) return launch_tp<6>(W, mask, gamma, n_out, k, packed, wq, s);
   return launch_tp<4>(W, mask, gamma, n_out, k, packed, wq, s);
+}
+
+hipError_t launch_act_quant_group(const void* plan, hipStream_t s) {
+  act_quant_group_kernel<<<1024, 256, 0, s>>>(reinterpret_cast<const char*>(plan));
+  return hipGetLastError();
 }
 
 hipError_t launch_act_quant(const uint16_t* X, int64_t tokens, int64_t k, int8_t* xq,

@@ -168,3 +168,73 @@ def test_host_errors_with_device_buffers():
     with pytest.raises(bl.BitLinearError) as e:
         bl.bitlinear_pack(W, lw.mask, lw.gamma, 64, 256, 6, 8, lw.packed, packed_bytes=100)
     assert e.value.status == bl.BL_ESHAPE
+
+
+@pytest.mark.parametrize("tokens", [1, 5, 16])
+@pytest.mark.parametrize("n,m", [(6, 8), (8, 8), (2, 4)])
+def test_grouped_decode_matches_oracle(tokens, n, m):
+    """One plan, several GEMVs of different shapes (including a ragged row
+    tile and a partial 512-wide k super-tile), two launches."""
+    shapes = [(48, 256), (128, 896), (40, 384), (896, 4864), (200, 1152)]
+    entries, refs = [], []
+    for i, (n_out, k) in enumerate(shapes):
+        W = synth.weights(n_out, k, seed=100 + i)
+        X = synth.activations(tokens, k, seed=200 + i)
+        lw, T, g = H.check_weight_path(W, n, m)
+        xq, sc = oracle.act_quant(X)
+        _, Yref = oracle.fwd(xq, sc, T, g)
+        e = dict(X=bf16_tensor(X), packed=lw.packed, gamma=lw.gamma, k=k, n_out=n_out,
+                 Y=torch.full((tokens * n_out,), float("nan"), dtype=torch.float32, device="cuda"),
+                 xq=torch.empty(tokens * k, dtype=torch.int8, device="cuda"),
+                 x_scale=torch.empty(tokens, dtype=torch.float32, device="cuda"), lw=lw)
+        entries.append(e)
+        refs.append((xq, sc, Yref))
+    items = bl.make_fwd_items(entries, tokens)
+    nbytes = bl.bitlinear_fwd_group_plan_bytes(items, len(entries), tokens)
+    plan = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    bl.bitlinear_fwd_group_plan(items, len(entries), tokens, n, m, plan)
+    for stages in ((3,), (1, 2)):
+        for e in entries:
+            e["Y"].fill_(float("nan"))
+        for s in stages:
+            bl.bitlinear_fwd_group(plan, n, m, s)
+        torch.cuda.synchronize()
+        for e, (xq, sc, Yref) in zip(entries, refs):
+            assert np.array_equal(e["xq"].cpu().numpy().reshape(xq.shape), xq)
+            assert np.array_equal(e["x_scale"].cpu().numpy(), sc.astype(np.float32))
+            H.assert_y_close(e["Y"].cpu().numpy().reshape(Yref.shape).astype(np.float64), Yref)
+
+
+@pytest.mark.parametrize("tokens", [1, 16, 100])
+def test_act_quant_plus_contract_equals_fwd(tokens):
+    W = synth.weights(2048, 1024, seed=31)
+    X = synth.activations(tokens, 1024, seed=31)
+    lw, T, g = H.check_weight_path(W, 6, 8)
+    ref = lw.fwd(bf16_tensor(X), tokens)
+    xq = torch.empty(tokens * 1024, dtype=torch.int8, device="cuda")
+    sc = torch.empty(tokens, dtype=torch.float32, device="cuda")
+    Y = torch.empty(tokens * 2048, dtype=torch.float32, device="cuda")
+    nws = bl.bitlinear_fwd_workspace_bytes(tokens, 1024, 2048)
+    ws = torch.zeros(nws, dtype=torch.uint8, device="cuda") if nws else None
+    bl.bitlinear_act_quant(bf16_tensor(X), tokens, 1024, xq, sc)
+    for _ in range(3):  # the split-k workspace is left zeroed by every call
+        bl.bitlinear_contract(xq, sc, tokens, 1024, lw.packed, 2048, 6, 8, lw.gamma, Y, ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy(), ref["Y"].cpu().numpy())
+    if ws is not None:
+        assert not ws.cpu().numpy().any()
+    assert np.array_equal(xq.cpu().numpy(), ref["xq"].cpu().numpy())
+
+
+def test_group_plan_validation():
+    lw = BitLinearWeight(64, 256, 6, 8)
+    e = dict(X=torch.zeros(256, dtype=torch.bfloat16, device="cuda"), packed=lw.packed, gamma=lw.gamma,
+             Y=torch.zeros(64, dtype=torch.float32, device="cuda"),
+             xq=torch.zeros(256, dtype=torch.int8, device="cuda"),
+             x_scale=torch.zeros(1, dtype=torch.float32, device="cuda"), k=256, n_out=64)
+    items = bl.make_fwd_items([e], 1)
+    plan = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(bl.BitLinearError) as err:
+        bl.bitlinear_fwd_group_plan(items, 1, 1, 6, 8, plan)
+    assert err.value.status == bl.BL_EWORKSPACE
+    assert bl.bitlinear_fwd_group_plan_bytes(items, 1, 17) == 0  # decode only: <= 16 tokens
