@@ -14,7 +14,7 @@ import re
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+LIB_PATH = os.environ.get("BITLINEAR_LIB") or os.path.join(_HERE, "libbitlinear.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "bitlinear.h")
 
 BL_OK, BL_EINVAL, BL_ESHAPE, BL_EUNSUPPORTED, BL_EWORKSPACE, BL_EHIP = range(6)

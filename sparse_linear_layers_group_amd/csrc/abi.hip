@@ -7,7 +7,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/bitlinear.h"
+#include "bitlinear.h"
 #include "common.h"
 #include "launch.h"
 
@@ -231,6 +231,7 @@ int group_shape(const bitlinear_fwd_item* items, int count, int64_t tokens, int6
       return fail(BL_ESHAPE, "item %d: tokens*k and tokens*n_out must stay below 2^31", i);
     const int64_t tiles = (it.n_out + 15) / 16;
     if (tiles > 65536) return fail(BL_ESHAPE, "item %d: n_out above 2^20 rows", i);
+    if (u + tiles >= ((int64_t)1 << 31)) return fail(BL_ESHAPE, "too many row tiles in one plan");
     u += tiles;
   }
   *units = u;
@@ -261,17 +262,22 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t
   const size_t need = bl::group_plan_bytes(count, count * tokens, units);
   TRY(check_ptr(plan, 16, "plan"));
   if (plan_bytes < need) return fail(BL_EWORKSPACE, "plan needs %zu bytes (got %zu)", need, plan_bytes);
-  std::vector<char> img(need);
+  std::vector<char> img(need, 0);
   bl::GroupHeader* h = reinterpret_cast<bl::GroupHeader*>(img.data());
+  const int nwaves = bl::kGroupBlocks * bl::kGroupWaves;
   h->count = count;
   h->tokens = (int32_t)tokens;
   h->S = bl::s_of(n, m);
-  h->pad = 0;
+  h->waves = nwaves;
   h->rows = count * tokens;
   h->units = units;
   bl::GroupItem* gi = reinterpret_cast<bl::GroupItem*>(img.data() + sizeof(bl::GroupHeader));
   uint32_t* rows = reinterpret_cast<uint32_t*>(gi + count);
-  uint32_t* utab = rows + count * tokens;
+  bl::WaveStart* starts =
+      reinterpret_cast<bl::WaveStart*>(img.data() + bl::group_starts_offset(count, count * tokens));
+  // unit u = (item, tile) in item order; super-tiles per unit = ceil(k/512)
+  std::vector<int64_t> prefix(units + 1, 0);
+  std::vector<int32_t> uitem(units), utile(units);
   int64_t r = 0, u = 0;
   for (int i = 0; i < count; ++i) {
     const bitlinear_fwd_item& it = items[i];
@@ -279,7 +285,26 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t
                           it.xq, it.x_scale, it.k, it.n_out};
     for (int64_t t = 0; t < tokens; ++t) rows[r++] = ((uint32_t)i << 4) | (uint32_t)t;
     const int64_t tiles = (it.n_out + 15) / 16;
-    for (int64_t tl = 0; tl < tiles; ++tl) utab[u++] = ((uint32_t)i << 16) | (uint32_t)tl;
+    const int64_t nst = (it.k / 128 + 3) / 4;
+    for (int64_t tl = 0; tl < tiles; ++tl) {
+      uitem[u] = i;
+      utile[u] = (int32_t)tl;
+      prefix[u + 1] = prefix[u] + nst;
+      ++u;
+    }
+  }
+  // wavefront w walks a contiguous range of units holding about the same
+  // number of super-tiles as every other wavefront
+  const int64_t total = prefix[units];
+  int64_t cur = 0;
+  for (int w = 0; w <= nwaves; ++w) {
+    const int64_t target = total * w / nwaves;
+    while (cur < units && prefix[cur] < target) ++cur;
+    const int64_t su = (w == nwaves) ? units : cur;
+    starts[w].unit = (int32_t)su;
+    starts[w].item = su < units ? uitem[su] : count;
+    starts[w].tile = su < units ? utile[su] : 0;
+    starts[w].pad = 0;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(plan, img.data(), need, hipMemcpyHostToDevice, s);

@@ -50,6 +50,18 @@ typedef short v8s __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// explicit global-address-space accesses: pointers that arrive through
+// memory (e.g. from a plan) would otherwise become flat accesses, which also
+// count against the LDS counter and force extra waits
+template <class T>
+__device__ __forceinline__ T ld_global(const T* p) {
+  return *(const __attribute__((address_space(1))) T*)(p);
+}
+template <class T>
+__device__ __forceinline__ void st_global(T* p, T v) {
+  *(__attribute__((address_space(1))) T*)(p) = v;
+}
+
 // wave-level reductions ------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

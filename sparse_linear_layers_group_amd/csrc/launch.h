@@ -41,10 +41,12 @@ hipError_t launch_gemv(const void* packed, const int8_t* xq, const float* scale,
 // grouped decode: one plan in device memory describes many GEMVs that share
 // the token count and N:M pattern; kernels read it, so a run needs only the
 // plan pointer.
+constexpr int kGroupBlocks = 256;   // one 1024-thread block per CU
+constexpr int kGroupWaves = 16;     // wavefronts per block
 struct GroupHeader {
-  int32_t count, tokens, S, pad;
-  int64_t rows;   // activation rows = count * tokens
-  int64_t units;  // 16-row tiles over all items
+  int32_t count, tokens, S, waves;  // waves = per-wavefront ranges stored
+  int64_t rows;                     // activation rows = count * tokens
+  int64_t units;                    // 16-row tiles over all items
 };
 struct GroupItem {
   const uint16_t* X;
@@ -55,10 +57,21 @@ struct GroupItem {
   float* scale;
   int64_t k, n_out;
 };
-// plan image: header | items[count] | row table[rows] | unit table[units]
-// row entry = item << 4 | token;  unit entry = item << 16 | tile
+// where wavefront w starts: its first unit (16-row tile) index, that
+// unit's item and tile; it walks units [start[w].unit, start[w+1].unit)
+struct WaveStart {
+  int32_t unit, item, tile, pad;
+};
+// plan image: header | items[count] | row table[rows] | pad to 64 |
+//             wave starts[waves + 1]
+// row entry = item << 4 | token
+__host__ __device__ inline size_t group_starts_offset(int64_t count, int64_t rows) {
+  size_t o = sizeof(GroupHeader) + (size_t)count * sizeof(GroupItem) + (size_t)rows * 4;
+  return (o + 63) & ~(size_t)63;
+}
 inline size_t group_plan_bytes(int64_t count, int64_t rows, int64_t units) {
-  return sizeof(GroupHeader) + (size_t)count * sizeof(GroupItem) + (size_t)(rows + units) * 4;
+  (void)units;
+  return group_starts_offset(count, rows) + (size_t)(kGroupBlocks * kGroupWaves + 1) * sizeof(WaveStart);
 }
 hipError_t launch_act_quant_group(const void* plan, hipStream_t s);
 hipError_t launch_gemv_group(const void* plan, int S, hipStream_t s);
