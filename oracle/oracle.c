@@ -417,13 +417,16 @@ void oracle_bwd_dw_pairs(const uint16_t *dY, const int8_t *xq,
 /*                     the i-th nonzero among t_4..t_7 at bit 4+S-1-i;  */
 /*                     every other sign bit is 0                        */
 /*     bits [4+S,8+S)  nonzero bitmap of t_4..t_7                       */
-/*  Block: the 16 group fields of one row and one 128-wide k block,     */
-/*     field g at bit offset g*(8+S) of a little-endian bit string of   */
-/*     2*(8+S) bytes (byte j holds string bits 8j..8j+7, LSB first).    */
-/*  Order: rows in tiles of 16 (the last tile padded with zero rows);  */
-/*     block (row r, k-block kb) sits at slot                           */
-/*        ((r/16) * (k/128) + kb) * 16 + r % 16                         */
-/*     and the buffer is the slots in order.                           */
+/*  Chunk: 16 group fields, field f at bit offset f*(8+S) of a          */
+/*     little-endian bit string of 2*(8+S) bytes (byte j holds string   */
+/*     bits 8j..8j+7, LSB first).                                       */
+/*  Order: rows in strips of 64 (the last strip padded with zero rows). */
+/*     Superblock (strip p, k-block kb) = 64 chunks, at index           */
+/*     p * (k/128) + kb; the buffer is the superblocks in order.        */
+/*     Chunk c = r + 16q (r in 0..15, q in 0..3) of a superblock holds, */
+/*     as field f = 4i + 2h + e (i in 0..3, h and e in 0..1), the group */
+/*     of row 64p + 16i + r at k = kb*128 + 8*(8h + 2q + e) ... +7.     */
+/*     (Every (row, group) of the superblock appears exactly once.)     */
 /* ------------------------------------------------------------------ */
 int oracle_s_of(int n, int m)
 {
@@ -436,8 +439,22 @@ int oracle_s_of(int n, int m)
 
 int64_t oracle_packed_bytes(int64_t n_out, int64_t k, int s)
 {
-    int64_t tiles = (n_out + 15) / 16;
-    return tiles * 16 * (k / 128) * 2 * (8 + s);
+    int64_t strips = (n_out + 63) / 64;
+    return strips * 64 * (k / 128) * 2 * (8 + s);
+}
+
+/* byte offset of the chunk, and bit offset within it, of the field that
+ * holds group g (0..15) of row r in k-block kb */
+static void field_place(int64_t r, int64_t kb, int g, int64_t nkb, int s, int64_t *chunk_byte,
+                        int64_t *bit)
+{
+    int64_t strip = r / 64;
+    int rr = (int)(r % 64);
+    int i = rr / 16, r16 = rr % 16;
+    int h = g / 8, q = (g % 8) / 2, e = g % 2;
+    int64_t chunk = (strip * nkb + kb) * 64 + r16 + 16 * q;
+    *chunk_byte = chunk * 2 * (8 + s);
+    *bit = (int64_t)(4 * i + 2 * h + e) * (8 + s);
 }
 
 static void put_bits(uint8_t *blk, int64_t bitpos, uint32_t value, int width)
@@ -458,12 +475,14 @@ static uint32_t get_bits(const uint8_t *blk, int64_t bitpos, int width)
  * half holds more than 4 (impossible for codes in {-1,0,1}). */
 int oracle_pack(const int8_t *T, int64_t n_out, int64_t k, int s, uint8_t *packed)
 {
-    int64_t nkb = k / 128, bsz = 2 * (8 + s);
+    int64_t nkb = k / 128;
     memset(packed, 0, (size_t)oracle_packed_bytes(n_out, k, s));
     for (int64_t r = 0; r < n_out; ++r)
         for (int64_t kb = 0; kb < nkb; ++kb) {
-            uint8_t *blk = packed + (((r / 16) * nkb + kb) * 16 + r % 16) * bsz;
             for (int g = 0; g < 16; ++g) {
+                int64_t cb, base;
+                field_place(r, kb, g, nkb, s, &cb, &base);
+                uint8_t *blk = packed + cb;
                 const int8_t *t = T + r * k + kb * 128 + g * 8;
                 uint32_t blo = 0, bhi = 0, sign = 0;
                 int nlo = 0, nhi = 0;
@@ -480,7 +499,6 @@ int oracle_pack(const int8_t *T, int64_t n_out, int64_t k, int s, uint8_t *packe
                         nhi++;
                     }
                 if (nlo + nhi > s) return -1;
-                int64_t base = (int64_t)g * (8 + s);
                 put_bits(blk, base, blo, 4);
                 put_bits(blk, base + 4, sign, s);
                 put_bits(blk, base + 4 + s, bhi, 4);
@@ -491,12 +509,13 @@ int oracle_pack(const int8_t *T, int64_t n_out, int64_t k, int s, uint8_t *packe
 
 void oracle_unpack(const uint8_t *packed, int64_t n_out, int64_t k, int s, int8_t *T)
 {
-    int64_t nkb = k / 128, bsz = 2 * (8 + s);
+    int64_t nkb = k / 128;
     for (int64_t r = 0; r < n_out; ++r)
         for (int64_t kb = 0; kb < nkb; ++kb) {
-            const uint8_t *blk = packed + (((r / 16) * nkb + kb) * 16 + r % 16) * bsz;
             for (int g = 0; g < 16; ++g) {
-                int64_t base = (int64_t)g * (8 + s);
+                int64_t cb, base;
+                field_place(r, kb, g, nkb, s, &cb, &base);
+                const uint8_t *blk = packed + cb;
                 uint32_t blo = get_bits(blk, base, 4);
                 uint32_t sign = get_bits(blk, base + 4, s);
                 uint32_t bhi = get_bits(blk, base + 4 + s, 4);

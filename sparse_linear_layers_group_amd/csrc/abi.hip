@@ -4,7 +4,12 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
+#include <cstring>
+#include <functional>
+#include <queue>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "bitlinear.h"
@@ -73,6 +78,37 @@ int hip_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+namespace {
+// Shape checks for a grouped decode plan; returns the total number of steps
+// (64 x 128 superblocks) and of 64-row strips over all items.
+int group_shape(const bitlinear_fwd_item* items, int count, int64_t tokens, int64_t* steps,
+                int64_t* strips) {
+  if (!items) return fail(BL_EINVAL, "items is NULL");
+  if (count < 1 || count > 65535) return fail(BL_ESHAPE, "count must be in 1..65535 (got %d)", count);
+  if (tokens < 1 || tokens > 16) return fail(BL_ESHAPE, "grouped decode takes 1..16 tokens (got %lld)", (long long)tokens);
+  int64_t t = 0, ns = 0;
+  for (int i = 0; i < count; ++i) {
+    const bitlinear_fwd_item& it = items[i];
+    int st = check_layer(it.n_out, it.k);
+    if (st != BL_OK) return fail(st, "item %d: %s", i, g_last_error.c_str());
+    if (tokens * it.k >= kLimit || tokens * it.n_out >= kLimit)
+      return fail(BL_ESHAPE, "item %d: tokens*k and tokens*n_out must stay below 2^31", i);
+    const int64_t strips = (it.n_out + bl::kStripRows - 1) / bl::kStripRows;
+    ns += strips;
+    t += strips * (it.k / 128);
+    if (t >= ((int64_t)1 << 31)) return fail(BL_ESHAPE, "too many 64x128 weight blocks in one plan");
+  }
+  *steps = t;
+  *strips = ns;
+  return BL_OK;
+}
+
+int64_t group_blocks(int64_t steps, int64_t strips) {
+  const int64_t nb = bl::decode_blocks(steps);
+  return nb < strips ? nb : strips;
+}
+}  // namespace
+
 extern "C" {
 
 size_t bitlinear_packed_bytes(int64_t n_out, int64_t k, int n, int m) {
@@ -80,8 +116,8 @@ size_t bitlinear_packed_bytes(int64_t n_out, int64_t k, int n, int m) {
   if (S < 0 || n_out < 1 || k < 128 || k % 128 != 0 || n_out >= kLimit || k >= kLimit ||
       n_out * k >= kLimit)
     return 0;
-  const int64_t tiles = (n_out + 15) / 16;
-  return (size_t)(tiles * 16 * (k / 128) * bl::block_bytes(S));
+  const int64_t strips = (n_out + bl::kStripRows - 1) / bl::kStripRows;
+  return (size_t)(strips * bl::kStripRows * (k / 128) * bl::block_bytes(S));
 }
 
 size_t bitlinear_workspace_bytes(int64_t n_out, int64_t k) {
@@ -92,7 +128,9 @@ size_t bitlinear_workspace_bytes(int64_t n_out, int64_t k) {
 
 size_t bitlinear_fwd_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out) {
   if (tokens < 1 || tokens > 16 || n_out < 1 || k < 128) return 0;
-  return bl::gemv_ws_bytes_max(tokens, k, n_out);
+  // one k block per strip: no strip is ever cut between wavefronts
+  if (k / 128 == 1) return 0;
+  return bl::decode_ws_bytes(tokens, n_out);
 }
 
 int bitlinear_quantize_mask(const uint16_t* W, int64_t n_out, int64_t k, int n, int m,
@@ -155,7 +193,7 @@ int bitlinear_fwd(const uint16_t* X, int64_t tokens, int64_t k, const void* pack
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int S = bl::s_of(n, m);
   if (tokens <= 16) {
-    const size_t need = bl::gemv_ws_bytes_max(tokens, k, n_out);
+    const size_t need = bitlinear_fwd_workspace_bytes(tokens, k, n_out);
     if (need && (!ws || ws_bytes < need))
       return fail(BL_EWORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
                   ws ? ws_bytes : (size_t)0);
@@ -205,7 +243,7 @@ int bitlinear_contract(const int8_t* xq, const float* x_scale, int64_t tokens, i
   const int S = bl::s_of(n, m);
   hipError_t e;
   if (tokens <= 16) {
-    const size_t need = bl::gemv_ws_bytes_max(tokens, k, n_out);
+    const size_t need = bitlinear_fwd_workspace_bytes(tokens, k, n_out);
     if (need && (!ws || ws_bytes < need))
       return fail(BL_EWORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
                   ws ? ws_bytes : (size_t)0);
@@ -217,39 +255,19 @@ int bitlinear_contract(const int8_t* xq, const float* x_scale, int64_t tokens, i
   return hip_status(e, "contraction launch");
 }
 
-namespace {
-int group_shape(const bitlinear_fwd_item* items, int count, int64_t tokens, int64_t* units) {
-  if (!items) return fail(BL_EINVAL, "items is NULL");
-  if (count < 1 || count > 65535) return fail(BL_ESHAPE, "count must be in 1..65535 (got %d)", count);
-  if (tokens < 1 || tokens > 16) return fail(BL_ESHAPE, "grouped decode takes 1..16 tokens (got %lld)", (long long)tokens);
-  int64_t u = 0;
-  for (int i = 0; i < count; ++i) {
-    const bitlinear_fwd_item& it = items[i];
-    int st = check_layer(it.n_out, it.k);
-    if (st != BL_OK) return fail(st, "item %d: %s", i, g_last_error.c_str());
-    if (tokens * it.k >= kLimit || tokens * it.n_out >= kLimit)
-      return fail(BL_ESHAPE, "item %d: tokens*k and tokens*n_out must stay below 2^31", i);
-    const int64_t tiles = (it.n_out + 15) / 16;
-    if (tiles > 65536) return fail(BL_ESHAPE, "item %d: n_out above 2^20 rows", i);
-    if (u + tiles >= ((int64_t)1 << 31)) return fail(BL_ESHAPE, "too many row tiles in one plan");
-    u += tiles;
-  }
-  *units = u;
-  return BL_OK;
-}
-}  // namespace
 
 size_t bitlinear_fwd_group_plan_bytes(const bitlinear_fwd_item* items, int count, int64_t tokens) {
-  int64_t units = 0;
-  if (group_shape(items, count, tokens, &units) != BL_OK) return 0;
-  return bl::group_plan_bytes(count, count * tokens, units);
+  int64_t steps = 0, strips = 0;
+  if (group_shape(items, count, tokens, &steps, &strips) != BL_OK) return 0;
+  const int64_t nb = group_blocks(steps, strips);
+  return bl::group_recs_offset(count, count * tokens, nb) + (size_t)strips * sizeof(bl::StripRec);
 }
 
 int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t tokens, int n,
                              int m, void* plan, size_t plan_bytes, void* stream) {
   TRY(check_nm(n, m));
-  int64_t units = 0;
-  TRY(group_shape(items, count, tokens, &units));
+  int64_t steps = 0, nstrips = 0;
+  TRY(group_shape(items, count, tokens, &steps, &nstrips));
   for (int i = 0; i < count; ++i) {
     const bitlinear_fwd_item& it = items[i];
     TRY(check_ptr(it.X, 16, "item X"));
@@ -259,52 +277,78 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t
     TRY(check_ptr(it.xq, 16, "item xq"));
     TRY(check_ptr(it.x_scale, 4, "item x_scale"));
   }
-  const size_t need = bl::group_plan_bytes(count, count * tokens, units);
+  const int64_t nb = group_blocks(steps, nstrips);
+  const size_t need = bl::group_recs_offset(count, count * tokens, nb) +
+                      (size_t)nstrips * sizeof(bl::StripRec);
   TRY(check_ptr(plan, 16, "plan"));
   if (plan_bytes < need) return fail(BL_EWORKSPACE, "plan needs %zu bytes (got %zu)", need, plan_bytes);
   std::vector<char> img(need, 0);
   bl::GroupHeader* h = reinterpret_cast<bl::GroupHeader*>(img.data());
-  const int nwaves = bl::kGroupBlocks * bl::kGroupWaves;
   h->count = count;
   h->tokens = (int32_t)tokens;
   h->S = bl::s_of(n, m);
-  h->waves = nwaves;
+  h->blocks = (int32_t)nb;
   h->rows = count * tokens;
-  h->units = units;
+  h->steps = steps;
   bl::GroupItem* gi = reinterpret_cast<bl::GroupItem*>(img.data() + sizeof(bl::GroupHeader));
   uint32_t* rows = reinterpret_cast<uint32_t*>(gi + count);
-  bl::WaveStart* starts =
-      reinterpret_cast<bl::WaveStart*>(img.data() + bl::group_starts_offset(count, count * tokens));
-  // unit u = (item, tile) in item order; super-tiles per unit = ceil(k/512)
-  std::vector<int64_t> prefix(units + 1, 0);
-  std::vector<int32_t> uitem(units), utile(units);
-  int64_t r = 0, u = 0;
+  int64_t r = 0;
+  // every strip of every item, with its step count
+  struct Strip {
+    int32_t item, strip, nkb;
+  };
+  std::vector<Strip> all;
+  all.reserve((size_t)nstrips);
   for (int i = 0; i < count; ++i) {
     const bitlinear_fwd_item& it = items[i];
     gi[i] = bl::GroupItem{it.X, reinterpret_cast<const uint32_t*>(it.packed), it.gamma, it.Y,
                           it.xq, it.x_scale, it.k, it.n_out};
     for (int64_t t = 0; t < tokens; ++t) rows[r++] = ((uint32_t)i << 4) | (uint32_t)t;
-    const int64_t tiles = (it.n_out + 15) / 16;
-    const int64_t nst = (it.k / 128 + 3) / 4;
-    for (int64_t tl = 0; tl < tiles; ++tl) {
-      uitem[u] = i;
-      utile[u] = (int32_t)tl;
-      prefix[u + 1] = prefix[u] + nst;
-      ++u;
-    }
+    const int64_t strips = (it.n_out + bl::kStripRows - 1) / bl::kStripRows;
+    for (int64_t st = 0; st < strips; ++st)
+      all.push_back(Strip{i, (int32_t)st, (int32_t)(it.k / 128)});
   }
-  // wavefront w walks a contiguous range of units holding about the same
-  // number of super-tiles as every other wavefront
-  const int64_t total = prefix[units];
-  int64_t cur = 0;
-  for (int w = 0; w <= nwaves; ++w) {
-    const int64_t target = total * w / nwaves;
-    while (cur < units && prefix[cur] < target) ++cur;
-    const int64_t su = (w == nwaves) ? units : cur;
-    starts[w].unit = (int32_t)su;
-    starts[w].item = su < units ? uitem[su] : count;
-    starts[w].tile = su < units ? utile[su] : 0;
-    starts[w].pad = 0;
+  // whole strips to workgroups, longest first onto the least loaded (LPT);
+  // each workgroup's list in (item, strip) order
+  std::vector<int32_t> order(all.size());
+  for (size_t j = 0; j < order.size(); ++j) order[j] = (int32_t)j;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return all[a].nkb > all[b].nkb; });
+  typedef std::pair<int64_t, int32_t> Load;  // (steps so far, workgroup)
+  std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+  for (int32_t b = 0; b < (int32_t)nb; ++b) heap.push(Load(0, b));
+  std::vector<std::vector<int32_t>> lists((size_t)nb);
+  for (int32_t j : order) {
+    Load l = heap.top();
+    heap.pop();
+    lists[(size_t)l.second].push_back(j);
+    l.first += all[j].nkb;
+    heap.push(l);
+  }
+  bl::BlockRec* brec = reinterpret_cast<bl::BlockRec*>(
+      img.data() + bl::group_blocks_offset(count, count * tokens));
+  bl::WaveStart* wst = reinterpret_cast<bl::WaveStart*>(
+      img.data() + bl::group_waves_offset(count, count * tokens, nb));
+  bl::StripRec* recs = reinterpret_cast<bl::StripRec*>(
+      img.data() + bl::group_recs_offset(count, count * tokens, nb));
+  int32_t next = 0;
+  for (int64_t b = 0; b < nb; ++b) {
+    std::vector<int32_t>& lst = lists[(size_t)b];
+    std::sort(lst.begin(), lst.end());  // strip index order = (item, strip) order
+    int64_t n_b = 0;
+    for (int32_t j : lst) n_b += all[j].nkb;
+    brec[b] = bl::BlockRec{next, (int32_t)n_b};
+    // wavefront w starts at local step n_b * w / 16
+    size_t pos = 0;
+    int64_t cum = 0;
+    for (int w = 0; w < bl::kDecodeWavesPerBlock; ++w) {
+      const int64_t sw = n_b * w / bl::kDecodeWavesPerBlock;
+      while (pos + 1 < lst.size() && cum + all[lst[pos]].nkb <= sw) cum += all[lst[pos++]].nkb;
+      const int32_t rec = lst.empty() ? 0 : next + (int32_t)pos;
+      const int32_t kb = lst.empty() ? 0 : (int32_t)(sw - cum);
+      wst[b * bl::kDecodeWavesPerBlock + w] = bl::WaveStart{rec, kb};
+    }
+    for (int32_t j : lst) recs[next++] = bl::StripRec{all[j].item, all[j].strip};
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(plan, img.data(), need, hipMemcpyHostToDevice, s);

@@ -81,20 +81,22 @@ __global__ __launch_bounds__(256) void dx_kernel(const uint16_t* __restrict__ dY
         dst[i] = ok ? *reinterpret_cast<const u32x4*>(dY + tt * n_out + r) : u32x4{0u, 0u, 0u, 0u};
       }
     }
-    {  // B: codes of rows r0 .. r0+63 for block kb, written transposed
-       // [c][r]; wavefront w decodes groups 4w..4w+3 of row r0 + lane
-      const int rr = lane;
-      const int64_t row = r0 + rr;
+    {  // B: codes of rows r0 .. r0+63 (one packed superblock) for block
+       // kb, written transposed [c][r]; wavefront w decodes fields
+       // 4w..4w+3 of chunk `lane` (row tile w of the strip; padding rows
+       // of the last strip hold zero codes)
+      const int ch = lane;
       uint32_t w[kW + 1];
 #pragma unroll
       for (int i = 0; i <= kW; ++i) w[i] = 0;
-      if (row < n_out) {
-        const uint32_t* src = packed + (((row / kTileRows) * nkb + kb) * kTileRows + row % kTileRows) * kW;
+      {
+        const uint32_t* src = packed + (((r0 / kStripRows) * nkb + kb) * kStripRows + ch) * kW;
 #pragma unroll
         for (int i = 0; i < kW; ++i) w[i] = src[i];
       }
       auto lk = [&](uint32_t key, int half) { return lut[half * 256 + key]; };
-      auto emit = [&](int gi, uint32_t lo, uint32_t hi) {
+      auto emit = [&](int f, uint32_t lo, uint32_t hi) {
+        const int rr = field_row(ch, f), gi = field_group(ch, f);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           Bs[(gi * 8 + p) * kP + rr] = code_bf16((lo >> (8 * p)) & 0xffu);

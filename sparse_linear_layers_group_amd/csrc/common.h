@@ -23,6 +23,26 @@ namespace bl {
 // ---------------------------------------------------------------------
 constexpr int kBlockK = 128;
 constexpr int kTileRows = 16;
+constexpr int kStripRows = 64;  // rows of a packed superblock
+
+// Packed layout: rows in strips of 64; the superblock of (strip, k block)
+// holds 64 chunks of 2(8+S) bytes.  Chunk c = r + 16q carries, as field
+// f = 4i + 2h + e, the 8-group 8h + 2q + e of strip row 16i + r, so chunk c
+// is exactly the A operand lane c needs for the 8 MFMAs (row tile i, k half
+// h) of one superblock.
+// Forward epilogue Y = acc * gamma * s_t: gamma * s_t is formed in binary64
+// and rounded once to binary32, then the product is rounded once more
+// (relative error below 2^-22; acc is exact in binary32 up to 2^24).  The
+// decode and prefill kernels share it, so they give identical outputs.
+__device__ __forceinline__ float out_scale(double gamma, float s_t) {
+  return (float)(gamma * (double)s_t);
+}
+__device__ __forceinline__ float out_value(int32_t acc, float gs) { return (float)acc * gs; }
+
+__host__ __device__ constexpr int field_row(int c, int f) { return 16 * (f >> 2) + (c & 15); }
+__host__ __device__ constexpr int field_group(int c, int f) {
+  return 8 * ((f >> 1) & 1) + 2 * (c >> 4) + (f & 1);
+}
 
 __host__ __device__ constexpr int block_bytes(int S) { return 2 * (8 + S); }
 
@@ -60,6 +80,38 @@ __device__ __forceinline__ T ld_global(const T* p) {
 template <class T>
 __device__ __forceinline__ void st_global(T* p, T v) {
   *(__attribute__((address_space(1))) T*)(p) = v;
+}
+
+// Device-scope integer atomics through global-address-space pointers: on a
+// generic pointer they would be FLAT operations, which may touch LDS, and a
+// pending FLAT operation makes every later wait drain all outstanding
+// loads.
+template <class T>
+__device__ __forceinline__ void atomic_add_global(T* p, T v) {
+  __hip_atomic_fetch_add((__attribute__((address_space(1))) T*)(p), v, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T atomic_fetch_add_global(T* p, T v) {
+  return __hip_atomic_fetch_add((__attribute__((address_space(1))) T*)(p), v, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T atomic_exchange_global(T* p, T v) {
+  return __hip_atomic_exchange((__attribute__((address_space(1))) T*)(p), v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every memory operation this wavefront issued has completed.
+// Partial sums that meet across workgroups go only through device-scope
+// atomics, which are performed at the device's coherence point; once they
+// have completed, a later atomic (a ticket) is ordered after them.  This
+// gives that order without the L2 write-back an agent-scope fence implies
+// (which, per wavefront, would cost far more than the whole contraction).
+__device__ __forceinline__ void wait_memory_ops() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // wave-level reductions ------------------------------------------------

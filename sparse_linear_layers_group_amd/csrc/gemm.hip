@@ -37,18 +37,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint32_t* __restrict__ 
   const int64_t m0 = (int64_t)blockIdx.y * kBM;
   const int64_t n0 = (int64_t)blockIdx.x * kBN;
   const int64_t nkb = k / kBlockK;
-  const int64_t tiles = (n_out + kTileRows - 1) / kTileRows;
+  const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l16 = lane & 15, lg = lane >> 4;
 
-  // loader roles: A -- row tid/2, 64-byte half; B -- row tid%128, half of
-  // the groups chosen per wavefront (tid/128) so group offsets are uniform
+  // loader roles: A -- row tid/2, 64-byte half; B -- chunk tid%64 of
+  // superblock (tid/64)%2 of the tile's two strips, fields 8*(tid/128) ..
+  // +7 (wave-uniform, so field offsets are compile-time constants)
   const int ld_row = tid >> 1, ld_half = tid & 1;
   const int64_t a_tok = m0 + ld_row;
-  const int b_lrow = tid & 127, b_half = tid >> 7;
-  const int64_t b_row = n0 + b_lrow;
-  const bool b_ok = (b_row / kTileRows) < tiles;
+  const int b_sb = (tid >> 6) & 1, b_chunk = tid & 63, b_part = tid >> 7;
+  const int64_t b_strip = n0 / kStripRows + b_sb;
+  const bool b_ok = b_strip < strips;
 
   v4i c[4][4];
 #pragma unroll
@@ -66,22 +67,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint32_t* __restrict__ 
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[i] = ok ? src[i] : u32x4{0u, 0u, 0u, 0u};
     }
-    // B tile: codes of rows n0 .. n0+127 for this k block; waves 0-1
-    // decode groups 0..7 of rows tid%128, waves 2-3 groups 8..15
+    // B tile: codes of rows n0 .. n0+127 (two packed superblocks) for this
+    // k block; each field lands at its (row, group) of the tile
     {
       uint32_t w[kW + 1];
 #pragma unroll
       for (int i = 0; i <= kW; ++i) w[i] = 0;
       if (b_ok) {
-        const uint32_t* src =
-            packed + (((b_row / kTileRows) * nkb + kb) * kTileRows + (b_row % kTileRows)) * kW;
+        const uint32_t* src = packed + ((b_strip * nkb + kb) * kStripRows + b_chunk) * kW;
 #pragma unroll
         for (int i = 0; i < kW; ++i) w[i] = src[i];
       }
-      uint2* dst = reinterpret_cast<uint2*>(Bs + b_lrow * kPitch);
       auto lk = [&](uint32_t key, int half) { return lut[half * 256 + key]; };
-      auto emit = [&](int g, uint32_t lo, uint32_t hi) { dst[g] = make_uint2(lo, hi); };
-      if (b_half == 0) decode_groups<S, 0, 8>(w, lk, emit);
+      auto emit = [&](int f, uint32_t lo, uint32_t hi) {
+        const int row = b_sb * kStripRows + field_row(b_chunk, f);
+        *reinterpret_cast<uint2*>(Bs + row * kPitch + 8 * field_group(b_chunk, f)) =
+            make_uint2(lo, hi);
+      };
+      if (b_part == 0) decode_groups<S, 0, 8>(w, lk, emit);
       else decode_groups<S, 8, 8>(w, lk, emit);
     }
     __syncthreads();
@@ -108,12 +111,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint32_t* __restrict__ 
     for (int q = 0; q < 4; ++q) {
       const int64_t t = m0 + wm * 64 + i * 16 + 4 * lg + q;
       if (t >= tokens) continue;
-      const double st = (double)scale[t];
+      const float gs = out_scale(g, scale[t]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t r = n0 + wn * 64 + j * 16 + l16;
         if (r < n_out) {
-          Y[t * n_out + r] = (float)((double)c[i][j][q] * g * st);
+          Y[t * n_out + r] = out_value(c[i][j][q], gs);
           if (acc_out) acc_out[t * n_out + r] = c[i][j][q];
         }
       }

@@ -7,34 +7,43 @@
 // bandwidth.  This kernel keeps that shape for the bitmap+sign format and
 // CDNA4:
 //
-//  * A wavefront owns a tile of 16 weight rows and walks k in 512-wide
-//    super-tiles.  Lane l (row l%16, block l/16) loads the 2*(8+S) packed
-//    bytes of one row's 128-wide k block; the 64 lanes read 64 consecutive
-//    blocks, i.e. one contiguous span of the packed buffer.
+//  * A step is one packed superblock: 64 weight rows x one 128-wide k block.
+//    Lane c loads chunk c -- the 2(8+S) bytes holding exactly the groups its
+//    A operands need -- so a wavefront's 64 loads are one contiguous span.
 //  * Each 8-group decodes from two 8-bit keys (low half: bitmap + first
 //    four signs; high half: last four signs + bitmap) through two 256-entry
-//    tables of int8x4 codes in LDS.  Every lane reads its own copy of the
-//    tables (32 copies, one per bank) so the lookups are free of bank
-//    conflicts.
+//    tables of int8x4 codes in LDS.  Lane l reads its own copy of the tables
+//    (64 copies, one per bank), so the lookups never conflict.
 //  * The codes go straight into v_mfma_i32_16x16x64_i8 as the A operand
-//    (16 rows); the activations of up to 16 tokens are the B operand.  A and
-//    B take the same k slice per lane group, so the dot product covers each
-//    k exactly once.  int32 accumulation is exact.
-//  * When a layer has too few row tiles to fill the chip, k is split into
-//    ranges; partial sums meet in an int32 workspace by integer atomics
-//    (order independent, hence bit-reproducible), and the last range to
-//    finish a tile writes its outputs.
-//  * The grouped kernel runs many such GEMVs (same token count and pattern)
-//    from one device-resident plan in a single launch.
+//    (row tile i, k half h); the B operand is the 16 activation bytes of
+//    token l%16 at k slice l/16 of that half -- two 16-byte loads per step
+//    serve all four row tiles and any token count.  int32 accumulation is
+//    exact.
+//  * Loads run kDepth-1 steps ahead of the decode (a register ring), across
+//    strip and item boundaries.
+//  * Each workgroup runs a list of steps, cut into 16 equal contiguous
+//    ranges, one per wavefront, so every wavefront streams the same number
+//    of bytes whatever the layer shapes.  Whole strips are written as they
+//    finish; a strip cut between wavefronts is summed in LDS (over the
+//    then-dead code tables) by its first wavefront once all are done.  A
+//    strip cut between workgroups -- only single calls with too few strips
+//    to fill the chip -- meets in an int32 workspace through integer
+//    atomics (order independent, hence bit-reproducible); the last
+//    workgroup to contribute writes it and leaves the workspace zeroed.
+//  * The grouped kernel runs many GEMVs (same token count and pattern) from
+//    one device-resident plan in a single launch; the plan gives every
+//    workgroup whole strips, packed on the host for equal step counts.
 #include "common.h"
 #include "launch.h"
 
 namespace bl {
 
-constexpr int kGemvThreads = 1024;  // 16 wavefronts, one block per CU
+constexpr int kGemvThreads = 1024;  // 16 wavefronts, one workgroup per CU
 constexpr int kGemvWaves = kGemvThreads / 64;
-constexpr int kLutCopies = 64;      // one table copy per LDS bank: lane l reads copy l
-constexpr int64_t kResidentWaves = 256 * kGemvWaves;
+static_assert(kGemvWaves == kDecodeWavesPerBlock, "wavefronts per workgroup");
+constexpr int kLutCopies = 64;  // one table copy per LDS bank: lane l reads copy l
+constexpr int kDepth = 3;       // register ring: steps in flight + 1
+constexpr int kSlotDwords = 16 * kStripRows;  // one wavefront's cut-strip sums [token][row]
 
 // Tables in LDS: entry (key, half) of copy c at dword (key * 2 + half) * 64 + c
 // (128 KB).  Lane l always reads copy l, i.e. bank l, so a wavefront's 64
@@ -51,406 +60,460 @@ __device__ __forceinline__ void fill_lut(uint32_t* lut, uint32_t* entries) {
     reinterpret_cast<uint4*>(lut)[ch] = make_uint4(v, v, v, v);
   }
 }
+static_assert(kGemvWaves * kSlotDwords <= 256 * 2 * kLutCopies, "cut-strip slots fit the tables");
 
 // wavefront index within the block, as a wave-uniform (scalar) value
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
-// ---------------------------------------------------------------------
-// Streaming loop.  A wavefront walks a contiguous range of units (16-row
-// tiles, or k ranges of a tile) as one flat sequence of 512-wide
-// super-tiles.  The loads of the next super-tile (packed codes and
-// activations) are issued before the current one is decoded, across unit
-// boundaries, so every wavefront keeps loads in flight while it computes.
-// Loads go through buffer resources: a lane whose block or token is out of
-// range gets an offset past the end of the buffer and reads zeros (no
-// branches, no zero fills).
-// ---------------------------------------------------------------------
+// Loads go through buffer resources: a lane past the end of the range gets
+// an offset beyond the buffer and reads zeros (no branches, no zero fills).
 constexpr uint32_t kOOB = 0x80000000u;  // beyond every buffer (all < 2^31 bytes)
-constexpr int kDepth = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-struct Unit {
-  __amdgpu_buffer_rsrc_t pk, xr;  // unit's packed blocks / item's activations
-  int32_t nst;                    // super-tiles in the unit
-  int32_t nkb;                    // k blocks from the unit's first column to the row end
-  int32_t k;                      // x_q row stride
-  int32_t x_col;                  // first k column of the unit
-  // epilogue
+// what a wavefront needs of one GEMV (wave-uniform, scalar registers)
+struct ItemView {
+  __amdgpu_buffer_rsrc_t pk, xr;  // packed weights / int8 activations
+  int32_t k, nkb, strips;
+  int64_t n_out;
   float* Y;
+  int32_t* acc;  // optional int32 sums
   const float* scale;
   const double* gamma;
-  int64_t row0, n_out, tile;
 };
 
+template <int S>
+__device__ __forceinline__ ItemView make_view(const void* packed, const int8_t* xq, int tokens,
+                                              int64_t k, int64_t n_out) {
+  ItemView v;
+  v.k = (int32_t)k;
+  v.nkb = (int32_t)(k / kBlockK);
+  v.n_out = n_out;
+  v.strips = (int32_t)((n_out + kStripRows - 1) / kStripRows);
+  v.pk = rsrc(packed, (uint32_t)((int64_t)v.strips * v.nkb * kStripRows * block_bytes(S)));
+  v.xr = rsrc(xq, (uint32_t)(tokens * k));
+  return v;
+}
+
+// position in a workgroup's list; sid numbers the strips of the list
+struct Cursor {
+  ItemView it;
+  int32_t item, strip, kb, sid;
+};
+
+// One step in flight: packed words, the B operand, and the token scale and
+// gamma of the step's item.  The two small scale loads ride with every step
+// (they hit the caches), so a strip's epilogue only needs data its own step
+// already waited for: a wait on any later load would also drain the steps
+// loaded behind it, since loads complete in order.
 template <int S>
 struct Stage {
   uint32_t w[block_bytes(S) / 4];
-  v4i b[8];
+  v4i b[2];
+  float sc;
+  double gm;
 };
 
 template <int S>
-__device__ __forceinline__ void issue(Stage<S>& st, const Unit& u, int sti, bool live, int lane,
+__device__ __forceinline__ void issue(Stage<S>& st, const Cursor& cur, bool live, int lane,
                                       int tokens) {
   constexpr int kBytes = block_bytes(S);
-  const int r16 = lane & 15, grp = lane >> 4;
-  const int kb = 4 * sti + grp;
-  const bool blk = live && kb < u.nkb;
-  const uint32_t po = blk ? (uint32_t)(sti * 64 + lane) * kBytes : kOOB;
+  const uint32_t sb = (uint32_t)(cur.strip * cur.it.nkb + cur.kb);
+  const uint32_t po = live ? (sb * kStripRows + (uint32_t)lane) * kBytes : kOOB;
+  uint32_t* w = st.w;
   if constexpr (kBytes == 32) {
-    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(u.pk, po, 0, 0);
-    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(u.pk, po + 16, 0, 0);
-    st.w[0] = a.x; st.w[1] = a.y; st.w[2] = a.z; st.w[3] = a.w;
-    st.w[4] = b.x; st.w[5] = b.y; st.w[6] = b.z; st.w[7] = b.w;
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cur.it.pk, po, 0, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(cur.it.pk, po + 16, 0, 0);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
   } else if constexpr (kBytes == 28) {
     typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
-    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(u.pk, po, 0, 0);
-    const u32x3 b = __builtin_amdgcn_raw_buffer_load_b96(u.pk, po + 16, 0, 0);
-    st.w[0] = a.x; st.w[1] = a.y; st.w[2] = a.z; st.w[3] = a.w;
-    st.w[4] = b.x; st.w[5] = b.y; st.w[6] = b.z;
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cur.it.pk, po, 0, 0);
+    const u32x3 b = __builtin_amdgcn_raw_buffer_load_b96(cur.it.pk, po + 16, 0, 0);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z;
   } else {
-    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(u.pk, po, 0, 0);
-    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(u.pk, po + 16, 0, 0);
-    st.w[0] = a.x; st.w[1] = a.y; st.w[2] = a.z; st.w[3] = a.w;
-    st.w[4] = b.x; st.w[5] = b.y;
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cur.it.pk, po, 0, 0);
+    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(cur.it.pk, po + 16, 0, 0);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y;
   }
-  // B operand: the MFMA's output columns >= tokens are never stored, so
-  // those lanes may hold anything -- they read token 0's row (a broadcast of
-  // the same address, cheap for the address unit) instead of a masked load.
-  // A block past the row end has all-zero codes, so its activations are
-  // irrelevant too; those lanes read block 0.
-  const uint32_t xo =
-      (uint32_t)((r16 < tokens ? r16 : 0) * u.k) + (uint32_t)u.x_col + (uint32_t)(blk ? kb * kBlockK : 0);
+  // B operand of k half h: token t = lane%16, k slice lane/16.  Columns
+  // t >= tokens are never stored, so those lanes read token 0 (in range).
+  const int t = lane & 15, g = lane >> 4;
+  const uint32_t xo = (uint32_t)((t < tokens ? t : 0) * cur.it.k + cur.kb * kBlockK + 16 * g);
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(u.xr, xo + 16 * m, 0, 0);
-    st.b[m] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+  for (int h = 0; h < 2; ++h) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(cur.it.xr, xo + 64 * h, 0, 0);
+    st.b[h] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
   }
+  st.sc = ld_global(&cur.it.scale[t < tokens ? t : 0]);
+  st.gm = ld_global(cur.it.gamma);
 }
 
+// A operand of MFMA m = 2i + h: codes of fields 2m and 2m+1 of the chunk
 template <int S>
-__device__ __forceinline__ v4i decode_mma(const Stage<S>& st, v4i c, const uint32_t* lut_lane) {
+__device__ __forceinline__ v4i a_operand(const uint32_t* w, int m, const uint32_t* lut_lane) {
   constexpr int kW = block_bytes(S) / 4;
   constexpr int kField = 8 + S;
+  v4i a;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    v4i a;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int off = (2 * m + q) * kField;
-      const int offh = off + S;
-      const uint32_t lo_hi = (off >> 5) + 1 < kW ? st.w[(off >> 5) + 1] : 0u;
-      const uint32_t hi_hi = (offh >> 5) + 1 < kW ? st.w[(offh >> 5) + 1] : 0u;
-      const uint32_t klo = funnel(lo_hi, st.w[off >> 5], off & 31) & 0xffu;
-      const uint32_t khi = funnel(hi_hi, st.w[offh >> 5], offh & 31) & 0xffu;
-      a[2 * q] = (int)lut_lane[(klo * 2 + 0) * kLutCopies];
-      a[2 * q + 1] = (int)lut_lane[(khi * 2 + 1) * kLutCopies];
-    }
-    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, st.b[m], c, 0, 0, 0);
+  for (int q = 0; q < 2; ++q) {
+    const int off = (2 * m + q) * kField;
+    const int offh = off + S;
+    const uint32_t lo_hi = (off >> 5) + 1 < kW ? w[(off >> 5) + 1] : 0u;
+    const uint32_t hi_hi = (offh >> 5) + 1 < kW ? w[(offh >> 5) + 1] : 0u;
+    const uint32_t klo = funnel(lo_hi, w[off >> 5], off & 31) & 0xffu;
+    const uint32_t khi = funnel(hi_hi, w[offh >> 5], offh & 31) & 0xffu;
+    a[2 * q] = (int)lut_lane[(klo * 2 + 0) * kLutCopies];
+    a[2 * q + 1] = (int)lut_lane[(khi * 2 + 1) * kLutCopies];
   }
-  return c;
+  return a;
 }
 
-__device__ __forceinline__ void store_tile(float* __restrict__ Y, int32_t* __restrict__ acc_out,
-                                           const v4i& c, int64_t row0, int64_t n_out, int token,
-                                           double g, double st) {
+// one superblock: row tile i, k half h -> c[i]
+template <int S>
+__device__ __forceinline__ void decode_step(const Stage<S>& st, v4i* c, const uint32_t* lut_lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      c[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_operand<S>(st.w, 2 * i + h, lut_lane),
+                                                   st.b[h], c[i], 0, 0, 0);
+}
+
+// Outputs of lane (t, g) for one strip: rows row0 + 16i + 4g + j.
+__device__ __forceinline__ void store_strip(const ItemView& it, int64_t row0, const v4i* c,
+                                            int lane, int tokens, float gs) {
+  const int t = lane & 15, g = lane >> 4;
+  if (t >= tokens) return;
+  const int64_t o = (int64_t)t * it.n_out + row0 + 4 * g;
+  float* y = it.Y + o;
+  const bool vec = row0 + kStripRows <= it.n_out && (tokens == 1 || (it.n_out & 3) == 0);
+  if (vec) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st_global(reinterpret_cast<v4f*>(y + 16 * i),
+                v4f{out_value(c[i][0], gs), out_value(c[i][1], gs), out_value(c[i][2], gs),
+                    out_value(c[i][3], gs)});
+      if (it.acc) st_global(reinterpret_cast<v4i*>(it.acc + o + 16 * i), c[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (row0 + 16 * i + 4 * g + j < it.n_out) {
+          st_global(y + 16 * i + j, out_value(c[i][j], gs));
+          if (it.acc) st_global(it.acc + o + 16 * i + j, (int32_t)c[i][j]);
+        }
+  }
+}
+
+__device__ __forceinline__ float item_scale(const ItemView& it, int lane, int tokens) {
+  const int t = lane & 15;
+  return out_scale(ld_global(it.gamma), ld_global(&it.scale[t < tokens ? t : 0]));
+}
+
+// A wavefront's first step and its number of steps.
+struct WaveRange {
+  Cursor first;
+  int64_t count;
+};
+
+// Run one workgroup.  A source policy provides tokens, item(idx),
+// advance(cursor), range(w) -- the first step and step count of wavefront
+// w of this workgroup -- and cross()/cross_sum() for strips that continue
+// in another workgroup.
+template <int S, class Src>
+__device__ __forceinline__ void run_block(const Src& src, uint32_t* lut, int lane) {
+  const int tokens = src.tokens;
+  const int w = wave_id();
+  const uint32_t* lut_lane = lut + lane;
+  const WaveRange wr = src.range(w);
+  const int64_t count = wr.count;
+  Cursor L = wr.first, C = wr.first;
+  int64_t lleft = count, cleft = count;
+  bool live = count > 0;
+  const bool started_mid = count > 0 && C.kb > 0;
+  bool first_open = started_mid;  // the first strip has not ended yet
+  v4i c[4], cf[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t row = row0 + i;
-    if (row < n_out) {
-      st_global(&Y[(int64_t)token * n_out + row], (float)((double)c[i] * g * st));
-      if (acc_out) st_global(&acc_out[(int64_t)token * n_out + row], (int32_t)c[i]);
-    }
+    c[i] = v4i{0, 0, 0, 0};
+    cf[i] = v4i{0, 0, 0, 0};
   }
-}
-
-// Walk `count` units of `src` from cursor `first`.  A source policy has a
-// cursor type Cur holding the current Unit (wave-uniform, in scalar
-// registers), next(cur) to move a cursor to the following unit -- plain
-// arithmetic except when a grouped plan changes item, which is rare -- and
-// finish(unit, acc, ...) for the epilogue.  No memory is read per step, so
-// no scalar-cache miss (whose counter the LDS lookups share) sits in the
-// loop.
-template <int S, class Src>
-__device__ __forceinline__ void stream(const Src& src, const uint32_t* lut_lane, int lane,
-                                       typename Src::Cur first, int64_t count) {
-  if (count <= 0) return;
-  const int tokens = src.tokens;
-  // the load cursor runs kDepth-1 super-tiles ahead of the compute cursor
-  typename Src::Cur L = first, C = first;
-  int64_t lleft = count, cleft = count;
-  int lst = 0, cst = 0;
-  bool live = true;
-  Stage<S> ring[kDepth];
-  auto load_step = [&](Stage<S>& st) {
-    issue<S>(st, L.u, lst, live, lane, tokens);
-    if (++lst == L.u.nst) {
-      lst = 0;
-      if (--lleft == 0) live = false;
-      else src.next(L);
-    }
-  };
+  bool ended_mid = false;
+  int32_t last_sid = -1, last_item = 0, last_strip = 0;
+  if (count > 0) {
+    Stage<S> ring[kDepth];
+    // once the load cursor has issued the last step it stops for good:
+    // advance() may read the plan, and must never step past the range
+    auto load_step = [&](Stage<S>& st) {
+      issue<S>(st, L, live, lane, tokens);
+      if (live) {
+        if (--lleft == 0) live = false;
+        else src.advance(L);
+      }
+    };
 #pragma unroll
-  for (int s = 0; s < kDepth - 1; ++s) load_step(ring[s]);
-  v4i c = {0, 0, 0, 0};
-  // token scale and gamma are loaded when a unit starts, long before its
-  // epilogue needs them: the epilogue never waits on a fresh load (which
-  // would also drain the prefetched loads behind it)
-  const int tok = lane & 15;
-  float s_tok = tok < tokens ? ld_global(&C.u.scale[tok]) : 0.f;
-  double g = ld_global(C.u.gamma);
-  while (true) {
+    for (int s = 0; s < kDepth - 1; ++s) load_step(ring[s]);
+    while (cleft > 0) {
 #pragma unroll
-    for (int s = 0; s < kDepth; ++s) {
-      load_step(ring[(s + kDepth - 1) % kDepth]);
-      c = decode_mma<S>(ring[s], c, lut_lane);
-      if (++cst == C.u.nst) {
-        src.finish(C.u, c, lane, s_tok, g);
-        c = v4i{0, 0, 0, 0};
-        cst = 0;
-        if (--cleft == 0) return;
-        src.next(C);
-        s_tok = tok < tokens ? ld_global(&C.u.scale[tok]) : 0.f;
-        g = ld_global(C.u.gamma);
+      for (int s = 0; s < kDepth; ++s) {
+        load_step(ring[(s + kDepth - 1) % kDepth]);
+        decode_step<S>(ring[s], c, lut_lane);
+        --cleft;
+        if (C.kb == C.it.nkb - 1) {  // strip end
+          if (first_open) {
+            // the tail of a strip begun by an earlier wavefront: keep it
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cf[i] = c[i];
+            first_open = false;
+          } else {
+            store_strip(C.it, (int64_t)C.strip * kStripRows, c, lane, tokens,
+                        out_scale(ring[s].gm, ring[s].sc));
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) c[i] = v4i{0, 0, 0, 0};
+        } else if (cleft == 0) {
+          ended_mid = true;
+          last_sid = C.sid;
+          last_item = C.item;
+          last_strip = C.strip;
+        }
+        if (cleft == 0) break;
+        src.advance(C);
       }
     }
   }
+  // ---- cut strips: the code tables are dead; their LDS holds one slot of
+  // sums per wavefront: the part of its first strip when that strip began
+  // in an earlier wavefront's range
+  __syncthreads();
+  int32_t* slots = reinterpret_cast<int32_t*>(lut);
+  const int t = lane & 15, g = lane >> 4;
+  if (started_mid && t < tokens) {
+    int32_t* d = slots + w * kSlotDwords + t * kStripRows + 4 * g;
+    const v4i* part = first_open ? c : cf;  // still open: the range lies inside that strip
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<v4i*>(d + 16 * i) = part[i];
+  }
+  __syncthreads();
+  // The first wavefront touching a cut strip sums it: the wavefront whose
+  // range ends inside a strip that began in its own range, and wavefront 0
+  // for a strip that began in an earlier workgroup (both can hold).
+  const bool head_last = ended_mid && !(started_mid && first_open);
+  const bool head_first = w == 0 && started_mid;
+  for (int role = 0; role < 2; ++role) {
+    const bool last = role == 1;
+    if (last ? !head_last : !head_first) continue;
+    v4i tot[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tot[i] = last ? c[i] : v4i{0, 0, 0, 0};
+    const int32_t sid = last ? last_sid : wr.first.sid;
+    const int32_t item = last ? last_item : wr.first.item;
+    const int32_t strip = last ? last_strip : wr.first.strip;
+    for (int v = last ? w + 1 : 0; v < kGemvWaves; ++v) {
+      const WaveRange o = src.range(v);
+      if (o.count == 0) continue;
+      if (o.first.sid != sid || o.first.kb == 0) break;
+      if (t < tokens) {
+        const int32_t* q = slots + v * kSlotDwords + t * kStripRows + 4 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tot[i] += *reinterpret_cast<const v4i*>(q + 16 * i);
+      }
+    }
+    const ItemView it = src.item(item);
+    if (src.cross(sid))
+      src.cross_sum(it, strip, tot, lane);
+    else
+      store_strip(it, (int64_t)strip * kStripRows, tot, lane, tokens, item_scale(it, lane, tokens));
+  }
 }
 
-// one GEMV, k optionally split into ranges of st_per_unit super-tiles
+// ---------------------------------------------------------------- single call
+// T = strips * nkb steps cut into NB equal workgroup ranges; a strip cut by
+// a workgroup boundary meets in the workspace.
+template <int S>
 struct SingleSrc {
   const void* packed;
   const int8_t* xq;
-  uint32_t x_bytes;
+  float* Y;
+  int32_t* acc;
   const float* scale;
   const double* gamma;
-  float* Y;
-  int32_t* acc_out;
-  int32_t* partial;
-  uint32_t* tickets;
-  int64_t units, n_out;
-  int32_t k, nkb, nst, ksplit, st_per_unit, tokens, kbytes;
-
-  struct Cur {
-    Unit u;
-    int64_t idx;
-  };
-
-  __device__ Unit unit(int64_t u) const {
-    const int64_t tile = u / ksplit;
-    const int part = (int)(u - tile * ksplit);
-    const int st0 = part * st_per_unit;
-    Unit r;
-    r.nst = min(st_per_unit, nst - st0);
-    r.pk = rsrc(reinterpret_cast<const char*>(packed) +
-                    (size_t)((tile * nkb + 4 * st0) * kTileRows) * kbytes,
-                (uint32_t)(r.nst * 64 * kbytes));
-    r.xr = rsrc(xq, x_bytes);
-    r.nkb = nkb - 4 * st0;
-    r.k = k;
-    r.x_col = 4 * st0 * kBlockK;
-    r.Y = Y;
-    r.scale = scale;
-    r.gamma = gamma;
-    r.row0 = tile * kTileRows;
-    r.n_out = n_out;
-    r.tile = tile;
+  int32_t* partial;   // [strips][tokens][64]
+  uint32_t* tickets;  // [strips]
+  int64_t k, n_out, T, NB;
+  int tokens;
+  int32_t nkb;
+  __device__ ItemView item(int32_t) const {
+    ItemView v = make_view<S>(packed, xq, tokens, k, n_out);
+    v.Y = Y;
+    v.acc = acc;
+    v.scale = scale;
+    v.gamma = gamma;
+    return v;
+  }
+  __device__ void advance(Cursor& c) const {
+    if (++c.kb == c.it.nkb) {
+      c.kb = 0;
+      ++c.strip;
+      ++c.sid;
+    }
+  }
+  __device__ WaveRange range(int w) const {
+    const int64_t b = blockIdx.x;
+    const int64_t b0 = T * b / NB, n = T * (b + 1) / NB - b0;
+    const int64_t s0 = b0 + n * w / kGemvWaves, s1 = b0 + n * (w + 1) / kGemvWaves;
+    WaveRange r;
+    r.count = s1 - s0;
+    r.first.it = item(0);
+    r.first.item = 0;
+    r.first.strip = (int32_t)(s0 / nkb);
+    r.first.kb = (int32_t)(s0 - (int64_t)r.first.strip * nkb);
+    r.first.sid = r.first.strip;
     return r;
   }
-  __device__ Cur start(int64_t u) const { return Cur{unit(u), u}; }
-  __device__ void next(Cur& c) const {
-    c.idx += 1;
-    c.u = unit(c.idx);
+  // does strip `sid` continue in another workgroup?
+  __device__ bool cross(int32_t sid) const {
+    const int64_t b = blockIdx.x;
+    const int64_t a = (int64_t)sid * nkb, e = a + nkb;
+    return a < T * b / NB || e > T * (b + 1) / NB;
   }
-
-  __device__ void finish(const Unit& u, const v4i& c, int lane, float s_tok, double g) const {
-    const int r16 = lane & 15, grp = lane >> 4;
-    const bool tok_ok = r16 < tokens;
-    const int64_t row0 = u.row0 + 4 * grp;
-    const double st = (double)s_tok;
-    if (ksplit == 1) {
-      if (tok_ok) store_tile(Y, acc_out, c, row0, n_out, r16, g, st);
-      return;
-    }
-    if (tok_ok) {
+  // add this workgroup's part of the strip; the last workgroup writes it
+  __device__ void cross_sum(const ItemView& it, int32_t strip, const v4i* tot, int lane) const {
+    const int t = lane & 15, g = lane >> 4;
+    int32_t* p = partial + ((int64_t)strip * tokens + (t < tokens ? t : 0)) * kStripRows + 4 * g;
+    if (t < tokens) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t row = row0 + i;
-        if (row < n_out && c[i] != 0) atomicAdd(&partial[(int64_t)r16 * n_out + row], c[i]);
-      }
-    }
-    __threadfence();
-    uint32_t t = 0;
-    if (lane == 0) t = atomicAdd(&tickets[u.tile], 1u);
-    t = __shfl(t, 0, 64);
-    if (t != (uint32_t)(ksplit - 1)) return;
-    // last range of this tile: collect the sums and leave the workspace
-    // zeroed for the next call (no memset needed)
-    __threadfence();
-    if (tok_ok) {
-      v4i tot;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t row = row0 + i;
-        tot[i] = row < n_out ? atomicExch(&partial[(int64_t)r16 * n_out + row], 0) : 0;
-      }
-      store_tile(Y, acc_out, tot, row0, n_out, r16, g, st);
+        for (int j = 0; j < 4; ++j)
+          if (tot[i][j] != 0) atomic_add_global(p + 16 * i + j, (int32_t)tot[i][j]);
     }
-    if (lane == 0) atomicExch(&tickets[u.tile], 0u);
+    const int64_t a = (int64_t)strip * nkb, e = a + nkb - 1;
+    const int64_t blocks = block_of_step(e, T, NB) - block_of_step(a, T, NB) + 1;
+    // every partial sum of this workgroup's part is performed before its ticket
+    wait_memory_ops();
+    uint32_t tk = 0;
+    if (lane == 0) tk = atomic_fetch_add_global(&tickets[strip], 1u);
+    tk = __shfl(tk, 0, 64);
+    if ((int64_t)tk != blocks - 1) return;
+    wait_memory_ops();
+    v4i sum[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sum[i][j] = t < tokens ? atomic_exchange_global(p + 16 * i + j, 0) : 0;
+    store_strip(it, (int64_t)strip * kStripRows, sum, lane, tokens, item_scale(it, lane, tokens));
+    if (lane == 0) atomic_exchange_global(&tickets[strip], 0u);
   }
 };
 
-// many GEMVs from a device plan; units are the 16-row tiles of the items,
-// in item order
+// --------------------------------------------------------------- grouped
 template <int S>
 struct GroupSrc {
   const GroupItem* items;
-  int32_t count, tokens;
-
-  struct Cur {
-    Unit u;
-    int32_t item, tiles;
-    uint64_t tile_stride;  // packed bytes per 16-row tile
-    const char* pk_base;   // packed blocks of the current tile
-  };
-
-  __device__ void load_item(Cur& c, int32_t item, int32_t tile) const {
-    const GroupItem& it = items[item];
-    const int32_t k = (int32_t)it.k;
-    const int32_t nkb = k / kBlockK;
-    const int64_t n_out = it.n_out;
-    c.item = item;
-    c.tiles = (int32_t)((n_out + kTileRows - 1) / kTileRows);
-    c.tile_stride = (uint64_t)nkb * kTileRows * block_bytes(S);
-    c.pk_base = reinterpret_cast<const char*>(it.packed) + (uint64_t)tile * c.tile_stride;
-    c.u.nst = (nkb + 3) / 4;
-    c.u.pk = rsrc(c.pk_base, (uint32_t)(c.u.nst * 64 * block_bytes(S)));
-    c.u.xr = rsrc(it.xq, (uint32_t)(tokens * k));
-    c.u.nkb = nkb;
-    c.u.k = k;
-    c.u.x_col = 0;
-    c.u.Y = it.Y;
-    c.u.scale = it.scale;
-    c.u.gamma = it.gamma;
-    c.u.row0 = (int64_t)tile * kTileRows;
-    c.u.n_out = n_out;
-    c.u.tile = tile;
+  const StripRec* recs;
+  const BlockRec* blocks;
+  const WaveStart* starts;
+  int tokens;
+  __device__ ItemView item(int32_t idx) const {
+    const GroupItem& gi = items[idx];
+    ItemView v = make_view<S>(gi.packed, gi.xq, tokens, gi.k, gi.n_out);
+    v.Y = gi.Y;
+    v.acc = nullptr;
+    v.scale = gi.scale;
+    v.gamma = gi.gamma;
+    return v;
   }
-  __device__ Cur start(int32_t item, int32_t tile) const {
-    Cur c;
-    load_item(c, item, tile);
-    return c;
-  }
-  __device__ void next(Cur& c) const {
-    if (c.u.tile + 1 < c.tiles) {  // same item: arithmetic only
-      c.u.tile += 1;
-      c.u.row0 += kTileRows;
-      c.pk_base += c.tile_stride;
-      c.u.pk = rsrc(c.pk_base, (uint32_t)(c.u.nst * 64 * block_bytes(S)));
-    } else if (c.item + 1 < count) {
-      load_item(c, c.item + 1, 0);
+  __device__ void set_rec(Cursor& c, int32_t rec) const {
+    const StripRec r = recs[rec];
+    c.sid = rec;
+    c.strip = r.strip;
+    if (r.item != c.item) {
+      c.item = r.item;
+      c.it = item(r.item);
     }
   }
-
-  __device__ void finish(const Unit& u, const v4i& c, int lane, float s_tok, double g) const {
-    const int r16 = lane & 15, grp = lane >> 4;
-    if (r16 < tokens) store_tile(u.Y, nullptr, c, u.row0 + 4 * grp, u.n_out, r16, g, (double)s_tok);
+  __device__ void advance(Cursor& c) const {
+    if (++c.kb == c.it.nkb) {
+      c.kb = 0;
+      set_rec(c, c.sid + 1);
+    }
   }
+  __device__ WaveRange range(int w) const {
+    const BlockRec br = blocks[blockIdx.x];
+    const int64_t n = br.steps;
+    WaveRange r;
+    r.count = n * (w + 1) / kGemvWaves - n * w / kGemvWaves;
+    const WaveStart ws = starts[(int64_t)blockIdx.x * kGemvWaves + w];
+    r.first.item = -1;
+    set_rec(r.first, ws.rec);
+    r.first.kb = ws.kb;
+    return r;
+  }
+  // the plan never cuts a strip between workgroups
+  __device__ bool cross(int32_t) const { return false; }
+  __device__ void cross_sum(const ItemView&, int32_t, const v4i*, int) const {}
 };
 
 template <int S>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(SingleSrc src) {
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(SingleSrc<S> src) {
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 2 * kLutCopies];
   __shared__ uint32_t entries[512];
   fill_lut(lut, entries);
   __syncthreads();
-  const int lane = threadIdx.x & 63;
-  // contiguous, equal ranges of units per wavefront
-  const int64_t nw = (int64_t)gridDim.x * kGemvWaves;
-  const int64_t w = (int64_t)blockIdx.x * kGemvWaves + wave_id();
-  const int64_t u0 = src.units * w / nw, u1 = src.units * (w + 1) / nw;
-  if (u0 < u1) stream<S>(src, lut + lane, lane, src.start(u0), u1 - u0);
+  run_block<S>(src, lut, threadIdx.x & 63);
 }
 
 template <int S>
 __global__ __launch_bounds__(kGemvThreads) void gemv_group_kernel(const char* __restrict__ plan) {
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 2 * kLutCopies];
   __shared__ uint32_t entries[512];
+  const GroupHeader* hdr = reinterpret_cast<const GroupHeader*>(plan);
+  if ((int)blockIdx.x >= hdr->blocks) return;  // whole workgroup
   fill_lut(lut, entries);
   __syncthreads();
-  const GroupHeader* hdr = reinterpret_cast<const GroupHeader*>(plan);
   GroupSrc<S> src;
   src.items = reinterpret_cast<const GroupItem*>(plan + sizeof(GroupHeader));
-  src.count = hdr->count;
+  src.blocks = reinterpret_cast<const BlockRec*>(plan + group_blocks_offset(hdr->count, hdr->rows));
+  src.starts = reinterpret_cast<const WaveStart*>(
+      plan + group_waves_offset(hdr->count, hdr->rows, hdr->blocks));
+  src.recs = reinterpret_cast<const StripRec*>(
+      plan + group_recs_offset(hdr->count, hdr->rows, hdr->blocks));
   src.tokens = hdr->tokens;
-  const WaveStart* starts =
-      reinterpret_cast<const WaveStart*>(plan + group_starts_offset(hdr->count, hdr->rows));
-  const int lane = threadIdx.x & 63;
-  const int w = blockIdx.x * kGemvWaves + wave_id();
-  const WaveStart a = starts[w], b = starts[w + 1];
-  if (a.unit < b.unit) stream<S>(src, lut + lane, lane, src.start(a.item, a.tile), b.unit - a.unit);
-}
-
-static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
-
-GemvPlan plan_gemv(int64_t tokens, int64_t k, int64_t n_out) {
-  GemvPlan p;
-  const int64_t tiles = (n_out + kTileRows - 1) / kTileRows;
-  const int64_t nst = (k / kBlockK + 3) / 4;
-  int64_t ks = 1;
-  if (tiles < kResidentWaves) ks = (kResidentWaves + tiles - 1) / tiles;
-  if (ks > nst) ks = nst;
-  if (ks < 1) ks = 1;
-  const int64_t per = (nst + ks - 1) / ks;
-  ks = (nst + per - 1) / per;
-  p.ksplit = (int)ks;
-  p.st_per_unit = (int)per;
-  p.units = tiles * ks;
-  p.ws_bytes = ks > 1 ? align256((size_t)tokens * n_out * 4) + align256((size_t)tiles * 4) : 0;
-  return p;
-}
-
-size_t gemv_ws_bytes_max(int64_t tokens, int64_t k, int64_t n_out) {
-  return plan_gemv(tokens, k, n_out).ws_bytes;
+  run_block<S>(src, lut, threadIdx.x & 63);
 }
 
 template <int S>
 static hipError_t launch_gemv_s(const void* packed, const int8_t* xq, const float* scale,
-                                const double* gamma, float* Y, int32_t* acc, void* ws, int tokens,
-                                int64_t k, int64_t n_out, hipStream_t s) {
-  const GemvPlan p = plan_gemv(tokens, k, n_out);
-  SingleSrc src;
-  const int64_t nkb = k / kBlockK;
+                                const double* gamma, float* Y, int32_t* acc, void* ws,
+                                int tokens, int64_t k, int64_t n_out, hipStream_t s) {
+  SingleSrc<S> src;
   src.packed = packed;
   src.xq = xq;
-  src.x_bytes = (uint32_t)(tokens * k);
+  src.Y = Y;
+  src.acc = acc;
   src.scale = scale;
   src.gamma = gamma;
-  src.Y = Y;
-  src.acc_out = acc;
-  src.partial = nullptr;
-  src.tickets = nullptr;
-  if (p.ksplit > 1) {
-    src.partial = reinterpret_cast<int32_t*>(ws);
-    src.tickets = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) +
-                                              align256((size_t)tokens * n_out * 4));
-  }
-  src.units = p.units;
+  src.partial = reinterpret_cast<int32_t*>(ws);
+  src.tickets = reinterpret_cast<uint32_t*>(
+      reinterpret_cast<char*>(ws) + ((decode_partial_bytes(tokens, n_out) + 255) & ~(size_t)255));
+  src.k = k;
   src.n_out = n_out;
-  src.k = (int32_t)k;
-  src.nkb = (int32_t)nkb;
-  src.nst = (int32_t)((nkb + 3) / 4);
-  src.ksplit = p.ksplit;
-  src.st_per_unit = p.st_per_unit;
   src.tokens = tokens;
-  src.kbytes = block_bytes(S);
-  int64_t blocks = (p.units + kGemvWaves - 1) / kGemvWaves;
-  if (blocks > 256) blocks = 256;
-  gemv_kernel<S><<<(unsigned)blocks, kGemvThreads, 0, s>>>(src);
+  src.nkb = (int32_t)(k / kBlockK);
+  src.T = ((n_out + kStripRows - 1) / kStripRows) * src.nkb;
+  src.NB = decode_blocks(src.T);
+  gemv_kernel<S><<<(unsigned)src.NB, kGemvThreads, 0, s>>>(src);
   return hipGetLastError();
 }
 
@@ -464,9 +527,9 @@ hipError_t launch_gemv(const void* packed, const int8_t* xq, const float* scale,
 
 hipError_t launch_gemv_group(const void* plan, int S, hipStream_t s) {
   const char* p = reinterpret_cast<const char*>(plan);
-  if (S == 8) gemv_group_kernel<8><<<kGroupBlocks, kGemvThreads, 0, s>>>(p);
-  else if (S == 6) gemv_group_kernel<6><<<kGroupBlocks, kGemvThreads, 0, s>>>(p);
-  else gemv_group_kernel<4><<<kGroupBlocks, kGemvThreads, 0, s>>>(p);
+  if (S == 8) gemv_group_kernel<8><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
+  else if (S == 6) gemv_group_kernel<6><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
+  else gemv_group_kernel<4><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 

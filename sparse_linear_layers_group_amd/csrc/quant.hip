@@ -120,7 +120,7 @@ __device__ __forceinline__ uint32_t group_abs_sum(const uint32_t w[4], uint32_t 
     uint32_t sh = e - (uint32_t)kWinLo;
     bool in = sh < (uint32_t)kWin;
     sum += in ? (sig << sh) : 0u;
-    if (!in && a != 0u) atomicAdd(&ws->hist[e], (unsigned long long)sig);
+    if (!in && a != 0u) atomic_add_global(&ws->hist[e], (unsigned long long)sig);
   }
   return sum;
 }
@@ -197,25 +197,28 @@ __global__ __launch_bounds__(256) void mask_gamma_kernel(const uint4* __restrict
   acc = wave_sum_u64(acc);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (lane == 0) part[wave] = acc;
+  // every wavefront's histogram atomics are performed before the block's
+  // ticket (all the accumulators are device-scope atomics)
+  wait_memory_ops();
   __syncthreads();
   if (threadIdx.x == 0) {
     unsigned long long s = 0;
     for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += part[i];
-    if (s) atomicAdd(&ws->main, s);
-    __threadfence();
-    unsigned int t = atomicAdd(&ws->ticket, 1u);
+    if (s) atomic_add_global(&ws->main, s);
+    wait_memory_ops();
+    unsigned int t = atomic_fetch_add_global(&ws->ticket, 1u);
     last = (t == gridDim.x - 1);
   }
   __syncthreads();
   if (!last || threadIdx.x != 0) return;
-  // last block: every other block's atomics were made visible before its
-  // ticket increment; read the accumulators from L2 with atomics.
-  __threadfence();
+  // last block: every other block's atomics were performed before its
+  // ticket increment; read the accumulators with atomics as well.
+  wait_memory_ops();
   Big b;
   for (int i = 0; i < 10; ++i) b.limb[i] = 0;
-  big_add(b, atomicAdd(&ws->main, 0ull), kWinLo - 1);
+  big_add(b, atomic_fetch_add_global(&ws->main, 0ull), kWinLo - 1);
   for (int e = 0; e < 256; ++e) {
-    unsigned long long h = atomicAdd(&ws->hist[e], 0ull);
+    unsigned long long h = atomic_fetch_add_global(&ws->hist[e], 0ull);
     if (h) big_add(b, h, e > 0 ? e - 1 : 0);
   }
   *gamma = big_round(b) / count;
@@ -238,6 +241,48 @@ __device__ uint32_t code_threshold(double g) {
   return lo;
 }
 
+// field (8+S bits) and int8 codes (two words, positions 0..3 / 4..7) of one
+// 8-group: w = 8 bf16 values, keep = the group's mask byte
+template <int S>
+__device__ __forceinline__ uint32_t group_field(const uint4& v, uint32_t keep, uint32_t thr,
+                                                uint32_t& lo, uint32_t& hi) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t nz = 0, neg = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t h = (w[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+    uint32_t on = ((keep >> j) & 1u) & ((h & 0x7fffu) >= thr ? 1u : 0u);
+    nz |= on << j;
+    neg |= (on & (h >> 15)) << j;
+  }
+  // signs: low half from the bottom, high half from the top
+  uint32_t sign = 0;
+  int nlo = 0, nhi = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    if ((nz >> p) & 1u) { sign |= ((neg >> p) & 1u) << nlo; ++nlo; }
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    if ((nz >> (4 + p)) & 1u) { sign |= ((neg >> (4 + p)) & 1u) << (S - 1 - nhi); ++nhi; }
+  }
+  lo = 0;
+  hi = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t cl = ((nz >> j) & 1u) ? (((neg >> j) & 1u) ? 0xffu : 0x01u) : 0u;
+    uint32_t ch = ((nz >> (4 + j)) & 1u) ? (((neg >> (4 + j)) & 1u) ? 0xffu : 0x01u) : 0u;
+    lo |= cl << (8 * j);
+    hi |= ch << (8 * j);
+  }
+  return (nz & 0xfu) | (sign << 4) | ((nz >> 4) << (4 + S));
+}
+
+// One thread per packed chunk: it gathers the 16 (row, group) fields the
+// chunk holds (field_row / field_group), builds them from the latent
+// weights, the mask and gamma, and writes the chunk with plain stores; the
+// int8 codes of those groups go to wq when it is requested.  Padding rows
+// of the last strip give zero fields.
 template <int S, bool PACKED, bool WQ>
 __global__ __launch_bounds__(256) void ternary_pack_kernel(const uint16_t* __restrict__ W,
                                                           const uint8_t* __restrict__ mask,
@@ -248,74 +293,33 @@ __global__ __launch_bounds__(256) void ternary_pack_kernel(const uint16_t* __res
   constexpr int kWords = block_bytes(S) / 4;
   constexpr int kField = 8 + S;
   const int64_t nkb = k / kBlockK;
-  const int64_t tiles = (n_out + kTileRows - 1) / kTileRows;
-  const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (slot >= tiles * kTileRows * nkb) return;
-  const int64_t tile = slot / (kTileRows * nkb);
-  const int64_t rem = slot - tile * kTileRows * nkb;
-  const int64_t kb = rem / kTileRows;
-  const int64_t row = tile * kTileRows + (rem % kTileRows);
+  const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
+  const int64_t chunk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (chunk >= strips * nkb * kStripRows) return;
+  const int64_t sb = chunk / kStripRows;  // superblock = strip * nkb + kb
+  const int c = (int)(chunk - sb * kStripRows);
+  const int64_t strip = sb / nkb, kb = sb - strip * nkb;
+  const uint32_t thr = code_threshold(*gamma);
 
   uint32_t out[kWords];
 #pragma unroll
   for (int i = 0; i < kWords; ++i) out[i] = 0;
-
-  if (row < n_out) {
-    const uint32_t thr = code_threshold(*gamma);
-    const uint4* wrow = reinterpret_cast<const uint4*>(W + row * k + kb * kBlockK);
-    const uint4 mk = *reinterpret_cast<const uint4*>(mask + row * (k / 8) + kb * 16);
-    const uint32_t mw[4] = {mk.x, mk.y, mk.z, mk.w};
-    uint4 codes_out[8];
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      const uint4 v = wrow[g];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      const uint32_t keep = (mw[g >> 2] >> (8 * (g & 3))) & 0xffu;
-      uint32_t nz = 0, neg = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t h = (w[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-        uint32_t on = ((keep >> j) & 1u) & ((h & 0x7fffu) >= thr ? 1u : 0u);
-        nz |= on << j;
-        neg |= (on & (h >> 15)) << j;
-      }
-      // field: low bitmap, signs (low half from the bottom, high half
-      // from the top), high bitmap
-      uint32_t sign = 0;
-      int nlo = 0, nhi = 0;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        if ((nz >> p) & 1u) { sign |= ((neg >> p) & 1u) << nlo; ++nlo; }
-      }
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        if ((nz >> (4 + p)) & 1u) { sign |= ((neg >> (4 + p)) & 1u) << (S - 1 - nhi); ++nhi; }
-      }
-      const uint32_t field = (nz & 0xfu) | (sign << 4) | ((nz >> 4) << (4 + S));
-      const int off = g * kField;
-      out[off >> 5] |= field << (off & 31);
-      if ((off & 31) + kField > 32) out[(off >> 5) + 1] |= field >> (32 - (off & 31));
-      if (WQ) {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t cl = ((nz >> j) & 1u) ? (((neg >> j) & 1u) ? 0xffu : 0x01u) : 0u;
-          uint32_t ch = ((nz >> (4 + j)) & 1u) ? (((neg >> (4 + j)) & 1u) ? 0xffu : 0x01u) : 0u;
-          lo |= cl << (8 * j);
-          hi |= ch << (8 * j);
-        }
-        if (g & 1) { codes_out[g >> 1].z = lo; codes_out[g >> 1].w = hi; }
-        else { codes_out[g >> 1].x = lo; codes_out[g >> 1].y = hi; }
-      }
-    }
-    if (WQ) {
-      uint4* dst = reinterpret_cast<uint4*>(wq + row * k + kb * kBlockK);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i] = codes_out[i];
-    }
+  for (int f = 0; f < 16; ++f) {
+    const int64_t row = strip * kStripRows + field_row(c, f);
+    const int grp = field_group(c, f);
+    if (row >= n_out) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(W + row * k + kb * kBlockK + 8 * grp);
+    const uint32_t keep = mask[row * (k / 8) + kb * 16 + grp];
+    uint32_t lo, hi;
+    const uint32_t field = group_field<S>(v, keep, thr, lo, hi);
+    const int off = f * kField;
+    out[off >> 5] |= field << (off & 31);
+    if ((off & 31) + kField > 32) out[(off >> 5) + 1] |= field >> (32 - (off & 31));
+    if (WQ) *reinterpret_cast<uint2*>(wq + row * k + kb * kBlockK + 8 * grp) = make_uint2(lo, hi);
   }
   if (PACKED) {
-    uint32_t* dst = packed + slot * kWords;
+    uint32_t* dst = packed + chunk * kWords;
 #pragma unroll
     for (int i = 0; i < kWords; ++i) dst[i] = out[i];
   }
@@ -426,8 +430,8 @@ hipError_t launch_mask_gamma(const uint16_t* W, int64_t n_out, int64_t k, int n,
 template <int S>
 static hipError_t launch_tp(const uint16_t* W, const uint8_t* mask, const double* gamma,
                             int64_t n_out, int64_t k, void* packed, int8_t* wq, hipStream_t s) {
-  const int64_t slots = ((n_out + 15) / 16) * 16 * (k / kBlockK);
-  const unsigned blocks = (unsigned)((slots + 255) / 256);
+  const int64_t chunks = ((n_out + kStripRows - 1) / kStripRows) * kStripRows * (k / kBlockK);
+  const unsigned blocks = (unsigned)((chunks + 255) / 256);
   uint32_t* p = reinterpret_cast<uint32_t*>(packed);
   if (packed && wq)
     ternary_pack_kernel<S, true, true><<<blocks, 256, 0, s>>>(W, mask, gamma, n_out, k, p, wq);

@@ -96,12 +96,14 @@ PAT = [(8, 8, 8), (6, 8, 6), (4, 8, 4), (2, 4, 4)]
 @pytest.mark.parametrize("n,m,s", PAT)
 def test_s_and_size(n, m, s):
     assert oracle.s_of(n, m) == s
-    assert oracle.packed_bytes(40, 384, s) == 48 * 3 * 2 * (8 + s)
+    # 40 rows occupy one 64-row strip; 384 = 3 k-blocks
+    assert oracle.packed_bytes(40, 384, s) == 64 * 3 * 2 * (8 + s)
+    assert oracle.packed_bytes(130, 128, s) == 192 * 1 * 2 * (8 + s)
 
 
 @pytest.mark.parametrize("n,m,s", PAT)
 def test_round_trip_on_workload_codes(n, m, s):
-    W = synth.weights(40, 384, seed=50)  # 40 rows: last 16-row tile is partial
+    W = synth.weights(40, 384, seed=50)  # 40 rows: the 64-row strip is partial
     mb = oracle.mask(W, n, m)
     T = oracle.ternary(W, mb, oracle.gamma(W))
     P = oracle.pack(T, s)
@@ -133,10 +135,48 @@ def test_pack_rejects_too_many_nonzeros():
         oracle.pack(T, 6)
 
 
-def test_padding_rows_are_zero_bytes():
+def test_padding_rows_are_zero_fields():
+    """20 rows of +1 codes at 8:8: a field (16 bits) is 0xF00F (both
+    bitmaps full, no signs) for rows < 20 and zero for the padding rows.
+    Chunk c, field f holds row 16*(f//4) + c%16."""
     T = np.ones((20, 128), np.int8)
-    P = oracle.pack(T, 8).reshape(2, 1, 16, 32)  # 2 tiles x 1 block x 16 rows x 32 bytes
-    assert not P[1, 0, 4:].any() and P[1, 0, :4].all()
+    P = oracle.pack(T, 8).reshape(64, 16, 2)  # 64 chunks x 16 fields x 2 bytes
+    for c in range(64):
+        for f in range(16):
+            row = 16 * (f // 4) + c % 16
+            field = int(P[c, f, 0]) | int(P[c, f, 1]) << 8
+            assert field == (0xF00F if row < 20 else 0), (c, f, hex(field))
+
+
+def load_golden_layout():
+    cases = []
+    with open(os.path.join(GOLDEN, "pack_layout.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            shape, code, out = line.split(";")
+            n_out, k, s = (int(v) for v in shape.split())
+            c = [int(v) for v in code.split()]
+            o = out.split()
+            cases.append((n_out, k, s, [tuple(c[i:i + 3]) for i in range(0, len(c), 3)],
+                          {int(o[i]): int(o[i + 1], 16) for i in range(0, len(o), 2)}))
+    return cases
+
+
+def test_hand_derived_layout_placements():
+    """Single nonzero codes land at the byte worked out by hand from the
+    layout definition (tests/golden/pack_layout.txt); nothing else is set."""
+    cases = load_golden_layout()
+    assert len(cases) == 4
+    for n_out, k, s, codes, want in cases:
+        T = np.zeros((n_out, k), np.int8)
+        for row, col, val in codes:
+            T[row, col] = val
+        P = oracle.pack(T, s)
+        got = {int(i): int(P[i]) for i in np.nonzero(P)[0]}
+        assert got == want, (n_out, k, s, codes, got)
+        assert np.array_equal(oracle.unpack(P, n_out, k, s), T)
 
 
 def load_golden_fields():

@@ -37,6 +37,9 @@ MUTANTS = {
     "dw_drops_token_scale": ("j->scale[t] *", "1.0 *"),
     "pack_high_sign_order": ("sign |= 1u << (s - 1 - nhi);", "sign |= 1u << (nlo + nhi);"),
     "unpack_high_sign_order": ("((sign >> (s - 1 - nhi)) & 1u)", "((sign >> (nlo + nhi)) & 1u)"),
+    "layout_group_roles_swapped": ("int h = g / 8, q = (g % 8) / 2, e = g % 2;",
+                                   "int h = g % 2, q = (g % 8) / 2, e = g / 8;"),
+    "layout_chunks_transposed": ("* 64 + r16 + 16 * q;", "* 64 + q + 4 * r16;"),
 }
 
 
