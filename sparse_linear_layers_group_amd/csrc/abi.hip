@@ -259,8 +259,7 @@ int bitlinear_contract(const int8_t* xq, const float* x_scale, int64_t tokens, i
 size_t bitlinear_fwd_group_plan_bytes(const bitlinear_fwd_item* items, int count, int64_t tokens) {
   int64_t steps = 0, strips = 0;
   if (group_shape(items, count, tokens, &steps, &strips) != BL_OK) return 0;
-  const int64_t nb = group_blocks(steps, strips);
-  return bl::group_recs_offset(count, count * tokens, nb) + (size_t)strips * sizeof(bl::StripRec);
+  return bl::group_plan_bytes(strips, count, count * tokens);
 }
 
 int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t tokens, int n,
@@ -278,26 +277,25 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t
     TRY(check_ptr(it.x_scale, 4, "item x_scale"));
   }
   const int64_t nb = group_blocks(steps, nstrips);
-  const size_t need = bl::group_recs_offset(count, count * tokens, nb) +
-                      (size_t)nstrips * sizeof(bl::StripRec);
+  const size_t need = bl::group_plan_bytes(nstrips, count, count * tokens);
   TRY(check_ptr(plan, 16, "plan"));
   if (plan_bytes < need) return fail(BL_EWORKSPACE, "plan needs %zu bytes (got %zu)", need, plan_bytes);
+  const int S = bl::s_of(n, m);
   std::vector<char> img(need, 0);
   bl::GroupHeader* h = reinterpret_cast<bl::GroupHeader*>(img.data());
   h->count = count;
   h->tokens = (int32_t)tokens;
-  h->S = bl::s_of(n, m);
+  h->S = S;
   h->blocks = (int32_t)nb;
   h->rows = count * tokens;
   h->steps = steps;
-  bl::GroupItem* gi = reinterpret_cast<bl::GroupItem*>(img.data() + sizeof(bl::GroupHeader));
-  uint32_t* rows = reinterpret_cast<uint32_t*>(gi + count);
+  h->strips = nstrips;
+  bl::GroupItem* gi = reinterpret_cast<bl::GroupItem*>(img.data() + bl::group_items_offset(nstrips));
+  uint32_t* rows = reinterpret_cast<uint32_t*>(img.data() + bl::group_rows_offset(nstrips, count));
   int64_t r = 0;
-  // every strip of every item, with its step count
-  struct Strip {
-    int32_t item, strip, nkb;
-  };
-  std::vector<Strip> all;
+  // every strip of every item: its descriptor and step count
+  std::vector<bl::StripDesc> all;
+  std::vector<int32_t> nkb;
   all.reserve((size_t)nstrips);
   for (int i = 0; i < count; ++i) {
     const bitlinear_fwd_item& it = items[i];
@@ -305,15 +303,20 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t
                           it.xq, it.x_scale, it.k, it.n_out};
     for (int64_t t = 0; t < tokens; ++t) rows[r++] = ((uint32_t)i << 4) | (uint32_t)t;
     const int64_t strips = (it.n_out + bl::kStripRows - 1) / bl::kStripRows;
-    for (int64_t st = 0; st < strips; ++st)
-      all.push_back(Strip{i, (int32_t)st, (int32_t)(it.k / 128)});
+    const int64_t strip_bytes = (it.k / 128) * bl::kStripRows * bl::block_bytes(S);
+    for (int64_t st = 0; st < strips; ++st) {
+      all.push_back(bl::StripDesc{reinterpret_cast<const char*>(it.packed) + st * strip_bytes,
+                                  it.xq, it.Y, it.x_scale, it.gamma, it.n_out, (int32_t)it.k,
+                                  (int32_t)(st * bl::kStripRows)});
+      nkb.push_back((int32_t)(it.k / 128));
+    }
   }
   // whole strips to workgroups, longest first onto the least loaded (LPT);
   // each workgroup's list in (item, strip) order
   std::vector<int32_t> order(all.size());
   for (size_t j = 0; j < order.size(); ++j) order[j] = (int32_t)j;
   std::stable_sort(order.begin(), order.end(),
-                   [&](int32_t a, int32_t b) { return all[a].nkb > all[b].nkb; });
+                   [&](int32_t a, int32_t b) { return nkb[a] > nkb[b]; });
   typedef std::pair<int64_t, int32_t> Load;  // (steps so far, workgroup)
   std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
   for (int32_t b = 0; b < (int32_t)nb; ++b) heap.push(Load(0, b));
@@ -322,33 +325,34 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t
     Load l = heap.top();
     heap.pop();
     lists[(size_t)l.second].push_back(j);
-    l.first += all[j].nkb;
+    l.first += nkb[j];
     heap.push(l);
   }
-  bl::BlockRec* brec = reinterpret_cast<bl::BlockRec*>(
-      img.data() + bl::group_blocks_offset(count, count * tokens));
-  bl::WaveStart* wst = reinterpret_cast<bl::WaveStart*>(
-      img.data() + bl::group_waves_offset(count, count * tokens, nb));
-  bl::StripRec* recs = reinterpret_cast<bl::StripRec*>(
-      img.data() + bl::group_recs_offset(count, count * tokens, nb));
+  bl::WaveStart* wst = reinterpret_cast<bl::WaveStart*>(img.data() + bl::group_waves_offset());
+  bl::StripDesc* descs = reinterpret_cast<bl::StripDesc*>(img.data() + bl::group_strips_offset());
   int32_t next = 0;
   for (int64_t b = 0; b < nb; ++b) {
     std::vector<int32_t>& lst = lists[(size_t)b];
     std::sort(lst.begin(), lst.end());  // strip index order = (item, strip) order
     int64_t n_b = 0;
-    for (int32_t j : lst) n_b += all[j].nkb;
-    brec[b] = bl::BlockRec{next, (int32_t)n_b};
-    // wavefront w starts at local step n_b * w / 16
+    for (int32_t j : lst) n_b += nkb[j];
+    // wavefront w runs local steps [n_b * w / 16, n_b * (w + 1) / 16)
     size_t pos = 0;
     int64_t cum = 0;
     for (int w = 0; w < bl::kDecodeWavesPerBlock; ++w) {
-      const int64_t sw = n_b * w / bl::kDecodeWavesPerBlock;
-      while (pos + 1 < lst.size() && cum + all[lst[pos]].nkb <= sw) cum += all[lst[pos++]].nkb;
-      const int32_t rec = lst.empty() ? 0 : next + (int32_t)pos;
-      const int32_t kb = lst.empty() ? 0 : (int32_t)(sw - cum);
-      wst[b * bl::kDecodeWavesPerBlock + w] = bl::WaveStart{rec, kb};
+      const int64_t s0 = n_b * w / bl::kDecodeWavesPerBlock;
+      const int64_t s1 = n_b * (w + 1) / bl::kDecodeWavesPerBlock;
+      while (pos + 1 < lst.size() && cum + nkb[lst[pos]] <= s0) cum += nkb[lst[pos++]];
+      bl::WaveStart& ws = wst[b * bl::kDecodeWavesPerBlock + w];
+      ws.active = n_b > 0 ? 1 : 0;
+      ws.count = (int32_t)(s1 - s0);
+      if (!lst.empty()) {
+        ws.first = all[lst[pos]];
+        ws.rec = next + (int32_t)pos;
+        ws.kb = (int32_t)(s0 - cum);
+      }
     }
-    for (int32_t j : lst) recs[next++] = bl::StripRec{all[j].item, all[j].strip};
+    for (int32_t j : lst) descs[next++] = all[j];
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(plan, img.data(), need, hipMemcpyHostToDevice, s);

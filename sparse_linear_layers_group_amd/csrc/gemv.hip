@@ -75,10 +75,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// what a wavefront needs of one GEMV (wave-uniform, scalar registers)
-struct ItemView {
-  __amdgpu_buffer_rsrc_t pk, xr;  // packed weights / int8 activations
-  int32_t k, nkb, strips;
+// what a wavefront needs of the strip it streams (wave-uniform, scalar
+// registers)
+struct StripView {
+  __amdgpu_buffer_rsrc_t pk, xr;  // the strip's superblocks / the item's activations
+  int32_t k, nkb, row0;
   int64_t n_out;
   float* Y;
   int32_t* acc;  // optional int32 sums
@@ -87,29 +88,30 @@ struct ItemView {
 };
 
 template <int S>
-__device__ __forceinline__ ItemView make_view(const void* packed, const int8_t* xq, int tokens,
-                                              int64_t k, int64_t n_out) {
-  ItemView v;
-  v.k = (int32_t)k;
-  v.nkb = (int32_t)(k / kBlockK);
+__device__ __forceinline__ StripView make_strip(const char* strip_packed, const int8_t* xq,
+                                                int tokens, int32_t k, int64_t n_out,
+                                                int32_t row0) {
+  StripView v;
+  v.k = k;
+  v.nkb = k / kBlockK;
+  v.row0 = row0;
   v.n_out = n_out;
-  v.strips = (int32_t)((n_out + kStripRows - 1) / kStripRows);
-  v.pk = rsrc(packed, (uint32_t)((int64_t)v.strips * v.nkb * kStripRows * block_bytes(S)));
+  v.pk = rsrc(strip_packed, (uint32_t)(v.nkb * kStripRows * block_bytes(S)));
   v.xr = rsrc(xq, (uint32_t)(tokens * k));
   return v;
 }
 
 // position in a workgroup's list; sid numbers the strips of the list
 struct Cursor {
-  ItemView it;
-  int32_t item, strip, kb, sid;
+  StripView sv;
+  int32_t kb, sid;
 };
 
-// One step in flight: packed words, the B operand, and the token scale and
-// gamma of the step's item.  The two small scale loads ride with every step
-// (they hit the caches), so a strip's epilogue only needs data its own step
-// already waited for: a wait on any later load would also drain the steps
-// loaded behind it, since loads complete in order.
+// One step in flight: packed words, the B operand, and -- for the first
+// step of a strip -- the strip's token scale and gamma.  Those two small
+// loads ride with that step, and the compute cursor takes them when it
+// decodes it, so a strip's epilogue never waits on a later load (which
+// would also drain the steps loaded behind it: loads complete in order).
 template <int S>
 struct Stage {
   uint32_t w[block_bytes(S) / 4];
@@ -122,37 +124,41 @@ template <int S>
 __device__ __forceinline__ void issue(Stage<S>& st, const Cursor& cur, bool live, int lane,
                                       int tokens) {
   constexpr int kBytes = block_bytes(S);
-  const uint32_t sb = (uint32_t)(cur.strip * cur.it.nkb + cur.kb);
-  const uint32_t po = live ? (sb * kStripRows + (uint32_t)lane) * kBytes : kOOB;
+  const uint32_t po = live ? ((uint32_t)cur.kb * kStripRows + (uint32_t)lane) * kBytes : kOOB;
   uint32_t* w = st.w;
   if constexpr (kBytes == 32) {
-    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cur.it.pk, po, 0, 0);
-    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(cur.it.pk, po + 16, 0, 0);
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cur.sv.pk, po, 0, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(cur.sv.pk, po + 16, 0, 0);
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
   } else if constexpr (kBytes == 28) {
     typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
-    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cur.it.pk, po, 0, 0);
-    const u32x3 b = __builtin_amdgcn_raw_buffer_load_b96(cur.it.pk, po + 16, 0, 0);
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cur.sv.pk, po, 0, 0);
+    const u32x3 b = __builtin_amdgcn_raw_buffer_load_b96(cur.sv.pk, po + 16, 0, 0);
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y; w[6] = b.z;
   } else {
-    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cur.it.pk, po, 0, 0);
-    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(cur.it.pk, po + 16, 0, 0);
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cur.sv.pk, po, 0, 0);
+    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(cur.sv.pk, po + 16, 0, 0);
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y;
   }
   // B operand of k half h: token t = lane%16, k slice lane/16.  Columns
   // t >= tokens are never stored, so those lanes read token 0 (in range).
   const int t = lane & 15, g = lane >> 4;
-  const uint32_t xo = (uint32_t)((t < tokens ? t : 0) * cur.it.k + cur.kb * kBlockK + 16 * g);
+  const uint32_t xo = (uint32_t)((t < tokens ? t : 0) * cur.sv.k + cur.kb * kBlockK + 16 * g);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(cur.it.xr, xo + 64 * h, 0, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(cur.sv.xr, xo + 64 * h, 0, 0);
     st.b[h] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
   }
-  st.sc = ld_global(&cur.it.scale[t < tokens ? t : 0]);
-  st.gm = ld_global(cur.it.gamma);
+}
+
+template <int S>
+__device__ __forceinline__ void issue_scale(Stage<S>& st, const Cursor& cur, int lane, int tokens) {
+  const int t = lane & 15;
+  st.sc = ld_global(&cur.sv.scale[t < tokens ? t : 0]);
+  st.gm = ld_global(cur.sv.gamma);
 }
 
 // A operand of MFMA m = 2i + h: codes of fields 2m and 2m+1 of the chunk
@@ -187,8 +193,9 @@ __device__ __forceinline__ void decode_step(const Stage<S>& st, v4i* c, const ui
 }
 
 // Outputs of lane (t, g) for one strip: rows row0 + 16i + 4g + j.
-__device__ __forceinline__ void store_strip(const ItemView& it, int64_t row0, const v4i* c,
-                                            int lane, int tokens, float gs) {
+__device__ __forceinline__ void store_strip(const StripView& it, const v4i* c, int lane,
+                                            int tokens, float gs) {
+  const int64_t row0 = it.row0;
   const int t = lane & 15, g = lane >> 4;
   if (t >= tokens) return;
   const int64_t o = (int64_t)t * it.n_out + row0 + 4 * g;
@@ -214,7 +221,7 @@ __device__ __forceinline__ void store_strip(const ItemView& it, int64_t row0, co
   }
 }
 
-__device__ __forceinline__ float item_scale(const ItemView& it, int lane, int tokens) {
+__device__ __forceinline__ float strip_scale(const StripView& it, int lane, int tokens) {
   const int t = lane & 15;
   return out_scale(ld_global(it.gamma), ld_global(&it.scale[t < tokens ? t : 0]));
 }
@@ -225,17 +232,21 @@ struct WaveRange {
   int64_t count;
 };
 
-// Run one workgroup.  A source policy provides tokens, item(idx),
-// advance(cursor), range(w) -- the first step and step count of wavefront
-// w of this workgroup -- and cross()/cross_sum() for strips that continue
-// in another workgroup.
+// Run one workgroup.  A source policy provides tokens, strip(sid) (the view
+// of strip sid of the list), advance(cursor), range(w) -- the first step
+// and step count of wavefront w of this workgroup -- and cross()/
+// cross_sum() for strips that continue in another workgroup.
 template <int S, class Src>
-__device__ __forceinline__ void run_block(const Src& src, uint32_t* lut, int lane) {
+__device__ __forceinline__ void run_block(const Src& src, uint32_t* lut, uint32_t* entries,
+                                          int lane) {
   const int tokens = src.tokens;
   const int w = wave_id();
   const uint32_t* lut_lane = lut + lane;
   const WaveRange wr = src.range(w);
   const int64_t count = wr.count;
+  // lane v < 16 holds wavefront v's (first strip, first k block, step count),
+  // fetched now and read with readlane by the end phase (no loads there)
+  const v4i winfo = src.wave_info(lane & 15);
   Cursor L = wr.first, C = wr.first;
   int64_t lleft = count, cleft = count;
   bool live = count > 0;
@@ -248,43 +259,56 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut, int lan
     cf[i] = v4i{0, 0, 0, 0};
   }
   bool ended_mid = false;
-  int32_t last_sid = -1, last_item = 0, last_strip = 0;
+  int32_t last_sid = -1;
+  Stage<S> ring[kDepth];
+  // once the load cursor has issued the last step it stops for good:
+  // advance() may read the plan, and must never step past the range
+  bool l_first = true, c_first = true;
+  float cur_sc = 0.f;
+  double cur_gm = 0.0;
+  auto load_step = [&](Stage<S>& st) {
+    issue<S>(st, L, live, lane, tokens);
+    if (L.kb == 0 || l_first) issue_scale<S>(st, L, lane, tokens);  // wave-uniform
+    l_first = false;
+    if (live) {
+      if (--lleft == 0) live = false;
+      else src.advance(L);
+    }
+  };
+  // the first steps' loads are in flight while the workgroup builds the
+  // code tables
   if (count > 0) {
-    Stage<S> ring[kDepth];
-    // once the load cursor has issued the last step it stops for good:
-    // advance() may read the plan, and must never step past the range
-    auto load_step = [&](Stage<S>& st) {
-      issue<S>(st, L, live, lane, tokens);
-      if (live) {
-        if (--lleft == 0) live = false;
-        else src.advance(L);
-      }
-    };
 #pragma unroll
     for (int s = 0; s < kDepth - 1; ++s) load_step(ring[s]);
+  }
+  fill_lut(lut, entries);
+  __syncthreads();
+  if (count > 0) {
     while (cleft > 0) {
 #pragma unroll
       for (int s = 0; s < kDepth; ++s) {
         load_step(ring[(s + kDepth - 1) % kDepth]);
         decode_step<S>(ring[s], c, lut_lane);
+        if (C.kb == 0 || c_first) {  // the strip's scales came with this step
+          cur_sc = ring[s].sc;
+          cur_gm = ring[s].gm;
+          c_first = false;
+        }
         --cleft;
-        if (C.kb == C.it.nkb - 1) {  // strip end
+        if (C.kb == C.sv.nkb - 1) {  // strip end
           if (first_open) {
             // the tail of a strip begun by an earlier wavefront: keep it
 #pragma unroll
             for (int i = 0; i < 4; ++i) cf[i] = c[i];
             first_open = false;
           } else {
-            store_strip(C.it, (int64_t)C.strip * kStripRows, c, lane, tokens,
-                        out_scale(ring[s].gm, ring[s].sc));
+            store_strip(C.sv, c, lane, tokens, out_scale(cur_gm, cur_sc));
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) c[i] = v4i{0, 0, 0, 0};
         } else if (cleft == 0) {
           ended_mid = true;
           last_sid = C.sid;
-          last_item = C.item;
-          last_strip = C.strip;
         }
         if (cleft == 0) break;
         src.advance(C);
@@ -316,32 +340,34 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut, int lan
 #pragma unroll
     for (int i = 0; i < 4; ++i) tot[i] = last ? c[i] : v4i{0, 0, 0, 0};
     const int32_t sid = last ? last_sid : wr.first.sid;
-    const int32_t item = last ? last_item : wr.first.item;
-    const int32_t strip = last ? last_strip : wr.first.strip;
     for (int v = last ? w + 1 : 0; v < kGemvWaves; ++v) {
-      const WaveRange o = src.range(v);
-      if (o.count == 0) continue;
-      if (o.first.sid != sid || o.first.kb == 0) break;
+      const int32_t v_sid = __builtin_amdgcn_readlane(winfo[0], v);
+      const int32_t v_kb = __builtin_amdgcn_readlane(winfo[1], v);
+      const int32_t v_count = __builtin_amdgcn_readlane(winfo[2], v);
+      if (v_count == 0) continue;
+      if (v_sid != sid || v_kb == 0) break;
       if (t < tokens) {
         const int32_t* q = slots + v * kSlotDwords + t * kStripRows + 4 * g;
 #pragma unroll
         for (int i = 0; i < 4; ++i) tot[i] += *reinterpret_cast<const v4i*>(q + 16 * i);
       }
     }
-    const ItemView it = src.item(item);
+    // the cursor still holds the view of the last strip; wavefront 0 the
+    // view of its first
+    const StripView sv = last ? C.sv : wr.first.sv;
     if (src.cross(sid))
-      src.cross_sum(it, strip, tot, lane);
+      src.cross_sum(sv, sid, tot, lane);
     else
-      store_strip(it, (int64_t)strip * kStripRows, tot, lane, tokens, item_scale(it, lane, tokens));
+      store_strip(sv, tot, lane, tokens, strip_scale(sv, lane, tokens));
   }
 }
 
 // ---------------------------------------------------------------- single call
 // T = strips * nkb steps cut into NB equal workgroup ranges; a strip cut by
-// a workgroup boundary meets in the workspace.
+// a workgroup boundary meets in the workspace.  sid = strip index.
 template <int S>
 struct SingleSrc {
-  const void* packed;
+  const char* packed;
   const int8_t* xq;
   float* Y;
   int32_t* acc;
@@ -349,11 +375,12 @@ struct SingleSrc {
   const double* gamma;
   int32_t* partial;   // [strips][tokens][64]
   uint32_t* tickets;  // [strips]
-  int64_t k, n_out, T, NB;
+  int64_t n_out, T, NB;
+  int32_t k, nkb;
   int tokens;
-  int32_t nkb;
-  __device__ ItemView item(int32_t) const {
-    ItemView v = make_view<S>(packed, xq, tokens, k, n_out);
+  __device__ StripView strip(int32_t sid) const {
+    StripView v = make_strip<S>(packed + (int64_t)sid * nkb * kStripRows * block_bytes(S), xq,
+                                tokens, k, n_out, sid * kStripRows);
     v.Y = Y;
     v.acc = acc;
     v.scale = scale;
@@ -361,10 +388,9 @@ struct SingleSrc {
     return v;
   }
   __device__ void advance(Cursor& c) const {
-    if (++c.kb == c.it.nkb) {
+    if (++c.kb == nkb) {
       c.kb = 0;
-      ++c.strip;
-      ++c.sid;
+      c.sv = strip(++c.sid);
     }
   }
   __device__ WaveRange range(int w) const {
@@ -373,12 +399,18 @@ struct SingleSrc {
     const int64_t s0 = b0 + n * w / kGemvWaves, s1 = b0 + n * (w + 1) / kGemvWaves;
     WaveRange r;
     r.count = s1 - s0;
-    r.first.it = item(0);
-    r.first.item = 0;
-    r.first.strip = (int32_t)(s0 / nkb);
-    r.first.kb = (int32_t)(s0 - (int64_t)r.first.strip * nkb);
-    r.first.sid = r.first.strip;
+    r.first.sid = (int32_t)(s0 / nkb);
+    r.first.kb = (int32_t)(s0 - (int64_t)r.first.sid * nkb);
+    r.first.sv = strip(r.first.sid);
     return r;
+  }
+  // (first strip, first k block, step count) of wavefront v
+  __device__ v4i wave_info(int v) const {
+    const int64_t b = blockIdx.x;
+    const int64_t b0 = T * b / NB, n = T * (b + 1) / NB - b0;
+    const int64_t s0 = b0 + n * v / kGemvWaves, s1 = b0 + n * (v + 1) / kGemvWaves;
+    const int32_t sid = (int32_t)(s0 / nkb);
+    return v4i{sid, (int32_t)(s0 - (int64_t)sid * nkb), (int32_t)(s1 - s0), 0};
   }
   // does strip `sid` continue in another workgroup?
   __device__ bool cross(int32_t sid) const {
@@ -387,9 +419,9 @@ struct SingleSrc {
     return a < T * b / NB || e > T * (b + 1) / NB;
   }
   // add this workgroup's part of the strip; the last workgroup writes it
-  __device__ void cross_sum(const ItemView& it, int32_t strip, const v4i* tot, int lane) const {
+  __device__ void cross_sum(const StripView& sv, int32_t sid, const v4i* tot, int lane) const {
     const int t = lane & 15, g = lane >> 4;
-    int32_t* p = partial + ((int64_t)strip * tokens + (t < tokens ? t : 0)) * kStripRows + 4 * g;
+    int32_t* p = partial + ((int64_t)sid * tokens + (t < tokens ? t : 0)) * kStripRows + 4 * g;
     if (t < tokens) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -397,12 +429,12 @@ struct SingleSrc {
         for (int j = 0; j < 4; ++j)
           if (tot[i][j] != 0) atomic_add_global(p + 16 * i + j, (int32_t)tot[i][j]);
     }
-    const int64_t a = (int64_t)strip * nkb, e = a + nkb - 1;
+    const int64_t a = (int64_t)sid * nkb, e = a + nkb - 1;
     const int64_t blocks = block_of_step(e, T, NB) - block_of_step(a, T, NB) + 1;
     // every partial sum of this workgroup's part is performed before its ticket
     wait_memory_ops();
     uint32_t tk = 0;
-    if (lane == 0) tk = atomic_fetch_add_global(&tickets[strip], 1u);
+    if (lane == 0) tk = atomic_fetch_add_global(&tickets[sid], 1u);
     tk = __shfl(tk, 0, 64);
     if ((int64_t)tk != blocks - 1) return;
     wait_memory_ops();
@@ -412,85 +444,71 @@ struct SingleSrc {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         sum[i][j] = t < tokens ? atomic_exchange_global(p + 16 * i + j, 0) : 0;
-    store_strip(it, (int64_t)strip * kStripRows, sum, lane, tokens, item_scale(it, lane, tokens));
-    if (lane == 0) atomic_exchange_global(&tickets[strip], 0u);
+    store_strip(sv, sum, lane, tokens, strip_scale(sv, lane, tokens));
+    if (lane == 0) atomic_exchange_global(&tickets[sid], 0u);
   }
 };
 
 // --------------------------------------------------------------- grouped
+// sid = index of the strip descriptor in the plan
 template <int S>
 struct GroupSrc {
-  const GroupItem* items;
-  const StripRec* recs;
-  const BlockRec* blocks;
+  const StripDesc* strips;
   const WaveStart* starts;
   int tokens;
-  __device__ ItemView item(int32_t idx) const {
-    const GroupItem& gi = items[idx];
-    ItemView v = make_view<S>(gi.packed, gi.xq, tokens, gi.k, gi.n_out);
-    v.Y = gi.Y;
+  __device__ StripView view(const StripDesc& d) const {
+    StripView v = make_strip<S>(d.packed, d.xq, tokens, d.k, d.n_out, d.row0);
+    v.Y = d.Y;
     v.acc = nullptr;
-    v.scale = gi.scale;
-    v.gamma = gi.gamma;
+    v.scale = d.scale;
+    v.gamma = d.gamma;
     return v;
   }
-  __device__ void set_rec(Cursor& c, int32_t rec) const {
-    const StripRec r = recs[rec];
-    c.sid = rec;
-    c.strip = r.strip;
-    if (r.item != c.item) {
-      c.item = r.item;
-      c.it = item(r.item);
-    }
-  }
+  __device__ StripView strip(int32_t sid) const { return view(strips[sid]); }
   __device__ void advance(Cursor& c) const {
-    if (++c.kb == c.it.nkb) {
+    if (++c.kb == c.sv.nkb) {
       c.kb = 0;
-      set_rec(c, c.sid + 1);
+      c.sv = strip(++c.sid);
     }
   }
   __device__ WaveRange range(int w) const {
-    const BlockRec br = blocks[blockIdx.x];
-    const int64_t n = br.steps;
+    const WaveStart& ws = starts[(int64_t)blockIdx.x * kGemvWaves + w];
     WaveRange r;
-    r.count = n * (w + 1) / kGemvWaves - n * w / kGemvWaves;
-    const WaveStart ws = starts[(int64_t)blockIdx.x * kGemvWaves + w];
-    r.first.item = -1;
-    set_rec(r.first, ws.rec);
+    r.count = ws.count;
+    r.first.sid = ws.rec;
     r.first.kb = ws.kb;
+    r.first.sv = view(ws.first);
     return r;
+  }
+  // (first strip, first k block, step count) of wavefront v: the 16 bytes
+  // after the wave start's descriptor
+  __device__ v4i wave_info(int v) const {
+    return ld_global(reinterpret_cast<const v4i*>(&starts[(int64_t)blockIdx.x * kGemvWaves + v].rec));
   }
   // the plan never cuts a strip between workgroups
   __device__ bool cross(int32_t) const { return false; }
-  __device__ void cross_sum(const ItemView&, int32_t, const v4i*, int) const {}
+  __device__ void cross_sum(const StripView&, int32_t, const v4i*, int) const {}
 };
 
 template <int S>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(SingleSrc<S> src) {
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 2 * kLutCopies];
   __shared__ uint32_t entries[512];
-  fill_lut(lut, entries);
-  __syncthreads();
-  run_block<S>(src, lut, threadIdx.x & 63);
+  run_block<S>(src, lut, entries, threadIdx.x & 63);
 }
 
 template <int S>
 __global__ __launch_bounds__(kGemvThreads) void gemv_group_kernel(const char* __restrict__ plan) {
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 2 * kLutCopies];
   __shared__ uint32_t entries[512];
-  const GroupHeader* hdr = reinterpret_cast<const GroupHeader*>(plan);
-  if ((int)blockIdx.x >= hdr->blocks) return;  // whole workgroup
-  fill_lut(lut, entries);
-  __syncthreads();
   GroupSrc<S> src;
-  src.items = reinterpret_cast<const GroupItem*>(plan + sizeof(GroupHeader));
-  src.blocks = reinterpret_cast<const BlockRec*>(plan + group_blocks_offset(hdr->count, hdr->rows));
-  src.starts = reinterpret_cast<const WaveStart*>(
-      plan + group_waves_offset(hdr->count, hdr->rows, hdr->blocks));
-  src.recs = reinterpret_cast<const StripRec*>(
-      plan + group_recs_offset(hdr->count, hdr->rows, hdr->blocks));
-  src.tokens = hdr->tokens;
-  run_block<S>(src, lut, threadIdx.x & 63);
+  src.starts = reinterpret_cast<const WaveStart*>(plan + group_waves_offset());
+  // every wavefront of a workgroup reads the same flag: the whole workgroup
+  // leaves or stays
+  if (!src.starts[(int64_t)blockIdx.x * kGemvWaves].active) return;
+  src.strips = reinterpret_cast<const StripDesc*>(plan + group_strips_offset());
+  src.tokens = reinterpret_cast<const GroupHeader*>(plan)->tokens;
+  run_block<S>(src, lut, entries, threadIdx.x & 63);
 }
 
 template <int S>
@@ -498,7 +516,7 @@ static hipError_t launch_gemv_s(const void* packed, const int8_t* xq, const floa
                                 const double* gamma, float* Y, int32_t* acc, void* ws,
                                 int tokens, int64_t k, int64_t n_out, hipStream_t s) {
   SingleSrc<S> src;
-  src.packed = packed;
+  src.packed = reinterpret_cast<const char*>(packed);
   src.xq = xq;
   src.Y = Y;
   src.acc = acc;
@@ -507,7 +525,7 @@ static hipError_t launch_gemv_s(const void* packed, const int8_t* xq, const floa
   src.partial = reinterpret_cast<int32_t*>(ws);
   src.tickets = reinterpret_cast<uint32_t*>(
       reinterpret_cast<char*>(ws) + ((decode_partial_bytes(tokens, n_out) + 255) & ~(size_t)255));
-  src.k = k;
+  src.k = (int32_t)k;
   src.n_out = n_out;
   src.tokens = tokens;
   src.nkb = (int32_t)(k / kBlockK);

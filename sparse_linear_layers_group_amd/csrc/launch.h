@@ -62,11 +62,14 @@ hipError_t launch_gemv(const void* packed, const int8_t* xq, const float* scale,
 // the token count and N:M pattern; kernels read it, so a run needs only the
 // plan pointer.  The plan hands every workgroup a list of whole strips
 // (packed on the host for equal step counts), so no strip is cut between
-// workgroups.
+// workgroups.  Each strip of the list is a self-contained descriptor, and
+// each wavefront's start record carries its first one, so a wavefront
+// starts streaming after a single scalar load.
 struct GroupHeader {
   int32_t count, tokens, S, blocks;
-  int64_t rows;   // activation rows = count * tokens
-  int64_t steps;  // superblocks over all items
+  int64_t rows;    // activation rows = count * tokens
+  int64_t steps;   // superblocks over all items
+  int64_t strips;  // strip descriptors
 };
 struct GroupItem {
   const uint16_t* X;
@@ -77,28 +80,43 @@ struct GroupItem {
   float* scale;
   int64_t k, n_out;
 };
-struct StripRec {  // one strip of the list: (item, strip within the item)
-  int32_t item, strip;
+struct StripDesc {            // one 64-row strip of one item (64 bytes)
+  const char* packed;         // the strip's first superblock
+  const int8_t* xq;           // the item's int8 activations [tokens][k]
+  float* Y;                   // the item's outputs [tokens][n_out]
+  const float* scale;         // the item's token scales
+  const double* gamma;        // the item's weight scale
+  int64_t n_out;
+  int32_t k;
+  int32_t row0;               // first row of the strip
+  int32_t pad[2];
 };
-struct BlockRec {  // a workgroup's list: first strip record and step count
-  int32_t first, steps;
+static_assert(sizeof(StripDesc) == 64, "strip descriptor size");
+struct WaveStart {            // a wavefront's range (80 bytes)
+  StripDesc first;            // its first strip
+  int32_t rec, kb;            // that strip's list index and the first k block
+  int32_t count;              // steps of the range (0: idle wavefront)
+  int32_t active;             // the workgroup has work
 };
-struct WaveStart {  // a wavefront's first step: strip record and k block
-  int32_t rec, kb;
-};
-// plan image: header | items[count] | row table[rows] | pad to 64 |
-//             blocks[blocks] | wave starts[blocks * 16] | strip records
+static_assert(sizeof(WaveStart) == 80, "wave start size");
+static_assert(offsetof(WaveStart, rec) == 64, "rec, kb, count, active: one 16-byte load");
+// plan image: header (64 bytes) | wave starts[kDecodeBlocks * 16] |
+//             strip descriptors | items[count] | row table[rows]
 // row entry = item << 4 | token
-__host__ __device__ inline size_t group_blocks_offset(int64_t count, int64_t rows) {
-  size_t o = sizeof(GroupHeader) + (size_t)count * sizeof(GroupItem) + (size_t)rows * 4;
-  return (o + 63) & ~(size_t)63;
+constexpr size_t kGroupHeaderBytes = 64;
+static_assert(sizeof(GroupHeader) <= kGroupHeaderBytes, "plan header size");
+__host__ __device__ inline size_t group_waves_offset() { return kGroupHeaderBytes; }
+__host__ __device__ inline size_t group_strips_offset() {
+  return kGroupHeaderBytes + (size_t)kDecodeBlocks * kDecodeWavesPerBlock * sizeof(WaveStart);
 }
-__host__ __device__ inline size_t group_waves_offset(int64_t count, int64_t rows, int64_t blocks) {
-  return group_blocks_offset(count, rows) + (size_t)blocks * sizeof(BlockRec);
+__host__ __device__ inline size_t group_items_offset(int64_t strips) {
+  return group_strips_offset() + (size_t)strips * sizeof(StripDesc);
 }
-__host__ __device__ inline size_t group_recs_offset(int64_t count, int64_t rows, int64_t blocks) {
-  return group_waves_offset(count, rows, blocks) +
-         (size_t)blocks * kDecodeWavesPerBlock * sizeof(WaveStart);
+__host__ __device__ inline size_t group_rows_offset(int64_t strips, int64_t count) {
+  return group_items_offset(strips) + (size_t)count * sizeof(GroupItem);
+}
+inline size_t group_plan_bytes(int64_t strips, int64_t count, int64_t rows) {
+  return group_rows_offset(strips, count) + (size_t)rows * 4;
 }
 hipError_t launch_act_quant_group(const void* plan, hipStream_t s);
 hipError_t launch_gemv_group(const void* plan, int S, hipStream_t s);

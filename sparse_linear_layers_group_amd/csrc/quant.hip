@@ -388,8 +388,9 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
 __global__ __launch_bounds__(256) void act_quant_group_kernel(const char* __restrict__ plan) {
   __shared__ float red[8];
   const GroupHeader* hdr = reinterpret_cast<const GroupHeader*>(plan);
-  const GroupItem* items = reinterpret_cast<const GroupItem*>(plan + sizeof(GroupHeader));
-  const uint32_t* rows = reinterpret_cast<const uint32_t*>(items + hdr->count);
+  const GroupItem* items = reinterpret_cast<const GroupItem*>(plan + group_items_offset(hdr->strips));
+  const uint32_t* rows =
+      reinterpret_cast<const uint32_t*>(plan + group_rows_offset(hdr->strips, hdr->count));
   for (int64_t r = blockIdx.x; r < hdr->rows; r += gridDim.x) {
     const uint32_t e = rows[r];
     const GroupItem it = items[e >> 4];
