@@ -1,24 +1,55 @@
 // gemm.hip -- prefill-shaped BitLinear contraction (many tokens) on gfx950.
 //
 // acc[t, r] = sum_c x_q[t, c] * code[r, c];  Y = acc * gamma * s_t.
-// The ternary codes are decoded once per 128-wide k block into an LDS tile
-// and reused by every token row of the workgroup, so the decode cost is
-// amortised over the token dimension and the loop is bound by the int8
-// matrix cores (v_mfma_i32_16x16x64_i8).  The pages' custom sparse operator
+// The ternary codes are decoded once per k step into an LDS tile and reused
+// by every token of the workgroup, so the decode cost is amortised over the
+// token dimension and the loop is bound by the int8 matrix cores
+// (v_mfma_i32_16x16x64_i8).  The pages' custom sparse operator
 // (Sparse-BitNet article §四) gains from hardware 6:8 support on other
 // hardware; gfx950 has no 6:8 matrix instruction, so the dense int8 MFMA
 // multiplies the pruned zeros and the format only saves weight bytes.
 //
-// Tile: 128 tokens x 128 weight rows per workgroup of 4 wavefronts (2 x 2,
-// 64 x 64 each, 4 x 4 MFMA tiles of 16 x 16), k step 128.
+// Workgroup tile: 128 weight rows x BT tokens (BT = 256 or 128), 4
+// wavefronts (2 along rows x 2 along tokens), each 64 rows x BT/2 tokens.
+// The codes are the MFMA A operand and the activations the B operand, so
+// each lane's results are 4 consecutive rows of one token: one 16-byte
+// store.  k advances 64 at a time through double-buffered LDS tiles (rows
+// padded to 80 bytes: the 16-byte operand reads of a quarter wavefront hit
+// 16 distinct 4-bank groups).  While the MFMAs of step j run, the
+// workgroup has the activations of step j+1 in flight and decodes its codes
+// from packed chunks held in registers; one barrier per step.
 #include "common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace bl {
 
-constexpr int kBM = 128, kBN = 128, kPitch = 144;  // LDS row pitch in bytes
+constexpr int kGBN = 128;       // weight rows per workgroup
+constexpr int kGKS = 64;        // k per step
+constexpr int kGPitch = 80;     // LDS row pitch in bytes
+constexpr int kGLutCopies = 8;  // copies of the decode tables (fewer bank conflicts)
 
-template <int S>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t g_rsrc(const void* p, int64_t bytes) {
+  const int64_t b = bytes < 0x7fffffff ? bytes : 0x7fffffff;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)b, 0x00020000);
+}
+
+// decode fields F0, F0+1 of a chunk held in w[0..kW] (w[kW] = 0) into the
+// code tile: field f is row 16*(f/4) + (c%16) of superblock sb, k bytes
+// 16*(c/16) + 8*(f%2) of the step
+template <int S, int F0>
+__device__ __forceinline__ void decode_pair(const uint32_t* w, const uint32_t* lut_lane, int8_t* Cs,
+                                            int sb, int c) {
+  auto lk = [&](uint32_t key, int half) { return lut_lane[(key * 2 + half) * kGLutCopies]; };
+  auto emit = [&](int f, uint32_t lo, uint32_t hi) {
+    const int row = sb * kStripRows + 16 * (f >> 2) + (c & 15);
+    *reinterpret_cast<uint2*>(Cs + row * kGPitch + 16 * (c >> 4) + 8 * (f & 1)) = make_uint2(lo, hi);
+  };
+  decode_groups<S, F0, 2>(w, lk, emit);
+}
+
+template <int S, int BT>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint32_t* __restrict__ packed,
                                                   const int8_t* __restrict__ xq,
                                                   const float* __restrict__ scale,
@@ -27,98 +58,165 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint32_t* __restrict__ 
                                                   int32_t* __restrict__ acc_out, int64_t tokens,
                                                   int64_t k, int64_t n_out) {
   constexpr int kW = block_bytes(S) / 4;
-  __shared__ __attribute__((aligned(16))) int8_t As[kBM * kPitch];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[kBN * kPitch];
-  __shared__ uint32_t lut[512];  // [half * 256 + key]
+  constexpr int kTT = BT / 32;  // 16-token tiles per wavefront
+  __shared__ __attribute__((aligned(16))) int8_t Xs[2][BT * kGPitch];
+  __shared__ __attribute__((aligned(16))) int8_t Cs[2][kGBN * kGPitch];
+  __shared__ __attribute__((aligned(16))) uint32_t lut[512 * kGLutCopies];
 
-  const int tid = threadIdx.x;
-  for (int idx = tid; idx < 512; idx += 256) lut[idx] = half_codes(idx & 255, idx >> 8);
-
-  const int64_t m0 = (int64_t)blockIdx.y * kBM;
-  const int64_t n0 = (int64_t)blockIdx.x * kBN;
-  const int64_t nkb = k / kBlockK;
-  const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 1, wt = wave >> 1;  // wavefront: rows 64*wn.., tokens (BT/2)*wt..
   const int l16 = lane & 15, lg = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * kGBN;
+  const int64_t t0 = (int64_t)blockIdx.y * BT;
+  const int64_t nkb = k / kBlockK;
+  const int nks = (int)(k / kGKS);
+  const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
 
-  // loader roles: A -- row tid/2, 64-byte half; B -- chunk tid%64 of
-  // superblock (tid/64)%2 of the tile's two strips, fields 8*(tid/128) ..
-  // +7 (wave-uniform, so field offsets are compile-time constants)
-  const int ld_row = tid >> 1, ld_half = tid & 1;
-  const int64_t a_tok = m0 + ld_row;
-  const int b_sb = (tid >> 6) & 1, b_chunk = tid & 63, b_part = tid >> 7;
-  const int64_t b_strip = n0 / kStripRows + b_sb;
-  const bool b_ok = b_strip < strips;
+  for (int idx = tid; idx < 512 * kGLutCopies; idx += 256)
+    lut[idx] = half_codes((idx / kGLutCopies) >> 1, (idx / kGLutCopies) & 1);
+  const uint32_t* lut_lane = lut + (lane & (kGLutCopies - 1));
 
-  v4i c[4][4];
+  // activations: thread -> token row (BT=256: one row, 64 bytes; BT=128:
+  // half a row, 32 bytes) of the step
+  constexpr int kXLoads = BT * kGKS / 16 / 256;  // 16-byte loads per thread
+  const int x_row = BT == 256 ? tid : tid >> 1;
+  const int x_col = BT == 256 ? 0 : 32 * (tid & 1);
+  const __amdgpu_buffer_rsrc_t xr = g_rsrc(xq, tokens * k);
+  const uint32_t x_off = (uint32_t)((t0 + x_row) * k + x_col);
+  const bool x_ok = t0 + x_row < tokens;
+  // codes: thread -> chunk c of superblock sb of the tile's two strips;
+  // fields of row tiles 2*part, 2*part+1
+  const int c_chunk = tid & 63, c_sb = (tid >> 6) & 1, c_part = tid >> 7;
+  const __amdgpu_buffer_rsrc_t pr = g_rsrc(packed, strips * nkb * kStripRows * block_bytes(S));
+  const int64_t c_strip = n0 / kStripRows + c_sb;
+  const bool c_ok = c_strip < strips;
+
+  // register rings: activations two steps ahead, packed chunks two k
+  // blocks ahead (so global latency is covered by two steps of MFMAs)
+  u32x4 xv[2][kXLoads];
+  uint32_t w[2][kW + 1];
+  w[0][kW] = 0;
+  w[1][kW] = 0;
+  auto load_x = [&](int ks, u32x4* dst) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < kXLoads; ++q)
+      dst[q] = __builtin_amdgcn_raw_buffer_load_b128(
+          xr, x_ok && ks < nks ? x_off + (uint32_t)(ks * kGKS + 16 * q) : 0x80000000u, 0, 0);
+  };
+  auto load_chunk = [&](int kb, uint32_t* dst) {
+    const uint32_t o =
+        c_ok && kb < nkb
+            ? (uint32_t)(((c_strip * nkb + kb) * kStripRows + c_chunk) * block_bytes(S))
+            : 0x80000000u;
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(pr, o, 0, 0);
+    dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
+    if constexpr (kW == 8) {
+      const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(pr, o + 16, 0, 0);
+      dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
+    } else if constexpr (kW == 7) {
+      typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
+      const u32x3 b = __builtin_amdgcn_raw_buffer_load_b96(pr, o + 16, 0, 0);
+      dst[4] = b.x; dst[5] = b.y; dst[6] = b.z;
+    } else {
+      const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(pr, o + 16, 0, 0);
+      dst[4] = b.x; dst[5] = b.y;
+    }
+  };
+  auto store_x = [&](int p, const u32x4* src) {
+#pragma unroll
+    for (int q = 0; q < kXLoads; ++q)
+      *reinterpret_cast<u32x4*>(&Xs[p][x_row * kGPitch + x_col + 16 * q]) = src[q];
+  };
+  // the codes of k half H of the chunk's 128-wide block
+  auto decode = [&](auto half, const uint32_t* wc, int p) {
+    constexpr int H = decltype(half)::value;
+    int8_t* cs = Cs[p];
+    if (c_part == 0) {
+      decode_pair<S, 2 * H + 0>(wc, lut_lane, cs, c_sb, c_chunk);
+      decode_pair<S, 2 * H + 4>(wc, lut_lane, cs, c_sb, c_chunk);
+    } else {
+      decode_pair<S, 2 * H + 8>(wc, lut_lane, cs, c_sb, c_chunk);
+      decode_pair<S, 2 * H + 12>(wc, lut_lane, cs, c_sb, c_chunk);
+    }
+  };
+
+  v4i c[kTT][4];
+#pragma unroll
+  for (int i = 0; i < kTT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) c[i][j] = v4i{0, 0, 0, 0};
 
-  for (int64_t kb = 0; kb < nkb; ++kb) {
-    __syncthreads();  // previous tile fully consumed (and the table ready)
-    // A tile: x_q[m0 .. m0+127][kb*128 .. +128]
-    {
-      const u32x4* src = reinterpret_cast<const u32x4*>(xq + a_tok * k + kb * kBlockK + ld_half * 64);
-      u32x4* dst = reinterpret_cast<u32x4*>(As + ld_row * kPitch + ld_half * 64);
-      const bool ok = a_tok < tokens;
+  // prologue: step 0 in LDS buffer 0, step 1 and k block 1 in flight
+  load_x(0, xv[0]);
+  load_chunk(0, w[0]);
+  load_x(1, xv[1]);
+  load_chunk(1, w[1]);
+  __syncthreads();  // tables ready
+  decode(std::integral_constant<int, 0>{}, w[0], 0);
+  store_x(0, xv[0]);
+  load_x(2, xv[0]);
+  __syncthreads();
+
+  // step ks (phase PH = ks % 4): MFMAs on LDS buffer ks%2; then step ks+1
+  // goes into the other buffer from the registers loaded two steps ago,
+  // and the loads for step ks+3 (and k block (ks+3)/2 + 1) are issued
+  auto step = [&](auto phase, int ks) {
+    constexpr int PH = decltype(phase)::value;
+    constexpr int p = PH & 1;
+    v4i a[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = ok ? src[i] : u32x4{0u, 0u, 0u, 0u};
-    }
-    // B tile: codes of rows n0 .. n0+127 (two packed superblocks) for this
-    // k block; each field lands at its (row, group) of the tile
-    {
-      uint32_t w[kW + 1];
+    for (int j = 0; j < 4; ++j)
+      a[j] = *reinterpret_cast<const v4i*>(&Cs[p][(64 * wn + 16 * j + l16) * kGPitch + 16 * lg]);
 #pragma unroll
-      for (int i = 0; i <= kW; ++i) w[i] = 0;
-      if (b_ok) {
-        const uint32_t* src = packed + ((b_strip * nkb + kb) * kStripRows + b_chunk) * kW;
-#pragma unroll
-        for (int i = 0; i < kW; ++i) w[i] = src[i];
-      }
-      auto lk = [&](uint32_t key, int half) { return lut[half * 256 + key]; };
-      auto emit = [&](int f, uint32_t lo, uint32_t hi) {
-        const int row = b_sb * kStripRows + field_row(b_chunk, f);
-        *reinterpret_cast<uint2*>(Bs + row * kPitch + 8 * field_group(b_chunk, f)) =
-            make_uint2(lo, hi);
-      };
-      if (b_part == 0) decode_groups<S, 0, 8>(w, lk, emit);
-      else decode_groups<S, 8, 8>(w, lk, emit);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      v4i a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const v4i*>(As + (wm * 64 + i * 16 + l16) * kPitch + kk * 64 + lg * 16);
+    for (int i = 0; i < kTT; ++i) {
+      const v4i b = *reinterpret_cast<const v4i*>(
+          &Xs[p][((BT / 2) * wt + 16 * i + l16) * kGPitch + 16 * lg]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const v4i*>(Bs + (wn * 64 + j * 16 + l16) * kPitch + kk * 64 + lg * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) c[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], c[i][j], 0, 0, 0);
+        c[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[j], b, c[i][j], 0, 0, 0);
     }
+    if (ks + 1 < nks) {
+      // step ks+1 = half (PH+1)%2 of k block (ks+1)/2, held in w[((PH+1)/2)%2]
+      decode(std::integral_constant<int, (PH + 1) & 1>{}, w[((PH + 1) >> 1) & 1], p ^ 1);
+      store_x(p ^ 1, xv[(PH + 1) & 1]);
+      load_x(ks + 3, xv[(PH + 1) & 1]);
+      // k block (ks+1)/2 + 1 goes into the chunk slot freed by block (ks+1)/2 - 1
+      if constexpr ((PH & 1) == 0) load_chunk((ks + 1) / 2 + 1, w[(((PH + 1) >> 1) + 1) & 1]);
+    }
+    __syncthreads();
+  };
+  for (int ks = 0; ks < nks; ks += 4) {
+    step(std::integral_constant<int, 0>{}, ks);
+    if (ks + 1 < nks) step(std::integral_constant<int, 1>{}, ks + 1);
+    if (ks + 2 < nks) step(std::integral_constant<int, 2>{}, ks + 2);
+    if (ks + 3 < nks) step(std::integral_constant<int, 3>{}, ks + 3);
   }
 
+  // epilogue: lane holds rows n0 + 64*wn + 16*j + 4*lg + q of token
+  // t0 + (BT/2)*wt + 16*i + l16
   const double g = *gamma;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kTT; ++i) {
+    const int64_t t = t0 + (BT / 2) * wt + 16 * i + l16;
+    if (t >= tokens) continue;
+    const float gs = out_scale(g, scale[t]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t t = m0 + wm * 64 + i * 16 + 4 * lg + q;
-      if (t >= tokens) continue;
-      const float gs = out_scale(g, scale[t]);
+    for (int j = 0; j < 4; ++j) {
+      const int64_t r = n0 + 64 * wn + 16 * j + 4 * lg;
+      float* y = Y + t * n_out + r;
+      if (r + 4 <= n_out && (n_out & 3) == 0) {
+        st_global(reinterpret_cast<v4f*>(y),
+                  v4f{out_value(c[i][j][0], gs), out_value(c[i][j][1], gs),
+                      out_value(c[i][j][2], gs), out_value(c[i][j][3], gs)});
+        if (acc_out) st_global(reinterpret_cast<v4i*>(acc_out + t * n_out + r), c[i][j]);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t r = n0 + wn * 64 + j * 16 + l16;
-        if (r < n_out) {
-          Y[t * n_out + r] = out_value(c[i][j][q], gs);
-          if (acc_out) acc_out[t * n_out + r] = c[i][j][q];
-        }
+        for (int q = 0; q < 4; ++q)
+          if (r + q < n_out) {
+            st_global(y + q, out_value(c[i][j][q], gs));
+            if (acc_out) st_global(acc_out + t * n_out + r + q, (int32_t)c[i][j][q]);
+          }
       }
     }
   }
@@ -128,9 +226,12 @@ template <int S>
 static hipError_t launch_gemm_s(const void* packed, const int8_t* xq, const float* scale,
                                 const double* gamma, float* Y, int32_t* acc, int64_t tokens,
                                 int64_t k, int64_t n_out, hipStream_t s) {
-  dim3 grid((unsigned)((n_out + kBN - 1) / kBN), (unsigned)((tokens + kBM - 1) / kBM));
-  gemm_kernel<S><<<grid, 256, 0, s>>>(reinterpret_cast<const uint32_t*>(packed), xq, scale, gamma,
-                                      Y, acc, tokens, k, n_out);
+  // 128-token tiles: two workgroups per CU (the 256-token tile needs more
+  // registers than fit twice) hide each other's load and barrier latency
+  const int64_t nb = (n_out + kGBN - 1) / kGBN;
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(packed);
+  dim3 grid((unsigned)nb, (unsigned)((tokens + 127) / 128));
+  gemm_kernel<S, 128><<<grid, 256, 0, s>>>(p, xq, scale, gamma, Y, acc, tokens, k, n_out);
   return hipGetLastError();
 }
 
