@@ -59,14 +59,22 @@ extern "C" {
  * pattern n:m, or 0 if the shape or pattern is unsupported.  The packed
  * layout stores each row's codes per 8-group as a nonzero bitmap plus one
  * sign bit per nonzero (S = 8, 6, 4, 4 sign slots for 8:8, 6:8, 4:8, 2:4),
- * 16 groups per 128-wide k block, rows in tiles of 16:
- *   ceil(n_out/16) * 16 * (k/128) * 2*(8+S) bytes.
+ * 16 groups per 128-wide k block, rows in strips of 64 (the last strip
+ * padded with zero fields):
+ *   ceil(n_out/64) * 64 * (k/128) * 2*(8+S) bytes.
+ * A field is 8+S bits: bitmap of positions 0..3, the S sign bits (the
+ * i-th nonzero of positions 0..3 at sign bit i, of positions 4..7 at sign
+ * bit S-1-i), bitmap of positions 4..7.  The (strip p, k block kb)
+ * superblock, at index p*(k/128)+kb, holds 64 chunks of 16 fields; chunk
+ * c = r + 16q holds, as its field f = 4i + 2h + e (at bit f*(8+S)), the
+ * 8-group 8h + 2q + e of row 64p + 16i + r. 
  * The 2-bit-per-weight storage of BitNet b1.58 (2B4T article §四) is the
  * 8:8 size of this format. */
 size_t bitlinear_packed_bytes(int64_t n_out, int64_t k, int n, int m);
 
-/* Workspace bytes bitlinear_quantize_mask needs (exact-sum accumulators and
- * a completion counter).  Host function; never fails for valid shapes. */
+/* Workspace bytes bitlinear_quantize_mask needs: one exact partial |W| sum
+ * per workgroup of the mask kernel plus its exponent bins (at most about
+ * 2 MiB).  Host function; 0 for invalid shapes. */
 size_t bitlinear_workspace_bytes(int64_t n_out, int64_t k);
 
 /* Workspace bytes bitlinear_fwd needs for `tokens` tokens (split-k partial

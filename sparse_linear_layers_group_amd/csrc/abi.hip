@@ -121,9 +121,8 @@ size_t bitlinear_packed_bytes(int64_t n_out, int64_t k, int n, int m) {
 }
 
 size_t bitlinear_workspace_bytes(int64_t n_out, int64_t k) {
-  (void)n_out;
-  (void)k;
-  return bl::kGammaWsBytes;
+  if (n_out < 1 || k < 1 || n_out >= kLimit || k >= kLimit || n_out * k >= kLimit) return 0;
+  return bl::gamma_ws_bytes(n_out, k);
 }
 
 size_t bitlinear_fwd_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out) {
@@ -144,8 +143,9 @@ int bitlinear_quantize_mask(const uint16_t* W, int64_t n_out, int64_t k, int n, 
   TRY(check_ptr(gamma, 8, "gamma"));
   if (gamma_over != BL_GAMMA_DENSE && gamma_over != BL_GAMMA_MASKED)
     return fail(BL_EINVAL, "gamma_over must be BL_GAMMA_DENSE or BL_GAMMA_MASKED (got %d)", gamma_over);
-  if (!ws || ws_bytes < bl::kGammaWsBytes)
-    return fail(BL_EWORKSPACE, "workspace needs %zu bytes (got %zu)", bl::kGammaWsBytes,
+  const size_t need = bl::gamma_ws_bytes(n_out, k);
+  if (!ws || ws_bytes < need)
+    return fail(BL_EWORKSPACE, "workspace needs %zu bytes (got %zu)", need,
                 ws ? ws_bytes : (size_t)0);
   TRY(check_ptr(ws, 16, "ws"));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -8,9 +8,22 @@
 
 namespace bl {
 
-constexpr size_t kGammaWsBytes = 4096;
+// Mask + exact absmean scale: kernel 1 (mask_blocks workgroups, each a
+// contiguous range of 8-groups) writes the mask and one exact partial sum
+// per workgroup into the workspace; kernel 2 (one workgroup) adds the
+// partials and writes gamma.  Workspace: a 32-byte record per workgroup,
+// then 256 64-bit exponent bins per workgroup (written only by workgroups
+// that met magnitudes outside the two fixed-point windows).
+constexpr int kMaskBlocksMax = 1024;
+constexpr int kMaskGroupsPerPass = 1024;  // 8-groups per workgroup pass
+__host__ __device__ inline int64_t mask_blocks(int64_t n_out, int64_t k) {
+  const int64_t passes = (n_out * k / 8 + kMaskGroupsPerPass - 1) / kMaskGroupsPerPass;
+  return passes < 1 ? 1 : passes > kMaskBlocksMax ? kMaskBlocksMax : passes;
+}
+__host__ __device__ inline size_t gamma_ws_bytes(int64_t n_out, int64_t k) {
+  return (size_t)mask_blocks(n_out, k) * (32 + 256 * 8);
+}
 
-// mask + exact absmean scale (two launches: workspace clear, mask/sum)
 hipError_t launch_mask_gamma(const uint16_t* W, int64_t n_out, int64_t k, int n, int m,
                              int gamma_over, uint8_t* mask, double* gamma, void* ws,
                              hipStream_t s);

@@ -1,8 +1,9 @@
 // quant.hip -- weight and activation quantisation kernels (gfx950).
 //
-//  mask_gamma_kernel  : N:M mask from latent |W| plus the exact |W| sum;
-//                       the last block to finish rounds the sum to binary64
-//                       and writes gamma.
+//  mask_gamma_kernel  : N:M mask from latent |W| plus exact partial |W|
+//                       sums, one per workgroup;
+//  gamma_finalize_kernel: adds the partials, rounds once to binary64 and
+//                       writes gamma.
 //  ternary_pack_kernel: masked ternary codes -> packed bitmap+sign blocks
 //                       (and/or plain int8 codes).
 //  act_quant_kernel   : per-token absmax int8 activations.
@@ -18,27 +19,23 @@ namespace bl {
 // ---------------------------------------------------------------------
 // Exact sum of |W|.  A finite bf16 magnitude is sig * 2^(max(E,1) - 134)
 // with E the 8-bit exponent field and sig = (E ? 128 : 0) + fraction.
-// Magnitudes with E in [kWinLo, kWinLo + kWin) (|W| in [2^-20, 2)) add
-// sig << (E - kWinLo) into a per-thread 64-bit integer; every other
-// nonzero magnitude (rare for weight-scale data) adds sig into hist[E]
-// with a 64-bit integer atomic.  Integer addition is associative, so the
+// Two fixed-point windows cover |W| in [2^-41, 2): E in [kHiLo, kHiLo+21)
+// adds sig << (E - kHiLo) to a 64-bit integer in units of 2^(kHiLo-134),
+// E in [kLoLo, kHiLo) adds sig << (E - kLoLo) to a second one in units of
+// 2^(kLoLo-134).  Any other nonzero magnitude adds sig into an exponent
+// bin of its workgroup (in LDS).  Integer addition is associative, so the
 // result does not depend on scheduling.
 // ---------------------------------------------------------------------
-constexpr int kWinLo = 107;
+constexpr int kHiLo = 107;
+constexpr int kLoLo = 86;
 constexpr int kWin = 21;  // sig << 20 < 2^28: eight of them fit in 32 bits
 
-struct GammaWS {
-  unsigned long long main;       // in units of 2^(kWinLo - 134)
-  unsigned long long hist[256];  // sig sums per exponent field
-  unsigned int ticket;
-  unsigned int pad;
+struct MaskPart {
+  unsigned long long hi, lo;  // window sums
+  uint32_t binned;            // nonzero: this workgroup wrote its 256 bins
+  uint32_t pad[3];
 };
-static_assert(sizeof(GammaWS) <= kGammaWsBytes, "gamma workspace");
-
-__global__ void gamma_ws_clear_kernel(GammaWS* ws) {
-  unsigned long long* p = reinterpret_cast<unsigned long long*>(ws);
-  for (int i = threadIdx.x; i < (int)(sizeof(GammaWS) / 8); i += blockDim.x) p[i] = 0ull;
-}
+static_assert(sizeof(MaskPart) == 32, "mask partial record");
 
 // keys: |h| (15 bits) above a 3-bit code that ranks a lower index higher;
 // all keys of a group are distinct and a larger key ranks first.
@@ -106,122 +103,189 @@ __device__ __forceinline__ uint32_t group_mask(const uint32_t w[4]) {
   return bits;
 }
 
-// exact |W| accumulation of one 8-group; returns the in-window sum
+// exact |W| accumulation of one 8-group into the two window sums
 template <bool MASKED>
-__device__ __forceinline__ uint32_t group_abs_sum(const uint32_t w[4], uint32_t keep,
-                                                 GammaWS* ws) {
-  uint32_t sum = 0;
+__device__ __forceinline__ void group_abs_sum(const uint32_t w[4], uint32_t keep,
+                                              unsigned long long& hi, unsigned long long& lo,
+                                              unsigned long long* bins, uint32_t& binned) {
+  uint32_t sh_sum = 0, sl_sum = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     uint32_t a = (w[j >> 1] >> (16 * (j & 1))) & 0x7fffu;
     if (MASKED && !((keep >> j) & 1u)) a = 0;
-    uint32_t e = a >> 7;
-    uint32_t sig = (a & 0x7fu) | (e ? 0x80u : 0u);
-    uint32_t sh = e - (uint32_t)kWinLo;
-    bool in = sh < (uint32_t)kWin;
-    sum += in ? (sig << sh) : 0u;
-    if (!in && a != 0u) atomic_add_global(&ws->hist[e], (unsigned long long)sig);
+    const uint32_t e = a >> 7;
+    const uint32_t sig = (a & 0x7fu) | (e ? 0x80u : 0u);
+    const uint32_t sh = e - (uint32_t)kHiLo, sl = e - (uint32_t)kLoLo;
+    const bool in_h = sh < (uint32_t)kWin, in_l = sl < (uint32_t)kWin;
+    sh_sum += in_h ? (sig << sh) : 0u;
+    sl_sum += in_l ? (sig << sl) : 0u;
+    if (!in_h && !in_l && a != 0u) {
+      atomicAdd(&bins[e], (unsigned long long)sig);
+      binned = 1;
+    }
   }
-  return sum;
+  hi += sh_sum;
+  lo += sl_sum;
 }
 
-// 320-bit unsigned integer in 32-bit limbs, units of 2^-133
+// 320-bit unsigned integer in 32-bit limbs, units of 2^-133; limb indices
+// are compile-time after unrolling, so the value stays in registers
 struct Big {
   uint32_t limb[10];
 };
 
-__device__ void big_add(Big& b, unsigned long long v, int shift) {
-  // b += v * 2^shift
-  // v * 2^bo spans three 32-bit limbs starting at limb li
-  int li = shift >> 5, bo = shift & 31;
+// b += v * 2^shift
+__device__ __forceinline__ void big_add(Big& b, unsigned long long v, int shift) {
+  const int li = shift >> 5, bo = shift & 31;
+  const uint32_t p0 = (uint32_t)(v << bo);
+  const uint32_t p1 = bo ? (uint32_t)(v >> (32 - bo)) : (uint32_t)(v >> 32);
+  const uint32_t p2 = bo ? (uint32_t)(v >> (64 - bo)) : 0u;
   unsigned long long carry = 0;
-  uint32_t parts[3];
-  parts[0] = (uint32_t)(v << bo);
-  parts[1] = bo ? (uint32_t)(v >> (32 - bo)) : (uint32_t)(v >> 32);
-  parts[2] = bo ? (uint32_t)(v >> (64 - bo)) : 0u;
-  for (int i = li; i < 10; ++i) {
-    unsigned long long add = (i - li < 3) ? parts[i - li] : 0u;
-    unsigned long long s = (unsigned long long)b.limb[i] + add + carry;
-    b.limb[i] = (uint32_t)s;
-    carry = s >> 32;
-    if (i - li >= 2 && carry == 0) break;
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i < li) continue;
+    const uint32_t add = i == li ? p0 : i == li + 1 ? p1 : i == li + 2 ? p2 : 0u;
+    const unsigned long long t = (unsigned long long)b.limb[i] + add + carry;
+    b.limb[i] = (uint32_t)t;
+    carry = t >> 32;
   }
 }
 
-__device__ int big_bit(const Big& b, int pos) { return (b.limb[pos >> 5] >> (pos & 31)) & 1; }
-
-// nearest binary64 (ties to even) of b * 2^-133
+// nearest binary64 (ties to even) of b * 2^-133: the top 64 bits, with
+// every lower nonzero bit folded into the last one (a sticky bit far below
+// the rounding position), converted by one correctly rounded u64 -> f64
+// conversion; the final power-of-two scaling is exact
 __device__ double big_round(const Big& b) {
-  int top = -1;
-  for (int i = 9; i >= 0 && top < 0; --i)
-    if (b.limb[i]) top = 32 * i + 31 - __clz(b.limb[i]);
-  if (top < 0) return 0.0;
-  unsigned long long sig = 0;
-  int low = top > 52 ? top - 52 : 0;
-  for (int pos = top; pos >= low; --pos) sig = (sig << 1) | (unsigned long long)big_bit(b, pos);
-  if (low > 0) {
-    int half = big_bit(b, low - 1);
-    int sticky = 0;
-    for (int pos = low - 2; pos >= 0 && !sticky; --pos) sticky = big_bit(b, pos);
-    if (half && (sticky || (sig & 1ull))) sig += 1;
+  int ti = -1;
+#pragma unroll
+  for (int i = 0; i < 10; ++i)
+    if (b.limb[i]) ti = i;
+  if (ti < 0) return 0.0;
+  uint32_t x2 = 0, x1 = 0, x0 = 0, sticky = 0;
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i == ti) x2 = b.limb[i];
+    if (i == ti - 1) x1 = b.limb[i];
+    if (i == ti - 2) x0 = b.limb[i];
+    if (i < ti - 2) sticky |= b.limb[i];
   }
-  return ldexp((double)sig, low - 133);
+  const int lz = __clz(x2);
+  const unsigned long long top = ((unsigned long long)x2 << 32) | x1;
+  unsigned long long m = lz ? (top << lz) | (x0 >> (32 - lz)) : top;
+  sticky |= lz ? (x0 << lz) : x0;
+  m |= sticky ? 1ull : 0ull;
+  // b = m * 2^(32 (ti - 2) + 32 - lz) (up to the sticky bit)
+  return ldexp((double)m, 32 * (ti - 2) + 32 - lz - 133);
 }
 
+// Kernel 1: mask bytes of every 8-group and the workgroup's exact partial
+// sums.  Workgroup b covers the contiguous 8-groups [b*per, (b+1)*per);
+// every load instruction of a wavefront reads 1 KiB of consecutive
+// weights.
 template <int N, int M, bool MASKED>
 __global__ __launch_bounds__(256) void mask_gamma_kernel(const uint4* __restrict__ W,
-                                                        int64_t nchunks,  // 4-group chunks
-                                                        uint32_t* __restrict__ mask_words,
-                                                        GammaWS* __restrict__ ws,
-                                                        double* __restrict__ gamma,
-                                                        double count) {
-  unsigned long long acc = 0;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
+                                                        int64_t ngroups, int64_t per,
+                                                        uint8_t* __restrict__ mask,
+                                                        char* __restrict__ ws) {
+  __shared__ unsigned long long bins[256];
+  __shared__ unsigned long long part[2][4];
+  __shared__ uint32_t any_binned;
+  bins[threadIdx.x] = 0ull;
+  if (threadIdx.x == 0) any_binned = 0;
+  __syncthreads();
+  unsigned long long hi = 0, lo = 0;
+  uint32_t binned = 0;
+  const int64_t g_begin = (int64_t)blockIdx.x * per;
+  const int64_t g_end = g_begin + per < ngroups ? g_begin + per : ngroups;
+  for (int64_t c0 = g_begin; c0 < g_end; c0 += kMaskGroupsPerPass) {
     uint4 v[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) v[g] = W[c * 4 + g];
-    uint32_t mword = 0;
+    for (int g = 0; g < 4; ++g) {
+      const int64_t grp = c0 + 256 * g + threadIdx.x;
+      v[g] = grp < g_end ? W[grp] : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
+      const int64_t grp = c0 + 256 * g + threadIdx.x;
+      if (grp >= g_end) break;
       const uint32_t w[4] = {v[g].x, v[g].y, v[g].z, v[g].w};
-      uint32_t keep = group_mask<N, M>(w);
-      mword |= keep << (8 * g);
-      acc += group_abs_sum<MASKED>(w, keep, ws);
+      const uint32_t keep = group_mask<N, M>(w);
+      mask[grp] = (uint8_t)keep;
+      group_abs_sum<MASKED>(w, keep, hi, lo, bins, binned);
     }
-    mask_words[c] = mword;
   }
-  // block reduction of the in-window sums, one 64-bit atomic per block
-  __shared__ unsigned long long part[8];
-  __shared__ int last;
-  acc = wave_sum_u64(acc);
+  hi = wave_sum_u64(hi);
+  lo = wave_sum_u64(lo);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) part[wave] = acc;
-  // every wavefront's histogram atomics are performed before the block's
-  // ticket (all the accumulators are device-scope atomics)
-  wait_memory_ops();
+  if (lane == 0) {
+    part[0][wave] = hi;
+    part[1][wave] = lo;
+  }
+  if (binned) any_binned = 1;
   __syncthreads();
+  MaskPart* rec = reinterpret_cast<MaskPart*>(ws) + blockIdx.x;
   if (threadIdx.x == 0) {
-    unsigned long long s = 0;
-    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += part[i];
-    if (s) atomic_add_global(&ws->main, s);
-    wait_memory_ops();
-    unsigned int t = atomic_fetch_add_global(&ws->ticket, 1u);
-    last = (t == gridDim.x - 1);
+    MaskPart r;
+    r.hi = part[0][0] + part[0][1] + part[0][2] + part[0][3];
+    r.lo = part[1][0] + part[1][1] + part[1][2] + part[1][3];
+    r.binned = any_binned;
+    r.pad[0] = r.pad[1] = r.pad[2] = 0;
+    *rec = r;
   }
+  if (any_binned) {
+    unsigned long long* out =
+        reinterpret_cast<unsigned long long*>(ws + (size_t)gridDim.x * sizeof(MaskPart)) +
+        (size_t)blockIdx.x * 256;
+    out[threadIdx.x] = bins[threadIdx.x];
+  }
+}
+
+// Kernel 2 (one workgroup of 256): gamma = (sum of the partials) / count,
+// the sum rounded once to binary64.
+__global__ __launch_bounds__(256) void gamma_finalize_kernel(const char* __restrict__ ws,
+                                                             int nblocks, double* __restrict__ gamma,
+                                                             double count) {
+  __shared__ unsigned long long part[2][4];
+  __shared__ unsigned long long bins[256];
+  __shared__ uint32_t any_binned;
+  if (threadIdx.x == 0) any_binned = 0;
+  const MaskPart* rec = reinterpret_cast<const MaskPart*>(ws);
+  unsigned long long hi = 0, lo = 0;
+  uint32_t binned = 0;
+  for (int b = threadIdx.x; b < nblocks; b += 256) {
+    hi += rec[b].hi;
+    lo += rec[b].lo;
+    binned |= rec[b].binned;
+  }
+  hi = wave_sum_u64(hi);
+  lo = wave_sum_u64(lo);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();  // any_binned initialised
+  if (lane == 0) {
+    part[0][wave] = hi;
+    part[1][wave] = lo;
+  }
+  if (binned) any_binned = 1;
   __syncthreads();
-  if (!last || threadIdx.x != 0) return;
-  // last block: every other block's atomics were performed before its
-  // ticket increment; read the accumulators with atomics as well.
-  wait_memory_ops();
-  Big b;
-  for (int i = 0; i < 10; ++i) b.limb[i] = 0;
-  big_add(b, atomic_fetch_add_global(&ws->main, 0ull), kWinLo - 1);
-  for (int e = 0; e < 256; ++e) {
-    unsigned long long h = atomic_fetch_add_global(&ws->hist[e], 0ull);
-    if (h) big_add(b, h, e > 0 ? e - 1 : 0);
+  unsigned long long bin = 0;
+  if (any_binned) {
+    const unsigned long long* all =
+        reinterpret_cast<const unsigned long long*>(ws + (size_t)nblocks * sizeof(MaskPart));
+    for (int b = 0; b < nblocks; ++b)
+      if (rec[b].binned) bin += all[(size_t)b * 256 + threadIdx.x];
   }
-  *gamma = big_round(b) / count;
+  bins[threadIdx.x] = bin;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  Big big;
+#pragma unroll
+  for (int i = 0; i < 10; ++i) big.limb[i] = 0;
+  big_add(big, part[0][0] + part[0][1] + part[0][2] + part[0][3], kHiLo - 1);
+  big_add(big, part[1][0] + part[1][1] + part[1][2] + part[1][3], kLoLo - 1);
+  if (any_binned)
+    for (int e = 0; e < 256; ++e)
+      if (bins[e]) big_add(big, bins[e], e > 0 ? e - 1 : 0);
+  *gamma = big_round(big) / count;
 }
 
 // ---------------------------------------------------------------------
@@ -403,19 +467,17 @@ __global__ __launch_bounds__(256) void act_quant_group_kernel(const char* __rest
 template <int N, int M>
 static hipError_t launch_mask(const uint16_t* W, int64_t n_out, int64_t k, int gamma_over,
                               uint8_t* mask, double* gamma, void* ws, hipStream_t s) {
-  GammaWS* g = reinterpret_cast<GammaWS*>(ws);
-  gamma_ws_clear_kernel<<<1, 256, 0, s>>>(g);
-  const int64_t nchunks = n_out * k / 32;
-  int64_t blocks = (nchunks + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
+  const int64_t ngroups = n_out * k / 8;
+  const int64_t blocks = mask_blocks(n_out, k);
+  int64_t per = (ngroups + blocks - 1) / blocks;
+  per = (per + kMaskGroupsPerPass - 1) / kMaskGroupsPerPass * kMaskGroupsPerPass;
+  char* w = reinterpret_cast<char*>(ws);
+  const uint4* W4 = reinterpret_cast<const uint4*>(W);
   if (gamma_over == 0)
-    mask_gamma_kernel<N, M, false><<<(unsigned)blocks, 256, 0, s>>>(
-        reinterpret_cast<const uint4*>(W), nchunks, reinterpret_cast<uint32_t*>(mask), g, gamma,
-        (double)(n_out * k));
+    mask_gamma_kernel<N, M, false><<<(unsigned)blocks, 256, 0, s>>>(W4, ngroups, per, mask, w);
   else
-    mask_gamma_kernel<N, M, true><<<(unsigned)blocks, 256, 0, s>>>(
-        reinterpret_cast<const uint4*>(W), nchunks, reinterpret_cast<uint32_t*>(mask), g, gamma,
-        (double)(n_out * k));
+    mask_gamma_kernel<N, M, true><<<(unsigned)blocks, 256, 0, s>>>(W4, ngroups, per, mask, w);
+  gamma_finalize_kernel<<<1, 256, 0, s>>>(w, (int)blocks, gamma, (double)(n_out * k));
   return hipGetLastError();
 }
 

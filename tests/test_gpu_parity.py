@@ -106,6 +106,20 @@ def test_gamma_exact_for_out_of_window_magnitudes():
     H.check_weight_path(bits, 6, 8, gamma_over=bl.BL_GAMMA_MASKED)
 
 
+def test_gamma_exact_over_many_workgroups():
+    """Enough 8-groups for the largest mask grid (1024 workgroups, two
+    passes each, a short last range), with magnitudes of every exponent
+    scattered so that many workgroups take the rare accumulation path."""
+    W = synth.weights(2304, 4096, seed=23)
+    rng = np.random.default_rng(23)
+    pos = rng.choice(W.size, size=3000, replace=False)
+    flat = W.reshape(-1)
+    flat[pos] = rng.integers(1, 0x7F80, size=pos.size, dtype=np.uint16)
+    flat[pos[::2]] |= 0x8000
+    assert bl.bitlinear_workspace_bytes(2304, 4096) == 1024 * (32 + 2048)
+    H.check_weight_path(W, 6, 8)
+
+
 def test_masked_gamma_ablation():
     W = synth.weights(96, 512, seed=17)
     lw, T, g = H.check_weight_path(W, 6, 8, gamma_over=bl.BL_GAMMA_MASKED)
