@@ -69,6 +69,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
 
 // explicit global-address-space accesses: pointers that arrive through
 // memory (e.g. from a plan) would otherwise become flat accesses, which also

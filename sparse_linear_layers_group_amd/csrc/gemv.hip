@@ -132,7 +132,6 @@ __device__ __forceinline__ void issue(Stage<S>& st, const Cursor& cur, bool live
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
   } else if constexpr (kBytes == 28) {
-    typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
     const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cur.sv.pk, po, 0, 0);
     const u32x3 b = __builtin_amdgcn_raw_buffer_load_b96(cur.sv.pk, po + 16, 0, 0);
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
