@@ -238,7 +238,7 @@ def prefill_step(torch, bl, n, m, tokens=2048, iters=10):
         for i, lw in enumerate(lws):
             src = bufs[0] if i == 1 else bufs[i]
             bl.bitlinear_contract(src["xq"], src["x_scale"], tokens, lw.k, lw.packed, lw.n_out, n, m,
-                                  lw.gamma, bufs[i]["Y"])
+                                  lw.gamma, bufs[i]["Y"], ws=bufs[i]["ws"])
 
     for f in (quant, act, gemm):
         f()
@@ -293,7 +293,7 @@ def train_step(torch, bl, n, m, tokens=4096, iters=3):
         for i, lw in enumerate(lws):
             a = fb[src[i]]
             bl.bitlinear_contract(a["xq"], a["x_scale"], tokens, lw.k, lw.packed, lw.n_out, n, m,
-                                  lw.gamma, fb[i]["Y"])
+                                  lw.gamma, fb[i]["Y"], ws=fb[i]["ws"])
 
     def bwd():
         for i, lw in enumerate(lws):

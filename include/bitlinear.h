@@ -77,8 +77,12 @@ size_t bitlinear_packed_bytes(int64_t n_out, int64_t k, int n, int m);
  * 2 MiB).  Host function; 0 for invalid shapes. */
 size_t bitlinear_workspace_bytes(int64_t n_out, int64_t k);
 
-/* Workspace bytes bitlinear_fwd needs for `tokens` tokens (split-k partial
- * sums of the decode kernel); 0 means ws may be NULL. */
+/* Workspace bytes bitlinear_fwd / bitlinear_contract need for `tokens`
+ * tokens: split-k partial sums and counters of the decode kernel (tokens
+ * <= 16), or, for the prefill kernel, counters and exact int32 partial
+ * tiles when the layer has too few 256 x 128 output tiles to fill the GPU
+ * and the k range is split (e.g. a 1536 x 8960 layer at 2048 tokens: about
+ * 61 MiB).  0 means ws may be NULL. */
 size_t bitlinear_fwd_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out);
 
 /* Steps 1-2 (and optionally 3): mask and absmean scale.
@@ -144,8 +148,10 @@ int bitlinear_fwd(const uint16_t *X, int64_t tokens, int64_t k,
  * once and contract them against several weights, or that time the steps
  * separately.  Same arguments and results as bitlinear_fwd.
  * bitlinear_contract's ws (bitlinear_fwd_workspace_bytes, may be NULL when
- * that is 0) must hold zeros on entry; every call leaves it zeroed
- * (bitlinear_fwd zero-fills it itself). */
+ * that is 0) must be all zeros before its first use; every call returns
+ * the counters in it to zero, so a workspace is zero-filled once and then
+ * reused by one call at a time (calls that overlap on one workspace race).
+ * bitlinear_fwd zero-fills what it needs itself. */
 int bitlinear_act_quant(const uint16_t *X, int64_t tokens, int64_t k, int8_t *xq,
                         float *x_scale, void *stream);
 int bitlinear_contract(const int8_t *xq, const float *x_scale, int64_t tokens,

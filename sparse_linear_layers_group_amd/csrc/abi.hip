@@ -126,7 +126,9 @@ size_t bitlinear_workspace_bytes(int64_t n_out, int64_t k) {
 }
 
 size_t bitlinear_fwd_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out) {
-  if (tokens < 1 || tokens > 16 || n_out < 1 || k < 128) return 0;
+  if (tokens < 1 || n_out < 1 || k < 128 || tokens >= kLimit || n_out >= kLimit) return 0;
+  // prefill: split-k tickets and partial tiles when the layer has few tiles
+  if (tokens > 16) return bl::gemm_ws_bytes(tokens, k, n_out);
   // one k block per strip: no strip is ever cut between wavefronts
   if (k / 128 == 1) return 0;
   return bl::decode_ws_bytes(tokens, n_out);
@@ -204,9 +206,16 @@ int bitlinear_fwd(const uint16_t* X, int64_t tokens, int64_t k, const void* pack
     e = bl::launch_gemv(packed, xq, x_scale, gamma, Y, acc, ws, (int)tokens, k, n_out, S, s);
     return hip_status(e, "decode launch");
   }
-  hipError_t e = bl::launch_act_quant(X, tokens, k, xq, x_scale, nullptr, 0, s);
+  const size_t need = bitlinear_fwd_workspace_bytes(tokens, k, n_out);
+  if (need && (!ws || ws_bytes < need))
+    return fail(BL_EWORKSPACE, "prefill workspace needs %zu bytes (got %zu)", need,
+                ws ? ws_bytes : (size_t)0);
+  if (need) TRY(check_ptr(ws, 16, "ws"));
+  // the tickets start at zero (the partial tiles need no clearing)
+  hipError_t e = bl::launch_act_quant(X, tokens, k, xq, x_scale, need ? ws : nullptr,
+                                      need ? (int64_t)bl::gemm_ticket_bytes(tokens, n_out) : 0, s);
   if (e != hipSuccess) return hip_status(e, "activation quant launch");
-  e = bl::launch_gemm(packed, xq, x_scale, gamma, Y, acc, tokens, k, n_out, S, s);
+  e = bl::launch_gemm(packed, xq, x_scale, gamma, Y, acc, ws, tokens, k, n_out, S, s);
   return hip_status(e, "prefill launch");
 }
 
@@ -241,17 +250,16 @@ int bitlinear_contract(const int8_t* xq, const float* x_scale, int64_t tokens, i
   TRY(check_opt_ptr(acc, 16, "acc"));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int S = bl::s_of(n, m);
+  const size_t need = bitlinear_fwd_workspace_bytes(tokens, k, n_out);
+  if (need && (!ws || ws_bytes < need))
+    return fail(BL_EWORKSPACE, "%s workspace needs %zu bytes (got %zu)",
+                tokens <= 16 ? "decode" : "prefill", need, ws ? ws_bytes : (size_t)0);
+  if (need) TRY(check_ptr(ws, 16, "ws"));
   hipError_t e;
-  if (tokens <= 16) {
-    const size_t need = bitlinear_fwd_workspace_bytes(tokens, k, n_out);
-    if (need && (!ws || ws_bytes < need))
-      return fail(BL_EWORKSPACE, "decode workspace needs %zu bytes (got %zu)", need,
-                  ws ? ws_bytes : (size_t)0);
-    if (need) TRY(check_ptr(ws, 16, "ws"));
+  if (tokens <= 16)
     e = bl::launch_gemv(packed, xq, x_scale, gamma, Y, acc, ws, (int)tokens, k, n_out, S, s);
-  } else {
-    e = bl::launch_gemm(packed, xq, x_scale, gamma, Y, acc, tokens, k, n_out, S, s);
-  }
+  else
+    e = bl::launch_gemm(packed, xq, x_scale, gamma, Y, acc, ws, tokens, k, n_out, S, s);
   return hip_status(e, "contraction launch");
 }
 

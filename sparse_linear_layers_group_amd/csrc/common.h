@@ -103,6 +103,22 @@ __device__ __forceinline__ T atomic_exchange_global(T* p, T v) {
                                __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 64-bit load at agent scope: served coherently for the whole device (not
+// from a CU's possibly stale L1), for data another workgroup published
+__device__ __forceinline__ unsigned long long ld_agent_u64(const unsigned long long* p) {
+  return __hip_atomic_load((const __attribute__((address_space(1))) unsigned long long*)(p),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 64-bit store at agent scope: written through to where every XCD reads
+// it.  A plain store may stay in the writing XCD's L2 (the L2s of the XCDs
+// are not kept coherent with each other within a kernel), where a
+// workgroup on another XCD would not see it.
+__device__ __forceinline__ void st_agent_u64(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store((__attribute__((address_space(1))) unsigned long long*)(p), v,
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Wait until every memory operation this wavefront issued has completed.
 // Partial sums that meet across workgroups go only through device-scope
 // atomics, which are performed at the device's coherence point; once they

@@ -53,7 +53,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint32_t* __restrict
                                                      float* __restrict__ Y,
                                                      int32_t* __restrict__ acc_out, int64_t tokens,
                                                      int64_t k, int64_t n_out, int row_blocks,
-                                                     int token_blocks) {
+                                                     int token_blocks, int splits,
+                                                     uint32_t* __restrict__ tickets,
+                                                     v4i* __restrict__ partials) {
   constexpr int kW = block_bytes(S) / 4;
   constexpr int kTT = BT / 16;           // 16-token tiles
   constexpr int kPieces = BT * 8 / 256;  // 16-byte activation pieces per thread per k block
@@ -64,21 +66,27 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint32_t* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs; give
-  // each XCD a contiguous run of tiles (row blocks fastest), so tiles that
-  // share activations share that XCD's L2.  The grid is a multiple of 8.
+  // each XCD a contiguous run of (part, tile) indices (row blocks fastest),
+  // so tiles that share activations share that XCD's L2.  The grid is a
+  // multiple of 8.
   const int nblk = row_blocks * token_blocks;
-  const int per_xcd = (nblk + 7) / 8;
+  const int nwork = nblk * splits;
+  const int per_xcd = (nwork + 7) / 8;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int full = nblk - (per_xcd - 1) * 8;  // XCDs that get per_xcd tiles
+  const int full = nwork - (per_xcd - 1) * 8;  // XCDs that get per_xcd items
   const int logical = xcd < full ? xcd * per_xcd + slot
                                  : full * per_xcd + (xcd - full) * (per_xcd - 1) + slot;
   if (slot >= (xcd < full ? per_xcd : per_xcd - 1)) return;
-  const int rb = logical % row_blocks, tb = logical / row_blocks;
+  const int part = logical / nblk, tile = logical - part * nblk;
+  const int rb = tile % row_blocks, tb = tile / row_blocks;
 
   const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
   const int64_t strip = (int64_t)rb * kGStrips + wave;
   const int64_t t0 = (int64_t)tb * BT;
-  const int nkb = (int)(k / kBlockK);
+  const int nkb_all = (int)(k / kBlockK);
+  // this part's k blocks [kb0, kb0 + nkb)
+  const int kb0 = (int)((int64_t)part * nkb_all / splits);
+  const int nkb = (int)((int64_t)(part + 1) * nkb_all / splits) - kb0;
 
   for (int idx = tid; idx < 512 * kGLutCopies; idx += 256)
     lut[idx] = half_codes((idx / kGLutCopies) >> 1, (idx / kGLutCopies) & 1);
@@ -105,22 +113,24 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint32_t* __restrict
   // and the last blocks run ahead by up to three) either reads the next
   // strip's or token's data, which is never used, or lands past the end of
   // the buffer range (or at kGOOB + small), where buffer loads return zeros.
-  const __amdgpu_buffer_rsrc_t pr = g_rsrc(packed, strips * nkb * kStripRows * block_bytes(S));
+  const __amdgpu_buffer_rsrc_t pr =
+      g_rsrc(packed, strips * nkb_all * kStripRows * block_bytes(S));
   const bool live = strip < strips;
   const uint32_t c_base =
-      live ? (uint32_t)((strip * nkb * kStripRows + lane) * block_bytes(S)) : kGOOB;
+      live ? (uint32_t)((strip * nkb_all * kStripRows + lane) * block_bytes(S)) : kGOOB;
 
   auto load_x = [&](int kb, u32x4* dst) {
 #pragma unroll
     for (int r = 0; r < kPieces; ++r)
-      dst[r] = __builtin_amdgcn_raw_buffer_load_b128(xr, x_off[r] + (uint32_t)(kb * kBlockK), 0, 0);
+      dst[r] = __builtin_amdgcn_raw_buffer_load_b128(xr, x_off[r] + (uint32_t)((kb0 + kb) * kBlockK),
+                                                     0, 0);
   };
   auto store_x = [&](int p, const u32x4* src) {
 #pragma unroll
     for (int r = 0; r < kPieces; ++r) Bs[p][x_slot[r]] = (v4i)src[r];
   };
   auto load_chunk = [&](int kb, uint32_t* dst) {
-    const uint32_t o = c_base + (uint32_t)kb * (uint32_t)(kStripRows * block_bytes(S));
+    const uint32_t o = c_base + (uint32_t)(kb0 + kb) * (uint32_t)(kStripRows * block_bytes(S));
     const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(pr, o, 0, 0);
     dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
     if constexpr (kW == 8) {
@@ -225,6 +235,43 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint32_t* __restrict
   if (kb < nkb) kblock(std::integral_constant<int, 0>{}, kb);
 
   if (!live) return;
+  if (splits > 1) {
+    // publish this part's tile (agent-scope stores: the reader may sit on
+    // another XCD), take the (tile, wavefront) ticket; the last part adds
+    // the others' tiles (agent-scope loads) and writes Y, then returns the
+    // ticket to zero
+    constexpr int kTileV4 = kTT * 4 * 64;  // v4i per wavefront tile
+    unsigned long long* own = reinterpret_cast<unsigned long long*>(
+        partials + ((size_t)(tile * splits + part) * kGStrips + wave) * kTileV4);
+#pragma unroll
+    for (int j = 0; j < kTT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const size_t e = 2 * ((size_t)(j * 4 + i) * 64 + lane);
+        st_agent_u64(own + e, (uint32_t)c[j][i][0] | ((unsigned long long)(uint32_t)c[j][i][1] << 32));
+        st_agent_u64(own + e + 1, (uint32_t)c[j][i][2] | ((unsigned long long)(uint32_t)c[j][i][3] << 32));
+      }
+    wait_memory_ops();
+    uint32_t t = 0;
+    if (lane == 0) t = atomic_fetch_add_global(&tickets[tile * kGStrips + wave], 1u);
+    t = __builtin_amdgcn_readfirstlane(t);
+    if (t != (uint32_t)splits - 1) return;
+    for (int z = 0; z < splits; ++z) {
+      if (z == part) continue;
+      const unsigned long long* other = reinterpret_cast<const unsigned long long*>(
+          partials + ((size_t)(tile * splits + z) * kGStrips + wave) * kTileV4);
+#pragma unroll
+      for (int j = 0; j < kTT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const size_t e = 2 * ((size_t)(j * 4 + i) * 64 + lane);
+          const unsigned long long lo = ld_agent_u64(other + e), hi = ld_agent_u64(other + e + 1);
+          c[j][i] += v4i{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi,
+                         (int)(uint32_t)(hi >> 32)};
+        }
+    }
+    if (lane == 0) atomic_exchange_global(&tickets[tile * kGStrips + wave], 0u);
+  }
   // epilogue: lane holds rows 64*strip + 16i + 4*(lane/16) + q of token
   // t0 + 16j + lane%16
   const double g = *gamma;
@@ -257,25 +304,32 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint32_t* __restrict
 
 template <int S>
 static hipError_t launch_gemm_s(const void* packed, const int8_t* xq, const float* scale,
-                                const double* gamma, float* Y, int32_t* acc, int64_t tokens,
-                                int64_t k, int64_t n_out, hipStream_t s) {
-  constexpr int BT = 128;
+                                const double* gamma, float* Y, int32_t* acc, void* ws,
+                                int64_t tokens, int64_t k, int64_t n_out, hipStream_t s) {
+  constexpr int BT = kGemmTileTokens;
+  static_assert(kGemmTileRows == kGStrips * kStripRows, "tile rows");
   const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
   const int row_blocks = (int)((strips + kGStrips - 1) / kGStrips);
   const int token_blocks = (int)((tokens + BT - 1) / BT);
-  const int nblk = row_blocks * token_blocks;
-  gemm_kernel<S, BT><<<(unsigned)((nblk + 7) / 8 * 8), 256, 0, s>>>(
+  const int splits = gemm_splits(tokens, k, n_out);
+  if (splits > 1 && !ws) return hipErrorInvalidValue;
+  uint32_t* tickets = splits > 1 ? reinterpret_cast<uint32_t*>(ws) : nullptr;
+  v4i* partials = splits > 1 ? reinterpret_cast<v4i*>(reinterpret_cast<char*>(ws) +
+                                                      gemm_ticket_bytes(tokens, n_out))
+                             : nullptr;
+  const int nwork = row_blocks * token_blocks * splits;
+  gemm_kernel<S, BT><<<(unsigned)((nwork + 7) / 8 * 8), 256, 0, s>>>(
       reinterpret_cast<const uint32_t*>(packed), xq, scale, gamma, Y, acc, tokens, k, n_out,
-      row_blocks, token_blocks);
+      row_blocks, token_blocks, splits, tickets, partials);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const void* packed, const int8_t* xq, const float* scale,
-                       const double* gamma, float* Y, int32_t* acc, int64_t tokens, int64_t k,
-                       int64_t n_out, int S, hipStream_t s) {
-  if (S == 8) return launch_gemm_s<8>(packed, xq, scale, gamma, Y, acc, tokens, k, n_out, s);
-  if (S == 6) return launch_gemm_s<6>(packed, xq, scale, gamma, Y, acc, tokens, k, n_out, s);
-  return launch_gemm_s<4>(packed, xq, scale, gamma, Y, acc, tokens, k, n_out, s);
+                       const double* gamma, float* Y, int32_t* acc, void* ws, int64_t tokens,
+                       int64_t k, int64_t n_out, int S, hipStream_t s) {
+  if (S == 8) return launch_gemm_s<8>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
+  if (S == 6) return launch_gemm_s<6>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
+  return launch_gemm_s<4>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
 }
 
 }  // namespace bl

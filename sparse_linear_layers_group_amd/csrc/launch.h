@@ -134,10 +134,37 @@ inline size_t group_plan_bytes(int64_t strips, int64_t count, int64_t rows) {
 hipError_t launch_act_quant_group(const void* plan, hipStream_t s);
 hipError_t launch_gemv_group(const void* plan, int S, hipStream_t s);
 
-// prefill-shaped contraction (any token count)
+// Prefill-shaped contraction (any token count).  Tiles are 256 rows x 128
+// tokens; when there are too few tiles to give every CU two workgroups,
+// the k blocks are split into gemm_splits() contiguous parts, one
+// workgroup each.  Parts write exact int32 partial tiles to the workspace
+// and take a ticket per (tile, wavefront); the last part adds the others
+// and writes Y, then returns the ticket to zero.  Workspace: tickets
+// (zero on entry, left zero), then the partial tiles.
+constexpr int kGemmTileRows = 256, kGemmTileTokens = 128;
+constexpr int kGemmSlots = 512;  // two workgroups per CU
+inline int64_t gemm_tiles(int64_t tokens, int64_t n_out) {
+  return ((n_out + kGemmTileRows - 1) / kGemmTileRows) *
+         ((tokens + kGemmTileTokens - 1) / kGemmTileTokens);
+}
+inline int gemm_splits(int64_t tokens, int64_t k, int64_t n_out) {
+  const int64_t tiles = gemm_tiles(tokens, n_out), nkb = k / 128;
+  int64_t sp = kGemmSlots / tiles;   // parts that still fit the CUs twice
+  if (sp > nkb / 4) sp = nkb / 4;    // each part keeps >= 4 k blocks
+  return sp < 2 ? 1 : (int)sp;
+}
+inline size_t gemm_ticket_bytes(int64_t tokens, int64_t n_out) {
+  return ((size_t)gemm_tiles(tokens, n_out) * 4 * 4 + 255) & ~(size_t)255;
+}
+inline size_t gemm_ws_bytes(int64_t tokens, int64_t k, int64_t n_out) {
+  const int sp = gemm_splits(tokens, k, n_out);
+  if (sp == 1) return 0;
+  return gemm_ticket_bytes(tokens, n_out) +
+         (size_t)gemm_tiles(tokens, n_out) * sp * kGemmTileRows * kGemmTileTokens * 4;
+}
 hipError_t launch_gemm(const void* packed, const int8_t* xq, const float* scale,
-                       const double* gamma, float* Y, int32_t* acc, int64_t tokens, int64_t k,
-                       int64_t n_out, int S, hipStream_t s);
+                       const double* gamma, float* Y, int32_t* acc, void* ws, int64_t tokens,
+                       int64_t k, int64_t n_out, int S, hipStream_t s);
 
 // backward
 hipError_t launch_bwd_dx(const uint16_t* dY, const void* packed, const double* gamma, float* dX,

@@ -49,7 +49,9 @@ class BitLinearWeight:
             "Y": torch.empty(tokens * self.n_out, dtype=torch.float32, device=d),
             "xq": torch.empty(tokens * self.k, dtype=torch.int8, device=d),
             "x_scale": torch.empty(max(tokens, 1), dtype=torch.float32, device=d)[:tokens],
-            "ws": torch.empty(ws_n, dtype=torch.uint8, device=d) if ws_n else None,
+            # zero-filled once: bitlinear_contract needs zero counters on entry
+            # and leaves them zero (bitlinear_fwd clears them itself)
+            "ws": torch.zeros(ws_n, dtype=torch.uint8, device=d) if ws_n else None,
         }
 
     def fwd(self, X, tokens, bufs=None, acc=None, stream=None):

@@ -70,6 +70,28 @@ def check_forward(lw, T, g, Xbits, check_acc=True):
     return bufs, xq, sc
 
 
+def check_forward_sampled(lw, T, g, Xbits, pairs=4096, seed=0):
+    """Full-size forward: x_q and s_t bit-exact everywhere; acc (bit-exact)
+    and Y (1e-5 relative) at random (token, row) pairs plus the four
+    corners of the output, each computed one by one by the oracle."""
+    tokens, k = Xbits.shape
+    acc_t = torch.empty(tokens * lw.n_out, dtype=torch.int32, device="cuda")
+    bufs = lw.fwd(bf16_tensor(Xbits), tokens, acc=acc_t)
+    torch.cuda.synchronize()
+    xq, sc = oracle.act_quant(Xbits)
+    assert np.array_equal(bufs["xq"].cpu().numpy().reshape(xq.shape), xq)
+    assert np.array_equal(bufs["x_scale"].cpu().numpy(), sc.astype(np.float32))
+    rng = np.random.default_rng(seed)
+    t_idx = np.concatenate([rng.integers(0, tokens, pairs), [0, 0, tokens - 1, tokens - 1]])
+    n_idx = np.concatenate([rng.integers(0, lw.n_out, pairs), [0, lw.n_out - 1, 0, lw.n_out - 1]])
+    acc_ref, Y_ref = oracle.fwd_pairs(xq, sc, T, g, t_idx, n_idx)
+    flat = t_idx * lw.n_out + n_idx
+    got = acc_t.cpu().numpy()[flat]
+    assert np.array_equal(got.astype(np.int64), acc_ref), f"acc differs at pairs {np.flatnonzero(got != acc_ref)[:5]}"
+    assert_y_close(bufs["Y"].cpu().numpy()[flat].astype(np.float64), Y_ref, acc_ref)
+    return bufs
+
+
 def assert_y_close(Y, Y_ref, acc_ref=None):
     err = np.abs(Y - Y_ref)
     assert np.all(err <= 1e-5 * np.abs(Y_ref)), f"max rel err {np.max(err / np.maximum(np.abs(Y_ref), 1e-300))}"

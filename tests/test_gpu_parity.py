@@ -219,6 +219,27 @@ def test_grouped_decode_matches_oracle(tokens, n, m):
             H.assert_y_close(e["Y"].cpu().numpy().reshape(Yref.shape).astype(np.float64), Yref)
 
 
+@pytest.mark.parametrize("n_out,k,tokens", [(200, 2304, 300), (512, 1024, 17), (1536, 8960, 2048)])
+def test_prefill_split_k(n_out, k, tokens):
+    """Layers with few output tiles split their k blocks over several
+    workgroups (uneven parts for 18 blocks over 4; 5 parts of 14 blocks at
+    the Qwen2.5-1.5B down-projection shape); the int32 sums must still be
+    exact and repeat calls must reuse the workspace."""
+    nws = bl.bitlinear_fwd_workspace_bytes(tokens, k, n_out)
+    assert nws > 0, "shape should take the split-k path"
+    W = synth.weights(n_out, k, seed=41)
+    X = synth.activations(tokens, k, seed=41)
+    lw, T, g = H.check_weight_path(W, 6, 8)
+    if tokens * n_out <= 600_000:
+        bufs, _, _ = H.check_forward(lw, T, g, X)
+    else:
+        bufs = H.check_forward_sampled(lw, T, g, X, seed=41)
+    Y0 = bufs["Y"].cpu().numpy().copy()
+    lw.fwd(bf16_tensor(X), tokens, bufs=bufs)
+    torch.cuda.synchronize()
+    assert np.array_equal(bufs["Y"].cpu().numpy(), Y0)
+
+
 @pytest.mark.parametrize("tokens", [1, 16, 100])
 def test_act_quant_plus_contract_equals_fwd(tokens):
     W = synth.weights(2048, 1024, seed=31)
@@ -231,12 +252,16 @@ def test_act_quant_plus_contract_equals_fwd(tokens):
     nws = bl.bitlinear_fwd_workspace_bytes(tokens, 1024, 2048)
     ws = torch.zeros(nws, dtype=torch.uint8, device="cuda") if nws else None
     bl.bitlinear_act_quant(bf16_tensor(X), tokens, 1024, xq, sc)
-    for _ in range(3):  # the split-k workspace is left zeroed by every call
+    for _ in range(3):  # every call returns the split-k counters to zero
         bl.bitlinear_contract(xq, sc, tokens, 1024, lw.packed, 2048, 6, 8, lw.gamma, Y, ws=ws)
         torch.cuda.synchronize()
         assert np.array_equal(Y.cpu().numpy(), ref["Y"].cpu().numpy())
     if ws is not None:
-        assert not ws.cpu().numpy().any()
+        # decode: the whole workspace; prefill: the ticket block in front of
+        # the partial tiles (one counter per 256 x 128 tile and wavefront)
+        tiles = -(-2048 // 256) * -(-tokens // 128)
+        n_zero = nws if tokens <= 16 else -(-tiles * 16 // 256) * 256
+        assert not ws[:n_zero].cpu().numpy().any()
     assert np.array_equal(xq.cpu().numpy(), ref["xq"].cpu().numpy())
 
 
