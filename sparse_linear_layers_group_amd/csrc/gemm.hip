@@ -88,8 +88,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint32_t* __restrict
   const int kb0 = (int)((int64_t)part * nkb_all / splits);
   const int nkb = (int)((int64_t)(part + 1) * nkb_all / splits) - kb0;
 
-  for (int idx = tid; idx < 512 * kGLutCopies; idx += 256)
-    lut[idx] = half_codes((idx / kGLutCopies) >> 1, (idx / kGLutCopies) & 1);
   const uint32_t* lut_lane = lut + (lane & (kGLutCopies - 1));
 
   // activation pieces of this thread: piece q = tid + 256 r is token q/8,
@@ -175,6 +173,21 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint32_t* __restrict
   load_chunk(0, w[0]);
   load_chunk(1, w[1]);
   load_x(1, xv[1]);
+  // tables, while those loads fly: the 512 distinct entries (key * 2 +
+  // half), two per thread, go to the idle LDS stage 1; then every thread
+  // writes 16-byte runs of copies
+  {
+    uint32_t* ent = reinterpret_cast<uint32_t*>(Bs[1]);
+    ent[tid] = half_codes((uint32_t)tid >> 1, (uint32_t)tid & 1u);
+    ent[tid + 256] = half_codes((uint32_t)(tid + 256) >> 1, (uint32_t)tid & 1u);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 512 * kGLutCopies / 4 / 256; ++r) {
+      const int ch = tid + 256 * r;  // 16-byte run: copies 4(ch%4).. of entry ch/4
+      const uint32_t v = ent[ch / (kGLutCopies / 4)];
+      reinterpret_cast<u32x4*>(lut)[ch] = u32x4{v, v, v, v};
+    }
+  }
   store_x(0, xv[0]);
   load_x(2, xv[0]);
   __syncthreads();  // tables and stage 0 ready
