@@ -80,7 +80,7 @@ size_t bitlinear_workspace_bytes(int64_t n_out, int64_t k);
 /* Workspace bytes bitlinear_fwd / bitlinear_contract need for `tokens`
  * tokens: split-k partial sums and counters of the decode kernel (tokens
  * <= 16), or, for the prefill kernel, counters and exact int32 partial
- * tiles when the layer has too few 256 x 128 output tiles to fill the GPU
+ * tiles when the layer has too few 256 x 64 output tiles to fill the GPU
  * and the k range is split (e.g. a 1536 x 8960 layer at 2048 tokens: about
  * 61 MiB).  0 means ws may be NULL. */
 size_t bitlinear_fwd_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out);

@@ -20,8 +20,10 @@
 // wavefront) both spread over all banks.  Per k block a wavefront issues
 // the MFMAs of block kb while it decodes block kb+1, writes the activations
 // of kb+1 and loads those of kb+2 and the chunk of kb+3; one barrier per k
-// block.  LDS stays at 64 KiB and registers at <= 256, so two workgroups
-// share a CU and one's output stores overlap the other's MFMAs.
+// block.  With BT = 64 (the launched size) LDS stays at 48 KiB and
+// registers at <= 168, so three workgroups share a CU; on MI355X that beat
+// 128-token tiles at two per CU on every measured shape (more tiles for
+// layers with few rows, shorter store bursts at the end of a round).
 #include "common.h"
 #include "launch.h"
 
@@ -46,7 +48,7 @@ __host__ __device__ constexpr int b_slot(int tt, int c) {
 }
 
 template <int S, int BT>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(const uint32_t* __restrict__ packed,
+__global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint32_t* __restrict__ packed,
                                                      const int8_t* __restrict__ xq,
                                                      const float* __restrict__ scale,
                                                      const double* __restrict__ gamma,
@@ -217,7 +219,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint32_t* __restrict
       b = bn;
     }
   };
-  static_assert(kTT == 8, "side work is laid out for eight segments per half");
+  // side work per segment: the 8 (row tile, field pair) decodes of a half
+  // spread over the kTT segments
+  static_assert(kTT == 8 || kTT == 4, "side work is laid out for 8 or 4 segments per half");
+  constexpr int kPairs = 8 / kTT;
   auto kblock = [&](auto parity, int kb) {
     constexpr int P = decltype(parity)::value;
     // chunk kb (loaded two blocks ago) moves to wc, and its registers take
@@ -231,12 +236,20 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint32_t* __restrict
     // loads read zeros (out-of-range offsets), the decoded codes and the
     // other LDS stage are never used
     half(parity, std::integral_constant<int, 0>{}, [&](int j) {
-      decode_field(wc, j >> 1, 1, j & 1, a[2 * (j >> 1) + 1]);
+#pragma unroll
+      for (int u = 0; u < kPairs; ++u) {
+        const int f = j * kPairs + u;
+        decode_field(wc, f >> 1, 1, f & 1, a[2 * (f >> 1) + 1]);
+      }
     });
     half(parity, std::integral_constant<int, 1>{}, [&](int j) {
-      decode_field(wn, j >> 1, 0, j & 1, a[2 * (j >> 1)]);
+#pragma unroll
+      for (int u = 0; u < kPairs; ++u) {
+        const int f = j * kPairs + u;
+        decode_field(wn, f >> 1, 0, f & 1, a[2 * (f >> 1)]);
+      }
       if (j < kPieces) Bs[P ^ 1][x_slot[j]] = (v4i)xv[P ^ 1][j];
-      if (j == 4) load_x(kb + 3, xv[P ^ 1]);
+      if (j == kTT / 2) load_x(kb + 3, xv[P ^ 1]);
     });
     __syncthreads();
   };
@@ -321,6 +334,7 @@ static hipError_t launch_gemm_s(const void* packed, const int8_t* xq, const floa
                                 int64_t tokens, int64_t k, int64_t n_out, hipStream_t s) {
   constexpr int BT = kGemmTileTokens;
   static_assert(kGemmTileRows == kGStrips * kStripRows, "tile rows");
+  static_assert(BT == 64, "launch bounds assume three workgroups per CU");
   const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
   const int row_blocks = (int)((strips + kGStrips - 1) / kGStrips);
   const int token_blocks = (int)((tokens + BT - 1) / BT);

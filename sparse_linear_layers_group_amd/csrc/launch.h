@@ -134,24 +134,28 @@ inline size_t group_plan_bytes(int64_t strips, int64_t count, int64_t rows) {
 hipError_t launch_act_quant_group(const void* plan, hipStream_t s);
 hipError_t launch_gemv_group(const void* plan, int S, hipStream_t s);
 
-// Prefill-shaped contraction (any token count).  Tiles are 256 rows x 128
-// tokens; when there are too few tiles to give every CU two workgroups,
+// Prefill-shaped contraction (any token count).  Tiles are 256 rows x 64
+// tokens; when there are too few tiles to give every CU three workgroups,
 // the k blocks are split into gemm_splits() contiguous parts, one
 // workgroup each.  Parts write exact int32 partial tiles to the workspace
 // and take a ticket per (tile, wavefront); the last part adds the others
 // and writes Y, then returns the ticket to zero.  Workspace: tickets
 // (zero on entry, left zero), then the partial tiles.
-constexpr int kGemmTileRows = 256, kGemmTileTokens = 128;
-constexpr int kGemmSlots = 512;  // two workgroups per CU
+constexpr int kGemmTileRows = 256, kGemmTileTokens = 64;
 inline int64_t gemm_tiles(int64_t tokens, int64_t n_out) {
   return ((n_out + kGemmTileRows - 1) / kGemmTileRows) *
          ((tokens + kGemmTileTokens - 1) / kGemmTileTokens);
 }
 inline int gemm_splits(int64_t tokens, int64_t k, int64_t n_out) {
   const int64_t tiles = gemm_tiles(tokens, n_out), nkb = k / 128;
-  int64_t sp = kGemmSlots / tiles;   // parts that still fit the CUs twice
-  if (sp > nkb / 4) sp = nkb / 4;    // each part keeps >= 4 k blocks
-  return sp < 2 ? 1 : (int)sp;
+  // Every extra part adds a full int32 copy of the layer's output to write
+  // and read back through memory; on MI355X that exchange cost more than
+  // the parallelism it buys unless most CUs would otherwise idle (1536 x
+  // 8960 at 2048 tokens, 192 tiles: 50.4 us unsplit, 50.7 us in 2 parts;
+  // 2048 x 11008, 256 tiles: 62.9 vs 67.8 us).  So: two parts, and only
+  // when the tiles would occupy at most half of the 256 CUs.
+  if (tiles > 128 || nkb < 8) return 1;
+  return 2;
 }
 inline size_t gemm_ticket_bytes(int64_t tokens, int64_t n_out) {
   return ((size_t)gemm_tiles(tokens, n_out) * 4 * 4 + 255) & ~(size_t)255;

@@ -219,12 +219,12 @@ def test_grouped_decode_matches_oracle(tokens, n, m):
             H.assert_y_close(e["Y"].cpu().numpy().reshape(Yref.shape).astype(np.float64), Yref)
 
 
-@pytest.mark.parametrize("n_out,k,tokens", [(200, 2304, 300), (512, 1024, 17), (1536, 8960, 2048)])
+@pytest.mark.parametrize("n_out,k,tokens", [(200, 2432, 300), (512, 1024, 17), (1536, 8960, 1024)])
 def test_prefill_split_k(n_out, k, tokens):
-    """Layers with few output tiles split their k blocks over several
-    workgroups (uneven parts for 18 blocks over 4; 5 parts of 14 blocks at
-    the Qwen2.5-1.5B down-projection shape); the int32 sums must still be
-    exact and repeat calls must reuse the workspace."""
+    """Layers with few output tiles split their k blocks over two
+    workgroups (uneven parts: 19 blocks as 9 + 10; 35 + 35 for the
+    Qwen2.5-1.5B down projection at 1024 tokens); the int32 sums must still
+    be exact and repeat calls must reuse the workspace."""
     nws = bl.bitlinear_fwd_workspace_bytes(tokens, k, n_out)
     assert nws > 0, "shape should take the split-k path"
     W = synth.weights(n_out, k, seed=41)
@@ -258,8 +258,8 @@ def test_act_quant_plus_contract_equals_fwd(tokens):
         assert np.array_equal(Y.cpu().numpy(), ref["Y"].cpu().numpy())
     if ws is not None:
         # decode: the whole workspace; prefill: the ticket block in front of
-        # the partial tiles (one counter per 256 x 128 tile and wavefront)
-        tiles = -(-2048 // 256) * -(-tokens // 128)
+        # the partial tiles (one counter per 256 x 64 tile and wavefront)
+        tiles = -(-2048 // 256) * -(-tokens // 64)
         n_zero = nws if tokens <= 16 else -(-tiles * 16 // 256) * 256
         assert not ws[:n_zero].cpu().numpy().any()
     assert np.array_equal(xq.cpu().numpy(), ref["xq"].cpu().numpy())
