@@ -302,6 +302,24 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
   // t0 + 16j + lane%16
   const double g = *gamma;
   const int64_t r0 = strip * kStripRows + 4 * (lane >> 4);
+  if (t0 + BT <= tokens && strip * kStripRows + kStripRows <= n_out && (n_out & 3) == 0) {
+    // whole tile in range: 16-byte stores, no per-element checks; element
+    // offsets fit 32 bits (tokens * n_out < 2^31)
+    const uint32_t base = (uint32_t)(t0 + (lane & 15)) * (uint32_t)n_out + (uint32_t)r0;
+#pragma unroll
+    for (int j = 0; j < kTT; ++j) {
+      const float gs = out_scale(g, scale[t0 + 16 * j + (lane & 15)]);
+      const uint32_t o = base + (uint32_t)(16 * j) * (uint32_t)n_out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        st_global(reinterpret_cast<v4f*>(Y + o + 16 * i),
+                  v4f{out_value(c[j][i][0], gs), out_value(c[j][i][1], gs),
+                      out_value(c[j][i][2], gs), out_value(c[j][i][3], gs)});
+        if (acc_out) st_global(reinterpret_cast<v4i*>(acc_out + o + 16 * i), c[j][i]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < kTT; ++j) {
     const int64_t t = t0 + 16 * j + (lane & 15);
