@@ -345,11 +345,15 @@ def train_step(torch, bl, n, m, tokens=4096, iters=3):
             bl.bitlinear_contract(a["xq"], a["x_scale"], tokens, lw.k, lw.packed, lw.n_out, n, m,
                                   lw.gamma, fb[i]["Y"], ws=fb[i]["ws"])
 
+    # one backward workspace, sized for the largest layer (calls run in order on one stream)
+    bws = torch.empty(max(bl.bitlinear_bwd_workspace_bytes(tokens, lw.k, lw.n_out) for lw in lws),
+                      dtype=torch.uint8, device="cuda")
+
     def bwd():
         for i, lw in enumerate(lws):
             a = fb[src[i]]
             bl.bitlinear_bwd(dys[i], a["xq"], a["x_scale"], lw.packed, lw.gamma, tokens, lw.k,
-                             lw.n_out, n, m, gx[i], gw[i])
+                             lw.n_out, n, m, gx[i], gw[i], ws=bws)
 
     for f in (quant, fwd, bwd):
         f()

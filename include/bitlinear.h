@@ -77,6 +77,13 @@ size_t bitlinear_packed_bytes(int64_t n_out, int64_t k, int n, int m);
  * 2 MiB).  Host function; 0 for invalid shapes. */
 size_t bitlinear_workspace_bytes(int64_t n_out, int64_t k);
 
+/* Workspace bytes bitlinear_bwd needs: the bf16 operands of its two
+ * products, bf16(dY * s_t) and x_q transposed to [n_out x tp] and [k x tp]
+ * (tp = tokens rounded up to 64) and the decoded codes transposed to
+ * [k x n_out rounded up to 64]; about 113 MB for a 6912 x 2560 layer at
+ * 4096 tokens.  0 for invalid shapes. */
+size_t bitlinear_bwd_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out);
+
 /* Workspace bytes bitlinear_fwd / bitlinear_contract need for `tokens`
  * tokens: split-k partial sums and counters of the decode kernel (tokens
  * <= 16), or, for the prefill kernel, counters and exact int32 partial
@@ -201,7 +208,10 @@ int bitlinear_fwd_group(const void *plan, int n, int m, int stages, void *stream
  *   packed, gamma  device, as for bitlinear_fwd.
  *   dX       device float [tokens x k] or NULL (skip).
  *   dW       device float [n_out x k] or NULL (skip).
- *   ws, ws_bytes  reserved; pass NULL, 0.
+ *   ws       device workspace of at least bitlinear_bwd_workspace_bytes()
+ *            bytes, 256-byte aligned; its contents need not be initialised
+ *            and are clobbered (may be NULL when tokens == 0).
+ * n_out must be a multiple of 16.  Calls that overlap on one workspace race.
  */
 int bitlinear_bwd(const uint16_t *dY, const int8_t *xq, const float *x_scale,
                   const void *packed, const double *gamma, int64_t tokens,

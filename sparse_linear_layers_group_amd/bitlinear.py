@@ -34,6 +34,7 @@ _SIGS = {
     "bitlinear_packed_bytes": (_sz, [_i64, _i64, _int, _int]),
     "bitlinear_workspace_bytes": (_sz, [_i64, _i64]),
     "bitlinear_fwd_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "bitlinear_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bitlinear_quantize_mask": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_pack": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _sz, _vp]),
     "bitlinear_fwd": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -159,6 +160,10 @@ def bitlinear_fwd(X, tokens, k, packed, n_out, n, m, gamma, Y, xq, x_scale, acc=
         (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes),
         _stream(stream))
     _check(st, "bitlinear_fwd")
+
+
+def bitlinear_bwd_workspace_bytes(tokens, k, n_out):
+    return int(lib().bitlinear_bwd_workspace_bytes(int(tokens), int(k), int(n_out)))
 
 
 def bitlinear_bwd(dY, xq, x_scale, packed, gamma, tokens, k, n_out, n, m, dX, dW, ws=None,

@@ -134,6 +134,13 @@ size_t bitlinear_fwd_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out) {
   return bl::decode_ws_bytes(tokens, n_out);
 }
 
+size_t bitlinear_bwd_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out) {
+  if (tokens < 0 || n_out < 1 || k < 128 || k % 128 != 0 || n_out % 16 != 0 ||
+      tokens >= kLimit || n_out >= kLimit || k >= kLimit)
+    return 0;
+  return bl::bwd_ws_bytes(tokens, k, n_out);
+}
+
 int bitlinear_quantize_mask(const uint16_t* W, int64_t n_out, int64_t k, int n, int m,
                             int gamma_over, uint8_t* mask, int8_t* wq, double* gamma, void* ws,
                             size_t ws_bytes, void* stream) {
@@ -387,8 +394,6 @@ int bitlinear_fwd_group(const void* plan, int n, int m, int stages, void* stream
 int bitlinear_bwd(const uint16_t* dY, const int8_t* xq, const float* x_scale, const void* packed,
                   const double* gamma, int64_t tokens, int64_t k, int64_t n_out, int n, int m,
                   float* dX, float* dW, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   TRY(check_nm(n, m));
   TRY(check_layer(n_out, k));
   if (n_out % 16 != 0)
@@ -400,27 +405,32 @@ int bitlinear_bwd(const uint16_t* dY, const int8_t* xq, const float* x_scale, co
   TRY(check_opt_ptr(dW, 16, "dW"));
   if (!dX && !dW) return ok();
   if (tokens == 0) {
-    // no tokens: dX is empty and dW is all zeros (the dW kernel's token
-    // loop is empty, so it reads nothing and stores zeros)
+    // no tokens: dX is empty and dW is all zeros (no workspace needed)
     if (dW) {
-      hipError_t e = bl::launch_bwd_dw(nullptr, nullptr, nullptr, dW, 0, k, n_out,
+      hipError_t e = bl::launch_bwd_dw(nullptr, nullptr, nullptr, dW, nullptr, 0, k, n_out,
                                        reinterpret_cast<hipStream_t>(stream));
       return hip_status(e, "dW clear");
     }
     return ok();
   }
+  const size_t need = bl::bwd_ws_bytes(tokens, k, n_out);
+  if (!ws || ws_bytes < need)
+    return fail(BL_EWORKSPACE, "backward workspace needs %zu bytes (got %zu)", need,
+                ws ? ws_bytes : (size_t)0);
+  TRY(check_ptr(ws, 256, "ws"));
   TRY(check_ptr(dY, 16, "dY"));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dX) {
     TRY(check_ptr(packed, 16, "packed"));
     TRY(check_ptr(gamma, 8, "gamma"));
-    hipError_t e = bl::launch_bwd_dx(dY, packed, gamma, dX, tokens, k, n_out, bl::s_of(n, m), s);
+    hipError_t e =
+        bl::launch_bwd_dx(dY, packed, gamma, dX, ws, tokens, k, n_out, bl::s_of(n, m), s);
     if (e != hipSuccess) return hip_status(e, "dX launch");
   }
   if (dW) {
     TRY(check_ptr(xq, 16, "xq"));
     TRY(check_ptr(x_scale, 4, "x_scale"));
-    hipError_t e = bl::launch_bwd_dw(dY, xq, x_scale, dW, tokens, k, n_out, s);
+    hipError_t e = bl::launch_bwd_dw(dY, xq, x_scale, dW, ws, tokens, k, n_out, s);
     if (e != hipSuccess) return hip_status(e, "dW launch");
   }
   return ok();

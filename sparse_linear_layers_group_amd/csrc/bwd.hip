@@ -6,216 +6,294 @@
 //   dX[t, c] = gamma * sum_r dY[t, r] * code[r, c]     (through the masked
 //              ternary weights the forward used)
 //   dW[r, c] = sum_t dY[t, r] * s_t * x_q[t, c]        (dense)
-// Both run on v_mfma_f32_16x16x32_bf16 with binary32 accumulation.  codes
-// and x_q are exact in bf16; dY * s_t is rounded to bf16 once.
-//
-// Tiles: 128 x 128 outputs per workgroup of 4 wavefronts (2 x 2, 64 x 64
-// each), contraction step 64.  Operands whose contraction index is not the
-// contiguous one in memory are transposed while staging into LDS.
+// Both are one bf16 "NT" product C[m, n] = alpha * sum_k A[m, k] B[n, k]
+// on v_mfma_f32_16x16x32_bf16 with binary32 accumulation, whose operands
+// both run along the contraction index in memory:
+//   dX: A = dY [tokens x n_out] as given, B = codes^T [k x n_out];
+//   dW: A = (dY * s)^T [n_out x tokens], B = x_q^T [k x tokens].
+// Prep kernels write the operands that are not in that form into the
+// workspace: the codes decoded from the packed layout and transposed
+// (exact in bf16), bf16(dY * s_t) transposed (rounded once), and x_q
+// transposed (exact).  Every conversion happens once per element, so the
+// product kernel is a plain copy-to-LDS and MFMA loop.
 #include "common.h"
 #include "launch.h"
 
 namespace bl {
-
-constexpr int kP = 72;  // LDS row pitch in bf16 elements (64 + 8)
 
 __device__ __forceinline__ uint16_t code_bf16(uint32_t byte) {
   // 0x01 -> +1.0, 0xff -> -1.0, 0 -> 0
   return byte == 0u ? (uint16_t)0 : (byte == 1u ? (uint16_t)0x3f80 : (uint16_t)0xbf80);
 }
 
-__device__ __forceinline__ void mma_tile(const uint16_t* As, const uint16_t* Bs, int wm, int wn,
-                                         int lane, v4f c[4][4]) {
+// ------------------------------------------------------------- prep
+// 64 x 64 transposes through LDS.  Source rows are the contraction index
+// of the product (tokens); each thread loads 16 bytes of a source row and
+// writes 16 bytes (8 consecutive source rows) of a destination row.
+constexpr int kTP = 66;  // LDS pitch (bf16) of the 64 x 64 transpose tile
+
+// dYsT[r][t] = bf16(dY[t][r] * s_t) for t < tokens, 0 for tokens <= t < tp
+__global__ __launch_bounds__(256) void prep_dys_t_kernel(const uint16_t* __restrict__ dY,
+                                                        const float* __restrict__ scale,
+                                                        int64_t tokens, int64_t n_out, int64_t tp,
+                                                        uint16_t* __restrict__ out) {
+  __shared__ uint16_t tile[64 * kTP];  // [t][r]
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int q = tid + 256 * p, t = q >> 3, r8 = 8 * (q & 7);
+    const int64_t tt = t0 + t;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    float s = 0.f;
+    if (tt < tokens && r0 + r8 < n_out) {  // n_out % 8 == 0: a run is all in or all out
+      v = ld_global(reinterpret_cast<const u32x4*>(dY + tt * n_out + r0 + r8));
+      s = scale[tt];
+    }
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+      tile[t * kTP + r8 + e] = f32_to_bf16_rne(x * s);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int q = tid + 256 * p, r = q >> 3, t8 = 8 * (q & 7);
+    if (r0 + r >= n_out) continue;
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (uint32_t)tile[(t8 + 2 * e) * kTP + r] | ((uint32_t)tile[(t8 + 2 * e + 1) * kTP + r] << 16);
+    st_global(reinterpret_cast<u32x4*>(out + (r0 + r) * tp + t0 + t8), u32x4{o[0], o[1], o[2], o[3]});
+  }
+}
+
+// xbT[c][t] = bf16(x_q[t][c]) (exact) for t < tokens, 0 up to tp
+__global__ __launch_bounds__(256) void prep_xq_t_kernel(const int8_t* __restrict__ xq,
+                                                       int64_t tokens, int64_t k, int64_t tp,
+                                                       uint16_t* __restrict__ out) {
+  __shared__ uint16_t tile[64 * kTP];  // [t][c]
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  {
+    const int t = tid >> 2, c16 = 16 * (tid & 3);
+    const int64_t tt = t0 + t;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (tt < tokens) v = ld_global(reinterpret_cast<const u32x4*>(xq + tt * k + c0 + c16));
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int8_t b = (int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
+      tile[t * kTP + c16 + e] = f32_to_bf16_rne((float)b);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int q = tid + 256 * p, c = q >> 3, t8 = 8 * (q & 7);
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (uint32_t)tile[(t8 + 2 * e) * kTP + c] | ((uint32_t)tile[(t8 + 2 * e + 1) * kTP + c] << 16);
+    st_global(reinterpret_cast<u32x4*>(out + (c0 + c) * tp + t0 + t8), u32x4{o[0], o[1], o[2], o[3]});
+  }
+}
+
+// codesT[c][r] = bf16(code[r][c]) for the rows of one packed superblock
+// (64 rows x 128 columns) per workgroup of 64 threads; padding rows of
+// the last strip are zero fields, so rows up to the strip end are written
+// (the row pitch np = 64 * strips)
+template <int S>
+__global__ __launch_bounds__(64) void prep_codes_t_kernel(const uint32_t* __restrict__ packed,
+                                                         int64_t nkb, int64_t np,
+                                                         uint16_t* __restrict__ out) {
+  constexpr int kW = block_bytes(S) / 4;
+  __shared__ uint16_t tile[kBlockK * kTP];  // [c][r]
+  __shared__ uint32_t lut[512];
+  const int lane = threadIdx.x;
+  for (int idx = lane; idx < 512; idx += 64) lut[idx] = half_codes(idx & 255, idx >> 8);
+  const int64_t sb = blockIdx.x;  // superblock = strip * nkb + kb
+  const int64_t strip = sb / nkb, kb = sb - strip * nkb;
+  uint32_t w[kW + 1];
+  const uint32_t* src = packed + (sb * kStripRows + lane) * kW;
+#pragma unroll
+  for (int i = 0; i < kW; ++i) w[i] = ld_global(src + i);
+  w[kW] = 0;
+  __syncthreads();
+  auto lk = [&](uint32_t key, int half) { return lut[half * 256 + key]; };
+  auto emit = [&](int f, uint32_t lo, uint32_t hi) {
+    const int rr = field_row(lane, f), gi = field_group(lane, f);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      tile[(gi * 8 + p) * kTP + rr] = code_bf16((lo >> (8 * p)) & 0xffu);
+      tile[(gi * 8 + 4 + p) * kTP + rr] = code_bf16((hi >> (8 * p)) & 0xffu);
+    }
+  };
+  decode_groups<S, 0, 16>(w, lk, emit);
+  __syncthreads();
+  // 128 columns x 64 rows: each thread writes 8 rows of 8 bf16 runs
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const int q = lane + 64 * p, c = q >> 3, r8 = 8 * (q & 7);
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (uint32_t)tile[c * kTP + r8 + 2 * e] | ((uint32_t)tile[c * kTP + r8 + 2 * e + 1] << 16);
+    st_global(reinterpret_cast<u32x4*>(out + (kb * kBlockK + c) * np + strip * kStripRows + r8),
+              u32x4{o[0], o[1], o[2], o[3]});
+  }
+}
+
+// ------------------------------------------------------------- product
+// C[m][n] = alpha * sum_k A[m][k] * B[n][k], A/B bf16 row-major with row
+// pitches lda/ldb (elements, multiples of 8), C binary32 [M][ldc].
+// Workgroup tile 128 x 128, four wavefronts of 64 x 64 (4 x 4 MFMA
+// tiles); k advances 64 at a time through double-buffered LDS tiles
+// (rows padded to 72 bf16: the 16-byte fragment reads of a quarter
+// wavefront fall on distinct bank groups).  The next step's tiles are in
+// registers while the MFMAs run; one barrier per step.  k positions at or
+// past K read as zero.
+constexpr int kBP = 72;
+
+__global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
+    float* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+    const double* __restrict__ alpha) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][128 * kBP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][128 * kBP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
   const int l16 = lane & 15, lg = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.y * 128, n0 = (int64_t)blockIdx.x * 128;
+  const int64_t nks = (K + 63) / 64;
+
+  // loads: piece q = tid + 256 p (p < 4) of each tile is row q/8, k
+  // columns 8*(q%8) .. +8 of the step
+  u32x4 ra[4], rb[4];
+  auto load = [&](int64_t ks) {
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    v8bf a[4], b[4];
+    for (int p = 0; p < 4; ++p) {
+      const int q = tid + 256 * p, row = q >> 3, kc = 8 * (q & 7);
+      const int64_t kk = ks * 64 + kc;
+      const bool ka = kk < K;
+      ra[p] = (ka && m0 + row < M) ? ld_global(reinterpret_cast<const u32x4*>(A + (m0 + row) * lda + kk))
+                                   : u32x4{0u, 0u, 0u, 0u};
+      rb[p] = (ka && n0 + row < N) ? ld_global(reinterpret_cast<const u32x4*>(B + (n0 + row) * ldb + kk))
+                                   : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&](int s) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const v8bf*>(As + (wm * 64 + i * 16 + l16) * kP + kk * 32 + lg * 8);
+    for (int p = 0; p < 4; ++p) {
+      const int q = tid + 256 * p, row = q >> 3, kc = 8 * (q & 7);
+      *reinterpret_cast<u32x4*>(&As[s][row * kBP + kc]) = ra[p];
+      *reinterpret_cast<u32x4*>(&Bs[s][row * kBP + kc]) = rb[p];
+    }
+  };
+
+  v4f c[4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const v8bf*>(Bs + (wn * 64 + j * 16 + l16) * kP + kk * 32 + lg * 8);
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) c[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  load(0);
+  store(0);
+  if (nks > 1) load(1);
+  __syncthreads();
+  for (int64_t ks = 0; ks < nks; ++ks) {
+    const int s = (int)(ks & 1);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      v8bf a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const v8bf*>(&As[s][(wm * 64 + i * 16 + l16) * kBP + kk * 32 + lg * 8]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], c[i][j], 0, 0, 0);
-  }
-}
-
-// dX tile: 128 tokens (blockIdx.y) x one 128-wide k block (blockIdx.x)
-template <int S>
-__global__ __launch_bounds__(256) void dx_kernel(const uint16_t* __restrict__ dY,
-                                                const uint32_t* __restrict__ packed,
-                                                const double* __restrict__ gamma,
-                                                float* __restrict__ dX, int64_t tokens, int64_t k,
-                                                int64_t n_out) {
-  constexpr int kW = block_bytes(S) / 4;
-  __shared__ __attribute__((aligned(16))) uint16_t As[128 * kP];  // [t][r]
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[128 * kP];  // [c][r]
-  __shared__ uint32_t lut[512];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  for (int idx = tid; idx < 512; idx += 256) lut[idx] = half_codes(idx & 255, idx >> 8);
-  const int64_t m0 = (int64_t)blockIdx.y * 128;
-  const int64_t kb = blockIdx.x;
-  const int64_t nkb = k / kBlockK;
-
-  v4f c[4][4];
+        b[j] = *reinterpret_cast<const v8bf*>(&Bs[s][(wn * 64 + j * 16 + l16) * kBP + kk * 32 + lg * 8]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t r0 = 0; r0 < n_out; r0 += 64) {
-    __syncthreads();
-    {  // A: dY[m0 + t][r0 .. r0+63], thread: token tid/2, 32 r's
-      const int t = tid >> 1, h = tid & 1;
-      const int64_t tt = m0 + t;
-      u32x4* dst = reinterpret_cast<u32x4*>(As + t * kP + h * 32);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t r = r0 + h * 32 + i * 8;
-        const bool ok = tt < tokens && r < n_out;
-        dst[i] = ok ? *reinterpret_cast<const u32x4*>(dY + tt * n_out + r) : u32x4{0u, 0u, 0u, 0u};
-      }
+        for (int j = 0; j < 4; ++j)
+          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], c[i][j], 0, 0, 0);
     }
-    {  // B: codes of rows r0 .. r0+63 (one packed superblock) for block
-       // kb, written transposed [c][r]; wavefront w decodes fields
-       // 4w..4w+3 of chunk `lane` (row tile w of the strip; padding rows
-       // of the last strip hold zero codes)
-      const int ch = lane;
-      uint32_t w[kW + 1];
-#pragma unroll
-      for (int i = 0; i <= kW; ++i) w[i] = 0;
-      {
-        const uint32_t* src = packed + (((r0 / kStripRows) * nkb + kb) * kStripRows + ch) * kW;
-#pragma unroll
-        for (int i = 0; i < kW; ++i) w[i] = src[i];
-      }
-      auto lk = [&](uint32_t key, int half) { return lut[half * 256 + key]; };
-      auto emit = [&](int f, uint32_t lo, uint32_t hi) {
-        const int rr = field_row(ch, f), gi = field_group(ch, f);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          Bs[(gi * 8 + p) * kP + rr] = code_bf16((lo >> (8 * p)) & 0xffu);
-          Bs[(gi * 8 + 4 + p) * kP + rr] = code_bf16((hi >> (8 * p)) & 0xffu);
-        }
-      };
-      switch (wave) {
-        case 0: decode_groups<S, 0, 4>(w, lk, emit); break;
-        case 1: decode_groups<S, 4, 4>(w, lk, emit); break;
-        case 2: decode_groups<S, 8, 4>(w, lk, emit); break;
-        default: decode_groups<S, 12, 4>(w, lk, emit); break;
-      }
+    if (ks + 1 < nks) {
+      store(s ^ 1);
+      if (ks + 2 < nks) load(ks + 2);
     }
     __syncthreads();
-    mma_tile(As, Bs, wm, wn, lane, c);
   }
-  const double g = *gamma;
-  const int l16 = lane & 15, lg = lane >> 4;
+
+  // lane holds C[m0 + 64wm + 16i + 4lg + q][n0 + 64wn + 16j + l16]
+  const double g = alpha ? *alpha : 1.0;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int64_t t = m0 + wm * 64 + i * 16 + 4 * lg + q;
-      if (t >= tokens) continue;
+      const int64_t m = m0 + wm * 64 + i * 16 + 4 * lg + q;
+      if (m >= M) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int64_t col = kb * kBlockK + wn * 64 + j * 16 + l16;
-        dX[t * k + col] = (float)((double)c[i][j][q] * g);
+        const int64_t n = n0 + wn * 64 + j * 16 + l16;
+        if (n < N) C[m * ldc + n] = alpha ? (float)((double)c[i][j][q] * g) : c[i][j][q];
       }
     }
 }
 
-// dW tile: 128 weight rows (blockIdx.y) x 128 input columns (blockIdx.x)
-__global__ __launch_bounds__(256) void dw_kernel(const uint16_t* __restrict__ dY,
-                                                const int8_t* __restrict__ xq,
-                                                const float* __restrict__ scale,
-                                                float* __restrict__ dW, int64_t tokens, int64_t k,
-                                                int64_t n_out) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[128 * kP];  // [r][t]
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[128 * kP];  // [c][t]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t r0 = (int64_t)blockIdx.y * 128;
-  const int64_t c0 = (int64_t)blockIdx.x * 128;
-
-  v4f c[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) c[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t t0 = 0; t0 < tokens; t0 += 64) {
-    __syncthreads();
-    const int t = tid >> 2, q = tid & 3;  // token, quarter (32 columns)
-    const int64_t tt = t0 + t;
-    {  // A: (dY[tt][r0 + ...] * s_tt) as bf16, transposed to [r][t]
-      const float s = tt < tokens ? scale[tt] : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t r = r0 + q * 32 + i * 8;
-        const bool ok = tt < tokens && r < n_out;
-        const u32x4 v = ok ? *reinterpret_cast<const u32x4*>(dY + tt * n_out + r) : u32x4{0u, 0u, 0u, 0u};
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
-          As[(q * 32 + i * 8 + e) * kP + t] = f32_to_bf16_rne(x * s);
-        }
-      }
-    }
-    {  // B: x_q[tt][c0 + ...] as bf16 (exact), transposed to [c][t]
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const u32x4 v = tt < tokens ? *reinterpret_cast<const u32x4*>(xq + tt * k + c0 + q * 32 + i * 16)
-                                    : u32x4{0u, 0u, 0u, 0u};
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int8_t b = (int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
-          Bs[(q * 32 + i * 16 + e) * kP + t] = f32_to_bf16_rne((float)b);
-        }
-      }
-    }
-    __syncthreads();
-    mma_tile(As, Bs, wm, wn, lane, c);
-  }
-  const int l16 = lane & 15, lg = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t r = r0 + wm * 64 + i * 16 + 4 * lg + q;
-      if (r >= n_out) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dW[r * k + c0 + wn * 64 + j * 16 + l16] = c[i][j][q];
-    }
+// zero fill (dW when there are no tokens)
+__global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
 }
 
-template <int S>
-static hipError_t launch_dx_s(const uint16_t* dY, const void* packed, const double* gamma, float* dX,
-                              int64_t tokens, int64_t k, int64_t n_out, hipStream_t s) {
-  dim3 grid((unsigned)(k / kBlockK), (unsigned)((tokens + 127) / 128));
-  dx_kernel<S><<<grid, 256, 0, s>>>(dY, reinterpret_cast<const uint32_t*>(packed), gamma, dX,
-                                    tokens, k, n_out);
+// ------------------------------------------------------------- launchers
+static hipError_t gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
+                          int64_t ldc, int64_t M, int64_t N, int64_t K, const double* alpha,
+                          hipStream_t s) {
+  dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
+  gemm_nt_bf16_kernel<<<grid, 256, 0, s>>>(A, lda, B, ldb, C, ldc, M, N, K, alpha);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dx(const uint16_t* dY, const void* packed, const double* gamma, float* dX,
-                         int64_t tokens, int64_t k, int64_t n_out, int S, hipStream_t s) {
-  if (S == 8) return launch_dx_s<8>(dY, packed, gamma, dX, tokens, k, n_out, s);
-  if (S == 6) return launch_dx_s<6>(dY, packed, gamma, dX, tokens, k, n_out, s);
-  return launch_dx_s<4>(dY, packed, gamma, dX, tokens, k, n_out, s);
+                         void* ws, int64_t tokens, int64_t k, int64_t n_out, int S, hipStream_t s) {
+  const int64_t nkb = k / kBlockK, strips = (n_out + kStripRows - 1) / kStripRows;
+  const int64_t np = strips * kStripRows;
+  uint16_t* codes_t = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + bwd_codes_offset(tokens, k, n_out));
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(packed);
+  const unsigned sbs = (unsigned)(strips * nkb);
+  if (S == 8) prep_codes_t_kernel<8><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
+  else if (S == 6) prep_codes_t_kernel<6><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
+  else prep_codes_t_kernel<4><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dX [tokens x k] = gamma * dY [tokens x n_out] . codes^T [k x n_out]^T
+  return gemm_nt(dY, n_out, codes_t, np, dX, k, tokens, k, n_out, gamma, s);
 }
 
 hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* xq, const float* scale, float* dW,
-                         int64_t tokens, int64_t k, int64_t n_out, hipStream_t s) {
-  dim3 grid((unsigned)(k / 128), (unsigned)((n_out + 127) / 128));
-  dw_kernel<<<grid, 256, 0, s>>>(dY, xq, scale, dW, tokens, k, n_out);
-  return hipGetLastError();
+                         void* ws, int64_t tokens, int64_t k, int64_t n_out, hipStream_t s) {
+  if (tokens == 0) {
+    zero_f32_kernel<<<1024, 256, 0, s>>>(dW, n_out * k);
+    return hipGetLastError();
+  }
+  const int64_t tp = bwd_tokens_padded(tokens);
+  char* w = reinterpret_cast<char*>(ws);
+  uint16_t* dys_t = reinterpret_cast<uint16_t*>(w + bwd_dys_offset(tokens, k, n_out));
+  uint16_t* xq_t = reinterpret_cast<uint16_t*>(w + bwd_xq_offset(tokens, k, n_out));
+  prep_dys_t_kernel<<<dim3((unsigned)(tp / 64), (unsigned)((n_out + 63) / 64)), 256, 0, s>>>(
+      dY, scale, tokens, n_out, tp, dys_t);
+  prep_xq_t_kernel<<<dim3((unsigned)(tp / 64), (unsigned)(k / 64)), 256, 0, s>>>(xq, tokens, k, tp,
+                                                                              xq_t);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dW [n_out x k] = (dY s)^T [n_out x tp] . x_q^T [k x tp]^T
+  return gemm_nt(dys_t, tp, xq_t, tp, dW, k, n_out, k, tp, nullptr, s);
 }
 
 }  // namespace bl

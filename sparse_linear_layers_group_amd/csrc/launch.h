@@ -170,10 +170,25 @@ hipError_t launch_gemm(const void* packed, const int8_t* xq, const float* scale,
                        const double* gamma, float* Y, int32_t* acc, void* ws, int64_t tokens,
                        int64_t k, int64_t n_out, int S, hipStream_t s);
 
-// backward
+// Backward.  Workspace (bf16 operands of the two products, each region
+// 256-byte aligned): (dY * s)^T [n_out x tp], x_q^T [k x tp] with tp the
+// token count rounded up to 64, and codes^T [k x 64 * strips].
+inline int64_t bwd_tokens_padded(int64_t tokens) { return (tokens + 63) / 64 * 64; }
+inline size_t bwd_align(size_t b) { return (b + 255) & ~(size_t)255; }
+inline size_t bwd_dys_offset(int64_t, int64_t, int64_t) { return 0; }
+inline size_t bwd_xq_offset(int64_t tokens, int64_t, int64_t n_out) {
+  return bwd_align((size_t)n_out * bwd_tokens_padded(tokens) * 2);
+}
+inline size_t bwd_codes_offset(int64_t tokens, int64_t k, int64_t n_out) {
+  return bwd_xq_offset(tokens, k, n_out) + bwd_align((size_t)k * bwd_tokens_padded(tokens) * 2);
+}
+inline size_t bwd_ws_bytes(int64_t tokens, int64_t k, int64_t n_out) {
+  const int64_t np = (n_out + 63) / 64 * 64;
+  return bwd_codes_offset(tokens, k, n_out) + bwd_align((size_t)k * np * 2);
+}
 hipError_t launch_bwd_dx(const uint16_t* dY, const void* packed, const double* gamma, float* dX,
-                         int64_t tokens, int64_t k, int64_t n_out, int S, hipStream_t s);
+                         void* ws, int64_t tokens, int64_t k, int64_t n_out, int S, hipStream_t s);
 hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* xq, const float* scale, float* dW,
-                         int64_t tokens, int64_t k, int64_t n_out, hipStream_t s);
+                         void* ws, int64_t tokens, int64_t k, int64_t n_out, hipStream_t s);
 
 }  // namespace bl

@@ -60,10 +60,17 @@ class BitLinearWeight:
                          b["Y"], b["xq"], b["x_scale"], acc=acc, ws=b["ws"], stream=stream)
         return b
 
-    def bwd(self, dY, xq, x_scale, tokens, dX=True, dW=True, stream=None):
+    def bwd_workspace(self, tokens):
+        """Device scratch of the backward (bf16 operands of its products)."""
+        n = bl.bitlinear_bwd_workspace_bytes(tokens, self.k, self.n_out)
+        return torch.empty(max(n, 1), dtype=torch.uint8, device=self.device)
+
+    def bwd(self, dY, xq, x_scale, tokens, dX=True, dW=True, ws=None, stream=None):
         d = self.device
         gx = torch.empty(tokens * self.k, dtype=torch.float32, device=d) if dX else None
         gw = torch.empty(self.n_out * self.k, dtype=torch.float32, device=d) if dW else None
+        if ws is None:
+            ws = self.bwd_workspace(tokens)
         bl.bitlinear_bwd(dY, xq, x_scale, self.packed, self.gamma, tokens, self.k, self.n_out,
-                         self.n, self.m, gx, gw, stream=stream)
+                         self.n, self.m, gx, gw, ws=ws, stream=stream)
         return gx, gw

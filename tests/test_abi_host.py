@@ -96,7 +96,12 @@ def test_bwd_validation(L):
     b = L.bitlinear_bwd
     assert b(A, A, A, A, A, 4, 256, 120, 6, 8, A, A, None, 0, None) == bl.BL_ESHAPE  # n_out % 16
     assert b(A, A, A, A, A, 4, 256, 128, 6, 8, A + 4, None, None, 0, None) == bl.BL_EINVAL
-    assert b(None, A, A, A, A, 4, 256, 128, 6, 8, A, None, None, 0, None) == bl.BL_EINVAL
+    need = bl.bitlinear_bwd_workspace_bytes(4, 256, 128)
+    assert need == L.bitlinear_bwd_workspace_bytes(4, 256, 128) > 0
+    assert bl.bitlinear_bwd_workspace_bytes(4, 256, 120) == 0  # n_out % 16
+    assert b(A, A, A, A, A, 4, 256, 128, 6, 8, A, None, None, 0, None) == bl.BL_EWORKSPACE
+    assert b(A, A, A, A, A, 4, 256, 128, 6, 8, A, None, A, need - 1, None) == bl.BL_EWORKSPACE
+    assert b(None, A, A, A, A, 4, 256, 128, 6, 8, A, None, A, need, None) == bl.BL_EINVAL
     assert b(A, A, A, A, A, 4, 256, 128, 6, 8, None, None, None, 0, None) == bl.BL_OK  # nothing asked
 
 
