@@ -413,6 +413,11 @@ int bitlinear_bwd(const uint16_t* dY, const int8_t* xq, const float* x_scale, co
     }
     return ok();
   }
+  {  // every bf16 operand of the two products stays below 2 GiB
+    const int64_t tp = bl::bwd_tokens_padded(tokens), np = (n_out + 63) / 64 * 64;
+    if (tp * n_out >= kLimit / 2 || tp * k >= kLimit / 2 || k * np >= kLimit / 2)
+      return fail(BL_ESHAPE, "the backward needs tokens*n_out, tokens*k and n_out*k below 2^30");
+  }
   const size_t need = bl::bwd_ws_bytes(tokens, k, n_out);
   if (!ws || ws_bytes < need)
     return fail(BL_EWORKSPACE, "backward workspace needs %zu bytes (got %zu)", need,

@@ -19,6 +19,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace bl {
 
 __device__ __forceinline__ uint16_t code_bf16(uint32_t byte) {
@@ -152,9 +154,9 @@ __global__ __launch_bounds__(64) void prep_codes_t_kernel(const uint32_t* __rest
 // Workgroup tile 128 x 128, four wavefronts of 64 x 64 (4 x 4 MFMA
 // tiles); k advances 64 at a time through double-buffered LDS tiles
 // (rows padded to 72 bf16: the 16-byte fragment reads of a quarter
-// wavefront fall on distinct bank groups).  The next step's tiles are in
-// registers while the MFMAs run; one barrier per step.  k positions at or
-// past K read as zero.
+// wavefront fall on distinct bank groups).  Global loads run two steps
+// ahead in a register ring; one barrier per step.  k positions at or past
+// K read as zero.
 constexpr int kBP = 72;
 
 __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(
@@ -171,26 +173,39 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(
   const int64_t nks = (K + 63) / 64;
 
   // loads: piece q = tid + 256 p (p < 4) of each tile is row q/8, k
-  // columns 8*(q%8) .. +8 of the step
-  u32x4 ra[4], rb[4];
-  auto load = [&](int64_t ks) {
+  // columns 8*(q%8) .. +8 of the step.  A register ring holds two steps in
+  // flight, so a step's global loads have two steps of MFMAs to land.
+  u32x4 ra[2][4], rb[2][4];
+  // buffer loads: an offset past the range (kOOB) reads zeros, so rows
+  // past M/N and k past K need no branches (operands stay below 2 GiB)
+  const __amdgpu_buffer_rsrc_t ar =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A), (short)0, (int)(M * lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t br =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(B), (short)0, (int)(N * ldb * 2), 0x00020000);
+  constexpr uint32_t kOOB = 0x80000000u;
+  uint32_t a_off[4], b_off[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int q = tid + 256 * p, row = q >> 3, kc = 8 * (q & 7);
+    a_off[p] = m0 + row < M ? (uint32_t)(((m0 + row) * lda + kc) * 2) : kOOB;
+    b_off[p] = n0 + row < N ? (uint32_t)(((n0 + row) * ldb + kc) * 2) : kOOB;
+  }
+  auto load = [&](int64_t ks, u32x4* xa, u32x4* xb) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int q = tid + 256 * p, row = q >> 3, kc = 8 * (q & 7);
-      const int64_t kk = ks * 64 + kc;
-      const bool ka = kk < K;
-      ra[p] = (ka && m0 + row < M) ? ld_global(reinterpret_cast<const u32x4*>(A + (m0 + row) * lda + kk))
-                                   : u32x4{0u, 0u, 0u, 0u};
-      rb[p] = (ka && n0 + row < N) ? ld_global(reinterpret_cast<const u32x4*>(B + (n0 + row) * ldb + kk))
-                                   : u32x4{0u, 0u, 0u, 0u};
+      const int kc = 8 * ((tid + 256 * p) & 7);
+      const bool ka = ks * 64 + kc < K;
+      const uint32_t ko = (uint32_t)(ks * 128);
+      xa[p] = __builtin_amdgcn_raw_buffer_load_b128(ar, ka ? a_off[p] + ko : kOOB, 0, 0);
+      xb[p] = __builtin_amdgcn_raw_buffer_load_b128(br, ka ? b_off[p] + ko : kOOB, 0, 0);
     }
   };
-  auto store = [&](int s) {
+  auto store = [&](int st, const u32x4* xa, const u32x4* xb) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int q = tid + 256 * p, row = q >> 3, kc = 8 * (q & 7);
-      *reinterpret_cast<u32x4*>(&As[s][row * kBP + kc]) = ra[p];
-      *reinterpret_cast<u32x4*>(&Bs[s][row * kBP + kc]) = rb[p];
+      *reinterpret_cast<u32x4*>(&As[st][row * kBP + kc]) = xa[p];
+      *reinterpret_cast<u32x4*>(&Bs[st][row * kBP + kc]) = xb[p];
     }
   };
 
@@ -200,36 +215,66 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) c[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  load(0);
-  store(0);
-  if (nks > 1) load(1);
-  __syncthreads();
-  for (int64_t ks = 0; ks < nks; ++ks) {
-    const int s = (int)(ks & 1);
+  // step ks (parity P): MFMAs from LDS stage P; in between, step ks+1
+  // (registers ra/rb[P^1], loaded two steps ago) goes to stage P^1 and
+  // those registers take the loads of step ks+3.  Loads past the last step
+  // read zeros (k >= K) and their stores are never read.
+  auto step = [&](auto parity, int64_t ks) {
+    constexpr int P = decltype(parity)::value;
+    // fragments of both k halves are read up front, so the second half's
+    // LDS latency hides behind the first half's MFMAs
+    v8bf a[2][4], b[2][4];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      v8bf a[4], b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const v8bf*>(&As[s][(wm * 64 + i * 16 + l16) * kBP + kk * 32 + lg * 8]);
+        a[kk][i] = *reinterpret_cast<const v8bf*>(&As[P][(wm * 64 + i * 16 + l16) * kBP + kk * 32 + lg * 8]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const v8bf*>(&Bs[s][(wn * 64 + j * 16 + l16) * kBP + kk * 32 + lg * 8]);
+        b[kk][j] = *reinterpret_cast<const v8bf*>(&Bs[P][(wn * 64 + j * 16 + l16) * kBP + kk * 32 + lg * 8]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], c[i][j], 0, 0, 0);
-    }
-    if (ks + 1 < nks) {
-      store(s ^ 1);
-      if (ks + 2 < nks) load(ks + 2);
+          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk][i], b[kk][j], c[i][j], 0, 0, 0);
+      if (kk == 0) {
+        store(P ^ 1, ra[P ^ 1], rb[P ^ 1]);
+        load(ks + 3, ra[P ^ 1], rb[P ^ 1]);
+      }
     }
     __syncthreads();
+  };
+
+  load(0, ra[0], rb[0]);
+  load(1, ra[1], rb[1]);
+  store(0, ra[0], rb[0]);
+  load(2, ra[0], rb[0]);
+  __syncthreads();
+  int64_t ks = 0;
+  for (; ks + 1 < nks; ks += 2) {
+    step(std::integral_constant<int, 0>{}, ks);
+    step(std::integral_constant<int, 1>{}, ks + 1);
   }
+  if (ks < nks) step(std::integral_constant<int, 0>{}, ks);
 
   // lane holds C[m0 + 64wm + 16i + 4lg + q][n0 + 64wn + 16j + l16]
   const double g = alpha ? *alpha : 1.0;
+  if (m0 + 128 <= M && n0 + 128 <= N) {  // whole tile in range: no checks
+    float* cb = C + (m0 + wm * 64 + 4 * lg) * ldc + n0 + wn * 64 + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float* cr = cb + (int64_t)(i * 16 + q) * ldc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          cr[j * 16] = alpha ? (float)((double)c[i][j][q] * g) : c[i][j][q];
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
