@@ -306,7 +306,7 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t
   h->steps = steps;
   h->strips = nstrips;
   bl::GroupItem* gi = reinterpret_cast<bl::GroupItem*>(img.data() + bl::group_items_offset(nstrips));
-  uint32_t* rows = reinterpret_cast<uint32_t*>(img.data() + bl::group_rows_offset(nstrips, count));
+  bl::RowDesc* rows = reinterpret_cast<bl::RowDesc*>(img.data() + bl::group_rows_offset(nstrips, count));
   int64_t r = 0;
   // every strip of every item: its descriptor and step count
   std::vector<bl::StripDesc> all;
@@ -316,7 +316,8 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t
     const bitlinear_fwd_item& it = items[i];
     gi[i] = bl::GroupItem{it.X, reinterpret_cast<const uint32_t*>(it.packed), it.gamma, it.Y,
                           it.xq, it.x_scale, it.k, it.n_out};
-    for (int64_t t = 0; t < tokens; ++t) rows[r++] = ((uint32_t)i << 4) | (uint32_t)t;
+    for (int64_t t = 0; t < tokens; ++t)
+      rows[r++] = bl::RowDesc{it.X + t * it.k, it.xq + t * it.k, it.x_scale + t, it.k};
     const int64_t strips = (it.n_out + bl::kStripRows - 1) / bl::kStripRows;
     const int64_t strip_bytes = (it.k / 128) * bl::kStripRows * bl::block_bytes(S);
     for (int64_t st = 0; st < strips; ++st) {

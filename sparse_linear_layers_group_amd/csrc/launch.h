@@ -113,9 +113,16 @@ struct WaveStart {            // a wavefront's range (80 bytes)
 };
 static_assert(sizeof(WaveStart) == 80, "wave start size");
 static_assert(offsetof(WaveStart, rec) == 64, "rec, kb, count, active: one 16-byte load");
+// one activation row of the plan (self-contained: one 32-byte load)
+struct RowDesc {
+  const uint16_t* X;  // bf16 [k]
+  int8_t* xq;         // int8 [k]
+  float* scale;       // one float
+  int64_t k;
+};
+static_assert(sizeof(RowDesc) == 32, "row descriptor size");
 // plan image: header (64 bytes) | wave starts[kDecodeBlocks * 16] |
-//             strip descriptors | items[count] | row table[rows]
-// row entry = item << 4 | token
+//             strip descriptors | items[count] | row descriptors[rows]
 constexpr size_t kGroupHeaderBytes = 64;
 static_assert(sizeof(GroupHeader) <= kGroupHeaderBytes, "plan header size");
 __host__ __device__ inline size_t group_waves_offset() { return kGroupHeaderBytes; }
@@ -129,7 +136,7 @@ __host__ __device__ inline size_t group_rows_offset(int64_t strips, int64_t coun
   return group_items_offset(strips) + (size_t)count * sizeof(GroupItem);
 }
 inline size_t group_plan_bytes(int64_t strips, int64_t count, int64_t rows) {
-  return group_rows_offset(strips, count) + (size_t)rows * 4;
+  return group_rows_offset(strips, count) + (size_t)rows * sizeof(RowDesc);
 }
 hipError_t launch_act_quant_group(const void* plan, hipStream_t s);
 hipError_t launch_gemv_group(const void* plan, int S, hipStream_t s);

@@ -398,40 +398,59 @@ __global__ __launch_bounds__(256) void ternary_pack_kernel(const uint16_t* __res
 // equals round-half-even of the exact quotient.  |x_q| <= 127, so the clip
 // to [-128, 127] never binds.  Optionally zeroes a workspace range.
 // ---------------------------------------------------------------------
+__device__ __forceinline__ uint2 quant8(const uint4& v, float a) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t q[2] = {0, 0};
+  if (a > 0.f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
+      const int qi = (int)rintf((127.0f * x) / a);
+      q[j >> 2] |= ((uint32_t)qi & 0xffu) << (8 * (j & 3));
+    }
+  }
+  return make_uint2(q[0], q[1]);
+}
+
+__device__ __forceinline__ float absmax8(const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a = fmaxf(a, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
+  return a;
+}
+
+// One row of k values by a 256-thread block.  Rows up to 256 * 8 * kHeld
+// values are read once and held in registers between the absmax and the
+// quantisation; longer rows take a second pass over memory.
+constexpr int kHeld = 4;  // 16-byte vectors held per thread (rows <= 8192)
 __device__ __forceinline__ void quant_row(const uint16_t* __restrict__ X, int64_t k,
                                           int8_t* __restrict__ xq, float* __restrict__ scale,
                                           float* red) {
   const uint4* row = reinterpret_cast<const uint4*>(X);
   const int64_t nvec = k / 8;
+  uint4 held[kHeld];
   float a = 0.f;
-  for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) {
-    uint4 v = row[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a = fmaxf(a, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
+  for (int h = 0; h < kHeld; ++h) {
+    const int64_t i = threadIdx.x + 256 * h;
+    held[h] = i < nvec ? row[i] : make_uint4(0, 0, 0, 0);
+    a = fmaxf(a, absmax8(held[h]));
   }
+  for (int64_t i = threadIdx.x + 256 * kHeld; i < nvec; i += 256) a = fmaxf(a, absmax8(row[i]));
   a = wave_max(a);
   __syncthreads();  // red[] free from a previous row
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
   __syncthreads();
-  a = red[0];
-  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) a = fmaxf(a, red[i]);
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   if (threadIdx.x == 0) *scale = a / 127.0f;
   uint2* out = reinterpret_cast<uint2*>(xq);
-  for (int64_t i = threadIdx.x; i < nvec; i += blockDim.x) {
-    uint4 v = row[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t q[2] = {0, 0};
-    if (a > 0.f) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float x = (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
-        int qi = (int)rintf((127.0f * x) / a);
-        q[j >> 2] |= ((uint32_t)qi & 0xffu) << (8 * (j & 3));
-      }
-    }
-    out[i] = make_uint2(q[0], q[1]);
+  for (int h = 0; h < kHeld; ++h) {
+    const int64_t i = threadIdx.x + 256 * h;
+    if (i < nvec) out[i] = quant8(held[h], a);
   }
+  for (int64_t i = threadIdx.x + 256 * kHeld; i < nvec; i += 256) out[i] = quant8(row[i], a);
 }
 
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ X, int64_t k,
@@ -439,7 +458,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
                                                        float* __restrict__ scale,
                                                        uint32_t* __restrict__ zero_ws,
                                                        int64_t zero_words) {
-  __shared__ float red[8];
+  __shared__ float red[4];
   const int64_t t = blockIdx.x;
   quant_row(X + t * k, k, xq + t * k, scale + t, red);
   if (zero_ws) {
@@ -448,18 +467,15 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
   }
 }
 
-// grouped: every (item, token) row of a decode plan, grid-stride
+// grouped: every row descriptor of a decode plan, grid-stride
 __global__ __launch_bounds__(256) void act_quant_group_kernel(const char* __restrict__ plan) {
-  __shared__ float red[8];
+  __shared__ float red[4];
   const GroupHeader* hdr = reinterpret_cast<const GroupHeader*>(plan);
-  const GroupItem* items = reinterpret_cast<const GroupItem*>(plan + group_items_offset(hdr->strips));
-  const uint32_t* rows =
-      reinterpret_cast<const uint32_t*>(plan + group_rows_offset(hdr->strips, hdr->count));
+  const RowDesc* rows =
+      reinterpret_cast<const RowDesc*>(plan + group_rows_offset(hdr->strips, hdr->count));
   for (int64_t r = blockIdx.x; r < hdr->rows; r += gridDim.x) {
-    const uint32_t e = rows[r];
-    const GroupItem it = items[e >> 4];
-    const int64_t t = e & 15u;
-    quant_row(it.X + t * it.k, it.k, it.xq + t * it.k, it.scale + t, red);
+    const RowDesc d = rows[r];
+    quant_row(d.X, d.k, d.xq, d.scale, red);
   }
 }
 
