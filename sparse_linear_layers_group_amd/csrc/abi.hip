@@ -305,8 +305,8 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t
   h->rows = count * tokens;
   h->steps = steps;
   h->strips = nstrips;
-  bl::GroupItem* gi = reinterpret_cast<bl::GroupItem*>(img.data() + bl::group_items_offset(nstrips));
-  bl::RowDesc* rows = reinterpret_cast<bl::RowDesc*>(img.data() + bl::group_rows_offset(nstrips, count));
+  bl::GroupItem* gi = reinterpret_cast<bl::GroupItem*>(img.data() + bl::group_items_offset(count * tokens, nstrips));
+  bl::RowDesc* rows = reinterpret_cast<bl::RowDesc*>(img.data() + bl::group_rows_offset());
   int64_t r = 0;
   // every strip of every item: its descriptor and step count
   std::vector<bl::StripDesc> all;
@@ -345,7 +345,7 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t
     heap.push(l);
   }
   bl::WaveStart* wst = reinterpret_cast<bl::WaveStart*>(img.data() + bl::group_waves_offset());
-  bl::StripDesc* descs = reinterpret_cast<bl::StripDesc*>(img.data() + bl::group_strips_offset());
+  bl::StripDesc* descs = reinterpret_cast<bl::StripDesc*>(img.data() + bl::group_strips_offset(count * tokens));
   int32_t next = 0;
   for (int64_t b = 0; b < nb; ++b) {
     std::vector<int32_t>& lst = lists[(size_t)b];

@@ -115,7 +115,8 @@ __global__ __launch_bounds__(64) void prep_codes_t_kernel(const uint32_t* __rest
   __shared__ uint16_t tile[kBlockK * kTP];  // [c][r]
   __shared__ uint32_t lut[512];
   const int lane = threadIdx.x;
-  for (int idx = lane; idx < 512; idx += 64) lut[idx] = half_codes(idx & 255, idx >> 8);
+  for (int idx = lane; idx < 512; idx += 64)  // lut[half * 256 + key]
+    lut[idx] = ld_global(&kHalfCodeTable.v[(idx & 255) * 2 + (idx >> 8)]);
   const int64_t sb = blockIdx.x;  // superblock = strip * nkb + kb
   const int64_t strip = sb / nkb, kb = sb - strip * nkb;
   uint32_t w[kW + 1];

@@ -152,7 +152,7 @@ __device__ __forceinline__ uint32_t funnel(uint32_t hi, uint32_t lo, uint32_t sh
 // int8x4 codes of one half-group from its 8-bit key.
 // half 0: key = bitmap(4) | signs(4) << 4, i-th nonzero's sign at bit 4+i
 // half 1: key = signs(4) | bitmap(4) << 4, i-th nonzero's sign at bit 3-i
-__device__ inline uint32_t half_codes(uint32_t key, uint32_t half) {
+__host__ __device__ constexpr uint32_t half_codes(uint32_t key, uint32_t half) {
   const uint32_t bm = half ? (key >> 4) : (key & 15u);
   const uint32_t sg = half ? (key & 15u) : (key >> 4);
   uint32_t out = 0, rank = 0;
@@ -166,6 +166,18 @@ __device__ inline uint32_t half_codes(uint32_t key, uint32_t half) {
   return out;
 }
 
+// The 512 table entries, entry key * 2 + half, built at compile time and
+// held in device memory: a kernel fills its LDS copies with plain loads.
+struct HalfCodeTable {
+  uint32_t v[512];
+};
+constexpr HalfCodeTable make_half_code_table() {
+  HalfCodeTable t{};
+  for (uint32_t e = 0; e < 512; ++e) t.v[e] = half_codes(e >> 1, e & 1u);
+  return t;
+}
+__device__ constexpr HalfCodeTable kHalfCodeTable = make_half_code_table();
+static_assert(make_half_code_table().v[2 * 0x1f + 0] == 0x010101ffu, "low half: bitmap 1111, sign of nonzero 0");
 
 // Decode groups [G0, G0+NG) of one packed block held in registers w[0..kW]
 // (w[kW] = 0): emit(g, lo, hi) receives the int8x4 codes of positions 0..3

@@ -175,20 +175,17 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
   load_chunk(0, w[0]);
   load_chunk(1, w[1]);
   load_x(1, xv[1]);
-  // tables, while those loads fly: the 512 distinct entries (key * 2 +
-  // half), two per thread, go to the idle LDS stage 1; then every thread
-  // writes 16-byte runs of copies
+  // tables, while those loads fly: 16-byte runs of copies of the
+  // compile-time entries (key * 2 + half) from device memory
   {
-    uint32_t* ent = reinterpret_cast<uint32_t*>(Bs[1]);
-    ent[tid] = half_codes((uint32_t)tid >> 1, (uint32_t)tid & 1u);
-    ent[tid + 256] = half_codes((uint32_t)(tid + 256) >> 1, (uint32_t)tid & 1u);
-    __syncthreads();
+    constexpr int kRuns = 512 * kGLutCopies / 4 / 256;
+    uint32_t v[kRuns];
 #pragma unroll
-    for (int r = 0; r < 512 * kGLutCopies / 4 / 256; ++r) {
-      const int ch = tid + 256 * r;  // 16-byte run: copies 4(ch%4).. of entry ch/4
-      const uint32_t v = ent[ch / (kGLutCopies / 4)];
-      reinterpret_cast<u32x4*>(lut)[ch] = u32x4{v, v, v, v};
-    }
+    for (int r = 0; r < kRuns; ++r)
+      v[r] = ld_global(&kHalfCodeTable.v[(tid + 256 * r) / (kGLutCopies / 4)]);
+#pragma unroll
+    for (int r = 0; r < kRuns; ++r)
+      reinterpret_cast<u32x4*>(lut)[tid + 256 * r] = u32x4{v[r], v[r], v[r], v[r]};
   }
   store_x(0, xv[0]);
   load_x(2, xv[0]);

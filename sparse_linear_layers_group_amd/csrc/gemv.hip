@@ -47,18 +47,19 @@ constexpr int kSlotDwords = 16 * kStripRows;  // one wavefront's cut-strip sums 
 
 // Tables in LDS: entry (key, half) of copy c at dword (key * 2 + half) * 64 + c
 // (128 KB).  Lane l always reads copy l, i.e. bank l, so a wavefront's 64
-// lookups never collide whatever the keys.  The fill first computes the 512
-// distinct entries into a small table, then writes the big one linearly
-// (consecutive lanes, consecutive 16-byte chunks: no bank conflicts).
-__device__ __forceinline__ void fill_lut(uint32_t* lut, uint32_t* entries) {
-  for (int idx = threadIdx.x; idx < 512; idx += blockDim.x)
-    entries[idx] = half_codes(idx >> 1, idx & 1);  // entry index = key * 2 + half
-  __syncthreads();
+// lookups never collide whatever the keys.  The fill reads the 512 entries
+// from the compile-time table in device memory and writes the big one
+// linearly (consecutive lanes, consecutive 16-byte chunks: no conflicts).
+__device__ __forceinline__ void fill_lut(uint32_t* lut) {
   constexpr int kChunks = 512 * kLutCopies / 4;  // 16-byte chunks
-  for (int ch = threadIdx.x; ch < kChunks; ch += blockDim.x) {
-    const uint32_t v = entries[ch / (kLutCopies / 4)];
-    reinterpret_cast<uint4*>(lut)[ch] = make_uint4(v, v, v, v);
-  }
+  static_assert(kChunks % kGemvThreads == 0, "every thread fills the same count");
+  uint32_t v[kChunks / kGemvThreads];
+#pragma unroll
+  for (int r = 0; r < kChunks / kGemvThreads; ++r)
+    v[r] = ld_global(&kHalfCodeTable.v[(threadIdx.x + kGemvThreads * r) / (kLutCopies / 4)]);
+#pragma unroll
+  for (int r = 0; r < kChunks / kGemvThreads; ++r)
+    reinterpret_cast<uint4*>(lut)[threadIdx.x + kGemvThreads * r] = make_uint4(v[r], v[r], v[r], v[r]);
 }
 static_assert(kGemvWaves * kSlotDwords <= 256 * 2 * kLutCopies, "cut-strip slots fit the tables");
 
@@ -236,7 +237,7 @@ struct WaveRange {
 // and step count of wavefront w of this workgroup -- and cross()/
 // cross_sum() for strips that continue in another workgroup.
 template <int S, class Src>
-__device__ __forceinline__ void run_block(const Src& src, uint32_t* lut, uint32_t* entries,
+__device__ __forceinline__ void run_block(const Src& src, uint32_t* lut,
                                           int lane) {
   const int tokens = src.tokens;
   const int w = wave_id();
@@ -280,7 +281,7 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut, uint32_
 #pragma unroll
     for (int s = 0; s < kDepth - 1; ++s) load_step(ring[s]);
   }
-  fill_lut(lut, entries);
+  fill_lut(lut);
   __syncthreads();
   if (count > 0) {
     while (cleft > 0) {
@@ -492,22 +493,21 @@ struct GroupSrc {
 template <int S>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(SingleSrc<S> src) {
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 2 * kLutCopies];
-  __shared__ uint32_t entries[512];
-  run_block<S>(src, lut, entries, threadIdx.x & 63);
+  run_block<S>(src, lut, threadIdx.x & 63);
 }
 
 template <int S>
 __global__ __launch_bounds__(kGemvThreads) void gemv_group_kernel(const char* __restrict__ plan) {
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 2 * kLutCopies];
-  __shared__ uint32_t entries[512];
   GroupSrc<S> src;
   src.starts = reinterpret_cast<const WaveStart*>(plan + group_waves_offset());
   // every wavefront of a workgroup reads the same flag: the whole workgroup
   // leaves or stays
   if (!src.starts[(int64_t)blockIdx.x * kGemvWaves].active) return;
-  src.strips = reinterpret_cast<const StripDesc*>(plan + group_strips_offset());
+  src.strips = reinterpret_cast<const StripDesc*>(
+      plan + group_strips_offset(reinterpret_cast<const GroupHeader*>(plan)->rows));
   src.tokens = reinterpret_cast<const GroupHeader*>(plan)->tokens;
-  run_block<S>(src, lut, entries, threadIdx.x & 63);
+  run_block<S>(src, lut, threadIdx.x & 63);
 }
 
 template <int S>

@@ -122,21 +122,25 @@ struct RowDesc {
 };
 static_assert(sizeof(RowDesc) == 32, "row descriptor size");
 // plan image: header (64 bytes) | wave starts[kDecodeBlocks * 16] |
-//             strip descriptors | items[count] | row descriptors[rows]
+//             row descriptors[rows] | strip descriptors | items[count]
+// (the row descriptors sit at a fixed offset, so the activation kernel
+// reads its row without waiting for the header; the region holds at least
+// one descriptor per activation workgroup, zero-padded)
 constexpr size_t kGroupHeaderBytes = 64;
+constexpr int kActGroupBlocks = 1024;  // activation workgroups of a grouped run
 static_assert(sizeof(GroupHeader) <= kGroupHeaderBytes, "plan header size");
 __host__ __device__ inline size_t group_waves_offset() { return kGroupHeaderBytes; }
-__host__ __device__ inline size_t group_strips_offset() {
+__host__ __device__ inline size_t group_rows_offset() {
   return kGroupHeaderBytes + (size_t)kDecodeBlocks * kDecodeWavesPerBlock * sizeof(WaveStart);
 }
-__host__ __device__ inline size_t group_items_offset(int64_t strips) {
-  return group_strips_offset() + (size_t)strips * sizeof(StripDesc);
+__host__ __device__ inline size_t group_strips_offset(int64_t rows) {
+  return group_rows_offset() + (size_t)(rows > kActGroupBlocks ? rows : kActGroupBlocks) * sizeof(RowDesc);
 }
-__host__ __device__ inline size_t group_rows_offset(int64_t strips, int64_t count) {
-  return group_items_offset(strips) + (size_t)count * sizeof(GroupItem);
+__host__ __device__ inline size_t group_items_offset(int64_t rows, int64_t strips) {
+  return group_strips_offset(rows) + (size_t)strips * sizeof(StripDesc);
 }
 inline size_t group_plan_bytes(int64_t strips, int64_t count, int64_t rows) {
-  return group_rows_offset(strips, count) + (size_t)rows * sizeof(RowDesc);
+  return group_items_offset(rows, strips) + (size_t)count * sizeof(GroupItem);
 }
 hipError_t launch_act_quant_group(const void* plan, hipStream_t s);
 hipError_t launch_gemv_group(const void* plan, int S, hipStream_t s);

@@ -471,10 +471,13 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
 __global__ __launch_bounds__(256) void act_quant_group_kernel(const char* __restrict__ plan) {
   __shared__ float red[4];
   const GroupHeader* hdr = reinterpret_cast<const GroupHeader*>(plan);
-  const RowDesc* rows =
-      reinterpret_cast<const RowDesc*>(plan + group_rows_offset(hdr->strips, hdr->count));
-  for (int64_t r = blockIdx.x; r < hdr->rows; r += gridDim.x) {
-    const RowDesc d = rows[r];
+  const RowDesc* rows = reinterpret_cast<const RowDesc*>(plan + group_rows_offset());
+  const int64_t nrows = hdr->rows;
+  // the first row descriptor is read together with the header (the row
+  // region holds at least kActGroupBlocks zero-padded descriptors)
+  RowDesc d = rows[blockIdx.x];
+  for (int64_t r = blockIdx.x; r < nrows; r += gridDim.x) {
+    if (r != blockIdx.x) d = rows[r];
     quant_row(d.X, d.k, d.xq, d.scale, red);
   }
 }
@@ -530,7 +533,7 @@ hipError_t launch_ternary_pack(const uint16_t* W, const uint8_t* mask, const dou
 }
 
 hipError_t launch_act_quant_group(const void* plan, hipStream_t s) {
-  act_quant_group_kernel<<<1024, 256, 0, s>>>(reinterpret_cast<const char*>(plan));
+  act_quant_group_kernel<<<kActGroupBlocks, 256, 0, s>>>(reinterpret_cast<const char*>(plan));
   return hipGetLastError();
 }
 
