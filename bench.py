@@ -55,8 +55,8 @@ DECODE_TRAFFIC = {
     "sources": ["sparse_linear_layers_group_amd/csrc/gemv.hip",
                 "sparse_linear_layers_group_amd/csrc/common.h",
                 "sparse_linear_layers_group_amd/csrc/launch.h"],
-    "sha256": "c37230644d718c866121f8a0df4b40433e3d4a0bffdd58724fca5e008b4ea2a7",
-    "fetch_kib": 39774.51, "fetch_scale": 2.0,
+    "sha256": "be5ba29fa4e9c61c646d16683c310f2df760a4d1fe67fd8cbe1c87b55cfe7a95",
+    "fetch_kib": 39769.39, "fetch_scale": 2.0,
     "write_kib": 1188.0, "write_scale": 1.0,
 }
 
