@@ -86,7 +86,38 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 256 MiB device copies (reference for the HBM byte counters)")
+    ap.add_argument("--library-reference", action="store_true",
+                    help="only time the vendor library's dense GEMMs (torch -> hipBLASLt) at the "
+                         "prefill and backward shapes, as context for the roofline fractions")
     return ap.parse_args()
+
+
+def library_reference(torch, reps=10):
+    """Dense bf16 and int8 GEMMs of the vendor library at the shapes this
+    path contracts (C[M x N] = A[M x K] B[N x K]^T), timed like the kernels.
+    Context only: nothing of the path runs through them."""
+    shapes = [("prefill gate/up", 2048, 8960, 1536), ("prefill down", 2048, 1536, 8960),
+              ("bwd dX gate", 4096, 2560, 6912), ("bwd dW gate", 6912, 2560, 4096)]
+    out = []
+    for name, M, N, K in shapes:
+        a = torch.randn(M, K, dtype=torch.bfloat16, device="cuda")
+        b = torch.randn(N, K, dtype=torch.bfloat16, device="cuda")
+        ai = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda")
+        bi = torch.randint(-1, 2, (N, K), dtype=torch.int8, device="cuda")
+        row = {"shape": name, "M": M, "N": N, "K": K}
+        for kind, f, peak in (("bf16", lambda: a @ b.t(), BF16_PEAK_TFLOPS),
+                              ("int8", lambda: torch._int_mm(ai, bi.t()), INT8_PEAK_TOPS)):
+            for _ in range(3):
+                f()
+            torch.cuda.synchronize()
+            with Timer(torch) as t:
+                for _ in range(reps):
+                    f()
+            tops = 2 * M * N * K / (t.ms() / reps * 1e-3) / 1e12
+            row[kind] = {"us": round(1000 * t.ms() / reps, 1), "tops": round(tops, 1),
+                         "frac": round(tops / peak, 4)}
+        out.append(row)
+    print(json.dumps({"library_reference": out}), flush=True)
 
 
 def copy_calibration(torch, reps=5):
@@ -411,6 +442,9 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.library_reference:
+        library_reference(torch)
         return
     from sparse_linear_layers_group_amd import bitlinear as bl
     if not os.path.exists(bl.LIB_PATH):
