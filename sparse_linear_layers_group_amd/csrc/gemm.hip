@@ -19,8 +19,8 @@
 // wavefront) and the writes (two tokens x eight pieces per quarter
 // wavefront) both spread over all banks.  Per k block a wavefront issues
 // the MFMAs of block kb while it decodes block kb+1, writes the activations
-// of kb+1 and loads those of kb+2 and the chunk of kb+3; one barrier per k
-// block.  With BT = 64 (the launched size) LDS stays at 48 KiB and
+// of kb+1 and loads those of kb+3 and the chunk of kb+3 (a three-slot
+// register ring for chunks); one barrier per k block.  With BT = 64 (the launched size) LDS stays at 48 KiB and
 // registers at <= 168, so three workgroups share a CU; on MI355X that beat
 // 128-token tiles at two per CU on every measured shape (more tiles for
 // layers with few rows, shorter store bursts at the end of a round).
@@ -166,14 +166,15 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
     for (int i = 0; i < 4; ++i) c[j][i] = v4i{0, 0, 0, 0};
 
   u32x4 xv[2][kPieces];  // activations, two k blocks ahead of their LDS stage
-  uint32_t w[2][kW];     // chunks of k blocks kb+1 and kb+2 (w[(kb+2)%2]) in flight
+  uint32_t w[3][kW];     // chunk ring: the chunk of k block kb sits in w[kb % 3]
   v4i a[8];              // A operands a[2i + h] (row tile i, k half h)
 
   // prologue: k block 0 in LDS stage 0 with its half 0 decoded; the
-  // activations of blocks 1, 2 and the chunk of block 1 in flight
+  // activations of blocks 1, 2 and the chunks of blocks 1, 2 in flight
   load_x(0, xv[0]);
   load_chunk(0, w[0]);
   load_chunk(1, w[1]);
+  load_chunk(2, w[2]);
   load_x(1, xv[1]);
   // tables, while those loads fly: 16-byte runs of copies of the
   // compile-time entries (key * 2 + half) from device memory
@@ -220,15 +221,16 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
   // spread over the kTT segments
   static_assert(kTT == 8 || kTT == 4, "side work is laid out for 8 or 4 segments per half");
   constexpr int kPairs = 8 / kTT;
-  auto kblock = [&](auto parity, int kb) {
+  // k block kb runs with LDS stage P = kb % 2 and chunk slot R = kb % 3.
+  // The chunk of kb is decoded (its half 1) during half 0; its slot then
+  // takes the load of chunk kb+3, so chunk loads have about three k blocks
+  // to land.  Each load writes a fixed register set that nothing copies,
+  // so the compiler needs no early wait for it.
+  auto kblock = [&](auto parity, auto slot, int kb) {
     constexpr int P = decltype(parity)::value;
-    // chunk kb (loaded two blocks ago) moves to wc, and its registers take
-    // the load of chunk kb+2 at once; chunk kb+1 sits in w[P^1]
-    uint32_t wc[kW];
-#pragma unroll
-    for (int q = 0; q < kW; ++q) wc[q] = w[P][q];
-    load_chunk(kb + 2, w[P]);
-    const uint32_t* wn = w[P ^ 1];
+    constexpr int R = decltype(slot)::value;
+    const uint32_t* wc = w[R];
+    const uint32_t* wn = w[(R + 1) % 3];
     // past the last block the side work is harmless and branch-free: the
     // loads read zeros (out-of-range offsets), the decoded codes and the
     // other LDS stage are never used
@@ -239,6 +241,7 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
         decode_field(wc, f >> 1, 1, f & 1, a[2 * (f >> 1) + 1]);
       }
     });
+    load_chunk(kb + 3, w[R]);
     half(parity, std::integral_constant<int, 1>{}, [&](int j) {
 #pragma unroll
       for (int u = 0; u < kPairs; ++u) {
@@ -250,12 +253,23 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
     });
     __syncthreads();
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   int kb = 0;
-  for (; kb + 1 < nkb; kb += 2) {
-    kblock(std::integral_constant<int, 0>{}, kb);
-    kblock(std::integral_constant<int, 1>{}, kb + 1);
+  for (; kb + 5 < nkb; kb += 6) {  // six blocks: both parities x three slots
+    kblock(I0{}, I0{}, kb);
+    kblock(I1{}, I1{}, kb + 1);
+    kblock(I0{}, I2{}, kb + 2);
+    kblock(I1{}, I0{}, kb + 3);
+    kblock(I0{}, I1{}, kb + 4);
+    kblock(I1{}, I2{}, kb + 5);
   }
-  if (kb < nkb) kblock(std::integral_constant<int, 0>{}, kb);
+  if (kb < nkb) kblock(I0{}, I0{}, kb);
+  if (kb + 1 < nkb) kblock(I1{}, I1{}, kb + 1);
+  if (kb + 2 < nkb) kblock(I0{}, I2{}, kb + 2);
+  if (kb + 3 < nkb) kblock(I1{}, I0{}, kb + 3);
+  if (kb + 4 < nkb) kblock(I0{}, I1{}, kb + 4);
 
   if (!live) return;
   if (splits > 1) {
