@@ -154,11 +154,11 @@ __global__ __launch_bounds__(64) void prep_codes_t_kernel(const uint32_t* __rest
 // pitches lda/ldb (elements, multiples of 8), C binary32 [M][ldc].
 // Workgroup tile 128 x 128, four wavefronts of 64 x 64 (4 x 4 MFMA
 // tiles); k advances 64 at a time through double-buffered LDS tiles
-// (rows padded to 72 bf16: the 16-byte fragment reads of a quarter
-// wavefront fall on distinct bank groups).  Global loads run two steps
+// (rows padded to 80 bf16; of the pitches 64, 68, 72 and 80 this one
+// measured fastest on MI355X, 64 slowest).  Global loads run two steps
 // ahead in a register ring; one barrier per step.  k positions at or past
-// K read as zero.
-constexpr int kBP = 72;
+// K read as zero.  The output goes out with streaming stores.
+constexpr int kBP = 80;
 
 __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(
         float* cr = cb + (int64_t)(i * 16 + q) * ldc;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          cr[j * 16] = alpha ? (float)((double)c[i][j][q] * g) : c[i][j][q];
+          st_stream(cr + j * 16, alpha ? (float)((double)c[i][j][q] * g) : c[i][j][q]);
       }
     return;
   }

@@ -82,6 +82,12 @@ template <class T>
 __device__ __forceinline__ void st_global(T* p, T v) {
   *(__attribute__((address_space(1))) T*)(p) = v;
 }
+// a store that streams past the caches (non-temporal): for large outputs
+// that no later access in the kernel reads
+template <class T>
+__device__ __forceinline__ void st_stream(T* p, T v) {
+  __builtin_nontemporal_store(v, (__attribute__((address_space(1))) T*)(p));
+}
 
 // Device-scope integer atomics through global-address-space pointers: on a
 // generic pointer they would be FLAT operations, which may touch LDS, and a

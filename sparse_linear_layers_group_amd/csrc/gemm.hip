@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
       const uint32_t o = base + (uint32_t)(16 * j) * (uint32_t)n_out;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        st_global(reinterpret_cast<v4f*>(Y + o + 16 * i),
+        st_stream(reinterpret_cast<v4f*>(Y + o + 16 * i),
                   v4f{out_value(c[j][i][0], gs), out_value(c[j][i][1], gs),
                       out_value(c[j][i][2], gs), out_value(c[j][i][3], gs)});
         if (acc_out) st_global(reinterpret_cast<v4i*>(acc_out + o + 16 * i), c[j][i]);
