@@ -352,12 +352,12 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t
     std::sort(lst.begin(), lst.end());  // strip index order = (item, strip) order
     int64_t n_b = 0;
     for (int32_t j : lst) n_b += nkb[j];
-    // wavefront w runs local steps [n_b * w / 16, n_b * (w + 1) / 16)
+    // wavefront w runs local steps [wave_split(n_b, w), wave_split(n_b, w + 1))
     size_t pos = 0;
     int64_t cum = 0;
     for (int w = 0; w < bl::kDecodeWavesPerBlock; ++w) {
-      const int64_t s0 = n_b * w / bl::kDecodeWavesPerBlock;
-      const int64_t s1 = n_b * (w + 1) / bl::kDecodeWavesPerBlock;
+      const int64_t s0 = bl::wave_split(n_b, w);
+      const int64_t s1 = bl::wave_split(n_b, w + 1);
       while (pos + 1 < lst.size() && cum + nkb[lst[pos]] <= s0) cum += nkb[lst[pos++]];
       bl::WaveStart& ws = wst[b * bl::kDecodeWavesPerBlock + w];
       ws.active = n_b > 0 ? 1 : 0;

@@ -171,23 +171,23 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
 
   // prologue: k block 0 in LDS stage 0 with its half 0 decoded; the
   // activations of blocks 1, 2 and the chunks of blocks 1, 2 in flight
+  // tables: 16-byte runs of copies of the compile-time entries (key * 2 +
+  // half) from device memory.  Their reads go out before the first blocks'
+  // loads (loads complete in order, so behind those they would wait for
+  // HBM); the LDS writes happen while those loads fly.
+  constexpr int kRuns = 512 * kGLutCopies / 4 / 256;
+  uint32_t tv[kRuns];
+#pragma unroll
+  for (int r = 0; r < kRuns; ++r)
+    tv[r] = ld_global(&kHalfCodeTable.v[(tid + 256 * r) / (kGLutCopies / 4)]);
   load_x(0, xv[0]);
   load_chunk(0, w[0]);
   load_chunk(1, w[1]);
   load_chunk(2, w[2]);
   load_x(1, xv[1]);
-  // tables, while those loads fly: 16-byte runs of copies of the
-  // compile-time entries (key * 2 + half) from device memory
-  {
-    constexpr int kRuns = 512 * kGLutCopies / 4 / 256;
-    uint32_t v[kRuns];
 #pragma unroll
-    for (int r = 0; r < kRuns; ++r)
-      v[r] = ld_global(&kHalfCodeTable.v[(tid + 256 * r) / (kGLutCopies / 4)]);
-#pragma unroll
-    for (int r = 0; r < kRuns; ++r)
-      reinterpret_cast<u32x4*>(lut)[tid + 256 * r] = u32x4{v[r], v[r], v[r], v[r]};
-  }
+  for (int r = 0; r < kRuns; ++r)
+    reinterpret_cast<u32x4*>(lut)[tid + 256 * r] = u32x4{tv[r], tv[r], tv[r], tv[r]};
   store_x(0, xv[0]);
   load_x(2, xv[0]);
   __syncthreads();  // tables and stage 0 ready

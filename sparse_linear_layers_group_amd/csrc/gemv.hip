@@ -46,20 +46,29 @@ constexpr int kDepth = 3;       // register ring: steps in flight + 1
 constexpr int kSlotDwords = 16 * kStripRows;  // one wavefront's cut-strip sums [token][row]
 
 // Tables in LDS: entry (key, half) of copy c at dword (key * 2 + half) * 64 + c
-// (128 KB).  Lane l always reads copy l, i.e. bank l, so a wavefront's 64
-// lookups never collide whatever the keys.  The fill reads the 512 entries
-// from the compile-time table in device memory and writes the big one
-// linearly (consecutive lanes, consecutive 16-byte chunks: no conflicts).
-__device__ __forceinline__ void fill_lut(uint32_t* lut) {
-  constexpr int kChunks = 512 * kLutCopies / 4;  // 16-byte chunks
-  static_assert(kChunks % kGemvThreads == 0, "every thread fills the same count");
-  uint32_t v[kChunks / kGemvThreads];
+// (128 KB).  Lane l always reads copy l, i.e. bank l % 32, so the lookups
+// of each half wavefront never collide whatever the keys.  The fill reads
+// the 512 entries from the compile-time table in device memory and writes
+// the big one linearly (consecutive lanes, consecutive 16-byte chunks: no
+// conflicts).  The reads are issued before the first steps' loads: loads
+// complete in order, and a table read queued behind them would wait for
+// HBM (measured: ~3 us from entry to the filled tables that way).
+constexpr int kLutChunks = 512 * kLutCopies / 4;  // 16-byte chunks
+static_assert(kLutChunks % kGemvThreads == 0, "every thread fills the same count");
+struct LutVals {
+  uint32_t v[kLutChunks / kGemvThreads];
+};
+__device__ __forceinline__ LutVals load_lut() {
+  LutVals t;
 #pragma unroll
-  for (int r = 0; r < kChunks / kGemvThreads; ++r)
-    v[r] = ld_global(&kHalfCodeTable.v[(threadIdx.x + kGemvThreads * r) / (kLutCopies / 4)]);
+  for (int r = 0; r < kLutChunks / kGemvThreads; ++r)
+    t.v[r] = ld_global(&kHalfCodeTable.v[(threadIdx.x + kGemvThreads * r) / (kLutCopies / 4)]);
+  return t;
+}
+__device__ __forceinline__ void write_lut(uint32_t* lut, const LutVals& t) {
 #pragma unroll
-  for (int r = 0; r < kChunks / kGemvThreads; ++r)
-    reinterpret_cast<uint4*>(lut)[threadIdx.x + kGemvThreads * r] = make_uint4(v[r], v[r], v[r], v[r]);
+  for (int r = 0; r < kLutChunks / kGemvThreads; ++r)
+    reinterpret_cast<uint4*>(lut)[threadIdx.x + kGemvThreads * r] = make_uint4(t.v[r], t.v[r], t.v[r], t.v[r]);
 }
 static_assert(kGemvWaves * kSlotDwords <= 256 * 2 * kLutCopies, "cut-strip slots fit the tables");
 
@@ -266,6 +275,7 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut,
   bool l_first = true, c_first = true;
   float cur_sc = 0.f;
   double cur_gm = 0.0;
+  float first_gs = 0.f;  // output scale of the wavefront's first strip
   auto load_step = [&](Stage<S>& st) {
     issue<S>(st, L, live, lane, tokens);
     if (L.kb == 0 || l_first) issue_scale<S>(st, L, lane, tokens);  // wave-uniform
@@ -275,13 +285,14 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut,
       else src.advance(L);
     }
   };
-  // the first steps' loads are in flight while the workgroup builds the
-  // code tables
+  // the table reads go first; the first steps' loads are in flight while
+  // the workgroup builds the code tables
+  const LutVals lv = load_lut();
   if (count > 0) {
 #pragma unroll
     for (int s = 0; s < kDepth - 1; ++s) load_step(ring[s]);
   }
-  fill_lut(lut);
+  write_lut(lut, lv);
   __syncthreads();
   if (count > 0) {
     while (cleft > 0) {
@@ -292,6 +303,7 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut,
         if (C.kb == 0 || c_first) {  // the strip's scales came with this step
           cur_sc = ring[s].sc;
           cur_gm = ring[s].gm;
+          if (c_first) first_gs = out_scale(cur_gm, cur_sc);
           c_first = false;
         }
         --cleft;
@@ -358,7 +370,9 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut,
     if (src.cross(sid))
       src.cross_sum(sv, sid, tot, lane);
     else
-      store_strip(sv, tot, lane, tokens, strip_scale(sv, lane, tokens));
+      // the scales came with the strip's first step (no load here: one at
+      // the end of the kernel would expose a full memory latency)
+      store_strip(sv, tot, lane, tokens, last ? out_scale(cur_gm, cur_sc) : first_gs);
   }
 }
 
@@ -396,7 +410,7 @@ struct SingleSrc {
   __device__ WaveRange range(int w) const {
     const int64_t b = blockIdx.x;
     const int64_t b0 = T * b / NB, n = T * (b + 1) / NB - b0;
-    const int64_t s0 = b0 + n * w / kGemvWaves, s1 = b0 + n * (w + 1) / kGemvWaves;
+    const int64_t s0 = b0 + wave_split(n, w), s1 = b0 + wave_split(n, w + 1);
     WaveRange r;
     r.count = s1 - s0;
     r.first.sid = (int32_t)(s0 / nkb);
@@ -408,7 +422,7 @@ struct SingleSrc {
   __device__ v4i wave_info(int v) const {
     const int64_t b = blockIdx.x;
     const int64_t b0 = T * b / NB, n = T * (b + 1) / NB - b0;
-    const int64_t s0 = b0 + n * v / kGemvWaves, s1 = b0 + n * (v + 1) / kGemvWaves;
+    const int64_t s0 = b0 + wave_split(n, v), s1 = b0 + wave_split(n, v + 1);
     const int32_t sid = (int32_t)(s0 / nkb);
     return v4i{sid, (int32_t)(s0 - (int64_t)sid * nkb), (int32_t)(s1 - s0), 0};
   }

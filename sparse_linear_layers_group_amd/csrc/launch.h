@@ -53,6 +53,22 @@ __host__ __device__ inline int64_t decode_blocks(int64_t steps) {
   int64_t nb = steps / kMinStepsPerBlock;
   return nb < 1 ? 1 : (nb > kDecodeBlocks ? kDecodeBlocks : nb);
 }
+// A workgroup's 16 wavefronts take contiguous ranges of its steps in
+// proportion to kWaveWeight[w / 4].  Wavefront w runs on SIMD w % 4, and
+// the SIMD favours its older wavefronts when several can issue, so with
+// equal ranges the older ones finished early (measured on MI355X: ~14 us
+// for wavefronts 0-3 against ~18 us for 12-15 in a 24-layer decode launch)
+// and each SIMD ran its last microseconds with one wavefront.  The weights
+// follow the measured rates (1 / duration).
+constexpr int kWaveWeight[4] = {19, 17, 15, 13};  // sum 64: 256 over 16 wavefronts
+__host__ __device__ inline int64_t wave_split(int64_t n, int w) {
+  int64_t c = 0;
+  for (int g = 0; g < 4; ++g) {
+    const int in = w - 4 * g;
+    c += (int64_t)kWaveWeight[g] * (in < 0 ? 0 : (in > 4 ? 4 : in));
+  }
+  return n * c / 256;  // first step of wavefront w, of n; wave_split(n, 16) == n
+}
 // workgroup owning global step s when T steps are cut into NB equal ranges
 // [T*b/NB, T*(b+1)/NB)
 __host__ __device__ inline int64_t block_of_step(int64_t s, int64_t T, int64_t NB) {

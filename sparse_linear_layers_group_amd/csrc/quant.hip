@@ -476,10 +476,22 @@ __global__ __launch_bounds__(256) void act_quant_group_kernel(const char* __rest
   // the first row descriptor is read together with the header (the row
   // region holds at least kActGroupBlocks zero-padded descriptors)
   RowDesc d = rows[blockIdx.x];
+  // Workgroup b < kDecodeBlocks also reads the 16 wavefront records of
+  // contraction workgroup b, which runs next on the same XCD (both grids
+  // are dealt round-robin over the XCDs): the contraction then finds them
+  // in that XCD's L2 instead of waiting for HBM before its first loads.
+  constexpr int kStartVecs = kDecodeWavesPerBlock * (int)sizeof(WaveStart) / 16;
+  const bool warm = blockIdx.x < kDecodeBlocks && threadIdx.x < kStartVecs;
+  u32x4 ws = u32x4{0u, 0u, 0u, 0u};
+  if (warm)
+    ws = ld_global(reinterpret_cast<const u32x4*>(plan + group_waves_offset() +
+                                                  (size_t)blockIdx.x * kDecodeWavesPerBlock * sizeof(WaveStart)) +
+                   threadIdx.x);
   for (int64_t r = blockIdx.x; r < nrows; r += gridDim.x) {
     if (r != blockIdx.x) d = rows[r];
     quant_row(d.X, d.k, d.xq, d.scale, red);
   }
+  if (warm) asm volatile("" : : "v"(ws.x));  // keeps the read
 }
 
 // ------------------------------------------------------------- launchers
