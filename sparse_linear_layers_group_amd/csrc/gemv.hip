@@ -248,14 +248,14 @@ struct WaveRange {
 template <int S, class Src>
 __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut,
                                           int lane) {
+  // the table reads go first (they depend on nothing); the first steps'
+  // loads are in flight while the workgroup builds the code tables
+  const LutVals lv = load_lut();
   const int tokens = src.tokens;
   const int w = wave_id();
   const uint32_t* lut_lane = lut + lane;
   const WaveRange wr = src.range(w);
   const int64_t count = wr.count;
-  // lane v < 16 holds wavefront v's (first strip, first k block, step count),
-  // fetched now and read with readlane by the end phase (no loads there)
-  const v4i winfo = src.wave_info(lane & 15);
   Cursor L = wr.first, C = wr.first;
   int64_t lleft = count, cleft = count;
   bool live = count > 0;
@@ -285,13 +285,14 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut,
       else src.advance(L);
     }
   };
-  // the table reads go first; the first steps' loads are in flight while
-  // the workgroup builds the code tables
-  const LutVals lv = load_lut();
   if (count > 0) {
 #pragma unroll
     for (int s = 0; s < kDepth - 1; ++s) load_step(ring[s]);
   }
+  // lane v < 16 holds wavefront v's (first strip, first k block, step
+  // count) for the end phase (no loads there); read after the first steps'
+  // loads so that nothing waits for it before then
+  const v4i winfo = src.wave_info(lane & 15);
   write_lut(lut, lv);
   __syncthreads();
   if (count > 0) {
@@ -515,12 +516,16 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_group_kernel(const char* __
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 2 * kLutCopies];
   GroupSrc<S> src;
   src.starts = reinterpret_cast<const WaveStart*>(plan + group_waves_offset());
-  // every wavefront of a workgroup reads the same flag: the whole workgroup
-  // leaves or stays
-  if (!src.starts[(int64_t)blockIdx.x * kGemvWaves].active) return;
-  src.strips = reinterpret_cast<const StripDesc*>(
-      plan + group_strips_offset(reinterpret_cast<const GroupHeader*>(plan)->rows));
-  src.tokens = reinterpret_cast<const GroupHeader*>(plan)->tokens;
+  // header and flag are read together (one round trip).  Each wavefront
+  // tests the flag in its own record, which its range comes from as well;
+  // all records of a workgroup carry the same flag, so the whole workgroup
+  // leaves or stays.
+  const GroupHeader* hdr = reinterpret_cast<const GroupHeader*>(plan);
+  const int64_t rows = hdr->rows;
+  src.tokens = hdr->tokens;
+  // (rows < 0 never holds; the test keeps the header read ahead of the branch)
+  if (!src.starts[(int64_t)blockIdx.x * kGemvWaves + wave_id()].active || rows < 0) return;
+  src.strips = reinterpret_cast<const StripDesc*>(plan + group_strips_offset(rows));
   run_block<S>(src, lut, threadIdx.x & 63);
 }
 
