@@ -55,8 +55,8 @@ DECODE_TRAFFIC = {
     "sources": ["sparse_linear_layers_group_amd/csrc/gemv.hip",
                 "sparse_linear_layers_group_amd/csrc/common.h",
                 "sparse_linear_layers_group_amd/csrc/launch.h"],
-    "sha256": "be5ba29fa4e9c61c646d16683c310f2df760a4d1fe67fd8cbe1c87b55cfe7a95",
-    "fetch_kib": 39769.39, "fetch_scale": 2.0,
+    "sha256": "01e434b3958abda9ee51a8fff7701321cbeac4d491ca16ce9c3dae10759a08c3",
+    "fetch_kib": 39923.41, "fetch_scale": 2.0,
     "write_kib": 1188.0, "write_scale": 1.0,
 }
 
