@@ -158,7 +158,16 @@ __global__ __launch_bounds__(64) void prep_codes_t_kernel(const uint32_t* __rest
 // measured fastest on MI355X, 64 slowest).  Global loads run two steps
 // ahead in a register ring; one barrier per step.  k positions at or past
 // K read as zero.  The output goes out with streaming stores.
+//
+// Tile order: workgroups are dealt round-robin to the 8 XCDs, each with its
+// own L2.  Workgroup b is mapped to the (b % 8)-th contiguous eighth of a
+// grouped tile order (groups of kGroupM row tiles, column tiles within a
+// group, row tiles fastest), so the workgroups an XCD runs at once cover a
+// compact block of rows and columns and share their operand rows in that
+// L2; with the plain row-major order every XCD read nearly all of both
+// operands.
 constexpr int kBP = 80;
+constexpr int kGroupM = 8;
 
 __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
@@ -170,7 +179,19 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.y * 128, n0 = (int64_t)blockIdx.x * 128;
+  const int64_t tiles_m = (M + 127) / 128, tiles_n = (N + 127) / 128;
+  int64_t m0, n0;
+  {
+    const int64_t T = tiles_m * tiles_n, per = (T + 7) / 8;
+    const int64_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int64_t full = T - (per - 1) * 8;  // XCDs that get `per` tiles
+    if (slot >= (xcd < full ? per : per - 1)) return;
+    const int64_t t = xcd < full ? xcd * per + slot : full * per + (xcd - full) * (per - 1) + slot;
+    const int64_t g = t / (kGroupM * tiles_n), r = t - g * kGroupM * tiles_n;
+    const int64_t gm = tiles_m - g * kGroupM < kGroupM ? tiles_m - g * kGroupM : kGroupM;
+    m0 = (g * kGroupM + r % gm) * 128;
+    n0 = (r / gm) * 128;
+  }
   const int64_t nks = (K + 63) / 64;
 
   // loads: piece q = tid + 256 p (p < 4) of each tile is row q/8, k
@@ -301,8 +322,8 @@ __global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
 static hipError_t gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
                           int64_t ldc, int64_t M, int64_t N, int64_t K, const double* alpha,
                           hipStream_t s) {
-  dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
-  gemm_nt_bf16_kernel<<<grid, 256, 0, s>>>(A, lda, B, ldb, C, ldc, M, N, K, alpha);
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  gemm_nt_bf16_kernel<<<(unsigned)((tiles + 7) / 8 * 8), 256, 0, s>>>(A, lda, B, ldb, C, ldc, M, N, K, alpha);
   return hipGetLastError();
 }
 
