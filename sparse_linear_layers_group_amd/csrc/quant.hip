@@ -292,17 +292,16 @@ __global__ __launch_bounds__(256) void gamma_finalize_kernel(const char* __restr
 // Ternary codes and packing.  The code of W is sign(W) where the mask
 // keeps it and 2|W| > gamma.  Since bf16 magnitudes are ordered like their
 // 15-bit patterns, that test is |h| >= thr for the smallest pattern thr
-// whose value v has 2v > gamma (found by bisection in binary64; exact).
+// whose value v has 2v > gamma, i.e. v > gamma/2 (halving is exact in
+// binary64): one past the largest bf16 <= gamma/2, which is the top half of
+// gamma/2 rounded toward zero to binary32 (every bf16 value is a binary32
+// value, so the next bf16 up exceeds gamma/2).  Past the largest finite
+// bf16 the infinity pattern is the threshold.
 // ---------------------------------------------------------------------
 __device__ uint32_t code_threshold(double g) {
   if (!(g > 0.0)) return 0x10000u;  // no entry qualifies
-  uint32_t lo = 0, hi = 0x7f80u;    // 0x7f80 = inf: always qualifies
-  while (lo < hi) {
-    uint32_t mid = (lo + hi) >> 1;
-    double v = (double)__uint_as_float(mid << 16);
-    if (2.0 * v > g) hi = mid; else lo = mid + 1;
-  }
-  return lo;
+  const uint32_t b = __float_as_uint(__double2float_rz(0.5 * g)) >> 16;  // largest bf16 <= g/2
+  return b + 1u > 0x7f80u ? 0x7f80u : b + 1u;
 }
 
 // field (8+S bits) and int8 codes (two words, positions 0..3 / 4..7) of one
