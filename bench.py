@@ -295,9 +295,9 @@ def verify_decode_sample(torch, d, n, m):
 # --------------------------------------------------------------- prefill / train
 def prefill_step(torch, bl, n, m, tokens=2048, iters=10):
     """Qwen2.5-1.5B-shaped prefill: per step, mask recompute + pack of gate,
-    up and down, activation quantisation, int8 GEMMs."""
+    up and down (one grouped plan), activation quantisation, int8 GEMMs."""
     from sparse_linear_layers_group_amd import synth
-    from sparse_linear_layers_group_amd.layer import BitLinearWeight, bf16_tensor
+    from sparse_linear_layers_group_amd.layer import BitLinearWeight, QuantGroup, bf16_tensor
     Ws, lws, bufs = [], [], []
     for li, (name, n_out, k) in enumerate(QWEN15_PREFILL):
         Ws.append(bf16_tensor(synth.weights(n_out, k, seed=0, config=3, layer=li)))
@@ -307,9 +307,10 @@ def prefill_step(torch, bl, n, m, tokens=2048, iters=10):
     X2 = bf16_tensor(synth.activations(tokens, 8960, seed=0, config=3, layer=2))
     xs = [X1, X1, X2]
 
+    qg = QuantGroup(list(zip(lws, Ws)))  # plan built once; each step: three launches
+
     def quant():
-        for W, lw in zip(Ws, lws):
-            lw.quantize(W)
+        qg.run()
 
     def act():
         bl.bitlinear_act_quant(X1, tokens, 1536, bufs[0]["xq"], bufs[0]["x_scale"])
@@ -344,9 +345,10 @@ def prefill_step(torch, bl, n, m, tokens=2048, iters=10):
 
 def train_step(torch, bl, n, m, tokens=4096, iters=3):
     """BitNet-b1.58-2B4T-shaped block: all 7 BitLinears, per step mask +
-    pack, forward (int8 MFMA) and dual-STE backward (bf16 MFMA)."""
+    pack (one grouped plan), forward (int8 MFMA) and dual-STE backward (bf16
+    MFMA)."""
     from sparse_linear_layers_group_amd import synth
-    from sparse_linear_layers_group_amd.layer import BitLinearWeight, bf16_tensor
+    from sparse_linear_layers_group_amd.layer import BitLinearWeight, QuantGroup, bf16_tensor
     hid = 2560
     Ws, lws, fb, dys, gx, gw = [], [], [], [], [], []
     for li, (name, n_out, k) in enumerate(BITNET2B_BLOCK):
@@ -364,9 +366,10 @@ def train_step(torch, bl, n, m, tokens=4096, iters=3):
     Xd = bf16_tensor(synth.activations(tokens, 6912, seed=0, config=5, layer=6))
     src = [0, 0, 0, 3, 0, 0, 6]  # which layer's x_q buffer each layer reads
 
+    qg = QuantGroup(list(zip(lws, Ws)))  # plan built once; each step: three launches
+
     def quant():
-        for W, lw in zip(Ws, lws):
-            lw.quantize(W)
+        qg.run()
 
     def fwd():
         for i, x in ((0, X), (3, Xo), (6, Xd)):

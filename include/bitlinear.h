@@ -195,6 +195,42 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item *items, int count,
                              size_t plan_bytes, void *stream);
 int bitlinear_fwd_group(const void *plan, int n, int m, int stages, void *stream);
 
+/* Grouped weight quantisation: steps 1-3 (mask, absmean scale, packing) of
+ * many layers with the same N:M pattern in three launches (every mask and
+ * partial sum, every gamma, every packed block), e.g. the per-step mask
+ * recompute of all BitLinears of a block.  Sparse-BitNet article §三 and
+ * §五, BitNet b1.58 2B4T article §一, as for bitlinear_quantize_mask and
+ * bitlinear_pack; each item's mask, gamma and packed bytes are bit-identical
+ * to what those two calls give.
+ *   items  host array of `count` (1..65535) descriptors; W, mask, gamma and
+ *          packed are device pointers with the shapes and alignments of
+ *          bitlinear_quantize_mask / bitlinear_pack (packed holds
+ *          bitlinear_packed_bytes(n_out, k, n, m) bytes).
+ *   ws     device workspace of bitlinear_quant_group_workspace_bytes()
+ *          bytes, 16-byte aligned; contents need not be initialised.  The
+ *          plan records it: runs of one plan share it, so they must not
+ *          overlap in time.
+ *   plan   device buffer of bitlinear_quant_group_plan_bytes() bytes,
+ *          written by bitlinear_quant_group_plan (which synchronises
+ *          `stream` once); the host array is not used afterwards.
+ * n, m and gamma_over passed to bitlinear_quant_group must be those the plan
+ * was made with.  Errors as for the single-layer calls, plus BL_EWORKSPACE
+ * for a short plan or workspace. */
+typedef struct bitlinear_quant_item {
+    const uint16_t *W;      /* bf16 [n_out x k], read            */
+    uint8_t *mask;          /* [n_out x k/8], written            */
+    double *gamma;          /* one double, written               */
+    void *packed;           /* packed codes, written             */
+    int64_t n_out, k;
+} bitlinear_quant_item;
+
+size_t bitlinear_quant_group_workspace_bytes(const bitlinear_quant_item *items, int count);
+size_t bitlinear_quant_group_plan_bytes(const bitlinear_quant_item *items, int count);
+int bitlinear_quant_group_plan(const bitlinear_quant_item *items, int count, int n, int m,
+                               int gamma_over, void *ws, size_t ws_bytes, void *plan,
+                               size_t plan_bytes, void *stream);
+int bitlinear_quant_group(const void *plan, int n, int m, int gamma_over, void *stream);
+
 /* Step 8-9: dual straight-through backward.  Sparse-BitNet article §三 and
  * §六: gradients pass straight through the ternary rounding and the
  * sparsification, and masked weights still receive their gradient.

@@ -44,6 +44,10 @@ _SIGS = {
     "bitlinear_fwd_group_plan_bytes": (_sz, [_vp, _int, _i64]),
     "bitlinear_fwd_group_plan": (_int, [_vp, _int, _i64, _int, _int, _vp, _sz, _vp]),
     "bitlinear_fwd_group": (_int, [_vp, _int, _int, _int, _vp]),
+    "bitlinear_quant_group_workspace_bytes": (_sz, [_vp, _int]),
+    "bitlinear_quant_group_plan_bytes": (_sz, [_vp, _int]),
+    "bitlinear_quant_group_plan": (_int, [_vp, _int, _int, _int, _int, _vp, _sz, _vp, _sz, _vp]),
+    "bitlinear_quant_group": (_int, [_vp, _int, _int, _int, _vp]),
     "bitlinear_status_string": (ctypes.c_char_p, [_int]),
     "bitlinear_last_error": (ctypes.c_char_p, []),
 }
@@ -235,3 +239,43 @@ def bitlinear_fwd_group(plan, n, m, stages=3, stream=None):
     st = lib().bitlinear_fwd_group(_ptr(plan, (torch.uint8,), None, "plan"), n, m, int(stages),
                                    _stream(stream))
     _check(st, "bitlinear_fwd_group")
+
+
+class bitlinear_quant_item(ctypes.Structure):
+    """Mirror of the C struct bitlinear_quant_item (device pointers as ints)."""
+    _fields_ = [("W", _vp), ("mask", _vp), ("gamma", _vp), ("packed", _vp), ("n_out", _i64), ("k", _i64)]
+
+
+def make_quant_items(entries, n, m):
+    """entries: dicts with tensors W, mask, gamma, packed and ints n_out, k."""
+    arr = (bitlinear_quant_item * len(entries))()
+    for i, e in enumerate(entries):
+        n_out, k = int(e["n_out"]), int(e["k"])
+        arr[i] = bitlinear_quant_item(
+            _ptr(e["W"], _BF16, n_out * k, "W"), _ptr(e["mask"], (torch.uint8,), n_out * (k // 8), "mask"),
+            _ptr(e["gamma"], (torch.float64,), 1, "gamma"),
+            _ptr(e["packed"], (torch.uint8,), bitlinear_packed_bytes(n_out, k, n, m), "packed"), n_out, k)
+    return arr
+
+
+def bitlinear_quant_group_workspace_bytes(items, count):
+    return int(lib().bitlinear_quant_group_workspace_bytes(items, int(count)))
+
+
+def bitlinear_quant_group_plan_bytes(items, count):
+    return int(lib().bitlinear_quant_group_plan_bytes(items, int(count)))
+
+
+def bitlinear_quant_group_plan(items, count, n, m, gamma_over, ws, plan, ws_bytes=None, plan_bytes=None,
+                               stream=None):
+    st = lib().bitlinear_quant_group_plan(
+        items, int(count), n, m, gamma_over, _ptr(ws, (torch.uint8,), None, "ws"),
+        ws.numel() if ws_bytes is None else int(ws_bytes), _ptr(plan, (torch.uint8,), None, "plan"),
+        plan.numel() if plan_bytes is None else int(plan_bytes), _stream(stream))
+    _check(st, "bitlinear_quant_group_plan")
+
+
+def bitlinear_quant_group(plan, n, m, gamma_over, stream=None):
+    st = lib().bitlinear_quant_group(_ptr(plan, (torch.uint8,), None, "plan"), n, m, gamma_over,
+                                     _stream(stream))
+    _check(st, "bitlinear_quant_group")

@@ -107,6 +107,30 @@ int64_t group_blocks(int64_t steps, int64_t strips) {
   const int64_t nb = bl::decode_blocks(steps);
   return nb < strips ? nb : strips;
 }
+
+// Shape checks for a grouped quantisation plan; returns the mask and pack
+// workgroups over all items and the workspace bytes (one 256-byte aligned
+// gamma region per item).
+int quant_shape(const bitlinear_quant_item* items, int count, int64_t* mask_blocks,
+                int64_t* pack_blocks, size_t* ws) {
+  if (!items) return fail(BL_EINVAL, "items is NULL");
+  if (count < 1 || count > 65535) return fail(BL_ESHAPE, "count must be in 1..65535 (got %d)", count);
+  int64_t mb = 0, pb = 0;
+  size_t w = 0;
+  for (int i = 0; i < count; ++i) {
+    const bitlinear_quant_item& it = items[i];
+    int st = check_layer(it.n_out, it.k);
+    if (st != BL_OK) return fail(st, "item %d: %s", i, g_last_error.c_str());
+    mb += bl::mask_blocks(it.n_out, it.k);
+    pb += bl::pack_blocks(it.n_out, it.k);
+    w += bl::bwd_align(bl::gamma_ws_bytes(it.n_out, it.k));
+    if (mb + pb >= ((int64_t)1 << 30)) return fail(BL_ESHAPE, "too many workgroups in one plan");
+  }
+  *mask_blocks = mb;
+  *pack_blocks = pb;
+  *ws = w;
+  return BL_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -390,6 +414,88 @@ int bitlinear_fwd_group(const void* plan, int n, int m, int stages, void* stream
     if (e != hipSuccess) return hip_status(e, "grouped decode launch");
   }
   return ok();
+}
+
+size_t bitlinear_quant_group_workspace_bytes(const bitlinear_quant_item* items, int count) {
+  int64_t mb = 0, pb = 0;
+  size_t w = 0;
+  if (quant_shape(items, count, &mb, &pb, &w) != BL_OK) return 0;
+  return w;
+}
+
+size_t bitlinear_quant_group_plan_bytes(const bitlinear_quant_item* items, int count) {
+  int64_t mb = 0, pb = 0;
+  size_t w = 0;
+  if (quant_shape(items, count, &mb, &pb, &w) != BL_OK) return 0;
+  return bl::quant_plan_bytes(count, mb, pb);
+}
+
+int bitlinear_quant_group_plan(const bitlinear_quant_item* items, int count, int n, int m,
+                               int gamma_over, void* ws, size_t ws_bytes, void* plan,
+                               size_t plan_bytes, void* stream) {
+  TRY(check_nm(n, m));
+  if (gamma_over != BL_GAMMA_DENSE && gamma_over != BL_GAMMA_MASKED)
+    return fail(BL_EINVAL, "gamma_over must be BL_GAMMA_DENSE or BL_GAMMA_MASKED (got %d)", gamma_over);
+  int64_t mb = 0, pb = 0;
+  size_t need_ws = 0;
+  TRY(quant_shape(items, count, &mb, &pb, &need_ws));
+  for (int i = 0; i < count; ++i) {
+    const bitlinear_quant_item& it = items[i];
+    TRY(check_ptr(it.W, 16, "item W"));
+    TRY(check_ptr(it.mask, 16, "item mask"));
+    TRY(check_ptr(it.gamma, 8, "item gamma"));
+    TRY(check_ptr(it.packed, 16, "item packed"));
+  }
+  if (!ws || ws_bytes < need_ws)
+    return fail(BL_EWORKSPACE, "workspace needs %zu bytes (got %zu)", need_ws, ws ? ws_bytes : (size_t)0);
+  TRY(check_ptr(ws, 16, "ws"));
+  const size_t need = bl::quant_plan_bytes(count, mb, pb);
+  TRY(check_ptr(plan, 16, "plan"));
+  if (plan_bytes < need) return fail(BL_EWORKSPACE, "plan needs %zu bytes (got %zu)", need, plan_bytes);
+  std::vector<char> img(need, 0);
+  bl::QuantGroupHeader* h = reinterpret_cast<bl::QuantGroupHeader*>(img.data());
+  h->count = count;
+  h->mask_blocks = mb;
+  h->pack_blocks = pb;
+  bl::QuantItemDesc* d = reinterpret_cast<bl::QuantItemDesc*>(img.data() + sizeof(bl::QuantGroupHeader));
+  int32_t* owner = reinterpret_cast<int32_t*>(img.data() + bl::quant_owner_offset(count));
+  int64_t m0 = 0, p0 = 0;
+  size_t w0 = 0;
+  for (int i = 0; i < count; ++i) {
+    const bitlinear_quant_item& it = items[i];
+    bl::QuantItemDesc& q = d[i];
+    q.W = it.W;
+    q.mask = it.mask;
+    q.gamma = it.gamma;
+    q.packed = it.packed;
+    q.ws = reinterpret_cast<char*>(ws) + w0;
+    q.n_out = it.n_out;
+    q.k = it.k;
+    q.ngroups = it.n_out * it.k / 8;
+    q.per = bl::mask_groups_per_block(it.n_out, it.k);
+    q.mblock0 = m0;
+    q.nmblocks = bl::mask_blocks(it.n_out, it.k);
+    q.pblock0 = p0;
+    for (int64_t b = 0; b < q.nmblocks; ++b) owner[m0 + b] = i;
+    const int64_t npb = bl::pack_blocks(it.n_out, it.k);
+    for (int64_t b = 0; b < npb; ++b) owner[mb + p0 + b] = i;
+    m0 += q.nmblocks;
+    p0 += npb;
+    w0 += bl::bwd_align(bl::gamma_ws_bytes(it.n_out, it.k));
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(plan, img.data(), need, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return hip_status(e, "plan upload");
+}
+
+int bitlinear_quant_group(const void* plan, int n, int m, int gamma_over, void* stream) {
+  TRY(check_nm(n, m));
+  if (gamma_over != BL_GAMMA_DENSE && gamma_over != BL_GAMMA_MASKED)
+    return fail(BL_EINVAL, "gamma_over must be BL_GAMMA_DENSE or BL_GAMMA_MASKED (got %d)", gamma_over);
+  TRY(check_ptr(plan, 16, "plan"));
+  hipError_t e = bl::launch_quant_group(plan, n, m, gamma_over, reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "grouped quantisation launch");
 }
 
 int bitlinear_bwd(const uint16_t* dY, const int8_t* xq, const float* x_scale, const void* packed,

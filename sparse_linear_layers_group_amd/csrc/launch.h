@@ -28,6 +28,52 @@ hipError_t launch_mask_gamma(const uint16_t* W, int64_t n_out, int64_t k, int n,
                              int gamma_over, uint8_t* mask, double* gamma, void* ws,
                              hipStream_t s);
 
+// Grouped weight quantisation: one device plan describes many layers; the
+// mask kernel, the gamma kernel and the pack kernel each run every layer
+// in one launch.  Plan image: header (64 bytes) | item descriptors[count] |
+// owner table (one int32 item index per mask workgroup, then one per pack
+// workgroup).  Each layer keeps its own gamma workspace region.
+struct QuantGroupHeader {
+  int32_t count, pad;
+  int64_t mask_blocks, pack_blocks;  // workgroups of the mask and pack launches
+  int64_t pad2[5];
+};
+static_assert(sizeof(QuantGroupHeader) == 64, "quant plan header size");
+struct QuantItemDesc {  // one layer (128 bytes)
+  const uint16_t* W;
+  uint8_t* mask;
+  double* gamma;
+  void* packed;
+  char* ws;                   // the layer's gamma workspace (gamma_ws_bytes)
+  int64_t n_out, k;
+  int64_t ngroups, per;       // 8-groups, and 8-groups per mask workgroup
+  int64_t mblock0, nmblocks;  // first mask workgroup of the layer, and how many
+  int64_t pblock0;            // first pack workgroup of the layer
+  int64_t pad[4];
+};
+static_assert(sizeof(QuantItemDesc) == 128, "quant item size");
+__host__ __device__ inline size_t quant_owner_offset(int64_t count) {
+  return sizeof(QuantGroupHeader) + (size_t)count * sizeof(QuantItemDesc);
+}
+inline size_t quant_plan_bytes(int64_t count, int64_t mask_blocks, int64_t pack_blocks) {
+  return quant_owner_offset(count) + (size_t)(mask_blocks + pack_blocks) * 4;
+}
+// 8-groups per mask workgroup of a layer (a whole number of passes)
+inline int64_t mask_groups_per_block(int64_t n_out, int64_t k) {
+  const int64_t ngroups = n_out * k / 8, blocks = mask_blocks(n_out, k);
+  const int64_t per = (ngroups + blocks - 1) / blocks;
+  return (per + kMaskGroupsPerPass - 1) / kMaskGroupsPerPass * kMaskGroupsPerPass;
+}
+inline int64_t pack_blocks(int64_t n_out, int64_t k) {
+  const int64_t chunks = ((n_out + 63) / 64) * 64 * (k / 128);
+  return (chunks + 255) / 256;
+}
+// The three launches have fixed grids (the host does not read the plan);
+// workgroup g of a launch takes the plan's workgroups g, g + grid, ...
+constexpr int kQuantGrid = 2048;      // mask and pack launches: 8 workgroups per CU
+constexpr int kQuantGammaGrid = 256;  // gamma launch: one workgroup per layer, strided
+hipError_t launch_quant_group(const void* plan, int n, int m, int gamma_over, hipStream_t s);
+
 // ternary codes -> packed blocks (packed may be null) and/or int8 codes (wq
 // may be null); S = sign slots per 8-group
 hipError_t launch_ternary_pack(const uint16_t* W, const uint8_t* mask, const double* gamma,

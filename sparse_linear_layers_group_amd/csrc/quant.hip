@@ -19,19 +19,23 @@ namespace bl {
 // ---------------------------------------------------------------------
 // Exact sum of |W|.  A finite bf16 magnitude is sig * 2^(max(E,1) - 134)
 // with E the 8-bit exponent field and sig = (E ? 128 : 0) + fraction.
-// Two fixed-point windows cover |W| in [2^-41, 2): E in [kHiLo, kHiLo+21)
-// adds sig << (E - kHiLo) to a 64-bit integer in units of 2^(kHiLo-134),
-// E in [kLoLo, kHiLo) adds sig << (E - kLoLo) to a second one in units of
-// 2^(kLoLo-134).  Any other nonzero magnitude adds sig into an exponent
-// bin of its workgroup (in LDS).  Integer addition is associative, so the
-// result does not depend on scheduling.
+// One fixed-point window covers |W| in [2^-59, 2): E in [kWinLo, 128)
+// adds sig << (E - kWinLo) (< 2^60; eight of them < 2^63) to an integer
+// in units of 2^(kWinLo-134).  A group whose eight magnitudes are all in
+// the window (the common case) takes that sum with no per-element test;
+// a group holding a zero or any magnitude outside it takes the exact
+// per-element path, where every other nonzero magnitude adds sig into an
+// exponent bin of its workgroup (in LDS).  Integer addition is
+// associative, so the result does not depend on scheduling.
 // ---------------------------------------------------------------------
-constexpr int kHiLo = 107;
-constexpr int kLoLo = 86;
-constexpr int kWin = 21;  // sig << 20 < 2^28: eight of them fit in 32 bits
+constexpr int kWinLo = 75;
+// rank keys (|h| << 3 | index code) bounding the window: a group is on
+// the fast path iff its smallest key >= kKeyLo and its largest < kKeyHi
+constexpr uint32_t kKeyLo = (uint32_t)kWinLo << 10;
+constexpr uint32_t kKeyHi = 128u << 10;
 
 struct MaskPart {
-  unsigned long long hi, lo;  // window sums
+  unsigned long long hi, lo;  // window sum = hi * 2^32 + lo
   uint32_t binned;            // nonzero: this workgroup wrote its 256 bins
   uint32_t pad[3];
 };
@@ -43,6 +47,9 @@ __device__ __forceinline__ uint32_t rank_key(uint32_t h, int j) {
   return ((h & 0x7fffu) << 3) | (uint32_t)(7 - j);
 }
 
+__device__ __forceinline__ uint32_t min3(uint32_t a, uint32_t b, uint32_t c) { return min(min(a, b), c); }
+__device__ __forceinline__ uint32_t max3(uint32_t a, uint32_t b, uint32_t c) { return max(max(a, b), c); }
+
 __device__ __forceinline__ void cswap(uint32_t& a, uint32_t& b) {
   uint32_t lo = min(a, b), hi = max(a, b);
   a = lo;
@@ -50,25 +57,34 @@ __device__ __forceinline__ void cswap(uint32_t& a, uint32_t& b) {
 }
 
 // mask bits of one 8-group (w = 8 bf16, element j in bits 16j..16j+15 of
-// the four words) for the pattern N:M
+// the four words) for the pattern N:M; kmin / kmax receive the smallest
+// and largest rank key of the group
 template <int N, int M>
-__device__ __forceinline__ uint32_t group_mask(const uint32_t w[4]) {
-  if (N == M) return 0xffu;
+__device__ __forceinline__ uint32_t group_mask(const uint32_t w[4], uint32_t& kmin, uint32_t& kmax) {
   uint32_t key[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) key[j] = rank_key((w[j >> 1] >> (16 * (j & 1))) & 0xffffu, j);
+  if (N == M) {
+    kmin = min(min3(key[0], key[1], key[2]), min3(key[3], key[4], min3(key[5], key[6], key[7])));
+    kmax = max(max3(key[0], key[1], key[2]), max3(key[3], key[4], max3(key[5], key[6], key[7])));
+    return 0xffu;
+  }
   uint32_t tau_lo, tau_hi;  // a key is kept iff it exceeds its half's / group's tau
   if (M == 4) {
     // 2:4 -- per half of four, drop the two smallest keys
-    uint32_t t[2];
+    uint32_t t[2], lo[2], hi[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t p0 = min(key[4 * h], key[4 * h + 1]), P0 = max(key[4 * h], key[4 * h + 1]);
       uint32_t p1 = min(key[4 * h + 2], key[4 * h + 3]), P1 = max(key[4 * h + 2], key[4 * h + 3]);
       t[h] = min(max(p0, p1), min(P0, P1));  // second smallest of four
+      lo[h] = min(p0, p1);
+      hi[h] = max(P0, P1);
     }
     tau_lo = t[0];
     tau_hi = t[1];
+    kmin = min(lo[0], lo[1]);
+    kmax = max(hi[0], hi[1]);
   } else if (N == 6) {
     // 6:8 -- tau = second smallest of eight
     uint32_t p[4], P[4];
@@ -80,6 +96,8 @@ __device__ __forceinline__ uint32_t group_mask(const uint32_t w[4]) {
     uint32_t q1 = min(p[0], p[1]), q2 = min(max(p[0], p[1]), min(P[0], P[1]));
     uint32_t r1 = min(p[2], p[3]), r2 = min(max(p[2], p[3]), min(P[2], P[3]));
     tau_lo = tau_hi = min(max(q1, r1), min(q2, r2));
+    kmin = min(q1, r1);
+    kmax = max(max3(P[0], P[1], P[2]), P[3]);
   } else {
     // general N of 8: sort (Batcher odd-even merge network, 19 swaps),
     // tau = (8-N)-th smallest
@@ -93,6 +111,8 @@ __device__ __forceinline__ uint32_t group_mask(const uint32_t w[4]) {
     cswap(s[2], s[4]); cswap(s[3], s[5]);
     cswap(s[1], s[2]); cswap(s[3], s[4]); cswap(s[5], s[6]);
     tau_lo = tau_hi = s[7 - N];
+    kmin = s[0];
+    kmax = s[7];
   }
   uint32_t bits = 0;
 #pragma unroll
@@ -103,29 +123,42 @@ __device__ __forceinline__ uint32_t group_mask(const uint32_t w[4]) {
   return bits;
 }
 
-// exact |W| accumulation of one 8-group into the two window sums
+// window sum of one 8-group whose eight magnitudes are all nonzero and in
+// the window
+__device__ __forceinline__ unsigned long long group_sum_window(const uint32_t w[4]) {
+  unsigned long long s = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t h = w[j >> 1] >> (16 * (j & 1));
+    const uint32_t e = (h >> 7) & 0xffu;
+    const uint32_t sig = (h & 0x7fu) | 0x80u;
+    s += (unsigned long long)sig << (e - (uint32_t)kWinLo);
+  }
+  return s;
+}
+
+// exact per-element path: the window sum of the in-window magnitudes
+// (kept ones only when MASKED); every other nonzero magnitude goes to its
+// exponent bin
 template <bool MASKED>
-__device__ __forceinline__ void group_abs_sum(const uint32_t w[4], uint32_t keep,
-                                              unsigned long long& hi, unsigned long long& lo,
-                                              unsigned long long* bins, uint32_t& binned) {
-  uint32_t sh_sum = 0, sl_sum = 0;
+__device__ __forceinline__ unsigned long long group_sum_exact(const uint32_t w[4], uint32_t keep,
+                                                              unsigned long long* bins,
+                                                              uint32_t& binned) {
+  unsigned long long s = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     uint32_t a = (w[j >> 1] >> (16 * (j & 1))) & 0x7fffu;
     if (MASKED && !((keep >> j) & 1u)) a = 0;
     const uint32_t e = a >> 7;
     const uint32_t sig = (a & 0x7fu) | (e ? 0x80u : 0u);
-    const uint32_t sh = e - (uint32_t)kHiLo, sl = e - (uint32_t)kLoLo;
-    const bool in_h = sh < (uint32_t)kWin, in_l = sl < (uint32_t)kWin;
-    sh_sum += in_h ? (sig << sh) : 0u;
-    sl_sum += in_l ? (sig << sl) : 0u;
-    if (!in_h && !in_l && a != 0u) {
+    if (e >= (uint32_t)kWinLo && e < 128u) {
+      s += (unsigned long long)sig << (e - (uint32_t)kWinLo);
+    } else if (a != 0u) {
       atomicAdd(&bins[e], (unsigned long long)sig);
       binned = 1;
     }
   }
-  hi += sh_sum;
-  lo += sl_sum;
+  return s;
 }
 
 // 320-bit unsigned integer in 32-bit limbs, units of 2^-133; limb indices
@@ -179,75 +212,95 @@ __device__ double big_round(const Big& b) {
 }
 
 // Kernel 1: mask bytes of every 8-group and the workgroup's exact partial
-// sums.  Workgroup b covers the contiguous 8-groups [b*per, (b+1)*per);
-// every load instruction of a wavefront reads 1 KiB of consecutive
-// weights.
+// sums.  Workgroup b (of nb) covers the contiguous 8-groups [b*per,
+// (b+1)*per); every load instruction of a wavefront reads 1 KiB of
+// consecutive weights.  The body is shared by the single-layer kernel and
+// the grouped one (which runs it for several (layer, b) in turn).
+struct MaskShared {
+  unsigned long long bins[256];
+  unsigned long long part[2][4];
+  uint32_t any_binned;
+};
 template <int N, int M, bool MASKED>
-__global__ __launch_bounds__(256) void mask_gamma_kernel(const uint4* __restrict__ W,
-                                                        int64_t ngroups, int64_t per,
-                                                        uint8_t* __restrict__ mask,
-                                                        char* __restrict__ ws) {
-  __shared__ unsigned long long bins[256];
-  __shared__ unsigned long long part[2][4];
-  __shared__ uint32_t any_binned;
+__device__ __forceinline__ void mask_gamma_body(const uint4* __restrict__ W, int64_t ngroups,
+                                                int64_t per, uint8_t* __restrict__ mask,
+                                                char* __restrict__ ws, int64_t b, int64_t nb,
+                                                MaskShared& sh) {
+  unsigned long long* bins = sh.bins;
+  __syncthreads();  // the shared arrays are free (a previous body may have used them)
   bins[threadIdx.x] = 0ull;
-  if (threadIdx.x == 0) any_binned = 0;
+  if (threadIdx.x == 0) sh.any_binned = 0;
   __syncthreads();
   unsigned long long hi = 0, lo = 0;
   uint32_t binned = 0;
-  const int64_t g_begin = (int64_t)blockIdx.x * per;
+  const int64_t g_begin = b * per;
   const int64_t g_end = g_begin + per < ngroups ? g_begin + per : ngroups;
   for (int64_t c0 = g_begin; c0 < g_end; c0 += kMaskGroupsPerPass) {
     uint4 v[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int64_t grp = c0 + 256 * g + threadIdx.x;
-      v[g] = grp < g_end ? W[grp] : make_uint4(0, 0, 0, 0);
+      u32x4 x = u32x4{0u, 0u, 0u, 0u};
+      if (grp < g_end) x = ld_global(reinterpret_cast<const u32x4*>(W + grp));
+      v[g] = make_uint4(x[0], x[1], x[2], x[3]);
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int64_t grp = c0 + 256 * g + threadIdx.x;
       if (grp >= g_end) break;
       const uint32_t w[4] = {v[g].x, v[g].y, v[g].z, v[g].w};
-      const uint32_t keep = group_mask<N, M>(w);
-      mask[grp] = (uint8_t)keep;
-      group_abs_sum<MASKED>(w, keep, hi, lo, bins, binned);
+      uint32_t kmin, kmax;
+      const uint32_t keep = group_mask<N, M>(w, kmin, kmax);
+      st_global(mask + grp, (uint8_t)keep);
+      unsigned long long gs = group_sum_window(w);
+      if (MASKED || kmin < kKeyLo || kmax >= kKeyHi) gs = group_sum_exact<MASKED>(w, keep, bins, binned);
+      lo += (uint32_t)gs;
+      hi += gs >> 32;
     }
   }
   hi = wave_sum_u64(hi);
   lo = wave_sum_u64(lo);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (lane == 0) {
-    part[0][wave] = hi;
-    part[1][wave] = lo;
+    sh.part[0][wave] = hi;
+    sh.part[1][wave] = lo;
   }
-  if (binned) any_binned = 1;
+  if (binned) sh.any_binned = 1;
   __syncthreads();
-  MaskPart* rec = reinterpret_cast<MaskPart*>(ws) + blockIdx.x;
+  MaskPart* rec = reinterpret_cast<MaskPart*>(ws) + b;
   if (threadIdx.x == 0) {
     MaskPart r;
-    r.hi = part[0][0] + part[0][1] + part[0][2] + part[0][3];
-    r.lo = part[1][0] + part[1][1] + part[1][2] + part[1][3];
-    r.binned = any_binned;
+    r.hi = sh.part[0][0] + sh.part[0][1] + sh.part[0][2] + sh.part[0][3];
+    r.lo = sh.part[1][0] + sh.part[1][1] + sh.part[1][2] + sh.part[1][3];
+    r.binned = sh.any_binned;
     r.pad[0] = r.pad[1] = r.pad[2] = 0;
     *rec = r;
   }
-  if (any_binned) {
+  if (sh.any_binned) {
     unsigned long long* out =
-        reinterpret_cast<unsigned long long*>(ws + (size_t)gridDim.x * sizeof(MaskPart)) +
-        (size_t)blockIdx.x * 256;
+        reinterpret_cast<unsigned long long*>(ws + (size_t)nb * sizeof(MaskPart)) + (size_t)b * 256;
     out[threadIdx.x] = bins[threadIdx.x];
   }
 }
 
+template <int N, int M, bool MASKED>
+__global__ __launch_bounds__(256) void mask_gamma_kernel(const uint4* __restrict__ W,
+                                                        int64_t ngroups, int64_t per,
+                                                        uint8_t* __restrict__ mask,
+                                                        char* __restrict__ ws) {
+  __shared__ MaskShared sh;
+  mask_gamma_body<N, M, MASKED>(W, ngroups, per, mask, ws, blockIdx.x, gridDim.x, sh);
+}
+
 // Kernel 2 (one workgroup of 256): gamma = (sum of the partials) / count,
 // the sum rounded once to binary64.
-__global__ __launch_bounds__(256) void gamma_finalize_kernel(const char* __restrict__ ws,
-                                                             int nblocks, double* __restrict__ gamma,
-                                                             double count) {
-  __shared__ unsigned long long part[2][4];
-  __shared__ unsigned long long bins[256];
-  __shared__ uint32_t any_binned;
+__device__ __forceinline__ void gamma_finalize_body(const char* __restrict__ ws, int nblocks,
+                                                    double* __restrict__ gamma, double count,
+                                                    MaskShared& sh) {
+  unsigned long long(&part)[2][4] = sh.part;
+  unsigned long long* bins = sh.bins;
+  uint32_t& any_binned = sh.any_binned;
+  __syncthreads();  // the shared arrays are free (a previous body may have used them)
   if (threadIdx.x == 0) any_binned = 0;
   const MaskPart* rec = reinterpret_cast<const MaskPart*>(ws);
   unsigned long long hi = 0, lo = 0;
@@ -276,16 +329,24 @@ __global__ __launch_bounds__(256) void gamma_finalize_kernel(const char* __restr
   }
   bins[threadIdx.x] = bin;
   __syncthreads();
-  if (threadIdx.x != 0) return;
-  Big big;
+  if (threadIdx.x == 0) {  // (no early return: the grouped kernel loops over layers)
+    Big big;
 #pragma unroll
-  for (int i = 0; i < 10; ++i) big.limb[i] = 0;
-  big_add(big, part[0][0] + part[0][1] + part[0][2] + part[0][3], kHiLo - 1);
-  big_add(big, part[1][0] + part[1][1] + part[1][2] + part[1][3], kLoLo - 1);
-  if (any_binned)
-    for (int e = 0; e < 256; ++e)
-      if (bins[e]) big_add(big, bins[e], e > 0 ? e - 1 : 0);
-  *gamma = big_round(big) / count;
+    for (int i = 0; i < 10; ++i) big.limb[i] = 0;
+    big_add(big, part[0][0] + part[0][1] + part[0][2] + part[0][3], kWinLo - 1 + 32);
+    big_add(big, part[1][0] + part[1][1] + part[1][2] + part[1][3], kWinLo - 1);
+    if (any_binned)
+      for (int e = 0; e < 256; ++e)
+        if (bins[e]) big_add(big, bins[e], e > 0 ? e - 1 : 0);
+    *gamma = big_round(big) / count;
+  }
+}
+
+__global__ __launch_bounds__(256) void gamma_finalize_kernel(const char* __restrict__ ws,
+                                                             int nblocks, double* __restrict__ gamma,
+                                                             double count) {
+  __shared__ MaskShared sh;
+  gamma_finalize_body(ws, nblocks, gamma, count, sh);
 }
 
 // ---------------------------------------------------------------------
@@ -347,17 +408,16 @@ __device__ __forceinline__ uint32_t group_field(const uint4& v, uint32_t keep, u
 // int8 codes of those groups go to wq when it is requested.  Padding rows
 // of the last strip give zero fields.
 template <int S, bool PACKED, bool WQ>
-__global__ __launch_bounds__(256) void ternary_pack_kernel(const uint16_t* __restrict__ W,
-                                                          const uint8_t* __restrict__ mask,
-                                                          const double* __restrict__ gamma,
-                                                          int64_t n_out, int64_t k,
-                                                          uint32_t* __restrict__ packed,
-                                                          int8_t* __restrict__ wq) {
+__device__ __forceinline__ void ternary_pack_body(const uint16_t* __restrict__ W,
+                                                  const uint8_t* __restrict__ mask,
+                                                  const double* __restrict__ gamma,
+                                                  int64_t n_out, int64_t k,
+                                                  uint32_t* __restrict__ packed,
+                                                  int8_t* __restrict__ wq, int64_t chunk) {
   constexpr int kWords = block_bytes(S) / 4;
   constexpr int kField = 8 + S;
   const int64_t nkb = k / kBlockK;
   const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
-  const int64_t chunk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (chunk >= strips * nkb * kStripRows) return;
   const int64_t sb = chunk / kStripRows;  // superblock = strip * nkb + kb
   const int c = (int)(chunk - sb * kStripRows);
@@ -385,6 +445,197 @@ __global__ __launch_bounds__(256) void ternary_pack_kernel(const uint16_t* __res
     uint32_t* dst = packed + chunk * kWords;
 #pragma unroll
     for (int i = 0; i < kWords; ++i) dst[i] = out[i];
+  }
+}
+
+// Packed blocks only (no int8 codes): the same fields as ternary_pack_body
+// with fewer instructions.  All sixteen group loads of a chunk are issued
+// before any field is formed (rows past n_out read the last row and get
+// keep = 0).  Per 8-group, with d = h - thr taken per 16-bit half, bit 15
+// of d is (|h| < thr) xor sign(h); v_perm spreads bit 15 / 31 of each word
+// into 0x00 / 0xff bytes and v_sad_u8 sums the selected bits, so the
+// kept-nonzero and negative bit sets take a few word operations.  The sign
+// bits are compacted through two 256-entry tables in LDS, indexed by
+// (nonzero nibble, negative nibble) of each half of four:
+//   lo[i] = nz | pext(neg, nz) << 4         (signs from the bottom)
+//   hi[i] = rev4(pext(neg, nz)) | nz << 4   (signs from the top)
+// so that field = lo[low half] | hi[high half] << S.
+struct PackTables {
+  uint8_t lo[256], hi[256];
+};
+
+__device__ __forceinline__ void build_pack_tables(PackTables& t) {
+  const uint32_t i = threadIdx.x;  // blockDim.x == 256
+  const uint32_t nz = i >> 4, neg = i & 15u;
+  uint32_t p = 0, n = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    if ((nz >> b) & 1u) {
+      p |= ((neg >> b) & 1u) << n;
+      ++n;
+    }
+  uint32_t r = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) r |= ((p >> b) & 1u) << (3 - b);
+  t.lo[i] = (uint8_t)(nz | (p << 4));
+  t.hi[i] = (uint8_t)(r | (nz << 4));
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// bit j of the result = bit 15 (j even) or 31 (j odd) of word j / 2
+__device__ __forceinline__ uint32_t gather_top_bits(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+  const uint32_t lo = __builtin_amdgcn_perm(x1, x0, 0x0b0a0908u) & 0x08040201u;
+  const uint32_t hi = __builtin_amdgcn_perm(x3, x2, 0x0b0a0908u) & 0x80402010u;
+  return __builtin_amdgcn_sad_u8(hi, 0u, __builtin_amdgcn_sad_u8(lo, 0u, 0u));
+}
+
+__device__ __forceinline__ uint32_t sub_halves(uint32_t x, uint32_t thr2) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, x) - __builtin_bit_cast(u16x2, thr2));
+}
+
+template <int S>
+__device__ __forceinline__ uint32_t fast_field(const u32x4& x, uint32_t keep, uint32_t thr2,
+                                               const PackTables& t) {
+  const uint32_t d8 = gather_top_bits(sub_halves(x[0], thr2), sub_halves(x[1], thr2),
+                                      sub_halves(x[2], thr2), sub_halves(x[3], thr2));
+  const uint32_t s8 = gather_top_bits(x[0], x[1], x[2], x[3]);
+  const uint32_t nz = keep & ~(d8 ^ s8);  // kept and |h| >= thr
+  const uint32_t neg = s8 & nz;
+  const uint32_t ilo = ((nz << 4) & 0xf0u) | (neg & 0x0fu);
+  const uint32_t ihi = (nz & 0xf0u) | (neg >> 4);
+  return (uint32_t)t.lo[ilo] | ((uint32_t)t.hi[ihi] << S);
+}
+
+template <int S>
+__device__ __forceinline__ void pack_fast_body(const uint16_t* __restrict__ W,
+                                               const uint8_t* __restrict__ mask, uint32_t thr,
+                                               int64_t n_out, int64_t k,
+                                               uint32_t* __restrict__ packed, int64_t chunk,
+                                               const PackTables& tab) {
+  constexpr int kWords = block_bytes(S) / 4;
+  constexpr int kField = 8 + S;
+  const int64_t nkb = k / kBlockK;
+  const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
+  if (chunk >= strips * nkb * kStripRows) return;
+  const int64_t sb = chunk / kStripRows;  // superblock = strip * nkb + kb
+  const int c = (int)(chunk - sb * kStripRows);
+  const int64_t strip = sb / nkb, kb = sb - strip * nkb;
+  const uint32_t thr2 = thr * 0x10001u;
+  // field f: row 16 (f >> 2) + (c & 15) of the strip, group
+  // 8 ((f >> 1) & 1) + 2 (c >> 4) + (f & 1) of the block (see field_row /
+  // field_group): per row, groups 2 (c >> 4) + {0, 1, 8, 9}
+  u32x4 v[16];
+  uint32_t keep[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t row = strip * kStripRows + 16 * q + (c & 15);
+    const bool ok = row < n_out;
+    const int64_t r = ok ? row : n_out - 1;
+    const uint16_t* wr = W + r * k + kb * kBlockK + 16 * (c >> 4);
+    v[4 * q + 0] = ld_global(reinterpret_cast<const u32x4*>(wr));
+    v[4 * q + 1] = ld_global(reinterpret_cast<const u32x4*>(wr + 8));
+    v[4 * q + 2] = ld_global(reinterpret_cast<const u32x4*>(wr + 64));
+    v[4 * q + 3] = ld_global(reinterpret_cast<const u32x4*>(wr + 72));
+    const uint8_t* mr = mask + r * (k / 8) + kb * 16 + 2 * (c >> 4);
+    const uint32_t m0 = ld_global(reinterpret_cast<const uint16_t*>(mr));
+    const uint32_t m1 = ld_global(reinterpret_cast<const uint16_t*>(mr + 8));
+    keep[2 * q] = ok ? m0 : 0u;
+    keep[2 * q + 1] = ok ? m1 : 0u;
+  }
+  uint32_t out[kWords];
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) out[i] = 0;
+#pragma unroll
+  for (int f = 0; f < 16; ++f) {
+    const uint32_t kp = (keep[f >> 1] >> (8 * (f & 1))) & 0xffu;
+    const uint32_t field = fast_field<S>(v[f], kp, thr2, tab);
+    const int off = f * kField;
+    out[off >> 5] |= field << (off & 31);
+    if ((off & 31) + kField > 32) out[(off >> 5) + 1] |= field >> (32 - (off & 31));
+  }
+  uint32_t* dst = packed + chunk * kWords;
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) st_global(dst + i, out[i]);
+}
+
+// code threshold as a 16-bit magnitude bound in [1, 0x8000] (0x8000: no
+// magnitude qualifies)
+__device__ __forceinline__ uint32_t code_threshold16(double g) {
+  const uint32_t t = code_threshold(g);
+  return t > 0x8000u ? 0x8000u : t;
+}
+
+template <int S>
+__global__ __launch_bounds__(256) void pack_fast_kernel(const uint16_t* __restrict__ W,
+                                                       const uint8_t* __restrict__ mask,
+                                                       const double* __restrict__ gamma,
+                                                       int64_t n_out, int64_t k,
+                                                       uint32_t* __restrict__ packed) {
+  __shared__ PackTables tab;
+  build_pack_tables(tab);
+  __syncthreads();
+  pack_fast_body<S>(W, mask, code_threshold16(*gamma), n_out, k, packed,
+                    (int64_t)blockIdx.x * blockDim.x + threadIdx.x, tab);
+}
+
+template <int S, bool PACKED, bool WQ>
+__global__ __launch_bounds__(256) void ternary_pack_kernel(const uint16_t* __restrict__ W,
+                                                          const uint8_t* __restrict__ mask,
+                                                          const double* __restrict__ gamma,
+                                                          int64_t n_out, int64_t k,
+                                                          uint32_t* __restrict__ packed,
+                                                          int8_t* __restrict__ wq) {
+  ternary_pack_body<S, PACKED, WQ>(W, mask, gamma, n_out, k, packed, wq,
+                                   (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// ---------------------------------------------------------------------
+// Grouped weight quantisation (several layers per launch).  Each launch
+// has a fixed grid; workgroup g takes the plan's workgroups g, g + grid, ...
+// and finds their layer in the plan's owner table.  Every workgroup of a
+// launch runs the same number of loop trips give or take one, and the loop
+// bound depends only on the plan, so every barrier inside is reached by the
+// whole workgroup.
+// ---------------------------------------------------------------------
+template <int N, int M, bool MASKED>
+__global__ __launch_bounds__(256) void mask_gamma_group_kernel(const char* __restrict__ plan) {
+  __shared__ MaskShared sh;
+  const QuantGroupHeader* h = reinterpret_cast<const QuantGroupHeader*>(plan);
+  const QuantItemDesc* items = reinterpret_cast<const QuantItemDesc*>(plan + sizeof(QuantGroupHeader));
+  const int32_t* owner = reinterpret_cast<const int32_t*>(plan + quant_owner_offset(h->count));
+  const int64_t total = h->mask_blocks;
+  for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+    const QuantItemDesc& it = items[owner[b]];
+    mask_gamma_body<N, M, MASKED>(reinterpret_cast<const uint4*>(it.W), it.ngroups, it.per,
+                                  it.mask, it.ws, b - it.mblock0, it.nmblocks, sh);
+  }
+}
+
+__global__ __launch_bounds__(256) void gamma_finalize_group_kernel(const char* __restrict__ plan) {
+  __shared__ MaskShared sh;
+  const QuantGroupHeader* h = reinterpret_cast<const QuantGroupHeader*>(plan);
+  const QuantItemDesc* items = reinterpret_cast<const QuantItemDesc*>(plan + sizeof(QuantGroupHeader));
+  for (int64_t i = blockIdx.x; i < h->count; i += gridDim.x) {
+    const QuantItemDesc& it = items[i];
+    gamma_finalize_body(it.ws, (int)it.nmblocks, it.gamma, (double)(it.n_out * it.k), sh);
+  }
+}
+
+template <int S>
+__global__ __launch_bounds__(256) void ternary_pack_group_kernel(const char* __restrict__ plan) {
+  __shared__ PackTables tab;
+  build_pack_tables(tab);
+  __syncthreads();
+  const QuantGroupHeader* h = reinterpret_cast<const QuantGroupHeader*>(plan);
+  const QuantItemDesc* items = reinterpret_cast<const QuantItemDesc*>(plan + sizeof(QuantGroupHeader));
+  const int32_t* owner =
+      reinterpret_cast<const int32_t*>(plan + quant_owner_offset(h->count)) + h->mask_blocks;
+  const int64_t total = h->pack_blocks;
+  for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+    const QuantItemDesc& it = items[owner[b]];
+    pack_fast_body<S>(it.W, it.mask, code_threshold16(*it.gamma), it.n_out, it.k,
+                      reinterpret_cast<uint32_t*>(it.packed), (b - it.pblock0) * 256 + threadIdx.x, tab);
   }
 }
 
@@ -499,8 +750,7 @@ static hipError_t launch_mask(const uint16_t* W, int64_t n_out, int64_t k, int g
                               uint8_t* mask, double* gamma, void* ws, hipStream_t s) {
   const int64_t ngroups = n_out * k / 8;
   const int64_t blocks = mask_blocks(n_out, k);
-  int64_t per = (ngroups + blocks - 1) / blocks;
-  per = (per + kMaskGroupsPerPass - 1) / kMaskGroupsPerPass * kMaskGroupsPerPass;
+  const int64_t per = mask_groups_per_block(n_out, k);
   char* w = reinterpret_cast<char*>(ws);
   const uint4* W4 = reinterpret_cast<const uint4*>(W);
   if (gamma_over == 0)
@@ -523,16 +773,34 @@ hipError_t launch_mask_gamma(const uint16_t* W, int64_t n_out, int64_t k, int n,
 template <int S>
 static hipError_t launch_tp(const uint16_t* W, const uint8_t* mask, const double* gamma,
                             int64_t n_out, int64_t k, void* packed, int8_t* wq, hipStream_t s) {
-  const int64_t chunks = ((n_out + kStripRows - 1) / kStripRows) * kStripRows * (k / kBlockK);
-  const unsigned blocks = (unsigned)((chunks + 255) / 256);
+  const unsigned blocks = (unsigned)pack_blocks(n_out, k);
   uint32_t* p = reinterpret_cast<uint32_t*>(packed);
   if (packed && wq)
     ternary_pack_kernel<S, true, true><<<blocks, 256, 0, s>>>(W, mask, gamma, n_out, k, p, wq);
   else if (packed)
-    ternary_pack_kernel<S, true, false><<<blocks, 256, 0, s>>>(W, mask, gamma, n_out, k, p, wq);
+    pack_fast_kernel<S><<<blocks, 256, 0, s>>>(W, mask, gamma, n_out, k, p);
   else
     ternary_pack_kernel<S, false, true><<<blocks, 256, 0, s>>>(W, mask, gamma, n_out, k, p, wq);
   return hipGetLastError();
+}
+
+template <int N, int M>
+static hipError_t launch_qg(const char* plan, int gamma_over, hipStream_t s) {
+  if (gamma_over == 0)
+    mask_gamma_group_kernel<N, M, false><<<kQuantGrid, 256, 0, s>>>(plan);
+  else
+    mask_gamma_group_kernel<N, M, true><<<kQuantGrid, 256, 0, s>>>(plan);
+  gamma_finalize_group_kernel<<<kQuantGammaGrid, 256, 0, s>>>(plan);
+  ternary_pack_group_kernel<s_of(N, M)><<<kQuantGrid, 256, 0, s>>>(plan);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_group(const void* plan, int n, int m, int gamma_over, hipStream_t s) {
+  const char* p = reinterpret_cast<const char*>(plan);
+  if (m == 8 && n == 8) return launch_qg<8, 8>(p, gamma_over, s);
+  if (m == 8 && n == 6) return launch_qg<6, 8>(p, gamma_over, s);
+  if (m == 8 && n == 4) return launch_qg<4, 8>(p, gamma_over, s);
+  return launch_qg<2, 4>(p, gamma_over, s);
 }
 
 hipError_t launch_ternary_pack(const uint16_t* W, const uint8_t* mask, const double* gamma,

@@ -74,3 +74,32 @@ class BitLinearWeight:
         bl.bitlinear_bwd(dY, xq, x_scale, self.packed, self.gamma, tokens, self.k, self.n_out,
                          self.n, self.m, gx, gw, ws=ws, stream=stream)
         return gx, gw
+
+
+class QuantGroup:
+    """Grouped weight quantisation of several BitLinearWeight layers that
+    share one N:M pattern and gamma mode: the plan (device descriptors) is
+    built once for fixed (weight, layer) pairs, then each `run` recomputes
+    every mask, gamma and packed block in three launches."""
+
+    def __init__(self, pairs, stream=None):
+        lws = [lw for lw, _ in pairs]
+        if not lws:
+            raise ValueError("QuantGroup needs at least one layer")
+        n, m, go = lws[0].n, lws[0].m, lws[0].gamma_over
+        if any((lw.n, lw.m, lw.gamma_over) != (n, m, go) for lw in lws):
+            raise ValueError("all layers of a QuantGroup share n, m and gamma_over")
+        self.n, self.m, self.gamma_over = n, m, go
+        self.weights = [W for _, W in pairs]
+        entries = [dict(W=W, mask=lw.mask, gamma=lw.gamma, packed=lw.packed, n_out=lw.n_out, k=lw.k)
+                   for lw, W in pairs]
+        self.items = bl.make_quant_items(entries, n, m)
+        d = lws[0].device
+        self.ws = torch.empty(max(bl.bitlinear_quant_group_workspace_bytes(self.items, len(entries)), 1),
+                              dtype=torch.uint8, device=d)
+        self.plan = torch.empty(bl.bitlinear_quant_group_plan_bytes(self.items, len(entries)),
+                                dtype=torch.uint8, device=d)
+        bl.bitlinear_quant_group_plan(self.items, len(entries), n, m, go, self.ws, self.plan, stream=stream)
+
+    def run(self, stream=None):
+        bl.bitlinear_quant_group(self.plan, self.n, self.m, self.gamma_over, stream=stream)

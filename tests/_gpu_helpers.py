@@ -49,6 +49,10 @@ def check_weight_path(Wbits, n, m, gamma_over=0):
     got_P = lw.packed.cpu().numpy()
     assert got_P.size == P.size
     assert np.array_equal(got_P, P), f"packed bytes differ at {np.flatnonzero(got_P != P)[:8]}"
+    # packed bytes alone (no int8 codes requested) take another pack kernel
+    lw2, _, _ = quantize_on_gpu(Wbits, n, m, gamma_over, want_wq=False)
+    got_P2 = lw2.packed.cpu().numpy()
+    assert np.array_equal(got_P2, P), f"packed-only bytes differ at {np.flatnonzero(got_P2 != P)[:8]}"
     return lw, T, g
 
 

@@ -124,3 +124,52 @@ def test_launch_without_device_reports_hip_error(L):
     st = L.bitlinear_pack(A, A, A, 128, 256, 6, 8, A, nb, None)
     assert st == bl.BL_EHIP
     assert bl.bitlinear_last_error()
+
+
+def _qitems(shapes, over=None):
+    arr = (bl.bitlinear_quant_item * len(shapes))()
+    for i, (n_out, k) in enumerate(shapes):
+        f = dict(W=A, mask=A, gamma=A, packed=A, n_out=n_out, k=k)
+        f.update((over or {}).get(i, {}))
+        arr[i] = bl.bitlinear_quant_item(f["W"], f["mask"], f["gamma"], f["packed"], f["n_out"], f["k"])
+    return arr
+
+
+def test_quant_group_sizes(L):
+    """The grouped workspace is one 256-byte aligned region per item, each at
+    least the single call's workspace; bad shapes give 0."""
+    shapes = [(896, 896), (128, 896), (4864, 896), (896, 4864)]
+    items = _qitems(shapes)
+    ws = bl.bitlinear_quant_group_workspace_bytes(items, len(shapes))
+    single = [bl.bitlinear_workspace_bytes(n_out, k) for n_out, k in shapes]
+    assert ws == sum((s + 255) // 256 * 256 for s in single)
+    plan = bl.bitlinear_quant_group_plan_bytes(items, len(shapes))
+    assert plan > 64 + 128 * len(shapes)
+    assert bl.bitlinear_quant_group_workspace_bytes(_qitems([(128, 100)]), 1) == 0
+    assert bl.bitlinear_quant_group_plan_bytes(items, 0) == 0
+    assert bl.bitlinear_quant_group_plan_bytes(None, 1) == 0
+
+
+def test_quant_group_validation(L):
+    shapes = [(128, 256), (256, 128)]
+    items = _qitems(shapes)
+    ws = bl.bitlinear_quant_group_workspace_bytes(items, 2)
+    pb = bl.bitlinear_quant_group_plan_bytes(items, 2)
+    f = L.bitlinear_quant_group_plan
+    assert f(items, 2, 5, 8, 0, A, ws, A, pb, None) == bl.BL_EUNSUPPORTED
+    assert f(items, 2, 6, 8, 2, A, ws, A, pb, None) == bl.BL_EINVAL
+    assert f(items, 0, 6, 8, 0, A, ws, A, pb, None) == bl.BL_ESHAPE
+    assert f(None, 2, 6, 8, 0, A, ws, A, pb, None) == bl.BL_EINVAL
+    assert f(_qitems([(128, 256), (128, 100)]), 2, 6, 8, 0, A, ws, A, pb, None) == bl.BL_ESHAPE
+    assert "item 1" in bl.bitlinear_last_error()
+    assert f(_qitems(shapes, {1: dict(W=A + 2)}), 2, 6, 8, 0, A, ws, A, pb, None) == bl.BL_EINVAL
+    assert f(_qitems(shapes, {0: dict(packed=None)}), 2, 6, 8, 0, A, ws, A, pb, None) == bl.BL_EINVAL
+    assert f(_qitems(shapes, {0: dict(gamma=A + 4)}), 2, 6, 8, 0, A, ws, A, pb, None) == bl.BL_EINVAL
+    assert f(items, 2, 6, 8, 0, A, ws - 1, A, pb, None) == bl.BL_EWORKSPACE
+    assert f(items, 2, 6, 8, 0, None, ws, A, pb, None) == bl.BL_EWORKSPACE
+    assert f(items, 2, 6, 8, 0, A, ws, A, pb - 1, None) == bl.BL_EWORKSPACE
+    assert f(items, 2, 6, 8, 0, A, ws, None, pb, None) == bl.BL_EINVAL
+    g = L.bitlinear_quant_group
+    assert g(A, 6, 8, 3, None) == bl.BL_EINVAL
+    assert g(None, 6, 8, 0, None) == bl.BL_EINVAL
+    assert g(A, 7, 8, 0, None) == bl.BL_EUNSUPPORTED

@@ -9,7 +9,7 @@ import torch
 import oracle
 from sparse_linear_layers_group_amd import bitlinear as bl
 from sparse_linear_layers_group_amd import synth
-from sparse_linear_layers_group_amd.layer import BitLinearWeight, bf16_tensor
+from sparse_linear_layers_group_amd.layer import BitLinearWeight, QuantGroup, bf16_tensor
 
 import _gpu_helpers as H
 
@@ -109,13 +109,16 @@ def test_gamma_exact_for_out_of_window_magnitudes():
 def test_gamma_exact_over_many_workgroups():
     """Enough 8-groups for the largest mask grid (1024 workgroups, two
     passes each, a short last range), with magnitudes of every exponent
-    scattered so that many workgroups take the rare accumulation path."""
+    and signed zeros scattered so that many wavefronts mix groups on the
+    window path with groups on the exact per-element path."""
     W = synth.weights(2304, 4096, seed=23)
     rng = np.random.default_rng(23)
     pos = rng.choice(W.size, size=3000, replace=False)
     flat = W.reshape(-1)
     flat[pos] = rng.integers(1, 0x7F80, size=pos.size, dtype=np.uint16)
     flat[pos[::2]] |= 0x8000
+    zeros = rng.choice(W.size, size=2000, replace=False)  # +0 and -0 among in-window groups
+    flat[zeros] = np.where(np.arange(zeros.size) % 2 == 0, 0, 0x8000).astype(np.uint16)
     assert bl.bitlinear_workspace_bytes(2304, 4096) == 1024 * (32 + 2048)
     H.check_weight_path(W, 6, 8)
 
@@ -277,3 +280,79 @@ def test_group_plan_validation():
         bl.bitlinear_fwd_group_plan(items, 1, 1, 6, 8, plan)
     assert err.value.status == bl.BL_EWORKSPACE
     assert bl.bitlinear_fwd_group_plan_bytes(items, 1, 17) == 0  # decode only: <= 16 tokens
+
+
+@pytest.mark.parametrize("n,m,gamma_over", [(6, 8, 0), (8, 8, 0), (2, 4, 0), (4, 8, 1)])
+def test_grouped_quantisation_matches_oracle(n, m, gamma_over):
+    """Grouped mask + gamma + pack of ragged layers in one plan: every mask,
+    gamma and packed byte bit-identical to the oracle, run twice (the plan
+    is reused and the shared workspace needs no clearing between runs)."""
+    shapes = [(48, 256), (200, 896), (16, 128), (896, 896), (128, 2432), (40, 384)]
+    pairs, refs = [], []
+    for i, (n_out, k) in enumerate(shapes):
+        Wbits = synth.weights(n_out, k, seed=40 + i)
+        mb = oracle.mask(Wbits, n, m)
+        g = oracle.gamma(Wbits, gamma_over == bl.BL_GAMMA_MASKED, mb)
+        P = oracle.pack(oracle.ternary(Wbits, mb, g), H.S_OF[(n, m)])
+        pairs.append((BitLinearWeight(n_out, k, n, m, gamma_over), bf16_tensor(Wbits)))
+        refs.append((mb, g, P))
+    qg = QuantGroup(pairs)
+    for rep in range(2):
+        for lw, _ in pairs:
+            lw.mask.fill_(0xA5)
+            lw.packed.fill_(0x5A)
+            lw.gamma.fill_(float("nan"))
+        qg.run()
+        torch.cuda.synchronize()
+        for (lw, _), (mb, g, P) in zip(pairs, refs):
+            assert np.array_equal(lw.mask.cpu().numpy().reshape(mb.shape), mb), (rep, lw.n_out, lw.k)
+            assert H.f64_bits(lw.gamma.cpu().numpy()[0]) == H.f64_bits(g), (rep, lw.n_out, lw.k)
+            assert np.array_equal(lw.packed.cpu().numpy(), P), (rep, lw.n_out, lw.k)
+
+
+def test_grouped_quantisation_full_size_matches_single_calls():
+    """A Qwen2.5-1.5B-shaped block (q, k, v, o, gate, up, down) in one plan:
+    bit-identical to the single-layer calls, which the weight-path tests
+    pin to the oracle; gamma also against the oracle, with magnitudes of
+    every exponent planted so workgroups take the rare accumulation path."""
+    shapes = [(1536, 1536), (256, 1536), (256, 1536), (1536, 1536), (8960, 1536), (8960, 1536),
+              (1536, 8960)]
+    rng = np.random.default_rng(77)
+    pairs, singles, gref = [], [], []
+    for i, (n_out, k) in enumerate(shapes):
+        Wbits = synth.weights(n_out, k, seed=0, config=3, layer=i)
+        flat = Wbits.reshape(-1)
+        pos = rng.choice(flat.size, size=500, replace=False)
+        flat[pos] = rng.integers(1, 0x7F80, size=pos.size, dtype=np.uint16)
+        W = bf16_tensor(Wbits)
+        single = BitLinearWeight(n_out, k, 6, 8)
+        single.quantize(W)
+        pairs.append((BitLinearWeight(n_out, k, 6, 8), W))
+        singles.append(single)
+        gref.append(oracle.gamma(Wbits, False, None))
+    qg = QuantGroup(pairs)
+    qg.run()
+    torch.cuda.synchronize()
+    for (lw, _), s, g in zip(pairs, singles, gref):
+        assert torch.equal(lw.mask, s.mask), (lw.n_out, lw.k)
+        assert torch.equal(lw.packed, s.packed), (lw.n_out, lw.k)
+        assert H.f64_bits(lw.gamma.cpu().numpy()[0]) == H.f64_bits(s.gamma.cpu().numpy()[0]) == H.f64_bits(g)
+
+
+def test_grouped_quantisation_plan_checks():
+    lw = BitLinearWeight(64, 256, 6, 8)
+    W = torch.zeros(64 * 256, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        QuantGroup([(lw, W), (BitLinearWeight(64, 256, 8, 8), W)])
+    qg = QuantGroup([(lw, W)])
+    with pytest.raises(bl.BitLinearError):
+        bl.bitlinear_quant_group_plan(qg.items, 1, 6, 8, 0, qg.ws[:0], qg.plan)
+    with pytest.raises(bl.BitLinearError):
+        bl.bitlinear_quant_group_plan(qg.items, 1, 6, 8, 0, qg.ws, qg.plan[:16])
+    qg.run()
+    torch.cuda.synchronize()
+    Z = np.zeros((64, 256), np.uint16)
+    mb = oracle.mask(Z, 6, 8)  # all magnitudes equal: the lower indices are kept
+    assert lw.gamma.cpu().item() == 0.0
+    assert np.array_equal(lw.mask.cpu().numpy().reshape(mb.shape), mb)
+    assert np.array_equal(lw.packed.cpu().numpy(), oracle.pack(oracle.ternary(Z, mb, 0.0), 6))
