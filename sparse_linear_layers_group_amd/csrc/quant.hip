@@ -22,17 +22,18 @@ namespace bl {
 // One fixed-point window covers |W| in [2^-59, 2): E in [kWinLo, 128)
 // adds sig << (E - kWinLo) (< 2^60; eight of them < 2^63) to an integer
 // in units of 2^(kWinLo-134).  A group whose eight magnitudes are all in
-// the window (the common case) takes that sum with no per-element test;
-// a group holding a zero or any magnitude outside it takes the exact
-// per-element path, where every other nonzero magnitude adds sig into an
-// exponent bin of its workgroup (in LDS).  Integer addition is
+// the window and within 2^13 of each other (the common case) is summed in
+// binary32, exactly; one with a wider spread takes the 64-bit window sum;
+// a group holding a zero or any magnitude outside the window takes the
+// exact per-element path, where every other nonzero magnitude adds sig
+// into an exponent bin of its workgroup (in LDS).  Integer addition is
 // associative, so the result does not depend on scheduling.
 // ---------------------------------------------------------------------
 constexpr int kWinLo = 75;
 // rank keys (|h| << 3 | index code) bounding the window: a group is on
 // the fast path iff its smallest key >= kKeyLo and its largest < kKeyHi
-constexpr uint32_t kKeyLo = (uint32_t)kWinLo << 10;
-constexpr uint32_t kKeyHi = 128u << 10;
+constexpr uint32_t kKeyLo = (uint32_t)kWinLo << 23;
+constexpr uint32_t kKeyHi = 128u << 23;
 
 struct MaskPart {
   unsigned long long hi, lo;  // window sum = hi * 2^32 + lo
@@ -41,11 +42,11 @@ struct MaskPart {
 };
 static_assert(sizeof(MaskPart) == 32, "mask partial record");
 
-// keys: |h| (15 bits) above a 3-bit code that ranks a lower index higher;
-// all keys of a group are distinct and a larger key ranks first.
-__device__ __forceinline__ uint32_t rank_key(uint32_t h, int j) {
-  return ((h & 0x7fffu) << 3) | (uint32_t)(7 - j);
-}
+// keys: |h| (15 bits) in bits 16..30 above a 3-bit code (bits 0..2) that
+// ranks a lower index higher; all keys of a group are distinct, a larger
+// key ranks first, and bits 3..15 are zero, so 0x80 >> key (the shift
+// takes bits 0..4) is the mask bit of the key's element.
+__device__ __forceinline__ uint32_t drop_bit(uint32_t key) { return 0x80u >> key; }
 
 __device__ __forceinline__ uint32_t min3(uint32_t a, uint32_t b, uint32_t c) { return min(min(a, b), c); }
 __device__ __forceinline__ uint32_t max3(uint32_t a, uint32_t b, uint32_t c) { return max(max(a, b), c); }
@@ -57,50 +58,55 @@ __device__ __forceinline__ void cswap(uint32_t& a, uint32_t& b) {
 }
 
 // mask bits of one 8-group (w = 8 bf16, element j in bits 16j..16j+15 of
-// the four words) for the pattern N:M; kmin / kmax receive the smallest
-// and largest rank key of the group
+// the four words) for the pattern N:M: every element but the M-N smallest
+// keys of each group of M; kmin / kmax receive the smallest and largest
+// rank key of the eight
 template <int N, int M>
 __device__ __forceinline__ uint32_t group_mask(const uint32_t w[4], uint32_t& kmin, uint32_t& kmax) {
   uint32_t key[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) key[j] = rank_key((w[j >> 1] >> (16 * (j & 1))) & 0xffffu, j);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = w[i] & 0x7fff7fffu;
+    key[2 * i] = (a << 16) | (uint32_t)(7 - 2 * i);
+    key[2 * i + 1] = (a & 0xffff0000u) | (uint32_t)(6 - 2 * i);
+  }
   if (N == M) {
     kmin = min(min3(key[0], key[1], key[2]), min3(key[3], key[4], min3(key[5], key[6], key[7])));
     kmax = max(max3(key[0], key[1], key[2]), max3(key[3], key[4], max3(key[5], key[6], key[7])));
     return 0xffu;
   }
-  uint32_t tau_lo, tau_hi;  // a key is kept iff it exceeds its half's / group's tau
   if (M == 4) {
     // 2:4 -- per half of four, drop the two smallest keys
-    uint32_t t[2], lo[2], hi[2];
+    uint32_t drop = 0, lo[2], hi[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t p0 = min(key[4 * h], key[4 * h + 1]), P0 = max(key[4 * h], key[4 * h + 1]);
       uint32_t p1 = min(key[4 * h + 2], key[4 * h + 3]), P1 = max(key[4 * h + 2], key[4 * h + 3]);
-      t[h] = min(max(p0, p1), min(P0, P1));  // second smallest of four
-      lo[h] = min(p0, p1);
+      lo[h] = min(p0, p1);                   // smallest of four
+      const uint32_t t = min3(max(p0, p1), P0, P1);  // second smallest of four
       hi[h] = max(P0, P1);
+      drop |= drop_bit(lo[h]) | drop_bit(t);
     }
-    tau_lo = t[0];
-    tau_hi = t[1];
     kmin = min(lo[0], lo[1]);
     kmax = max(hi[0], hi[1]);
+    return 0xffu & ~drop;
   } else if (N == 6) {
-    // 6:8 -- tau = second smallest of eight
+    // 6:8 -- drop the smallest and the second smallest of eight
     uint32_t p[4], P[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       p[i] = min(key[2 * i], key[2 * i + 1]);
       P[i] = max(key[2 * i], key[2 * i + 1]);
     }
-    uint32_t q1 = min(p[0], p[1]), q2 = min(max(p[0], p[1]), min(P[0], P[1]));
-    uint32_t r1 = min(p[2], p[3]), r2 = min(max(p[2], p[3]), min(P[2], P[3]));
-    tau_lo = tau_hi = min(max(q1, r1), min(q2, r2));
+    const uint32_t q1 = min(p[0], p[1]), q2 = min3(max(p[0], p[1]), P[0], P[1]);
+    const uint32_t r1 = min(p[2], p[3]), r2 = min3(max(p[2], p[3]), P[2], P[3]);
     kmin = min(q1, r1);
+    const uint32_t second = min3(max(q1, r1), q2, r2);
     kmax = max(max3(P[0], P[1], P[2]), P[3]);
+    return 0xffu ^ drop_bit(kmin) ^ drop_bit(second);
   } else {
     // general N of 8: sort (Batcher odd-even merge network, 19 swaps),
-    // tau = (8-N)-th smallest
+    // drop the 8-N smallest
     uint32_t s[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) s[j] = key[j];
@@ -110,17 +116,31 @@ __device__ __forceinline__ uint32_t group_mask(const uint32_t w[4], uint32_t& km
     cswap(s[0], s[4]); cswap(s[1], s[5]); cswap(s[2], s[6]); cswap(s[3], s[7]);
     cswap(s[2], s[4]); cswap(s[3], s[5]);
     cswap(s[1], s[2]); cswap(s[3], s[4]); cswap(s[5], s[6]);
-    tau_lo = tau_hi = s[7 - N];
+    uint32_t drop = 0;
+#pragma unroll
+    for (int j = 0; j < 8 - N; ++j) drop |= drop_bit(s[j]);
     kmin = s[0];
     kmax = s[7];
+    return 0xffu & ~drop;
   }
-  uint32_t bits = 0;
+}
+
+// window sum of one 8-group whose eight magnitudes are nonzero, in the
+// window and within 2^13 of each other (exponent fields at most 13 apart),
+// as hi * 2^32 + lo: in units of the smallest one's last bit they are
+// integers below 2^21, so every partial sum in binary32 is exact (below
+// 2^24 of those units) and so is the total s < 16, a multiple of 2^-59;
+// hi = floor(s 2^27), lo = frac(s 2^27) 2^32 (both conversions exact)
+__device__ __forceinline__ void group_sum_f32(const uint32_t w[4], uint32_t& hi, uint32_t& lo) {
+  float s = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t tau = (j < 4) ? tau_lo : tau_hi;
-    bits |= ((tau - key[j]) >> 31) << j;  // key > tau (keys < 2^18)
+  for (int i = 0; i < 4; ++i) {
+    s += __builtin_fabsf(__uint_as_float(w[i] << 16));
+    s += __builtin_fabsf(__uint_as_float(w[i] & 0xffff0000u));
   }
-  return bits;
+  const float t = s * 0x1p27f;
+  hi = (uint32_t)t;
+  lo = (uint32_t)(__builtin_amdgcn_fractf(t) * 0x1p32f);
 }
 
 // window sum of one 8-group whose eight magnitudes are all nonzero and in
@@ -252,10 +272,20 @@ __device__ __forceinline__ void mask_gamma_body(const uint4* __restrict__ W, int
       uint32_t kmin, kmax;
       const uint32_t keep = group_mask<N, M>(w, kmin, kmax);
       st_global(mask + grp, (uint8_t)keep);
-      unsigned long long gs = group_sum_window(w);
-      if (MASKED || kmin < kKeyLo || kmax >= kKeyHi) gs = group_sum_exact<MASKED>(w, keep, bins, binned);
-      lo += (uint32_t)gs;
-      hi += gs >> 32;
+      uint32_t ghi, glo;
+      group_sum_f32(w, ghi, glo);
+      const bool inwin = kmin >= kKeyLo && kmax < kKeyHi;
+      if (MASKED || !inwin || (kmax >> 23) - (kmin >> 23) > 13u) {
+        unsigned long long gs;
+        if (!MASKED && inwin)
+          gs = group_sum_window(w);
+        else
+          gs = group_sum_exact<MASKED>(w, keep, bins, binned);
+        ghi = (uint32_t)(gs >> 32);
+        glo = (uint32_t)gs;
+      }
+      lo += glo;
+      hi += ghi;
     }
   }
   hi = wave_sum_u64(hi);
