@@ -55,7 +55,7 @@ DECODE_TRAFFIC = {
     "sources": ["sparse_linear_layers_group_amd/csrc/gemv.hip",
                 "sparse_linear_layers_group_amd/csrc/common.h",
                 "sparse_linear_layers_group_amd/csrc/launch.h"],
-    "sha256": "01e434b3958abda9ee51a8fff7701321cbeac4d491ca16ce9c3dae10759a08c3",
+    "sha256": "38bc4cb16278521aaa8470ea00d9aaf50553996ca0f2961bed90aeb867139f62",
     "fetch_kib": 39923.41, "fetch_scale": 2.0,
     "write_kib": 1188.0, "write_scale": 1.0,
 }
