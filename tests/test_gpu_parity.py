@@ -356,3 +356,49 @@ def test_grouped_quantisation_plan_checks():
     assert lw.gamma.cpu().item() == 0.0
     assert np.array_equal(lw.mask.cpu().numpy().reshape(mb.shape), mb)
     assert np.array_equal(lw.packed.cpu().numpy(), oracle.pack(oracle.ternary(Z, mb, 0.0), 6))
+
+
+def _near_half_way_rows(rng, rows, k):
+    """Rows whose quotients 127 x / a sit on or within 2^-11 of half-integers
+    (exact ties included), for random bf16 maxima a, plus rows whose maximum
+    is tiny (subnormal, and the smallest magnitudes around 2^-100)."""
+    out = np.zeros((rows, k), np.uint16)
+    for r in range(rows):
+        if r == rows - 1:
+            a_bits = 0x0040  # subnormal maximum
+        elif r == rows - 2:
+            a_bits = 0x0D80  # 2^-100
+        elif r == rows - 3:
+            a_bits = 0x0D7F  # just below 2^-100
+        else:
+            a_bits = int(rng.integers(0x3000, 0x4C00))  # about 2^-31 .. 2^25
+        mags = np.arange(1, a_bits + 1, dtype=np.uint32).astype(np.uint16)
+        vals = synth.bf16_bits_to_f32(mags).astype(np.float64)
+        a = vals[-1]
+        q = 127.0 * vals / a
+        near = np.abs(np.abs(q - np.floor(q)) - 0.5) <= 2.0 ** -11
+        pick = mags[near]
+        if pick.size == 0 or a_bits < 0x0080:
+            pick = mags
+        sel = rng.choice(pick, size=k - 1, replace=True)
+        sel = sel | (rng.integers(0, 2, size=k - 1).astype(np.uint16) << 15)
+        out[r, 0] = a_bits | (0x8000 if r % 2 else 0)
+        out[r, 1:] = sel
+    return out
+
+
+@pytest.mark.parametrize("rows,k", [(40, 1024), (9, 8960)])
+def test_act_quant_near_half_way_quotients(rows, k):
+    """The activation codes are round-half-even of the exact quotient,
+    including quotients on or next to half-integers (taken exactly), and
+    rows whose maximum is below 2^-100 (division path)."""
+    rng = np.random.default_rng(rows + k)
+    X = _near_half_way_rows(rng, rows, k)
+    xq_ref, sc_ref = oracle.act_quant(X)
+    xq = torch.empty(rows * k, dtype=torch.int8, device="cuda")
+    sc = torch.empty(rows, dtype=torch.float32, device="cuda")
+    bl.bitlinear_act_quant(bf16_tensor(X), rows, k, xq, sc)
+    torch.cuda.synchronize()
+    got = xq.cpu().numpy().reshape(rows, k)
+    assert np.array_equal(got, xq_ref), f"x_q differs at {np.argwhere(got != xq_ref)[:5]}"
+    assert np.array_equal(sc.cpu().numpy(), sc_ref.astype(np.float32))
