@@ -524,7 +524,26 @@ def main():
         }
         log(f"decode 8:8: step {s88 * 1000:.1f} us, contraction {g88 * 1000:.1f} us")
         out["single_call_us"] = single_call_latency(torch, bl, d68)
+        p88 = d88["per_step"]["packed"]
         del d88
+        # the same decode step at the other patterns the pages sweep (8:8
+        # down to 2:8; 2:4 for reference): packed bytes and measured times
+        sweep = {}
+        for n, m in ((4, 8), (3, 8), (2, 8), (2, 4)):
+            dn = build_decode(torch, bl, n, m)
+            sn, _, gn = time_decode(torch, bl, dn, n, m, args.steps, args.warmup)
+            pk = dn["per_step"]["packed"]
+            sweep[f"{n}:{m}"] = {
+                "step_us": round(sn * 1000, 3),
+                "contraction_us": round(gn * 1000, 3),
+                "packed_bytes_per_step": pk,
+                "bytes_ratio_vs_8_8": round(p88 / pk, 4),
+                "step_speedup_vs_8_8": round(s88 / sn, 4),
+                "contraction_speedup_vs_8_8": round(g88 / gn, 4),
+            }
+            log(f"decode {n}:{m}: step {sn * 1000:.1f} us, contraction {gn * 1000:.1f} us")
+            del dn
+        out["decode_nm_sweep"] = sweep
         log("prefill ...")
         out["prefill_qwen15_6_8"] = prefill_step(torch, bl, 6, 8)
         out["prefill_qwen15_8_8"] = prefill_step(torch, bl, 8, 8)

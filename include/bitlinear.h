@@ -17,7 +17,8 @@
  *     device memory and no global state between calls.
  *   - bf16 tensors are passed as uint16_t bit patterns.  W is [n_out x k],
  *     X is [tokens x k], dY is [tokens x n_out]; all row-major, contiguous.
- *   - Supported patterns (n, m): 8:8 (dense), 6:8, 4:8, 2:4.  k must be a
+ *   - Supported patterns (n, m): 8:8 (dense), 6:8, 4:8, 3:8, 2:8 (the
+ *     sweep of the Sparse-BitNet article, §四) and 2:4.  k must be a
  *     positive multiple of 128; n_out >= 1; n_out*k, tokens*k and
  *     tokens*n_out below 2^31.
  *   - Outputs must not alias inputs or each other.
@@ -58,7 +59,8 @@ extern "C" {
 /* Bytes of the packed ternary weights for an [n_out x k] layer under
  * pattern n:m, or 0 if the shape or pattern is unsupported.  The packed
  * layout stores each row's codes per 8-group as a nonzero bitmap plus one
- * sign bit per nonzero (S = 8, 6, 4, 4 sign slots for 8:8, 6:8, 4:8, 2:4),
+ * sign bit per nonzero (S = 8, 6, 4, 4, 4, 2 sign slots for 8:8, 6:8, 4:8,
+ * 3:8, 2:4, 2:8: the nonzeros an 8-group can hold, rounded up to even),
  * 16 groups per 128-wide k block, rows in strips of 64 (the last strip
  * padded with zero fields):
  *   ceil(n_out/64) * 64 * (k/128) * 2*(8+S) bytes.

@@ -434,6 +434,8 @@ int oracle_s_of(int n, int m)
     if (m == 8 && n == 6) return 6;
     if (m == 8 && n == 4) return 4;
     if (m == 4 && n == 2) return 4;
+    if (m == 8 && n == 3) return 4;
+    if (m == 8 && n == 2) return 2;
     return -1;
 }
 

@@ -336,6 +336,7 @@ hipError_t launch_bwd_dx(const uint16_t* dY, const void* packed, const double* g
   const unsigned sbs = (unsigned)(strips * nkb);
   if (S == 8) prep_codes_t_kernel<8><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
   else if (S == 6) prep_codes_t_kernel<6><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
+  else if (S == 2) prep_codes_t_kernel<2><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
   else prep_codes_t_kernel<4><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -46,10 +46,12 @@ __host__ __device__ constexpr int field_group(int c, int f) {
 
 __host__ __device__ constexpr int block_bytes(int S) { return 2 * (8 + S); }
 
-// sign slots per 8-group for a supported n:m, else -1
+// sign slots per 8-group for a supported n:m, else -1 (an even count at
+// least the nonzeros an 8-group can hold, so a chunk is whole 32-bit words:
+// 3:8 shares the 4-slot layout of 4:8 and 2:4)
 __host__ __device__ constexpr int s_of(int n, int m) {
   return (m == 8 && n == 8) ? 8 : (m == 8 && n == 6) ? 6 : (m == 8 && n == 4) ? 4
-       : (m == 4 && n == 2) ? 4 : -1;
+       : (m == 4 && n == 2) ? 4 : (m == 8 && n == 3) ? 4 : (m == 8 && n == 2) ? 2 : -1;
 }
 
 // bf16 helpers ---------------------------------------------------------

@@ -139,9 +139,12 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
     } else if constexpr (kW == 7) {
       const u32x3 b = __builtin_amdgcn_raw_buffer_load_b96(pr, o + 16, 0, 0);
       dst[4] = b.x; dst[5] = b.y; dst[6] = b.z;
-    } else {
+    } else if constexpr (kW == 6) {
       const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(pr, o + 16, 0, 0);
       dst[4] = b.x; dst[5] = b.y;
+    } else {
+      static_assert(kW == 5, "chunk size");
+      dst[4] = __builtin_amdgcn_raw_buffer_load_b32(pr, o + 16, 0, 0);
     }
   };
   // one field of a chunk: the codes of field 4i + 2h + q go to lanes
@@ -385,6 +388,7 @@ hipError_t launch_gemm(const void* packed, const int8_t* xq, const float* scale,
                        int64_t k, int64_t n_out, int S, hipStream_t s) {
   if (S == 8) return launch_gemm_s<8>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
   if (S == 6) return launch_gemm_s<6>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
+  if (S == 2) return launch_gemm_s<2>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
   return launch_gemm_s<4>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
 }
 

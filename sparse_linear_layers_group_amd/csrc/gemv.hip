@@ -146,11 +146,16 @@ __device__ __forceinline__ void issue(Stage<S>& st, const Cursor& cur, bool live
     const u32x3 b = __builtin_amdgcn_raw_buffer_load_b96(cur.sv.pk, po + 16, 0, 0);
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y; w[6] = b.z;
-  } else {
+  } else if constexpr (kBytes == 24) {
     const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cur.sv.pk, po, 0, 0);
     const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(cur.sv.pk, po + 16, 0, 0);
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y;
+  } else {
+    static_assert(kBytes == 20, "chunk size");
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(cur.sv.pk, po, 0, 0);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = __builtin_amdgcn_raw_buffer_load_b32(cur.sv.pk, po + 16, 0, 0);
   }
   // B operand of k half h: token t = lane%16, k slice lane/16.  Columns
   // t >= tokens are never stored, so those lanes read token 0 (in range).
@@ -558,6 +563,7 @@ hipError_t launch_gemv(const void* packed, const int8_t* xq, const float* scale,
                        int64_t k, int64_t n_out, int S, hipStream_t s) {
   if (S == 8) return launch_gemv_s<8>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
   if (S == 6) return launch_gemv_s<6>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
+  if (S == 2) return launch_gemv_s<2>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
   return launch_gemv_s<4>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
 }
 
@@ -565,6 +571,7 @@ hipError_t launch_gemv_group(const void* plan, int S, hipStream_t s) {
   const char* p = reinterpret_cast<const char*>(plan);
   if (S == 8) gemv_group_kernel<8><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
   else if (S == 6) gemv_group_kernel<6><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
+  else if (S == 2) gemv_group_kernel<2><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
   else gemv_group_kernel<4><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
   return hipGetLastError();
 }

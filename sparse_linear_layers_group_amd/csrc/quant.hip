@@ -797,6 +797,8 @@ hipError_t launch_mask_gamma(const uint16_t* W, int64_t n_out, int64_t k, int n,
   if (m == 8 && n == 8) return launch_mask<8, 8>(W, n_out, k, gamma_over, mask, gamma, ws, s);
   if (m == 8 && n == 6) return launch_mask<6, 8>(W, n_out, k, gamma_over, mask, gamma, ws, s);
   if (m == 8 && n == 4) return launch_mask<4, 8>(W, n_out, k, gamma_over, mask, gamma, ws, s);
+  if (m == 8 && n == 3) return launch_mask<3, 8>(W, n_out, k, gamma_over, mask, gamma, ws, s);
+  if (m == 8 && n == 2) return launch_mask<2, 8>(W, n_out, k, gamma_over, mask, gamma, ws, s);
   return launch_mask<2, 4>(W, n_out, k, gamma_over, mask, gamma, ws, s);
 }
 
@@ -830,6 +832,8 @@ hipError_t launch_quant_group(const void* plan, int n, int m, int gamma_over, hi
   if (m == 8 && n == 8) return launch_qg<8, 8>(p, gamma_over, s);
   if (m == 8 && n == 6) return launch_qg<6, 8>(p, gamma_over, s);
   if (m == 8 && n == 4) return launch_qg<4, 8>(p, gamma_over, s);
+  if (m == 8 && n == 3) return launch_qg<3, 8>(p, gamma_over, s);
+  if (m == 8 && n == 2) return launch_qg<2, 8>(p, gamma_over, s);
   return launch_qg<2, 4>(p, gamma_over, s);
 }
 
@@ -838,6 +842,7 @@ hipError_t launch_ternary_pack(const uint16_t* W, const uint8_t* mask, const dou
                                hipStream_t s) {
   if (S == 8) return launch_tp<8>(W, mask, gamma, n_out, k, packed, wq, s);
   if (S == 6) return launch_tp<6>(W, mask, gamma, n_out, k, packed, wq, s);
+  if (S == 2) return launch_tp<2>(W, mask, gamma, n_out, k, packed, wq, s);
   return launch_tp<4>(W, mask, gamma, n_out, k, packed, wq, s);
 }
 

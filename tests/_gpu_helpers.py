@@ -7,7 +7,7 @@ import oracle
 from sparse_linear_layers_group_amd import bitlinear as bl
 from sparse_linear_layers_group_amd.layer import BitLinearWeight, bf16_tensor
 
-S_OF = {(8, 8): 8, (6, 8): 6, (4, 8): 4, (2, 4): 4}
+S_OF = {(8, 8): 8, (6, 8): 6, (4, 8): 4, (2, 4): 4, (3, 8): 4, (2, 8): 2}
 
 
 def ensure_built():

@@ -25,7 +25,7 @@ def test_exports_every_declared_function(L):
         assert hasattr(L, name), f"{name} declared in bitlinear.h but not exported"
 
 
-@pytest.mark.parametrize("n,m", [(8, 8), (6, 8), (4, 8), (2, 4)])
+@pytest.mark.parametrize("n,m", [(8, 8), (6, 8), (4, 8), (2, 4), (3, 8), (2, 8)])
 @pytest.mark.parametrize("n_out,k", [(128, 256), (896, 896), (40, 384), (11008, 2048), (1, 128)])
 def test_packed_bytes_matches_format_definition(L, n, m, n_out, k):
     assert bl.bitlinear_packed_bytes(n_out, k, n, m) == oracle.packed_bytes(n_out, k, oracle.s_of(n, m))
@@ -75,7 +75,7 @@ def test_pack_validation(L):
     nb = bl.bitlinear_packed_bytes(128, 256, 6, 8)
     assert L.bitlinear_pack(A, A, A, 128, 256, 6, 8, A, nb - 4, None) == bl.BL_ESHAPE
     assert L.bitlinear_pack(A, A, A, 128, 256, 6, 8, None, nb, None) == bl.BL_EINVAL
-    assert L.bitlinear_pack(A, A, A, 128, 256, 3, 8, A, nb, None) == bl.BL_EUNSUPPORTED
+    assert L.bitlinear_pack(A, A, A, 128, 256, 5, 8, A, nb, None) == bl.BL_EUNSUPPORTED
 
 
 def test_fwd_validation(L):

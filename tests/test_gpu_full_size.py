@@ -66,7 +66,7 @@ def test_qwen15_prefill_full_size(n_out, k):
     H.check_forward_sampled(lw, T, g, X, seed=n_out)
 
 
-@pytest.mark.parametrize("n,m", [(8, 8), (6, 8), (4, 8), (2, 4)])
+@pytest.mark.parametrize("n,m", [(8, 8), (6, 8), (4, 8), (2, 4), (2, 8)])
 @pytest.mark.parametrize("n_out,k", [(11008, 2048), (2048, 11008)])
 def test_qwen3b_sweep_full_size(n_out, k, n, m):
     """Qwen2.5-3B-shaped sweep: both shapes, every pattern, token counts

@@ -15,7 +15,7 @@ import _gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
-PATTERNS = [(8, 8), (6, 8), (4, 8), (2, 4)]
+PATTERNS = [(8, 8), (6, 8), (4, 8), (2, 4), (3, 8), (2, 8)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -188,7 +188,7 @@ def test_host_errors_with_device_buffers():
 
 
 @pytest.mark.parametrize("tokens", [1, 5, 16])
-@pytest.mark.parametrize("n,m", [(6, 8), (8, 8), (2, 4)])
+@pytest.mark.parametrize("n,m", [(6, 8), (8, 8), (2, 4), (2, 8)])
 def test_grouped_decode_matches_oracle(tokens, n, m):
     """One plan, several GEMVs of different shapes (including a ragged row
     tile and a partial 512-wide k super-tile), two launches."""

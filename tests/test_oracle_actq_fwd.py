@@ -81,7 +81,7 @@ def small_problem(n, m, tokens=5, k=256, n_out=48, seed=30):
     return oracle.forward_all(W, X, n, m)
 
 
-@pytest.mark.parametrize("n,m", [(8, 8), (6, 8), (4, 8), (2, 4)])
+@pytest.mark.parametrize("n,m", [(8, 8), (6, 8), (4, 8), (2, 4), (3, 8), (2, 8)])
 def test_acc_matches_integer_matmul(n, m):
     r = small_problem(n, m)
     ref = r["xq"].astype(np.int64) @ r["T"].astype(np.int64).T

@@ -90,7 +90,7 @@ def test_pairs_and_threads_agree():
 
 # ---------------------------------------------------------------- packing
 
-PAT = [(8, 8, 8), (6, 8, 6), (4, 8, 4), (2, 4, 4)]
+PAT = [(8, 8, 8), (6, 8, 6), (4, 8, 4), (2, 4, 4), (3, 8, 4), (2, 8, 2)]
 
 
 @pytest.mark.parametrize("n,m,s", PAT)

@@ -99,7 +99,7 @@ def exact_code(w, g):
     return max(-1, min(1, round(q)))  # round(Fraction) is ties-to-even
 
 
-@pytest.mark.parametrize("n,m", [(8, 8), (6, 8), (4, 8), (2, 4)])
+@pytest.mark.parametrize("n,m", [(8, 8), (6, 8), (4, 8), (2, 4), (3, 8), (2, 8)])
 def test_ternary_matches_exact_quotient_rounding(n, m):
     W = synth.weights(24, 256, seed=12)
     mb = oracle.mask(W, n, m)

@@ -9,7 +9,7 @@ import pytest
 import oracle
 from sparse_linear_layers_group_amd import synth
 
-PATTERNS = [(8, 8), (6, 8), (4, 8), (2, 4)]
+PATTERNS = [(8, 8), (6, 8), (4, 8), (2, 4), (3, 8), (2, 8)]
 
 
 def bits_of(mask_bytes, k):
