@@ -345,10 +345,11 @@ def prefill_step(torch, bl, n, m, tokens=2048, iters=10):
 
 def train_step(torch, bl, n, m, tokens=4096, iters=3):
     """BitNet-b1.58-2B4T-shaped block: all 7 BitLinears, per step mask +
-    pack (one grouped plan), forward (int8 MFMA) and dual-STE backward (bf16
-    MFMA)."""
+    pack (one grouped plan), forward (int8 MFMA), dual-STE backward (bf16
+    MFMA) and the latent-weight update (plain gradient step on binary32
+    latent weights, writing the bf16 W the next step's mask reads)."""
     from sparse_linear_layers_group_amd import synth
-    from sparse_linear_layers_group_amd.layer import BitLinearWeight, QuantGroup, bf16_tensor
+    from sparse_linear_layers_group_amd.layer import BitLinearWeight, LatentWeights, QuantGroup, bf16_tensor
     hid = 2560
     Ws, lws, fb, dys, gx, gw = [], [], [], [], [], []
     for li, (name, n_out, k) in enumerate(BITNET2B_BLOCK):
@@ -389,11 +390,19 @@ def train_step(torch, bl, n, m, tokens=4096, iters=3):
             bl.bitlinear_bwd(dys[i], a["xq"], a["x_scale"], lw.packed, lw.gamma, tokens, lw.k,
                              lw.n_out, n, m, gx[i], gw[i], ws=bws)
 
-    for f in (quant, fwd, bwd):
+    # binary32 latent weights; the update writes the bf16 W the plan reads
+    lats = [LatentWeights(W) for W in Ws]
+    assert all(lat.W.data_ptr() == W.data_ptr() for lat, W in zip(lats, Ws))
+
+    def update():
+        for i, lat in enumerate(lats):
+            lat.update(gw[i], 1e-3)
+
+    for f in (quant, fwd, bwd, update):
         f()
     torch.cuda.synchronize()
     res = {}
-    for name, f in (("mask_pack_ms", quant), ("fwd_ms", fwd), ("bwd_ms", bwd)):
+    for name, f in (("mask_pack_ms", quant), ("fwd_ms", fwd), ("bwd_ms", bwd), ("update_ms", update)):
         with Timer(torch) as t:
             for _ in range(iters):
                 f()
@@ -402,7 +411,9 @@ def train_step(torch, bl, n, m, tokens=4096, iters=3):
     res["fwd_tops_issued"] = 2 * mac / (res["fwd_ms"] * 1e-3) / 1e12
     res["bwd_tflops_issued"] = 4 * mac / (res["bwd_ms"] * 1e-3) / 1e12
     res["bwd_frac_bf16_peak"] = res["bwd_tflops_issued"] / BF16_PEAK_TFLOPS
-    res["step_ms"] = res["mask_pack_ms"] + res["fwd_ms"] + res["bwd_ms"]
+    wts = sum(n_out * k for _, n_out, k in BITNET2B_BLOCK)
+    res["update_gbs"] = wts * 14 / (res["update_ms"] * 1e-3) / 1e9  # 4+4 read, 4+2 written per weight
+    res["step_ms"] = res["mask_pack_ms"] + res["fwd_ms"] + res["bwd_ms"] + res["update_ms"]
     return {k2: round(v, 4) for k2, v in res.items()}
 
 

@@ -233,6 +233,27 @@ int bitlinear_quant_group_plan(const bitlinear_quant_item *items, int count, int
                                size_t plan_bytes, void *stream);
 int bitlinear_quant_group(const void *plan, int n, int m, int gamma_over, void *stream);
 
+/* Latent-weight update, closing a training step.  Sparse-BitNet article
+ * §三 and §六: the latent full-precision weights receive the dense gradient
+ * (both straight-through estimators pass it through the mask and the
+ * ternary rounding) and the next step recomputes mask, gamma and codes
+ * from the updated latent weights.  The pages name no optimiser; this is
+ * the plain gradient step, with the latent weights held in binary32:
+ *   W_master[i] = RN32(W_master[i] - lr * dW[i])   (one fused rounding)
+ *   W[i]        = bf16 nearest to W_master[i] (ties to even), the W the
+ *                 next bitlinear_quantize_mask / bitlinear_pack read.
+ * A dense-to-sparse schedule (the paper abstract) is the caller passing
+ * n:m = 8:8 to the weight-path calls before its switch step and the sparse
+ * pattern after it; nothing else changes.
+ *   W_master  device float [count], updated in place.
+ *   dW        device float [count] (e.g. bitlinear_bwd's dW), read.
+ *   W         device bf16 [count], written.
+ *   count     a multiple of 8 below 2^31 (n_out*k of a layer); 0 is a
+ *             no-op.  BL_ESHAPE otherwise, BL_EINVAL for a null or
+ *             misaligned pointer. */
+int bitlinear_latent_update(float *W_master, const float *dW, int64_t count, float lr,
+                            uint16_t *W, void *stream);
+
 /* Step 8-9: dual straight-through backward.  Sparse-BitNet article §三 and
  * §六: gradients pass straight through the ternary rounding and the
  * sparsification, and masked weights still receive their gradient.

@@ -50,6 +50,7 @@ def _load():
         "oracle_packed_bytes": (_i64, [_i64, _i64, _int]),
         "oracle_pack": (_int, [_vp, _i64, _i64, _int, _vp]),
         "oracle_unpack": (None, [_vp, _i64, _i64, _int, _vp]),
+        "oracle_latent_update": (None, [_vp, _vp, _i64, ctypes.c_float, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -218,3 +219,13 @@ def forward_all(W, X, n, m, over_masked=False, threads=1):
     xq, sc = act_quant(X)
     acc, Y = fwd(xq, sc, T, g, threads=threads)
     return {"mask": mb, "gamma": g, "T": T, "xq": xq, "scale": sc, "acc": acc, "Y": Y}
+
+
+def latent_update(w_master, dw, lr):
+    """Plain gradient step on binary32 latent weights -> (new binary32
+    weights, their bf16 bit patterns); the inputs are not modified."""
+    wm = np.array(w_master, dtype=np.float32, copy=True).reshape(-1)
+    g = _c(np.asarray(dw, dtype=np.float32).reshape(-1), np.float32)
+    out = np.zeros(wm.size, dtype=np.uint16)
+    _load().oracle_latent_update(_p(wm), _p(g), wm.size, float(np.float32(lr)), _p(out))
+    return wm, out

@@ -534,3 +534,39 @@ void oracle_unpack(const uint8_t *packed, int64_t n_out, int64_t k, int s, int8_
             }
         }
 }
+
+/* ------------------------------------------------------------------ */
+/* Latent-weight update ([SB] 三, 六: the latent full-precision weights */
+/* take the dense gradient that both straight-through estimators pass; */
+/* the next step re-derives mask, gamma and codes from them).  The     */
+/* pages name no optimiser; the reading taken is the plain gradient    */
+/* step, with the latent weights held in binary32:                     */
+/*   w' = the binary32 nearest to the exact w - lr*g (ties to even),   */
+/*        which is what C's fmaf returns (one rounding);               */
+/*   W  = the bf16 nearest to w' (ties to even), found by comparing    */
+/*        the two bf16 neighbours of w' in exact binary64.             */
+/* ------------------------------------------------------------------ */
+static uint16_t nearest_bf16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    uint32_t lo = u & 0xffff0000u;          /* same sign, magnitude rounded down */
+    uint32_t hi = lo + 0x00010000u;         /* next magnitude up                  */
+    float flo, fhi;
+    memcpy(&flo, &lo, 4);
+    memcpy(&fhi, &hi, 4);
+    double dlo = fabs((double)x - (double)flo);
+    double dhi = fabs((double)fhi - (double)x);
+    if (dlo < dhi) return (uint16_t)(lo >> 16);
+    if (dhi < dlo) return (uint16_t)(hi >> 16);
+    return (uint16_t)((((lo >> 16) & 1u) == 0) ? (lo >> 16) : (hi >> 16));
+}
+
+void oracle_latent_update(float *w_master, const float *dw, int64_t count, float lr,
+                          uint16_t *w)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        w_master[i] = fmaf(-lr, dw[i], w_master[i]);
+        w[i] = nearest_bf16(w_master[i]);
+    }
+}

@@ -48,6 +48,7 @@ _SIGS = {
     "bitlinear_quant_group_plan_bytes": (_sz, [_vp, _int]),
     "bitlinear_quant_group_plan": (_int, [_vp, _int, _int, _int, _int, _vp, _sz, _vp, _sz, _vp]),
     "bitlinear_quant_group": (_int, [_vp, _int, _int, _int, _vp]),
+    "bitlinear_latent_update": (_int, [_vp, _vp, _i64, ctypes.c_float, _vp, _vp]),
     "bitlinear_status_string": (ctypes.c_char_p, [_int]),
     "bitlinear_last_error": (ctypes.c_char_p, []),
 }
@@ -183,6 +184,13 @@ def bitlinear_bwd(dY, xq, x_scale, packed, gamma, tokens, k, n_out, n, m, dX, dW
         (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes),
         _stream(stream))
     _check(st, "bitlinear_bwd")
+
+
+def bitlinear_latent_update(W_master, dW, count, lr, W, stream=None):
+    st = lib().bitlinear_latent_update(
+        _ptr(W_master, (torch.float32,), count, "W_master"), _ptr(dW, (torch.float32,), count, "dW"),
+        int(count), float(lr), _ptr(W, _BF16, count, "W"), _stream(stream))
+    _check(st, "bitlinear_latent_update")
 
 
 def bitlinear_act_quant(X, tokens, k, xq, x_scale, stream=None):

@@ -265,6 +265,18 @@ int bitlinear_act_quant(const uint16_t* X, int64_t tokens, int64_t k, int8_t* xq
   return hip_status(e, "activation quant launch");
 }
 
+int bitlinear_latent_update(float* W_master, const float* dW, int64_t count, float lr, uint16_t* W,
+                            void* stream) {
+  if (count < 0 || count >= kLimit || count % 8 != 0)
+    return fail(BL_ESHAPE, "count must be a multiple of 8 in [0, 2^31) (got %lld)", (long long)count);
+  if (count == 0) return ok();
+  TRY(check_ptr(W_master, 16, "W_master"));
+  TRY(check_ptr(dW, 16, "dW"));
+  TRY(check_ptr(W, 16, "W"));
+  hipError_t e = bl::launch_latent_update(W_master, dW, count, lr, W, reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "latent update launch");
+}
+
 int bitlinear_contract(const int8_t* xq, const float* x_scale, int64_t tokens, int64_t k,
                        const void* packed, int64_t n_out, int n, int m, const double* gamma,
                        float* Y, int32_t* acc, void* ws, size_t ws_bytes, void* stream) {

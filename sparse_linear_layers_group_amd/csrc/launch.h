@@ -81,6 +81,11 @@ hipError_t launch_ternary_pack(const uint16_t* W, const uint8_t* mask, const dou
                                hipStream_t s);
 
 // per-token int8 activations; also zero-fills zero_bytes of zero_ws
+// latent-weight update: Wm = RN32(Wm - lr * dW) (one fused rounding), W =
+// bf16 (nearest, ties to even) of the result; count a multiple of 8
+hipError_t launch_latent_update(float* Wm, const float* dW, int64_t count, float lr, uint16_t* W,
+                                hipStream_t s);
+
 hipError_t launch_act_quant(const uint16_t* X, int64_t tokens, int64_t k, int8_t* xq,
                             float* scale, void* zero_ws, int64_t zero_bytes, hipStream_t s);
 

@@ -774,6 +774,53 @@ __global__ __launch_bounds__(256) void act_quant_group_kernel(const char* __rest
   if (warm) asm volatile("" : : "v"(ws.x));  // keeps the read
 }
 
+// ---------------------------------------------------------------------
+// Latent-weight update.  The latent weights are kept in binary32 (the
+// bf16 W the mask and codes read is derived from them): per element
+// Wm = RN32(Wm - lr * dW) with one fused multiply-add, then W = the bf16
+// nearest to Wm (ties to even).  Eight elements per thread and trip.
+// ---------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
+__global__ __launch_bounds__(256) void latent_update_kernel(float* __restrict__ Wm,
+                                                           const float* __restrict__ dW,
+                                                           int64_t n8, float lr,
+                                                           uint16_t* __restrict__ W) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const f32x4 w0 = ld_global(reinterpret_cast<const f32x4*>(Wm) + 2 * i);
+    const f32x4 w1 = ld_global(reinterpret_cast<const f32x4*>(Wm) + 2 * i + 1);
+    const f32x4 g0 = ld_global(reinterpret_cast<const f32x4*>(dW) + 2 * i);
+    const f32x4 g1 = ld_global(reinterpret_cast<const f32x4*>(dW) + 2 * i + 1);
+    f32x4 r0, r1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r0[e] = __builtin_fmaf(-lr, g0[e], w0[e]);
+      r1[e] = __builtin_fmaf(-lr, g1[e], w1[e]);
+    }
+    st_global(reinterpret_cast<f32x4*>(Wm) + 2 * i, r0);
+    st_global(reinterpret_cast<f32x4*>(Wm) + 2 * i + 1, r1);
+    u32x4 h;
+    h[0] = bf16_rne(r0[0]) | (bf16_rne(r0[1]) << 16);
+    h[1] = bf16_rne(r0[2]) | (bf16_rne(r0[3]) << 16);
+    h[2] = bf16_rne(r1[0]) | (bf16_rne(r1[1]) << 16);
+    h[3] = bf16_rne(r1[2]) | (bf16_rne(r1[3]) << 16);
+    st_global(reinterpret_cast<u32x4*>(W) + i, h);
+  }
+}
+
+hipError_t launch_latent_update(float* Wm, const float* dW, int64_t count, float lr, uint16_t* W,
+                                hipStream_t s) {
+  const int64_t n8 = count / 8;
+  const int64_t blocks = (n8 + 255) / 256;
+  latent_update_kernel<<<(unsigned)(blocks < 2048 ? blocks : 2048), 256, 0, s>>>(Wm, dW, n8, lr, W);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------- launchers
 template <int N, int M>
 static hipError_t launch_mask(const uint16_t* W, int64_t n_out, int64_t k, int gamma_over,

@@ -103,3 +103,21 @@ class QuantGroup:
 
     def run(self, stream=None):
         bl.bitlinear_quant_group(self.plan, self.n, self.m, self.gamma_over, stream=stream)
+
+
+class LatentWeights:
+    """binary32 latent weights of one layer and the bf16 copy the weight
+    path reads; `update` applies one plain gradient step on the device."""
+
+    def __init__(self, W_bf16, device="cuda"):
+        self.W = W_bf16.contiguous().to(device)
+        self.master = self.W.float().contiguous()
+
+    def update(self, dW, lr, stream=None):
+        bl.bitlinear_latent_update(self.master, dW, self.master.numel(), lr, self.W, stream=stream)
+
+
+def dense_to_sparse(step, switch_step, n, m):
+    """N:M pattern of a dense-to-sparse schedule: dense (8:8) before
+    switch_step, n:m from it on."""
+    return (8, 8) if step < switch_step else (n, m)

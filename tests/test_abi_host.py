@@ -173,3 +173,13 @@ def test_quant_group_validation(L):
     assert g(A, 6, 8, 3, None) == bl.BL_EINVAL
     assert g(None, 6, 8, 0, None) == bl.BL_EINVAL
     assert g(A, 7, 8, 0, None) == bl.BL_EUNSUPPORTED
+
+
+def test_latent_update_validation(L):
+    f = L.bitlinear_latent_update
+    assert f(A, A, 12, 0.1, A, None) == bl.BL_ESHAPE   # not a multiple of 8
+    assert f(A, A, -8, 0.1, A, None) == bl.BL_ESHAPE
+    assert f(None, A, 16, 0.1, A, None) == bl.BL_EINVAL
+    assert f(A, A + 4, 16, 0.1, A, None) == bl.BL_EINVAL
+    assert f(A, A, 16, 0.1, None, None) == bl.BL_EINVAL
+    assert f(None, None, 0, 0.1, None, None) == bl.BL_OK  # no-op

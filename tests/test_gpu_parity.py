@@ -9,7 +9,8 @@ import torch
 import oracle
 from sparse_linear_layers_group_amd import bitlinear as bl
 from sparse_linear_layers_group_amd import synth
-from sparse_linear_layers_group_amd.layer import BitLinearWeight, QuantGroup, bf16_tensor
+from sparse_linear_layers_group_amd.layer import (BitLinearWeight, LatentWeights, QuantGroup, bf16_bits,
+                                                   bf16_tensor, dense_to_sparse)
 
 import _gpu_helpers as H
 
@@ -402,3 +403,52 @@ def test_act_quant_near_half_way_quotients(rows, k):
     got = xq.cpu().numpy().reshape(rows, k)
     assert np.array_equal(got, xq_ref), f"x_q differs at {np.argwhere(got != xq_ref)[:5]}"
     assert np.array_equal(sc.cpu().numpy(), sc_ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("count", [8, 3 * 2048 + 8, 256 * 4864])
+def test_latent_update_matches_oracle(count):
+    """binary32 latent weights after one gradient step and their bf16 copy:
+    bit-exact against the oracle, with half-way cases planted up front."""
+    rng = np.random.default_rng(count)
+    w = (rng.standard_normal(count) * 0.02).astype(np.float32)
+    g = (rng.standard_normal(count) * 1e-2).astype(np.float32)
+    lr = np.float32(0.25)
+    if count >= 8:  # w - lr*g exactly half-way between two binary32 / bf16 values
+        w[:4] = [1.0 + 2.0 ** -23, 1.0 + 2.0 ** -22, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8]
+        g[:4] = [2.0 ** -22, 2.0 ** -22, 0.0, 0.0]
+    ref_w, ref_b = oracle.latent_update(w, g, lr)
+    Wm = torch.from_numpy(w.copy()).cuda()
+    Wb = torch.empty(count, dtype=torch.bfloat16, device="cuda")
+    bl.bitlinear_latent_update(Wm, torch.from_numpy(g).cuda(), count, float(lr), Wb)
+    torch.cuda.synchronize()
+    assert np.array_equal(Wm.cpu().numpy().view(np.uint32), ref_w.view(np.uint32))
+    assert np.array_equal(Wb.view(torch.int16).cpu().numpy().view(np.uint16), ref_b)
+
+
+def test_dense_to_sparse_training_steps():
+    """Four training steps of one layer, dense (8:8) for two then 6:8: each
+    step's mask, gamma and packed bytes from the current latent weights,
+    the forward, and the latent update (with this step's dW) match the
+    oracle on the same inputs; dW within the bf16-product tolerance."""
+    n_out, k, tokens, lr = 64, 256, 32, 0.5
+    lat = LatentWeights(bf16_tensor(synth.weights(n_out, k, seed=50)))
+    for step in range(4):
+        n, m = dense_to_sparse(step, 2, 6, 8)
+        Wbits = bf16_bits(lat.W).reshape(n_out, k)
+        lw, T, g = H.check_weight_path(Wbits, n, m)
+        X = synth.activations(tokens, k, seed=60 + step)
+        bufs, xq, sc = H.check_forward(lw, T, g, X)
+        dY = synth.grad_output(tokens, n_out, seed=70 + step)
+        _, dW = lw.bwd(bf16_tensor(dY), bufs["xq"], bufs["x_scale"], tokens, dX=False)
+        torch.cuda.synchronize()
+        dW_ref = oracle.bwd_dw_pairs(dY, xq, sc, np.repeat(np.arange(n_out), k), np.tile(np.arange(k), n_out))
+        got = dW.cpu().numpy().astype(np.float64)
+        bound = oracle.bwd_dw_pairs((dY & np.uint16(0x7FFF)).astype(np.uint16), np.abs(xq), sc,
+                                    np.repeat(np.arange(n_out), k), np.tile(np.arange(k), n_out))
+        assert np.all(np.abs(got - dW_ref) <= 1e-2 * bound + 1e-30)
+        master_before = lat.master.cpu().numpy()
+        ref_w, ref_b = oracle.latent_update(master_before, dW.cpu().numpy(), lr)
+        lat.update(dW, lr)
+        torch.cuda.synchronize()
+        assert np.array_equal(lat.master.cpu().numpy().reshape(-1).view(np.uint32), ref_w.view(np.uint32)), step
+        assert np.array_equal(bf16_bits(lat.W).reshape(-1), ref_b), step
