@@ -347,7 +347,10 @@ def train_step(torch, bl, n, m, tokens=4096, iters=3):
     """BitNet-b1.58-2B4T-shaped block: all 7 BitLinears, per step mask +
     pack (one grouped plan), forward (int8 MFMA), dual-STE backward (bf16
     MFMA) and the latent-weight update (plain gradient step on binary32
-    latent weights, writing the bf16 W the next step's mask reads)."""
+    latent weights, writing the bf16 W the next step's mask reads).  The
+    feed-forward is chained: squared-ReLU gating of the gate/up outputs
+    forms the down projection's int8 input, and its backward turns the down
+    projection's dX into the gate/up dY."""
     from sparse_linear_layers_group_amd import synth
     from sparse_linear_layers_group_amd.layer import BitLinearWeight, LatentWeights, QuantGroup, bf16_tensor
     hid = 2560
@@ -359,36 +362,46 @@ def train_step(torch, bl, n, m, tokens=4096, iters=3):
         dys.append(bf16_tensor(synth.grad_output(tokens, n_out, seed=0, config=5, layer=li)))
         gx.append(torch.empty(tokens * k, dtype=torch.float32, device="cuda"))
         gw.append(torch.empty(n_out * k, dtype=torch.float32, device="cuda"))
-    # q/k/v and gate/up read the same block input (attention, norms and the
-    # squared-ReLU gating are out of scope, so o and down get their own
-    # synthetic inputs); its activations are quantised once
+    # q/k/v and gate/up read the same block input, quantised once;
+    # attention and norms are out of scope, so o gets its own synthetic
+    # input; down reads the gating of gate and up
     X = bf16_tensor(synth.activations(tokens, hid, seed=0, config=5, layer=0))
     Xo = bf16_tensor(synth.activations(tokens, hid, seed=0, config=5, layer=3))
-    Xd = bf16_tensor(synth.activations(tokens, 6912, seed=0, config=5, layer=6))
     src = [0, 0, 0, 3, 0, 0, 6]  # which layer's x_q buffer each layer reads
+    ffn = 6912
 
     qg = QuantGroup(list(zip(lws, Ws)))  # plan built once; each step: three launches
 
     def quant():
         qg.run()
 
+    def contract(i):
+        lw, a = lws[i], fb[src[i]]
+        bl.bitlinear_contract(a["xq"], a["x_scale"], tokens, lw.k, lw.packed, lw.n_out, n, m,
+                              lw.gamma, fb[i]["Y"], ws=fb[i]["ws"])
+
     def fwd():
-        for i, x in ((0, X), (3, Xo), (6, Xd)):
+        for i, x in ((0, X), (3, Xo)):
             bl.bitlinear_act_quant(x, tokens, lws[i].k, fb[i]["xq"], fb[i]["x_scale"])
-        for i, lw in enumerate(lws):
-            a = fb[src[i]]
-            bl.bitlinear_contract(a["xq"], a["x_scale"], tokens, lw.k, lw.packed, lw.n_out, n, m,
-                                  lw.gamma, fb[i]["Y"], ws=fb[i]["ws"])
+        for i in range(6):
+            contract(i)
+        bl.bitlinear_relu2_gate(fb[4]["Y"], fb[5]["Y"], tokens, ffn, None, fb[6]["xq"], fb[6]["x_scale"])
+        contract(6)
 
     # one backward workspace, sized for the largest layer (calls run in order on one stream)
     bws = torch.empty(max(bl.bitlinear_bwd_workspace_bytes(tokens, lw.k, lw.n_out) for lw in lws),
                       dtype=torch.uint8, device="cuda")
 
+    def bwd_layer(i):
+        lw, a = lws[i], fb[src[i]]
+        bl.bitlinear_bwd(dys[i], a["xq"], a["x_scale"], lw.packed, lw.gamma, tokens, lw.k,
+                         lw.n_out, n, m, gx[i], gw[i], ws=bws)
+
     def bwd():
-        for i, lw in enumerate(lws):
-            a = fb[src[i]]
-            bl.bitlinear_bwd(dys[i], a["xq"], a["x_scale"], lw.packed, lw.gamma, tokens, lw.k,
-                             lw.n_out, n, m, gx[i], gw[i], ws=bws)
+        bwd_layer(6)  # down (synthetic dY), then the gating backward: dY of gate and up
+        bl.bitlinear_relu2_gate_bwd(gx[6], fb[4]["Y"], fb[5]["Y"], tokens * ffn, dys[4], dys[5])
+        for i in (4, 5, 3, 0, 1, 2):
+            bwd_layer(i)
 
     # binary32 latent weights; the update writes the bf16 W the plan reads
     lats = [LatentWeights(W) for W in Ws]

@@ -233,6 +233,30 @@ int bitlinear_quant_group_plan(const bitlinear_quant_item *items, int count, int
                                size_t plan_bytes, void *stream);
 int bitlinear_quant_group(const void *plan, int n, int m, int gamma_over, void *stream);
 
+/* Squared-ReLU gating of a block's feed-forward, fused with the down
+ * projection's activation quantisation.  BitNet b1.58 2B4T article §一
+ * (squared ReLU in place of SwiGLU; 8-bit activations into every
+ * BitLinear).  With G and U the fp32 outputs of the gate and up
+ * BitLinears ([tokens x n], row-major), per element, in binary32:
+ *   r = max(g, 0),  h = bf16 nearest to RN32(RN32(r * r) * u) (ties even)
+ * and then, per token, x_q and x_scale of h exactly as bitlinear_act_quant
+ * forms them from a bf16 tensor (so they are the down BitLinear's inputs).
+ *   H        device bf16 [tokens x n], written, or NULL.
+ *   xq       device int8 [tokens x n]; x_scale device float [tokens].
+ * n a positive multiple of 128, tokens*n below 2^31; tokens == 0 is a
+ * no-op. */
+int bitlinear_relu2_gate(const float *G, const float *U, int64_t tokens, int64_t n,
+                         uint16_t *H, int8_t *xq, float *x_scale, void *stream);
+
+/* Its backward (the derivative of h = relu(g)^2 u, with relu'(0) = 0),
+ * given dH = dL/dh (fp32, e.g. the down BitLinear's dX), per element, in
+ * binary32 with each product rounded:
+ *   dU = bf16(RN32(dh * RN32(r * r))),  dG = bf16(RN32(RN32(dh * u) * 2r))
+ * (bf16 nearest, ties to even): the dY inputs of the gate and up
+ * BitLinears' bitlinear_bwd.  count a multiple of 8 below 2^31. */
+int bitlinear_relu2_gate_bwd(const float *dH, const float *G, const float *U, int64_t count,
+                             uint16_t *dG, uint16_t *dU, void *stream);
+
 /* Latent-weight update, closing a training step.  Sparse-BitNet article
  * §三 and §六: the latent full-precision weights receive the dense gradient
  * (both straight-through estimators pass it through the mask and the

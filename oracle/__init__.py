@@ -51,6 +51,8 @@ def _load():
         "oracle_pack": (_int, [_vp, _i64, _i64, _int, _vp]),
         "oracle_unpack": (None, [_vp, _i64, _i64, _int, _vp]),
         "oracle_latent_update": (None, [_vp, _vp, _i64, ctypes.c_float, _vp]),
+        "oracle_relu2_gate": (None, [_vp, _vp, _i64, _vp]),
+        "oracle_relu2_gate_bwd": (None, [_vp, _vp, _vp, _i64, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -229,3 +231,23 @@ def latent_update(w_master, dw, lr):
     out = np.zeros(wm.size, dtype=np.uint16)
     _load().oracle_latent_update(_p(wm), _p(g), wm.size, float(np.float32(lr)), _p(out))
     return wm, out
+
+
+def relu2_gate(G, U):
+    """Squared-ReLU gating -> bf16 bit patterns of h (same shape as G)."""
+    g = _c(G, np.float32)
+    u = _c(U, np.float32)
+    h = np.zeros(g.shape, dtype=np.uint16)
+    _load().oracle_relu2_gate(_p(g), _p(u), g.size, _p(h))
+    return h
+
+
+def relu2_gate_bwd(dH, G, U):
+    """Its backward -> (dG, dU) as bf16 bit patterns."""
+    d = _c(dH, np.float32)
+    g = _c(G, np.float32)
+    u = _c(U, np.float32)
+    dg = np.zeros(g.shape, dtype=np.uint16)
+    du = np.zeros(g.shape, dtype=np.uint16)
+    _load().oracle_relu2_gate_bwd(_p(d), _p(g), _p(u), g.size, _p(dg), _p(du))
+    return dg, du

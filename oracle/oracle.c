@@ -570,3 +570,38 @@ void oracle_latent_update(float *w_master, const float *dw, int64_t count, float
         w[i] = nearest_bf16(w_master[i]);
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* Squared-ReLU gating of the feed-forward ([2B4T] 一: squared ReLU in  */
+/* place of SwiGLU).  The reading taken: gated like the SwiGLU it      */
+/* replaces, h = relu(g)^2 * u, with g and u the gate and up           */
+/* BitLinears' fp32 outputs; each product rounded to binary32 in the   */
+/* order written, then h rounded to bf16 (the down BitLinear's input,  */
+/* quantised per token like any bf16 activation).  The backward is the */
+/* derivative of that product (relu'(0) = 0), each product rounded to  */
+/* binary32, the results rounded to bf16 (the gate and up BitLinears'  */
+/* dY).                                                                */
+/* ------------------------------------------------------------------ */
+void oracle_relu2_gate(const float *G, const float *U, int64_t count, uint16_t *H)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        float r = G[i] > 0.0f ? G[i] : 0.0f;
+        float r2 = r * r;
+        float h = r2 * U[i];
+        H[i] = nearest_bf16(h);
+    }
+}
+
+void oracle_relu2_gate_bwd(const float *dH, const float *G, const float *U, int64_t count,
+                           uint16_t *dG, uint16_t *dU)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        float r = G[i] > 0.0f ? G[i] : 0.0f;
+        float r2 = r * r;
+        float du = dH[i] * r2;            /* dL/du = dh * r^2          */
+        float dhu = dH[i] * U[i];
+        float dg = dhu * (2.0f * r);      /* dL/dg = dh * u * 2r       */
+        dU[i] = nearest_bf16(du);
+        dG[i] = nearest_bf16(dg);
+    }
+}

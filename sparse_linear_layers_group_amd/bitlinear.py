@@ -49,6 +49,8 @@ _SIGS = {
     "bitlinear_quant_group_plan": (_int, [_vp, _int, _int, _int, _int, _vp, _sz, _vp, _sz, _vp]),
     "bitlinear_quant_group": (_int, [_vp, _int, _int, _int, _vp]),
     "bitlinear_latent_update": (_int, [_vp, _vp, _i64, ctypes.c_float, _vp, _vp]),
+    "bitlinear_relu2_gate": (_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "bitlinear_relu2_gate_bwd": (_int, [_vp, _vp, _vp, _i64, _vp, _vp, _vp]),
     "bitlinear_status_string": (ctypes.c_char_p, [_int]),
     "bitlinear_last_error": (ctypes.c_char_p, []),
 }
@@ -191,6 +193,22 @@ def bitlinear_latent_update(W_master, dW, count, lr, W, stream=None):
         _ptr(W_master, (torch.float32,), count, "W_master"), _ptr(dW, (torch.float32,), count, "dW"),
         int(count), float(lr), _ptr(W, _BF16, count, "W"), _stream(stream))
     _check(st, "bitlinear_latent_update")
+
+
+def bitlinear_relu2_gate(G, U, tokens, n, H, xq, x_scale, stream=None):
+    st = lib().bitlinear_relu2_gate(
+        _ptr(G, (torch.float32,), tokens * n, "G"), _ptr(U, (torch.float32,), tokens * n, "U"), tokens, n,
+        _ptr(H, _BF16, tokens * n, "H", optional=True), _ptr(xq, (torch.int8,), tokens * n, "xq"),
+        _ptr(x_scale, (torch.float32,), tokens, "x_scale"), _stream(stream))
+    _check(st, "bitlinear_relu2_gate")
+
+
+def bitlinear_relu2_gate_bwd(dH, G, U, count, dG, dU, stream=None):
+    st = lib().bitlinear_relu2_gate_bwd(
+        _ptr(dH, (torch.float32,), count, "dH"), _ptr(G, (torch.float32,), count, "G"),
+        _ptr(U, (torch.float32,), count, "U"), int(count), _ptr(dG, _BF16, count, "dG"),
+        _ptr(dU, _BF16, count, "dU"), _stream(stream))
+    _check(st, "bitlinear_relu2_gate_bwd")
 
 
 def bitlinear_act_quant(X, tokens, k, xq, x_scale, stream=None):

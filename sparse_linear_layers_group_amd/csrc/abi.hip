@@ -265,6 +265,36 @@ int bitlinear_act_quant(const uint16_t* X, int64_t tokens, int64_t k, int8_t* xq
   return hip_status(e, "activation quant launch");
 }
 
+int bitlinear_relu2_gate(const float* G, const float* U, int64_t tokens, int64_t n, uint16_t* H,
+                         int8_t* xq, float* x_scale, void* stream) {
+  if (n < 128 || n % 128 != 0)
+    return fail(BL_ESHAPE, "n must be a positive multiple of 128 (got %lld)", (long long)n);
+  if (tokens < 0 || tokens >= kLimit || tokens * n >= kLimit)
+    return fail(BL_ESHAPE, "tokens must be >= 0 with tokens*n below 2^31");
+  if (tokens == 0) return ok();
+  TRY(check_ptr(G, 16, "G"));
+  TRY(check_ptr(U, 16, "U"));
+  if (H) TRY(check_ptr(H, 16, "H"));
+  TRY(check_ptr(xq, 16, "xq"));
+  TRY(check_ptr(x_scale, 4, "x_scale"));
+  hipError_t e = bl::launch_relu2_gate(G, U, tokens, n, H, xq, x_scale, reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "gating launch");
+}
+
+int bitlinear_relu2_gate_bwd(const float* dH, const float* G, const float* U, int64_t count,
+                             uint16_t* dG, uint16_t* dU, void* stream) {
+  if (count < 0 || count >= kLimit || count % 8 != 0)
+    return fail(BL_ESHAPE, "count must be a multiple of 8 in [0, 2^31) (got %lld)", (long long)count);
+  if (count == 0) return ok();
+  TRY(check_ptr(dH, 16, "dH"));
+  TRY(check_ptr(G, 16, "G"));
+  TRY(check_ptr(U, 16, "U"));
+  TRY(check_ptr(dG, 16, "dG"));
+  TRY(check_ptr(dU, 16, "dU"));
+  hipError_t e = bl::launch_relu2_gate_bwd(dH, G, U, count, dG, dU, reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "gating backward launch");
+}
+
 int bitlinear_latent_update(float* W_master, const float* dW, int64_t count, float lr, uint16_t* W,
                             void* stream) {
   if (count < 0 || count >= kLimit || count % 8 != 0)

@@ -86,6 +86,15 @@ hipError_t launch_ternary_pack(const uint16_t* W, const uint8_t* mask, const dou
 hipError_t launch_latent_update(float* Wm, const float* dW, int64_t count, float lr, uint16_t* W,
                                 hipStream_t s);
 
+// squared-ReLU gating of a block's feed-forward: h = bf16((relu(g)^2) * u)
+// (binary32 products), written to H (may be null), then per-token int8
+// activations of h exactly as launch_act_quant forms them; and its
+// backward, dU = bf16(dh * r^2), dG = bf16((dh * u) * 2r), r = relu(g)
+hipError_t launch_relu2_gate(const float* G, const float* U, int64_t tokens, int64_t n, uint16_t* H,
+                             int8_t* xq, float* scale, hipStream_t s);
+hipError_t launch_relu2_gate_bwd(const float* dH, const float* G, const float* U, int64_t count,
+                                 uint16_t* dG, uint16_t* dU, hipStream_t s);
+
 hipError_t launch_act_quant(const uint16_t* X, int64_t tokens, int64_t k, int8_t* xq,
                             float* scale, void* zero_ws, int64_t zero_bytes, hipStream_t s);
 

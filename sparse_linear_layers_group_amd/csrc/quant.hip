@@ -813,6 +813,117 @@ __global__ __launch_bounds__(256) void latent_update_kernel(float* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------------
+// Squared-ReLU gating (BitNet b1.58 2B4T article §一: squared ReLU in
+// place of SwiGLU), fused with the down projection's activation
+// quantisation.  One block per token; the bf16 values of h are held in
+// registers (rows up to 256 * 8 * kGateHeld) between the absmax and the
+// quantisation, longer rows recompute them from G and U.
+// ---------------------------------------------------------------------
+__device__ __forceinline__ uint32_t gate_h(float g, float u) {
+  const float r = g > 0.f ? g : 0.f;
+  const float r2 = r * r;
+  return bf16_rne(r2 * u);
+}
+
+__device__ __forceinline__ uint4 gate_h8(const float* G, const float* U, int64_t v) {
+  const f32x4 g0 = ld_global(reinterpret_cast<const f32x4*>(G) + 2 * v);
+  const f32x4 g1 = ld_global(reinterpret_cast<const f32x4*>(G) + 2 * v + 1);
+  const f32x4 u0 = ld_global(reinterpret_cast<const f32x4*>(U) + 2 * v);
+  const f32x4 u1 = ld_global(reinterpret_cast<const f32x4*>(U) + 2 * v + 1);
+  uint4 h;
+  h.x = gate_h(g0[0], u0[0]) | (gate_h(g0[1], u0[1]) << 16);
+  h.y = gate_h(g0[2], u0[2]) | (gate_h(g0[3], u0[3]) << 16);
+  h.z = gate_h(g1[0], u1[0]) | (gate_h(g1[1], u1[1]) << 16);
+  h.w = gate_h(g1[2], u1[2]) | (gate_h(g1[3], u1[3]) << 16);
+  return h;
+}
+
+constexpr int kGateHeld = 4;
+__global__ __launch_bounds__(256) void relu2_gate_kernel(const float* __restrict__ G,
+                                                        const float* __restrict__ U, int64_t n,
+                                                        uint16_t* __restrict__ H,
+                                                        int8_t* __restrict__ xq,
+                                                        float* __restrict__ scale) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const float* g = G + t * n;
+  const float* u = U + t * n;
+  const int64_t nvec = n / 8;
+  uint4 held[kGateHeld];
+  float a = 0.f;
+#pragma unroll
+  for (int h = 0; h < kGateHeld; ++h) {
+    const int64_t i = threadIdx.x + 256 * h;
+    held[h] = i < nvec ? gate_h8(g, u, i) : make_uint4(0, 0, 0, 0);
+    if (i < nvec && H)
+      st_global(reinterpret_cast<u32x4*>(H + t * n) + i, u32x4{held[h].x, held[h].y, held[h].z, held[h].w});
+    a = fmaxf(a, absmax8(held[h]));
+  }
+  for (int64_t i = threadIdx.x + 256 * kGateHeld; i < nvec; i += 256) {
+    const uint4 hv = gate_h8(g, u, i);
+    if (H) st_global(reinterpret_cast<u32x4*>(H + t * n) + i, u32x4{hv.x, hv.y, hv.z, hv.w});
+    a = fmaxf(a, absmax8(hv));
+  }
+  a = wave_max(a);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (threadIdx.x == 0) scale[t] = a / 127.0f;
+  uint2* out = reinterpret_cast<uint2*>(xq + t * n);
+#pragma unroll
+  for (int h = 0; h < kGateHeld; ++h) {
+    const int64_t i = threadIdx.x + 256 * h;
+    if (i < nvec) out[i] = quant8(held[h], a);
+  }
+  for (int64_t i = threadIdx.x + 256 * kGateHeld; i < nvec; i += 256) out[i] = quant8(gate_h8(g, u, i), a);
+}
+
+__global__ __launch_bounds__(256) void relu2_gate_bwd_kernel(const float* __restrict__ dH,
+                                                            const float* __restrict__ G,
+                                                            const float* __restrict__ U, int64_t n8,
+                                                            uint16_t* __restrict__ dG,
+                                                            uint16_t* __restrict__ dU) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    uint32_t og[4], ou[4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const f32x4 d = ld_global(reinterpret_cast<const f32x4*>(dH) + 2 * i + q);
+      const f32x4 g = ld_global(reinterpret_cast<const f32x4*>(G) + 2 * i + q);
+      const f32x4 u = ld_global(reinterpret_cast<const f32x4*>(U) + 2 * i + q);
+      uint32_t bg[4], bu[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float r = g[e] > 0.f ? g[e] : 0.f;
+        const float r2 = r * r;
+        bu[e] = bf16_rne(d[e] * r2);
+        const float du = d[e] * u[e];
+        bg[e] = bf16_rne(du * (2.f * r));
+      }
+      og[2 * q] = bg[0] | (bg[1] << 16);
+      og[2 * q + 1] = bg[2] | (bg[3] << 16);
+      ou[2 * q] = bu[0] | (bu[1] << 16);
+      ou[2 * q + 1] = bu[2] | (bu[3] << 16);
+    }
+    st_global(reinterpret_cast<u32x4*>(dG) + i, u32x4{og[0], og[1], og[2], og[3]});
+    st_global(reinterpret_cast<u32x4*>(dU) + i, u32x4{ou[0], ou[1], ou[2], ou[3]});
+  }
+}
+
+hipError_t launch_relu2_gate(const float* G, const float* U, int64_t tokens, int64_t n, uint16_t* H,
+                             int8_t* xq, float* scale, hipStream_t s) {
+  relu2_gate_kernel<<<(unsigned)tokens, 256, 0, s>>>(G, U, n, H, xq, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_relu2_gate_bwd(const float* dH, const float* G, const float* U, int64_t count,
+                                 uint16_t* dG, uint16_t* dU, hipStream_t s) {
+  const int64_t n8 = count / 8;
+  const int64_t blocks = (n8 + 255) / 256;
+  relu2_gate_bwd_kernel<<<(unsigned)(blocks < 2048 ? blocks : 2048), 256, 0, s>>>(dH, G, U, n8, dG, dU);
+  return hipGetLastError();
+}
+
 hipError_t launch_latent_update(float* Wm, const float* dW, int64_t count, float lr, uint16_t* W,
                                 hipStream_t s) {
   const int64_t n8 = count / 8;

@@ -183,3 +183,17 @@ def test_latent_update_validation(L):
     assert f(A, A + 4, 16, 0.1, A, None) == bl.BL_EINVAL
     assert f(A, A, 16, 0.1, None, None) == bl.BL_EINVAL
     assert f(None, None, 0, 0.1, None, None) == bl.BL_OK  # no-op
+
+
+def test_relu2_gate_validation(L):
+    f = L.bitlinear_relu2_gate
+    assert f(A, A, 4, 100, None, A, A, None) == bl.BL_ESHAPE   # n % 128
+    assert f(A, A, -1, 256, None, A, A, None) == bl.BL_ESHAPE
+    assert f(None, A, 4, 256, None, A, A, None) == bl.BL_EINVAL
+    assert f(A, A, 4, 256, A + 2, A, A, None) == bl.BL_EINVAL  # misaligned H
+    assert f(A, A, 4, 256, None, A, A + 2, None) == bl.BL_EINVAL
+    assert f(None, None, 0, 256, None, None, None, None) == bl.BL_OK
+    b = L.bitlinear_relu2_gate_bwd
+    assert b(A, A, A, 12, A, A, None) == bl.BL_ESHAPE
+    assert b(A, A, A, 16, None, A, None) == bl.BL_EINVAL
+    assert b(None, None, None, 0, None, None, None) == bl.BL_OK

@@ -452,3 +452,46 @@ def test_dense_to_sparse_training_steps():
         torch.cuda.synchronize()
         assert np.array_equal(lat.master.cpu().numpy().reshape(-1).view(np.uint32), ref_w.view(np.uint32)), step
         assert np.array_equal(bf16_bits(lat.W).reshape(-1), ref_b), step
+
+
+@pytest.mark.parametrize("tokens,n", [(37, 6912), (5, 9216), (1, 128)])
+def test_relu2_gate_matches_oracle(tokens, n):
+    """Squared-ReLU gating: h (bf16), and the down projection's x_q and
+    x_scale formed from it, bit-exact against the oracle (gating, then the
+    oracle's activation quantisation of h); rows wider than the registers
+    hold take the recomputing path."""
+    rng = np.random.default_rng(tokens * n)
+    G = rng.standard_normal((tokens, n)).astype(np.float32)
+    U = rng.standard_normal((tokens, n)).astype(np.float32)
+    G[0, :16] = [0.0, -0.0, -1.0, 2.0, 1e-30, -1e-30, 3.0, 0.5] * 2
+    H_ref = oracle.relu2_gate(G, U)
+    xq_ref, sc_ref = oracle.act_quant(H_ref)
+    Gd, Ud = torch.from_numpy(G).cuda(), torch.from_numpy(U).cuda()
+    H = torch.empty(tokens * n, dtype=torch.bfloat16, device="cuda")
+    xq = torch.empty(tokens * n, dtype=torch.int8, device="cuda")
+    sc = torch.empty(tokens, dtype=torch.float32, device="cuda")
+    bl.bitlinear_relu2_gate(Gd, Ud, tokens, n, H, xq, sc)
+    xq2 = torch.empty_like(xq)
+    sc2 = torch.empty_like(sc)
+    bl.bitlinear_relu2_gate(Gd, Ud, tokens, n, None, xq2, sc2)  # without H
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(H).reshape(tokens, n), H_ref)
+    assert np.array_equal(xq.cpu().numpy().reshape(tokens, n), xq_ref)
+    assert np.array_equal(sc.cpu().numpy(), sc_ref.astype(np.float32))
+    assert torch.equal(xq, xq2) and torch.equal(sc, sc2)
+
+
+@pytest.mark.parametrize("count", [8, 2048 * 3 + 8, 4096 * 6912])
+def test_relu2_gate_bwd_matches_oracle(count):
+    rng = np.random.default_rng(count)
+    d = rng.standard_normal(count).astype(np.float32)
+    g = rng.standard_normal(count).astype(np.float32)
+    u = rng.standard_normal(count).astype(np.float32)
+    dg_ref, du_ref = oracle.relu2_gate_bwd(d, g, u)
+    dG = torch.empty(count, dtype=torch.bfloat16, device="cuda")
+    dU = torch.empty(count, dtype=torch.bfloat16, device="cuda")
+    bl.bitlinear_relu2_gate_bwd(torch.from_numpy(d).cuda(), torch.from_numpy(g).cuda(),
+                                torch.from_numpy(u).cuda(), count, dG, dU)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(dG), dg_ref)
+    assert np.array_equal(bf16_bits(dU), du_ref)

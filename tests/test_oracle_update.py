@@ -27,8 +27,12 @@ def nearest_bf16_bits(x: np.float32) -> int:
     comparison of the candidates' values."""
     v = Fraction(float(x))
     u = int(np.array(x, np.float32).view(np.uint32))
+    if v == 0:
+        return u >> 16  # signed zero
     cands = []
     for h in {u >> 16, (u >> 16) + 1, (u >> 16) - 1}:
+        if not 0 <= h <= 0xFFFF:
+            continue
         hv = np.array([h << 16], np.uint32).view(np.float32)[0]
         if np.isfinite(hv):
             cands.append((abs(Fraction(float(hv)) - v), h & 1, h))
