@@ -55,8 +55,8 @@ DECODE_TRAFFIC = {
     "sources": ["sparse_linear_layers_group_amd/csrc/gemv.hip",
                 "sparse_linear_layers_group_amd/csrc/common.h",
                 "sparse_linear_layers_group_amd/csrc/launch.h"],
-    "sha256": "079fe4556d9465454f2637b2c2efb1ab29fb21607d9e5442b47c9308ad063c7f",
-    "fetch_kib": 39918.4, "fetch_scale": 2.0,
+    "sha256": "3c754799e73bc0094c145fb1ce6c98d91581c7d6885016080f9b99b7700552c6",
+    "fetch_kib": 39918.6, "fetch_scale": 2.0,
     "write_kib": 1188.0, "write_scale": 1.0,
 }
 

@@ -172,7 +172,7 @@ constexpr int kGroupM = 8;
 __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(
     const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
     float* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-    const double* __restrict__ alpha) {
+    const double* __restrict__ alpha, int64_t klen) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][128 * kBP];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][128 * kBP];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -192,6 +192,11 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(
     m0 = (g * kGroupM + r % gm) * 128;
     n0 = (r / gm) * 128;
   }
+  // k range of this workgroup's split (blockIdx.y): [k0, k0 + klen) of K;
+  // a split writes its partial tile to plane blockIdx.y of C
+  const int64_t k0 = (int64_t)blockIdx.y * klen;
+  K = K - k0 < klen ? K - k0 : klen;
+  C += (int64_t)blockIdx.y * M * ldc;
   const int64_t nks = (K + 63) / 64;
 
   // loads: piece q = tid + 256 p (p < 4) of each tile is row q/8, k
@@ -209,8 +214,8 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int q = tid + 256 * p, row = q >> 3, kc = 8 * (q & 7);
-    a_off[p] = m0 + row < M ? (uint32_t)(((m0 + row) * lda + kc) * 2) : kOOB;
-    b_off[p] = n0 + row < N ? (uint32_t)(((n0 + row) * ldb + kc) * 2) : kOOB;
+    a_off[p] = m0 + row < M ? (uint32_t)(((m0 + row) * lda + k0 + kc) * 2) : kOOB;
+    b_off[p] = n0 + row < N ? (uint32_t)(((n0 + row) * ldb + k0 + kc) * 2) : kOOB;
   }
   auto load = [&](int64_t ks, u32x4* xa, u32x4* xb) {
 #pragma unroll
@@ -311,6 +316,26 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(
     }
 }
 
+// C = alpha * (sum of the split planes, in order), binary32 sums
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ P, int splits,
+                                                       int64_t n4, const double* __restrict__ alpha,
+                                                       float* __restrict__ C) {
+  const double g = alpha ? *alpha : 1.0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    v4f acc = ld_global(reinterpret_cast<const v4f*>(P) + i);
+    for (int s = 1; s < splits; ++s) {
+      const v4f v = ld_global(reinterpret_cast<const v4f*>(P) + (int64_t)s * n4 + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += v[e];
+    }
+    if (alpha) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = (float)((double)acc[e] * g);
+    }
+    st_global(reinterpret_cast<v4f*>(C) + i, acc);
+  }
+}
+
 // zero fill (dW when there are no tokens)
 __global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -319,11 +344,25 @@ __global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
 }
 
 // ------------------------------------------------------------- launchers
+// C has row pitch ldc = N when the product is split (the partial planes in
+// `partials`, M * N floats each)
 static hipError_t gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
                           int64_t ldc, int64_t M, int64_t N, int64_t K, const double* alpha,
-                          hipStream_t s) {
+                          float* partials, hipStream_t s) {
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  gemm_nt_bf16_kernel<<<(unsigned)((tiles + 7) / 8 * 8), 256, 0, s>>>(A, lda, B, ldb, C, ldc, M, N, K, alpha);
+  const unsigned gx = (unsigned)((tiles + 7) / 8 * 8);
+  const int splits = bwd_splits(M, N, K);
+  if (splits == 1) {
+    gemm_nt_bf16_kernel<<<gx, 256, 0, s>>>(A, lda, B, ldb, C, ldc, M, N, K, alpha, K);
+    return hipGetLastError();
+  }
+  const int64_t klen = bwd_split_len(K, splits);
+  const int used = (int)((K + klen - 1) / klen);
+  gemm_nt_bf16_kernel<<<dim3(gx, (unsigned)used), 256, 0, s>>>(A, lda, B, ldb, partials, N, M, N, K,
+                                                               nullptr, klen);
+  const int64_t n4 = M * N / 4;
+  const int64_t blocks = (n4 + 255) / 256;
+  split_sum_kernel<<<(unsigned)(blocks < 2048 ? blocks : 2048), 256, 0, s>>>(partials, used, n4, alpha, C);
   return hipGetLastError();
 }
 
@@ -341,7 +380,8 @@ hipError_t launch_bwd_dx(const uint16_t* dY, const void* packed, const double* g
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dX [tokens x k] = gamma * dY [tokens x n_out] . codes^T [k x n_out]^T
-  return gemm_nt(dY, n_out, codes_t, np, dX, k, tokens, k, n_out, gamma, s);
+  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + bwd_partial_offset(tokens, k, n_out));
+  return gemm_nt(dY, n_out, codes_t, np, dX, k, tokens, k, n_out, gamma, partials, s);
 }
 
 hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* xq, const float* scale, float* dW,
@@ -361,7 +401,8 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* xq, const float* scal
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dW [n_out x k] = (dY s)^T [n_out x tp] . x_q^T [k x tp]^T
-  return gemm_nt(dys_t, tp, xq_t, tp, dW, k, n_out, k, tp, nullptr, s);
+  float* partials = reinterpret_cast<float*>(w + bwd_partial_offset(tokens, k, n_out));
+  return gemm_nt(dys_t, tp, xq_t, tp, dW, k, n_out, k, tp, nullptr, partials, s);
 }
 
 }  // namespace bl

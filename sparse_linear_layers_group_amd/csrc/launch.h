@@ -269,9 +269,31 @@ inline size_t bwd_xq_offset(int64_t tokens, int64_t, int64_t n_out) {
 inline size_t bwd_codes_offset(int64_t tokens, int64_t k, int64_t n_out) {
   return bwd_xq_offset(tokens, k, n_out) + bwd_align((size_t)k * bwd_tokens_padded(tokens) * 2);
 }
-inline size_t bwd_ws_bytes(int64_t tokens, int64_t k, int64_t n_out) {
+// A product C[M x N] (k depth K) with few 128 x 128 tiles (at most 128,
+// half the CUs) and a deep k range is cut along k into `splits` ranges of
+// bwd_split_len() (a multiple of 64): binary32 partial tiles in the
+// workspace, summed in order by a second kernel.
+inline int bwd_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  if (tiles > 128 || K < 2048) return 1;
+  int64_t s = 512 / tiles;
+  if (s > 8) s = 8;
+  if (s > K / 512) s = K / 512;
+  return s < 2 ? 1 : (int)s;
+}
+inline int64_t bwd_split_len(int64_t K, int splits) {
+  return ((K + splits - 1) / splits + 63) / 64 * 64;
+}
+inline size_t bwd_partial_offset(int64_t tokens, int64_t k, int64_t n_out) {
   const int64_t np = (n_out + 63) / 64 * 64;
   return bwd_codes_offset(tokens, k, n_out) + bwd_align((size_t)k * np * 2);
+}
+inline size_t bwd_ws_bytes(int64_t tokens, int64_t k, int64_t n_out) {
+  // dX: M = tokens, N = k, K = n_out; dW: M = n_out, N = k, K = tokens padded
+  const int sx = bwd_splits(tokens, k, n_out), sw = bwd_splits(n_out, k, bwd_tokens_padded(tokens));
+  const size_t px = sx > 1 ? (size_t)sx * tokens * k * 4 : 0;
+  const size_t pw = sw > 1 ? (size_t)sw * n_out * k * 4 : 0;
+  return bwd_partial_offset(tokens, k, n_out) + bwd_align(px > pw ? px : pw);
 }
 hipError_t launch_bwd_dx(const uint16_t* dY, const void* packed, const double* gamma, float* dX,
                          void* ws, int64_t tokens, int64_t k, int64_t n_out, int S, hipStream_t s);

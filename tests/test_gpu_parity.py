@@ -95,6 +95,26 @@ def test_backward_parity(n, m, n_out, k, tokens):
                         dyv.T @ (np.abs(xq) * sc[:, None]))
 
 
+@pytest.mark.parametrize("n_out,k,tokens", [(2048, 256, 64), (128, 256, 4096), (640, 384, 2100)])
+def test_backward_split_along_k(n_out, k, tokens):
+    """Products with few output tiles and a deep contraction are cut along k
+    into binary32 partial tiles (dX of a 64-token batch over 2048 rows, dW
+    of a 4096-token batch, a ragged last range): same tolerance against the
+    oracle, and bit-identical on a rerun (the partials are summed in a
+    fixed order)."""
+    test_backward_parity(6, 8, n_out, k, tokens)
+    W = synth.weights(n_out, k, seed=9)
+    lw, _, _ = H.quantize_on_gpu(W, 6, 8, want_wq=False)
+    X = synth.activations(tokens, k, seed=9)
+    dY = bf16_tensor(synth.grad_output(tokens, n_out, seed=9))
+    bufs = lw.fwd(bf16_tensor(X), tokens)
+    ws = lw.bwd_workspace(tokens)
+    a = lw.bwd(dY, bufs["xq"], bufs["x_scale"], tokens, ws=ws)
+    b = lw.bwd(dY, bufs["xq"], bufs["x_scale"], tokens, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
 def test_gamma_exact_for_out_of_window_magnitudes():
     """Magnitudes >= 2 and bf16 subnormals take the rare accumulation path;
     gamma must still be the exact sum rounded once."""
