@@ -216,7 +216,9 @@ int bitlinear_fwd_group(const void *plan, int n, int m, int stages, void *stream
  *          written by bitlinear_quant_group_plan (which synchronises
  *          `stream` once); the host array is not used afterwards.
  * n, m and gamma_over passed to bitlinear_quant_group must be those the plan
- * was made with.  Errors as for the single-layer calls, plus BL_EWORKSPACE
+ * was made with; the plan records them, and a run with other values writes
+ * nothing (no mask, gamma or packed byte; the status is still BL_OK, as
+ * the host does not read the plan back).  Errors as for the single-layer calls, plus BL_EWORKSPACE
  * for a short plan or workspace. */
 typedef struct bitlinear_quant_item {
     const uint16_t *W;      /* bf16 [n_out x k], read            */

@@ -499,6 +499,9 @@ int bitlinear_quant_group_plan(const bitlinear_quant_item* items, int count, int
   h->count = count;
   h->mask_blocks = mb;
   h->pack_blocks = pb;
+  h->n = n;
+  h->m = m;
+  h->gamma_over = gamma_over;
   bl::QuantItemDesc* d = reinterpret_cast<bl::QuantItemDesc*>(img.data() + sizeof(bl::QuantGroupHeader));
   int32_t* owner = reinterpret_cast<int32_t*>(img.data() + bl::quant_owner_offset(count));
   int64_t m0 = 0, p0 = 0;

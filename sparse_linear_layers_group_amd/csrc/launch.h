@@ -36,7 +36,9 @@ hipError_t launch_mask_gamma(const uint16_t* W, int64_t n_out, int64_t k, int n,
 struct QuantGroupHeader {
   int32_t count, pad;
   int64_t mask_blocks, pack_blocks;  // workgroups of the mask and pack launches
-  int64_t pad2[5];
+  int32_t n, m, gamma_over, pad1;    // what the plan was made for; a launch with
+                                     // other values writes nothing
+  int64_t pad2[3];
 };
 static_assert(sizeof(QuantGroupHeader) == 64, "quant plan header size");
 struct QuantItemDesc {  // one layer (128 bytes)

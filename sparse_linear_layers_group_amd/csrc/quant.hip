@@ -634,7 +634,8 @@ __global__ __launch_bounds__(256) void mask_gamma_group_kernel(const char* __res
   const QuantGroupHeader* h = reinterpret_cast<const QuantGroupHeader*>(plan);
   const QuantItemDesc* items = reinterpret_cast<const QuantItemDesc*>(plan + sizeof(QuantGroupHeader));
   const int32_t* owner = reinterpret_cast<const int32_t*>(plan + quant_owner_offset(h->count));
-  const int64_t total = h->mask_blocks;
+  // a plan made for another pattern or gamma mode: write nothing
+  const int64_t total = (h->n == N && h->m == M && h->gamma_over == (MASKED ? 1 : 0)) ? h->mask_blocks : 0;
   for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
     const QuantItemDesc& it = items[owner[b]];
     mask_gamma_body<N, M, MASKED>(reinterpret_cast<const uint4*>(it.W), it.ngroups, it.per,
@@ -642,18 +643,21 @@ __global__ __launch_bounds__(256) void mask_gamma_group_kernel(const char* __res
   }
 }
 
-__global__ __launch_bounds__(256) void gamma_finalize_group_kernel(const char* __restrict__ plan) {
+__global__ __launch_bounds__(256) void gamma_finalize_group_kernel(const char* __restrict__ plan, int n,
+                                                                   int m, int gamma_over) {
   __shared__ MaskShared sh;
   const QuantGroupHeader* h = reinterpret_cast<const QuantGroupHeader*>(plan);
   const QuantItemDesc* items = reinterpret_cast<const QuantItemDesc*>(plan + sizeof(QuantGroupHeader));
-  for (int64_t i = blockIdx.x; i < h->count; i += gridDim.x) {
+  const int64_t count = (h->n == n && h->m == m && h->gamma_over == gamma_over) ? h->count : 0;
+  for (int64_t i = blockIdx.x; i < count; i += gridDim.x) {
     const QuantItemDesc& it = items[i];
     gamma_finalize_body(it.ws, (int)it.nmblocks, it.gamma, (double)(it.n_out * it.k), sh);
   }
 }
 
 template <int S>
-__global__ __launch_bounds__(256) void ternary_pack_group_kernel(const char* __restrict__ plan) {
+__global__ __launch_bounds__(256) void ternary_pack_group_kernel(const char* __restrict__ plan, int n,
+                                                                 int m, int gamma_over) {
   __shared__ PackTables tab;
   build_pack_tables(tab);
   __syncthreads();
@@ -661,7 +665,10 @@ __global__ __launch_bounds__(256) void ternary_pack_group_kernel(const char* __r
   const QuantItemDesc* items = reinterpret_cast<const QuantItemDesc*>(plan + sizeof(QuantGroupHeader));
   const int32_t* owner =
       reinterpret_cast<const int32_t*>(plan + quant_owner_offset(h->count)) + h->mask_blocks;
-  const int64_t total = h->pack_blocks;
+  // a plan made for another pattern or gamma mode: write nothing (its
+  // packed buffers are sized for that pattern's sign slots)
+  const int64_t total =
+      (h->n == n && h->m == m && h->gamma_over == gamma_over && s_of(n, m) == S) ? h->pack_blocks : 0;
   for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
     const QuantItemDesc& it = items[owner[b]];
     pack_fast_body<S>(it.W, it.mask, code_threshold16(*it.gamma), it.n_out, it.k,
@@ -980,8 +987,8 @@ static hipError_t launch_qg(const char* plan, int gamma_over, hipStream_t s) {
     mask_gamma_group_kernel<N, M, false><<<kQuantGrid, 256, 0, s>>>(plan);
   else
     mask_gamma_group_kernel<N, M, true><<<kQuantGrid, 256, 0, s>>>(plan);
-  gamma_finalize_group_kernel<<<kQuantGammaGrid, 256, 0, s>>>(plan);
-  ternary_pack_group_kernel<s_of(N, M)><<<kQuantGrid, 256, 0, s>>>(plan);
+  gamma_finalize_group_kernel<<<kQuantGammaGrid, 256, 0, s>>>(plan, N, M, gamma_over);
+  ternary_pack_group_kernel<s_of(N, M)><<<kQuantGrid, 256, 0, s>>>(plan, N, M, gamma_over);
   return hipGetLastError();
 }
 

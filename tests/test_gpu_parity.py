@@ -370,6 +370,14 @@ def test_grouped_quantisation_plan_checks():
         bl.bitlinear_quant_group_plan(qg.items, 1, 6, 8, 0, qg.ws[:0], qg.plan)
     with pytest.raises(bl.BitLinearError):
         bl.bitlinear_quant_group_plan(qg.items, 1, 6, 8, 0, qg.ws, qg.plan[:16])
+    # a run with another pattern or gamma mode than the plan's writes nothing
+    lw.mask.fill_(0x33)
+    lw.packed.fill_(0x44)
+    lw.gamma.fill_(7.0)
+    bl.bitlinear_quant_group(qg.plan, 2, 8, 0)
+    bl.bitlinear_quant_group(qg.plan, 6, 8, 1)
+    torch.cuda.synchronize()
+    assert (lw.mask == 0x33).all() and (lw.packed == 0x44).all() and lw.gamma.item() == 7.0
     qg.run()
     torch.cuda.synchronize()
     Z = np.zeros((64, 256), np.uint16)
