@@ -55,7 +55,7 @@ DECODE_TRAFFIC = {
     "sources": ["sparse_linear_layers_group_amd/csrc/gemv.hip",
                 "sparse_linear_layers_group_amd/csrc/common.h",
                 "sparse_linear_layers_group_amd/csrc/launch.h"],
-    "sha256": "3c754799e73bc0094c145fb1ce6c98d91581c7d6885016080f9b99b7700552c6",
+    "sha256": "15dd177c999cbbe3ef9470b5e52b62aadb3a75990f1a7daba7ed02302f01b6f8",
     "fetch_kib": 39918.6, "fetch_scale": 2.0,
     "write_kib": 1188.0, "write_scale": 1.0,
 }
