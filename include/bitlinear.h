@@ -83,7 +83,10 @@ size_t bitlinear_workspace_bytes(int64_t n_out, int64_t k);
  * products, bf16(dY * s_t) and x_q transposed to [n_out x tp] and [k x tp]
  * (tp = tokens rounded up to 64) and the decoded codes transposed to
  * [k x n_out rounded up to 64]; about 113 MB for a 6912 x 2560 layer at
- * 4096 tokens.  0 for invalid shapes. */
+ * 4096 tokens.  A product with few output tiles and a deep contraction
+ * (e.g. dW of a 640 x 2560 layer at 4096 tokens) is split along it, and
+ * the workspace then also holds its binary32 partial results (up to 8
+ * planes of the product's output; 33 MB there).  0 for invalid shapes. */
 size_t bitlinear_bwd_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out);
 
 /* Workspace bytes bitlinear_fwd / bitlinear_contract need for `tokens`
