@@ -303,7 +303,7 @@ def test_group_plan_validation():
     assert bl.bitlinear_fwd_group_plan_bytes(items, 1, 17) == 0  # decode only: <= 16 tokens
 
 
-@pytest.mark.parametrize("n,m,gamma_over", [(6, 8, 0), (8, 8, 0), (2, 4, 0), (4, 8, 1)])
+@pytest.mark.parametrize("n,m,gamma_over", [(6, 8, 0), (8, 8, 0), (2, 4, 0), (4, 8, 1), (3, 8, 0), (2, 8, 1)])
 def test_grouped_quantisation_matches_oracle(n, m, gamma_over):
     """Grouped mask + gamma + pack of ragged layers in one plan: every mask,
     gamma and packed byte bit-identical to the oracle, run twice (the plan
