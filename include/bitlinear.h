@@ -182,7 +182,11 @@ int bitlinear_contract(const int8_t *xq, const float *x_scale, int64_t tokens,
  *          it must stay allocated and unchanged while the plan is used.
  *   stages 1 = activation quantisation only, 2 = contraction only (x_q and
  *          x_scale already written), 3 = both.
- * n, m passed to bitlinear_fwd_group must be those the plan was made with. */
+ * n, m passed to bitlinear_fwd_group must be those the plan was made with;
+ * the plan records its sign-slot count, and a contraction run whose n:m
+ * has another count (4:8, 3:8 and 2:4 share one) reads no packed byte and
+ * sets every Y of every item to a quiet NaN instead (the status is still
+ * BL_OK: the host does not read the plan back). */
 typedef struct bitlinear_fwd_item {
     const uint16_t *X;      /* bf16 [tokens x k]      */
     const void *packed;     /* packed codes           */
@@ -219,10 +223,13 @@ int bitlinear_fwd_group(const void *plan, int n, int m, int stages, void *stream
  *          written by bitlinear_quant_group_plan (which synchronises
  *          `stream` once); the host array is not used afterwards.
  * n, m and gamma_over passed to bitlinear_quant_group must be those the plan
- * was made with; the plan records them, and a run with other values writes
- * nothing (no mask, gamma or packed byte; the status is still BL_OK, as
- * the host does not read the plan back).  Errors as for the single-layer calls, plus BL_EWORKSPACE
- * for a short plan or workspace. */
+ * was made with (a dense-to-sparse schedule builds one plan per pattern).
+ * The plan records them; a run with other values writes no mask or packed
+ * byte (the packed buffers are sized for the planned pattern) and sets
+ * every item's gamma to a quiet NaN, so every forward or backward output
+ * formed from those stale codes is NaN (the status is still BL_OK, as the
+ * host does not read the plan back).  Errors as for the single-layer
+ * calls, plus BL_EWORKSPACE for a short plan or workspace. */
 typedef struct bitlinear_quant_item {
     const uint16_t *W;      /* bf16 [n_out x k], read            */
     uint8_t *mask;          /* [n_out x k/8], written            */

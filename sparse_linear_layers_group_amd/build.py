@@ -2,7 +2,10 @@
 sparse_linear_layers_group_amd/libbitlinear.so in the source tree.
 
 Flags: -O3, correctly rounded binary32 division (the activation quantiser
-relies on it), packed-fp32 code generation disabled, no fast-math.
+relies on it), no contraction of a multiply and an add into one fused
+operation (the bit-exact elementwise kernels round every product; explicit
+fmaf calls are unaffected), packed-fp32 code generation disabled, no
+fast-math.
 """
 import concurrent.futures
 import os
@@ -19,7 +22,7 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
-    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -41,7 +41,7 @@ constexpr int64_t kLimit = (int64_t)1 << 31;
 
 int check_nm(int n, int m) {
   if (bl::s_of(n, m) < 0)
-    return fail(BL_EUNSUPPORTED, "N:M pattern %d:%d unsupported (use 8:8, 6:8, 4:8 or 2:4)", n, m);
+    return fail(BL_EUNSUPPORTED, "N:M pattern %d:%d unsupported (use 8:8, 6:8, 4:8, 3:8, 2:8 or 2:4)", n, m);
   return BL_OK;
 }
 
@@ -576,17 +576,22 @@ int bitlinear_bwd(const uint16_t* dY, const int8_t* xq, const float* x_scale, co
                 ws ? ws_bytes : (size_t)0);
   TRY(check_ptr(ws, 256, "ws"));
   TRY(check_ptr(dY, 16, "dY"));
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // every input of every requested output is checked before the first launch
   if (dX) {
     TRY(check_ptr(packed, 16, "packed"));
     TRY(check_ptr(gamma, 8, "gamma"));
+  }
+  if (dW) {
+    TRY(check_ptr(xq, 16, "xq"));
+    TRY(check_ptr(x_scale, 4, "x_scale"));
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dX) {
     hipError_t e =
         bl::launch_bwd_dx(dY, packed, gamma, dX, ws, tokens, k, n_out, bl::s_of(n, m), s);
     if (e != hipSuccess) return hip_status(e, "dX launch");
   }
   if (dW) {
-    TRY(check_ptr(xq, 16, "xq"));
-    TRY(check_ptr(x_scale, 4, "x_scale"));
     hipError_t e = bl::launch_bwd_dw(dY, xq, x_scale, dW, ws, tokens, k, n_out, s);
     if (e != hipSuccess) return hip_status(e, "dW launch");
   }

@@ -516,6 +516,19 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(SingleSrc<S> src) {
   run_block<S>(src, lut, threadIdx.x & 63);
 }
 
+// every Y of every item of a plan set to a quiet NaN (grid-stride)
+__device__ __noinline__ void poison_outputs(const char* plan, const GroupHeader* hdr) {
+  const GroupItem* items =
+      reinterpret_cast<const GroupItem*>(plan + group_items_offset(hdr->rows, hdr->strips));
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int32_t i = 0; i < hdr->count; ++i) {
+    const int64_t n = (int64_t)hdr->tokens * items[i].n_out;
+    float* y = items[i].Y;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride)
+      st_global(y + e, __builtin_nanf(""));
+  }
+}
+
 template <int S>
 __global__ __launch_bounds__(kGemvThreads) void gemv_group_kernel(const char* __restrict__ plan) {
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 2 * kLutCopies];
@@ -528,6 +541,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_group_kernel(const char* __
   const GroupHeader* hdr = reinterpret_cast<const GroupHeader*>(plan);
   const int64_t rows = hdr->rows;
   src.tokens = hdr->tokens;
+  if (hdr->S != S) {
+    // a plan made for another sign-slot count: its strips are laid out for
+    // that count, so no packed byte is read; every output becomes a quiet
+    // NaN instead
+    poison_outputs(plan, hdr);
+    return;
+  }
   // (rows < 0 never holds; the test keeps the header read ahead of the branch)
   if (!src.starts[(int64_t)blockIdx.x * kGemvWaves + wave_id()].active || rows < 0) return;
   src.strips = reinterpret_cast<const StripDesc*>(plan + group_strips_offset(rows));

@@ -44,9 +44,11 @@ static_assert(sizeof(MaskPart) == 32, "mask partial record");
 
 // keys: |h| (15 bits) in bits 16..30 above a 3-bit code (bits 0..2) that
 // ranks a lower index higher; all keys of a group are distinct, a larger
-// key ranks first, and bits 3..15 are zero, so 0x80 >> key (the shift
-// takes bits 0..4) is the mask bit of the key's element.
-__device__ __forceinline__ uint32_t drop_bit(uint32_t key) { return 0x80u >> key; }
+// key ranks first, and bits 3..15 are zero, so 0x80 >> (key & 31) is the
+// mask bit of the key's element (the mask keeps the shift defined; the
+// shift instruction reads only those five bits anyway, so it costs
+// nothing).
+__device__ __forceinline__ uint32_t drop_bit(uint32_t key) { return 0x80u >> (key & 31u); }
 
 __device__ __forceinline__ uint32_t min3(uint32_t a, uint32_t b, uint32_t c) { return min(min(a, b), c); }
 __device__ __forceinline__ uint32_t max3(uint32_t a, uint32_t b, uint32_t c) { return max(max(a, b), c); }
@@ -648,10 +650,17 @@ __global__ __launch_bounds__(256) void gamma_finalize_group_kernel(const char* _
   __shared__ MaskShared sh;
   const QuantGroupHeader* h = reinterpret_cast<const QuantGroupHeader*>(plan);
   const QuantItemDesc* items = reinterpret_cast<const QuantItemDesc*>(plan + sizeof(QuantGroupHeader));
-  const int64_t count = (h->n == n && h->m == m && h->gamma_over == gamma_over) ? h->count : 0;
-  for (int64_t i = blockIdx.x; i < count; i += gridDim.x) {
+  // a plan made for another pattern or gamma mode: the mask and pack
+  // launches write nothing, and every item's gamma becomes a quiet NaN, so
+  // the stale codes cannot pass unnoticed (every output formed with that
+  // gamma is NaN)
+  const bool match = h->n == n && h->m == m && h->gamma_over == gamma_over;
+  for (int64_t i = blockIdx.x; i < h->count; i += gridDim.x) {
     const QuantItemDesc& it = items[i];
-    gamma_finalize_body(it.ws, (int)it.nmblocks, it.gamma, (double)(it.n_out * it.k), sh);
+    if (match)
+      gamma_finalize_body(it.ws, (int)it.nmblocks, it.gamma, (double)(it.n_out * it.k), sh);
+    else if (threadIdx.x == 0)
+      st_global(it.gamma, __builtin_nan(""));
   }
 }
 

@@ -105,6 +105,27 @@ def test_bwd_validation(L):
     assert b(A, A, A, A, A, 4, 256, 128, 6, 8, None, None, None, 0, None) == bl.BL_OK  # nothing asked
 
 
+def test_bwd_checks_every_input_before_the_first_launch(L):
+    """With dX and dW both requested, a bad input of dW (NULL or misaligned
+    x_q or x_scale) is reported before the dX kernels are queued: on a host
+    without a GPU a launch would have returned BL_EHIP instead."""
+    b = L.bitlinear_bwd
+    need = bl.bitlinear_bwd_workspace_bytes(4, 256, 128)
+    assert b(A, None, A, A, A, 4, 256, 128, 6, 8, A, A, A, need, None) == bl.BL_EINVAL
+    assert "xq" in bl.bitlinear_last_error()
+    assert b(A, A, A + 2, A, A, 4, 256, 128, 6, 8, A, A, A, need, None) == bl.BL_EINVAL
+    assert "x_scale" in bl.bitlinear_last_error()
+    assert b(A, A, A, None, A, 4, 256, 128, 6, 8, A, A, A, need, None) == bl.BL_EINVAL
+    assert b(A, A, A, A, A + 4, 4, 256, 128, 6, 8, A, A, A, need, None) == bl.BL_EINVAL
+
+
+def test_unsupported_pattern_message_lists_every_pattern(L):
+    assert call_qm(L, n=5) == bl.BL_EUNSUPPORTED
+    msg = bl.bitlinear_last_error()
+    for p in ("8:8", "6:8", "4:8", "3:8", "2:8", "2:4"):
+        assert p in msg
+
+
 def test_status_strings(L):
     for s in range(6):
         assert bl.bitlinear_status_string(s)

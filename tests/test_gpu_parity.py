@@ -289,6 +289,41 @@ def test_act_quant_plus_contract_equals_fwd(tokens):
     assert np.array_equal(xq.cpu().numpy(), ref["xq"].cpu().numpy())
 
 
+@pytest.mark.parametrize("plan_nm,run_nm", [((6, 8), (8, 8)), ((2, 8), (6, 8)), ((8, 8), (2, 4))])
+def test_grouped_decode_rejects_other_pattern(plan_nm, run_nm):
+    """A grouped contraction run with an N:M pattern whose sign-slot count
+    differs from the plan's reads no packed byte and sets every output of
+    every item to NaN; the plan then still runs correctly with its own
+    pattern."""
+    tokens = 2
+    shapes = [(200, 1152), (48, 256), (896, 4864)]
+    n, m = plan_nm
+    entries, refs = [], []
+    for i, (n_out, k) in enumerate(shapes):
+        W = synth.weights(n_out, k, seed=300 + i)
+        X = synth.activations(tokens, k, seed=400 + i)
+        lw, T, g = H.check_weight_path(W, n, m)
+        xq, sc = oracle.act_quant(X)
+        _, Yref = oracle.fwd(xq, sc, T, g)
+        entries.append(dict(X=bf16_tensor(X), packed=lw.packed, gamma=lw.gamma, k=k, n_out=n_out,
+                            Y=torch.zeros(tokens * n_out, dtype=torch.float32, device="cuda"),
+                            xq=torch.empty(tokens * k, dtype=torch.int8, device="cuda"),
+                            x_scale=torch.empty(tokens, dtype=torch.float32, device="cuda"), lw=lw))
+        refs.append(Yref)
+    items = bl.make_fwd_items(entries, tokens)
+    plan = torch.empty(bl.bitlinear_fwd_group_plan_bytes(items, len(entries), tokens), dtype=torch.uint8,
+                       device="cuda")
+    bl.bitlinear_fwd_group_plan(items, len(entries), tokens, n, m, plan)
+    bl.bitlinear_fwd_group(plan, run_nm[0], run_nm[1], 3)
+    torch.cuda.synchronize()
+    for e in entries:
+        assert torch.isnan(e["Y"]).all()
+    bl.bitlinear_fwd_group(plan, n, m, 3)
+    torch.cuda.synchronize()
+    for e, Yref in zip(entries, refs):
+        H.assert_y_close(e["Y"].cpu().numpy().reshape(Yref.shape).astype(np.float64), Yref)
+
+
 def test_group_plan_validation():
     lw = BitLinearWeight(64, 256, 6, 8)
     e = dict(X=torch.zeros(256, dtype=torch.bfloat16, device="cuda"), packed=lw.packed, gamma=lw.gamma,
@@ -370,14 +405,21 @@ def test_grouped_quantisation_plan_checks():
         bl.bitlinear_quant_group_plan(qg.items, 1, 6, 8, 0, qg.ws[:0], qg.plan)
     with pytest.raises(bl.BitLinearError):
         bl.bitlinear_quant_group_plan(qg.items, 1, 6, 8, 0, qg.ws, qg.plan[:16])
-    # a run with another pattern or gamma mode than the plan's writes nothing
-    lw.mask.fill_(0x33)
-    lw.packed.fill_(0x44)
-    lw.gamma.fill_(7.0)
-    bl.bitlinear_quant_group(qg.plan, 2, 8, 0)
-    bl.bitlinear_quant_group(qg.plan, 6, 8, 1)
+    # a run with another pattern or gamma mode than the plan's writes no
+    # mask or packed byte and turns gamma into NaN, so the stale codes show
+    for n_run, m_run, go_run in ((2, 8, 0), (6, 8, 1), (4, 8, 0)):
+        lw.mask.fill_(0x33)
+        lw.packed.fill_(0x44)
+        lw.gamma.fill_(7.0)
+        bl.bitlinear_quant_group(qg.plan, n_run, m_run, go_run)
+        torch.cuda.synchronize()
+        assert (lw.mask == 0x33).all() and (lw.packed == 0x44).all()
+        assert np.isnan(lw.gamma.item()), (n_run, m_run, go_run)
+    # and everything formed with that gamma is NaN
+    X = bf16_tensor(synth.activations(4, 256, seed=3))
+    bufs = lw.fwd(X, 4)
     torch.cuda.synchronize()
-    assert (lw.mask == 0x33).all() and (lw.packed == 0x44).all() and lw.gamma.item() == 7.0
+    assert torch.isnan(bufs["Y"]).all()
     qg.run()
     torch.cuda.synchronize()
     Z = np.zeros((64, 256), np.uint16)
