@@ -14,7 +14,8 @@
  *   - Pointers named as device pointers must be device memory of the
  *     current HIP device, 16-byte aligned (gamma: 8-byte; x_scale: 4-byte).
  *     The caller allocates and frees every buffer; the library keeps no
- *     device memory and no global state between calls.
+ *     device memory and no global state between calls, except the static
+ *     scratch of bitlinear_fwd_noalloc.
  *   - bf16 tensors are passed as uint16_t bit patterns.  W is [n_out x k],
  *     X is [tokens x k], dY is [tokens x n_out]; all row-major, contiguous.
  *   - Supported patterns (n, m): 8:8 (dense), 6:8, 4:8, 3:8, 2:8 (the
@@ -93,8 +94,8 @@ size_t bitlinear_bwd_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out);
  * tokens: split-k partial sums and counters of the decode kernel (tokens
  * <= 16), or, for the prefill kernel, counters and exact int32 partial
  * tiles when the layer has too few 256 x 64 output tiles to fill the GPU
- * and the k range is split (e.g. a 1536 x 8960 layer at 2048 tokens: about
- * 61 MiB).  0 means ws may be NULL. */
+ * and the k range is split (e.g. a 1536-row layer with k >= 1024 at 1024
+ * tokens: 12 MiB).  0 means ws may be NULL. */
 size_t bitlinear_fwd_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out);
 
 /* Steps 1-2 (and optionally 3): mask and absmean scale.
@@ -155,6 +156,25 @@ int bitlinear_fwd(const uint16_t *X, int64_t tokens, int64_t k,
                   const void *packed, int64_t n_out, int n, int m,
                   const double *gamma, float *Y, int8_t *xq, float *x_scale,
                   int32_t *acc, void *ws, size_t ws_bytes, void *stream);
+
+/* bitlinear_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and results without ws/ws_bytes.  The forward's
+ * workspace lives in a static device array of 8 MiB that the library
+ * holds on each device it runs on until the process ends; a call whose
+ * bitlinear_fwd_workspace_bytes() exceeds 8 MiB (a prefill split along k
+ * over more than 63 output tiles, or a decode with n_out * tokens above
+ * about 2 million) returns BL_EWORKSPACE before anything is enqueued.  The
+ * call allocates nothing and records no memset: the counters that must
+ * start at zero are cleared inside its activation kernel.  The first call
+ * on a device resolves the array's address there (hipGetSymbolAddress;
+ * make it outside graph capture).  Every call on a device shares that
+ * device's array, so calls that overlap in time on one device (several
+ * streams, several host threads) race; serialise them. */
+int bitlinear_fwd_noalloc(const uint16_t *X, int64_t tokens, int64_t k,
+                          const void *packed, int64_t n_out, int n, int m,
+                          const double *gamma, float *Y, int8_t *xq,
+                          float *x_scale, int32_t *acc, void *stream);
 
 /* The two halves of bitlinear_fwd, for callers that quantise activations
  * once and contract them against several weights, or that time the steps

@@ -39,6 +39,7 @@ _SIGS = {
     "bitlinear_pack": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _sz, _vp]),
     "bitlinear_fwd": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _sz, _vp]),
+    "bitlinear_fwd_noalloc": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp]),
     "bitlinear_act_quant": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "bitlinear_contract": (_int, [_vp, _vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_fwd_group_plan_bytes": (_sz, [_vp, _int, _i64]),
@@ -167,6 +168,16 @@ def bitlinear_fwd(X, tokens, k, packed, n_out, n, m, gamma, Y, xq, x_scale, acc=
         (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes),
         _stream(stream))
     _check(st, "bitlinear_fwd")
+
+
+def bitlinear_fwd_noalloc(X, tokens, k, packed, n_out, n, m, gamma, Y, xq, x_scale, acc=None, stream=None):
+    st = lib().bitlinear_fwd_noalloc(
+        _ptr(X, _BF16, tokens * k, "X"), tokens, k, _ptr(packed, (torch.uint8,), None, "packed"),
+        n_out, n, m, _ptr(gamma, (torch.float64,), 1, "gamma"),
+        _ptr(Y, (torch.float32,), tokens * n_out, "Y"), _ptr(xq, (torch.int8,), tokens * k, "xq"),
+        _ptr(x_scale, (torch.float32,), tokens, "x_scale"),
+        _ptr(acc, (torch.int32,), tokens * n_out, "acc", optional=True), _stream(stream))
+    _check(st, "bitlinear_fwd_noalloc")
 
 
 def bitlinear_bwd_workspace_bytes(tokens, k, n_out):

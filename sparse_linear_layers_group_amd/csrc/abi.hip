@@ -5,8 +5,10 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <queue>
 #include <string>
 #include <utility>
@@ -133,6 +135,47 @@ int quant_shape(const bitlinear_quant_item* items, int count, int64_t* mask_bloc
 }
 }  // namespace
 
+// ---------------------------------------------------------------------
+// Static scratch of bitlinear_fwd_noalloc: the forward's workspace (decode
+// split-k partial sums and counters, prefill split-k tickets and partial
+// tiles) in a file-scope device array, so that call allocates nothing.
+// Host code never passes the array's name to a kernel or a copy (on the
+// host it is only a stand-in symbol): the first call on each device
+// resolves the array's address on that device with hipGetSymbolAddress and
+// keeps it; every later call on that device uses the kept address.
+// ---------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// the scratch array's address on the current device (resolved once per
+// device); BL_OK or BL_EHIP
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BL_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(BL_EHIP, "device index %d out of range", dev);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(BL_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                    hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return BL_OK;
+}
+}  // namespace
+
 extern "C" {
 
 size_t bitlinear_packed_bytes(int64_t n_out, int64_t k, int n, int m) {
@@ -248,6 +291,29 @@ int bitlinear_fwd(const uint16_t* X, int64_t tokens, int64_t k, const void* pack
   if (e != hipSuccess) return hip_status(e, "activation quant launch");
   e = bl::launch_gemm(packed, xq, x_scale, gamma, Y, acc, ws, tokens, k, n_out, S, s);
   return hip_status(e, "prefill launch");
+}
+
+int bitlinear_fwd_noalloc(const uint16_t* X, int64_t tokens, int64_t k, const void* packed,
+                          int64_t n_out, int n, int m, const double* gamma, float* Y, int8_t* xq,
+                          float* x_scale, int32_t* acc, void* stream) {
+  TRY(check_nm(n, m));
+  TRY(check_layer(n_out, k));
+  if (tokens < 0) return fail(BL_ESHAPE, "tokens must be >= 0 (got %lld)", (long long)tokens);
+  if (tokens >= kLimit || tokens * k >= kLimit || tokens * n_out >= kLimit)
+    return fail(BL_ESHAPE, "tokens*k and tokens*n_out must stay below 2^31");
+  if (tokens == 0) return ok();
+  const size_t need = bitlinear_fwd_workspace_bytes(tokens, k, n_out);
+  if (need > kNoAllocScratchBytes)
+    return fail(BL_EWORKSPACE,
+                "this forward needs %zu bytes of workspace; the static scratch holds %zu "
+                "(use bitlinear_fwd with a caller workspace)",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need) TRY(scratch_address(&ws));
+  // the same kernels as bitlinear_fwd, which clears the counters it needs
+  // inside its activation kernel (no memset node)
+  return bitlinear_fwd(X, tokens, k, packed, n_out, n, m, gamma, Y, xq, x_scale, acc, ws,
+                       need ? kNoAllocScratchBytes : 0, stream);
 }
 
 int bitlinear_act_quant(const uint16_t* X, int64_t tokens, int64_t k, int8_t* xq, float* x_scale,

@@ -126,6 +126,19 @@ def test_unsupported_pattern_message_lists_every_pattern(L):
         assert p in msg
 
 
+def test_fwd_noalloc_validation(L):
+    """The allocation-free forward validates like bitlinear_fwd and rejects a
+    forward whose workspace exceeds its static scratch before touching any
+    device state."""
+    f = L.bitlinear_fwd_noalloc
+    assert f(A, 4, 250, A, 128, 6, 8, A, A, A, A, None, None) == bl.BL_ESHAPE
+    assert f(A, 4, 256, A, 128, 5, 8, A, A, A, A, None, None) == bl.BL_EUNSUPPORTED
+    assert f(None, 0, 256, None, 128, 6, 8, None, None, None, None, None, None) == bl.BL_OK
+    assert bl.bitlinear_fwd_workspace_bytes(1024, 1024, 1536) > 8 << 20
+    assert f(A, 1024, 1024, A, 1536, 6, 8, A, A, A, A, None, None) == bl.BL_EWORKSPACE
+    assert "static scratch" in bl.bitlinear_last_error()
+
+
 def test_status_strings(L):
     for s in range(6):
         assert bl.bitlinear_status_string(s)
