@@ -50,6 +50,9 @@ def _load():
         "oracle_packed_bytes": (_i64, [_i64, _i64, _int]),
         "oracle_pack": (_int, [_vp, _i64, _i64, _int, _vp]),
         "oracle_unpack": (None, [_vp, _i64, _i64, _int, _vp]),
+        "oracle_sp24_packed_bytes": (_i64, [_i64, _i64]),
+        "oracle_pack_sp24": (_int, [_vp, _i64, _i64, _vp]),
+        "oracle_unpack_sp24": (None, [_vp, _i64, _i64, _vp]),
         "oracle_latent_update": (None, [_vp, _vp, _i64, ctypes.c_float, _vp]),
         "oracle_relu2_gate": (None, [_vp, _vp, _i64, _vp]),
         "oracle_relu2_gate_bwd": (None, [_vp, _vp, _vp, _i64, _vp, _vp]),
@@ -209,6 +212,27 @@ def unpack(packed, n_out, k, s):
     packed = _c(packed, np.uint8)
     T = np.zeros((n_out, k), dtype=np.int8)
     _load().oracle_unpack(_p(packed), int(n_out), int(k), int(s), _p(T))
+    return T
+
+
+def sp24_packed_bytes(n_out, k):
+    return _load().oracle_sp24_packed_bytes(int(n_out), int(k))
+
+
+def pack_sp24(T):
+    """2:4 codes T [n_out, k] in the sparse-operand + index layout (uint8)."""
+    T = _c(T, np.int8)
+    n_out, k = T.shape
+    out = np.zeros(sp24_packed_bytes(n_out, k), dtype=np.uint8)
+    if _load().oracle_pack_sp24(_p(T), n_out, k, _p(out)) != 0:
+        raise ValueError("a quad holds more than two nonzero codes")
+    return out
+
+
+def unpack_sp24(packed, n_out, k):
+    packed = _c(packed, np.uint8)
+    T = np.zeros((n_out, k), dtype=np.int8)
+    _load().oracle_unpack_sp24(_p(packed), int(n_out), int(k), _p(T))
     return T
 
 

@@ -536,6 +536,115 @@ void oracle_unpack(const uint8_t *packed, int64_t n_out, int64_t k, int s, int8_
 }
 
 /* ------------------------------------------------------------------ */
+/* 2:4 codes as "sparse operand + index" (this project's second packed */
+/* format, for matrix instructions that take a 2:4-sparse operand:     */
+/* the structured-sparsity hardware [SB] 七 describes, here gfx950's   */
+/* sparse int8 matrix multiply).  Under a 2:4 mask every quad (4       */
+/* consecutive k) holds at most two nonzero codes; each quad is stored */
+/* as two (position, value) slots:                                     */
+/*   2 nonzeros at positions a < b:  slots (a, T[a]), (b, T[b]);       */
+/*   1 nonzero at position a:        a = 0: (0, T[0]), (1, 0);         */
+/*                                   a > 0: (0, 0), (a, T[a]);         */
+/*   no nonzero:                     (0, 0), (1, 0).                   */
+/* (positions ascending and distinct in every case).                   */
+/* Layout: rows in strips of 64 (the last padded with zero codes), k   */
+/* in blocks of 128; superblock (strip p, block kb) at index           */
+/* p*(k/128) + kb, 64 chunks of 32 bytes.  Chunk c = r + 16q holds rows */
+/* 64p + 16i + r (i = 0..3) over k = 128kb + 32q ... +31: element      */
+/* e = 2u + s (quad u = 0..7 at k = 128kb + 32q + 4u, slot s) of row   */
+/* tile i sits in                                                      */
+/*   word 2i   (index word):  bits 2e, 2e+1 = the slot's position;     */
+/*   word 2i+1 (value word):  bits 8(e%4) + 2(e/4), +1 = its code,     */
+/*                            0 for 0, 1 for +1, 3 for -1;             */
+/* words little-endian, word w at byte 4w of the chunk.                 */
+/* ------------------------------------------------------------------ */
+int64_t oracle_sp24_packed_bytes(int64_t n_out, int64_t k)
+{
+    return (n_out + 63) / 64 * 64 * (k / 128) * 32;
+}
+
+static uint8_t *sp24_chunk(uint8_t *packed, int64_t row, int64_t kb, int q, int64_t nkb, int *i)
+{
+    int64_t strip = row / 64;
+    int rr = (int)(row % 64);
+    *i = rr / 16;
+    return packed + ((strip * nkb + kb) * 64 + rr % 16 + 16 * q) * 32;
+}
+
+static void put_word(uint8_t *p, uint32_t w)
+{
+    for (int b = 0; b < 4; ++b) p[b] = (uint8_t)(w >> (8 * b));
+}
+
+static uint32_t get_word(const uint8_t *p)
+{
+    return (uint32_t)p[0] | (uint32_t)p[1] << 8 | (uint32_t)p[2] << 16 | (uint32_t)p[3] << 24;
+}
+
+/* Returns 0, or -1 if a quad holds more than two nonzero codes. */
+int oracle_pack_sp24(const int8_t *T, int64_t n_out, int64_t k, uint8_t *packed)
+{
+    int64_t nkb = k / 128, rows = (n_out + 63) / 64 * 64;
+    static const int8_t zero_quad[4] = {0, 0, 0, 0};
+    memset(packed, 0, (size_t)oracle_sp24_packed_bytes(n_out, k));
+    for (int64_t r = 0; r < rows; ++r)  /* rows past n_out: zero codes */
+        for (int64_t kb = 0; kb < nkb; ++kb)
+            for (int q = 0; q < 4; ++q) {
+                int i;
+                uint8_t *ch = sp24_chunk(packed, r, kb, q, nkb, &i);
+                uint32_t idx = 0, val = 0;
+                for (int u = 0; u < 8; ++u) {
+                    const int8_t *t = r < n_out ? T + r * k + kb * 128 + 32 * q + 4 * u : zero_quad;
+                    int pos[2], n = 0;
+                    for (int a = 0; a < 4; ++a)
+                        if (t[a] != 0) {
+                            if (n == 2) return -1;
+                            pos[n++] = a;
+                        }
+                    if (n == 0) { pos[0] = 0; pos[1] = 1; }
+                    if (n == 1) {
+                        if (pos[0] == 0) pos[1] = 1;
+                        else { pos[1] = pos[0]; pos[0] = 0; }
+                    }
+                    for (int sl = 0; sl < 2; ++sl) {
+                        int e = 2 * u + sl;
+                        int8_t v = t[pos[sl]];
+                        uint32_t code = v == 0 ? 0u : (v > 0 ? 1u : 3u);
+                        idx |= (uint32_t)pos[sl] << (2 * e);
+                        val |= code << (8 * (e % 4) + 2 * (e / 4));
+                    }
+                }
+                put_word(ch + 8 * i, idx);
+                put_word(ch + 8 * i + 4, val);
+            }
+    return 0;
+}
+
+/* The codes the format represents: every slot adds its value at its
+ * position (so a slot holding 0 contributes nothing), as the sparse
+ * matrix instruction multiplies and adds every stored element. */
+void oracle_unpack_sp24(const uint8_t *packed, int64_t n_out, int64_t k, int8_t *T)
+{
+    int64_t nkb = k / 128;
+    uint8_t *pk = (uint8_t *)packed;
+    for (int64_t r = 0; r < n_out; ++r)
+        for (int64_t kb = 0; kb < nkb; ++kb)
+            for (int q = 0; q < 4; ++q) {
+                int i;
+                const uint8_t *ch = sp24_chunk(pk, r, kb, q, nkb, &i);
+                uint32_t idx = get_word(ch + 8 * i), val = get_word(ch + 8 * i + 4);
+                int8_t *t = T + r * k + kb * 128 + 32 * q;
+                for (int a = 0; a < 32; ++a) t[a] = 0;
+                for (int e = 0; e < 16; ++e) {
+                    int pos = (int)((idx >> (2 * e)) & 3u);
+                    uint32_t code = (val >> (8 * (e % 4) + 2 * (e / 4))) & 3u;
+                    int v = code == 1u ? 1 : code == 3u ? -1 : 0;
+                    t[4 * (e / 2) + pos] = (int8_t)(t[4 * (e / 2) + pos] + v);
+                }
+            }
+}
+
+/* ------------------------------------------------------------------ */
 /* Latent-weight update ([SB] 三, 六: the latent full-precision weights */
 /* take the dense gradient that both straight-through estimators pass; */
 /* the next step re-derives mask, gamma and codes from them).  The     */

@@ -202,3 +202,101 @@ def test_hand_derived_group_fields():
         assert got == field, (s, codes, hex(got), hex(field))
         # the remaining 15 groups are all-zero codes
         assert int.from_bytes(bytes(P[: 2 * (8 + s)]), "little") >> (8 + s) == 0
+
+
+# ---------------------------------------------------------------- 2:4 sparse-operand layout
+def load_golden_sp24():
+    cases = []
+    with open(os.path.join(GOLDEN, "sp24_layout.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            shape, code, out = line.split(";")
+            n_out, k = (int(v) for v in shape.split())
+            c = [int(v) for v in code.split()]
+            o = out.split()
+            cases.append((n_out, k, [tuple(c[i:i + 3]) for i in range(0, len(c), 3)],
+                          {int(o[i]): int(o[i + 1], 16) for i in range(0, len(o), 2)}))
+    return cases
+
+
+def _sp24_words(P):
+    return np.frombuffer(P.tobytes(), dtype="<u4")
+
+
+def test_sp24_hand_derived_placements():
+    """Codes land in the index and value words worked out by hand from the
+    layout definition (tests/golden/sp24_layout.txt); every other word has
+    the all-zero-quad pattern."""
+    cases = load_golden_sp24()
+    assert len(cases) == 4
+    for n_out, k, codes, want in cases:
+        T = np.zeros((n_out, k), np.int8)
+        for row, col, val in codes:
+            T[row, col] = val
+        P = oracle.pack_sp24(T)
+        assert P.size == (n_out + 63) // 64 * 64 * (k // 128) * 32
+        w = _sp24_words(P)
+        for i, got in enumerate(w):
+            exp = want.get(4 * i, 0x44444444 if i % 2 == 0 else 0)
+            assert got == exp, (n_out, k, codes, 4 * i, hex(got), hex(exp))
+        assert np.array_equal(oracle.unpack_sp24(P, n_out, k), T)
+
+
+@pytest.mark.parametrize("n_out,k", [(128, 256), (40, 384), (1, 128), (200, 896)])
+def test_sp24_round_trip_on_workload_codes(n_out, k):
+    W = synth.weights(n_out, k, seed=n_out * 7 + k)
+    mb = oracle.mask(W, 2, 4)
+    T = oracle.ternary(W, mb, oracle.gamma(W))
+    assert np.array_equal(oracle.unpack_sp24(oracle.pack_sp24(T), n_out, k), T)
+
+
+def test_sp24_round_trip_on_every_quad():
+    """All 33 quads a 2:4 code pattern allows (no, one or two nonzeros with
+    either sign) in every quad position, row tile, lane group and strip."""
+    quads = [np.zeros(4, np.int8)]
+    for a in range(4):
+        for va in (1, -1):
+            q = np.zeros(4, np.int8); q[a] = va; quads.append(q)
+            for b in range(a + 1, 4):
+                for vb in (1, -1):
+                    q2 = q.copy(); q2[b] = vb; quads.append(q2)
+    assert len(quads) == 33
+    rng = np.random.default_rng(5)
+    n_out, k = 130, 256
+    T = np.stack([quads[i] for i in rng.integers(0, 33, n_out * k // 4)]).reshape(n_out, k)
+    P = oracle.pack_sp24(T)
+    assert np.array_equal(oracle.unpack_sp24(P, n_out, k), T)
+
+
+def test_sp24_rejects_three_nonzeros_in_a_quad():
+    T = np.zeros((16, 128), np.int8)
+    T[3, 8:11] = (1, -1, 1)
+    with pytest.raises(ValueError):
+        oracle.pack_sp24(T)
+
+
+def test_sp24_unpack_adds_slots_that_share_a_position():
+    """Unpacking follows the sparse instruction: every stored element is
+    multiplied and added, so two slots at one position add up (the packer
+    never writes that; the definition still fixes what it means)."""
+    P = oracle.pack_sp24(np.zeros((16, 128), np.int8))
+    w = _sp24_words(P).copy()
+    w[0] = 0x44444440   # quad 0 of row 0: both slots at position 0
+    w[1] = 0x00000101   # e=0 and e=1 both +1
+    T = oracle.unpack_sp24(np.frombuffer(w.astype("<u4").tobytes(), np.uint8), 16, 128)
+    assert T[0, 0] == 2 and np.count_nonzero(T) == 1
+
+
+def test_sp24_contraction_equals_dense_codes():
+    """Contracting the unpacked layout reproduces the forward of the codes
+    themselves (the layout changes storage only)."""
+    W = synth.weights(64, 256, seed=9)
+    mb = oracle.mask(W, 2, 4)
+    g = oracle.gamma(W)
+    T = oracle.ternary(W, mb, g)
+    xq, sc = oracle.act_quant(synth.activations(5, 256, seed=10))
+    a1, y1 = oracle.fwd(xq, sc, T, g)
+    a2, y2 = oracle.fwd(xq, sc, oracle.unpack_sp24(oracle.pack_sp24(T), 64, 256), g)
+    assert np.array_equal(a1, a2) and np.array_equal(y1, y2)

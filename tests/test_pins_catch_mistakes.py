@@ -40,6 +40,10 @@ MUTANTS = {
     "layout_group_roles_swapped": ("int h = g / 8, q = (g % 8) / 2, e = g % 2;",
                                    "int h = g % 2, q = (g % 8) / 2, e = g / 8;"),
     "layout_chunks_transposed": ("* 64 + r16 + 16 * q;", "* 64 + q + 4 * r16;"),
+    "sp24_index_bits_reversed": ("idx |= (uint32_t)pos[sl] << (2 * e);", "idx |= (uint32_t)pos[sl] << (30 - 2 * e);"),
+    "sp24_value_codes_linear": ("val |= code << (8 * (e % 4) + 2 * (e / 4));", "val |= code << (2 * e);"),
+    "sp24_one_nonzero_slot": ("else { pos[1] = pos[0]; pos[0] = 0; }", "else { pos[1] = pos[0] == 3 ? 2 : 3; }"),
+    "sp24_lane_groups_swapped": ("(strip * nkb + kb) * 64 + rr % 16 + 16 * q", "(strip * nkb + kb) * 64 + q + 4 * (rr % 16)"),
 }
 
 
