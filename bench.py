@@ -588,6 +588,65 @@ def train_step(torch, bl, n, m, tokens=4096, iters=3):
     return {k2: round(v, 4) for k2, v in res.items()}
 
 
+def sweep_sp24(torch, bl, iters=20):
+    """2:4 prefill on the sparse int8 matrix instruction against the dense
+    int8 kernel on the same 2:4 codes and on 8:8 codes, at the Qwen2.5-1.5B
+    prefill shapes (2048 tokens) and the Qwen2.5-3B shapes at 512 and 4096
+    tokens; every point rotates over copies of its operands spanning more
+    than twice the Infinity Cache."""
+    from sparse_linear_layers_group_amd import synth
+    from sparse_linear_layers_group_amd.layer import BitLinearWeight, bf16_tensor
+    shapes = [("qwen15_gate", 8960, 1536, 2048, 3, 0), ("qwen15_down", 1536, 8960, 2048, 3, 2),
+              ("qwen3b_up", 11008, 2048, 512, 4, 0), ("qwen3b_up", 11008, 2048, 4096, 4, 0),
+              ("qwen3b_down", 2048, 11008, 512, 4, 1), ("qwen3b_down", 2048, 11008, 4096, 4, 1)]
+    out = {}
+    for name, n_out, k, tokens, cfg, li in shapes:
+        W = bf16_tensor(synth.weights(n_out, k, seed=0, config=cfg, layer=li))
+        X = bf16_tensor(synth.activations(tokens, k, seed=tokens, config=cfg, layer=li))
+        ops = 2 * tokens * n_out * k
+        res = {}
+        for label, (n, m), sparse in (("dense_8_8", (8, 8), False), ("dense_2_4", (2, 4), False),
+                                      ("smfmac_2_4", (2, 4), True)):
+            lw = BitLinearWeight(n_out, k, n, m)
+            lw.quantize(W)
+            bufs = lw.fwd_buffers(tokens)
+            bl.bitlinear_act_quant(X, tokens, k, bufs["xq"], bufs["x_scale"])
+            if sparse:
+                pk = torch.empty(bl.bitlinear_sp24_packed_bytes(n_out, k), dtype=torch.uint8, device="cuda")
+                bl.bitlinear_pack_sp24(W, lw.mask, lw.gamma, n_out, k, pk)
+                need = bl.bitlinear_sp24_workspace_bytes(tokens, k, n_out)
+                ws = torch.zeros(need, dtype=torch.uint8, device="cuda") if need else None
+            else:
+                pk, ws = lw.packed, bufs["ws"]
+            pool = [(pk.clone(), bufs["xq"].clone()) for _ in range(pool_copies(pk.numel() + tokens * k))]
+
+            def run(i, sparse=sparse, pool=pool, lw=lw, ws=ws, bufs=bufs, n=n, m=m):
+                p_, x_ = pool[i % len(pool)]
+                if sparse:
+                    bl.bitlinear_contract_sp24(x_, bufs["x_scale"], tokens, k, p_, n_out, lw.gamma, bufs["Y"], ws=ws)
+                else:
+                    bl.bitlinear_contract(x_, bufs["x_scale"], tokens, k, p_, n_out, n, m, lw.gamma, bufs["Y"],
+                                          ws=ws)
+
+            for i in range(3):
+                run(i)
+            torch.cuda.synchronize()
+            with Timer(torch, ahead_ms=0.3 * (iters + 3), pre=lambda: [run(i) for i in range(3)]) as t:
+                for i in range(iters):
+                    run(i)
+            us = 1000.0 * t.ms() / iters
+            tops = ops / (us * 1e-6) / 1e12
+            res[label] = {"kernel_us": round(us, 2), "tops_dense_equivalent": round(tops, 1),
+                          "frac_int8_dense_peak": round(tops / INT8_PEAK_TOPS, 4)}
+            del pool
+        res["smfmac_speedup_vs_dense_2_4"] = round(res["dense_2_4"]["kernel_us"] / res["smfmac_2_4"]["kernel_us"], 4)
+        res["smfmac_speedup_vs_dense_8_8"] = round(res["dense_8_8"]["kernel_us"] / res["smfmac_2_4"]["kernel_us"], 4)
+        out[f"{name}_{n_out}x{k}_T{tokens}"] = res
+        log(f"sp24 {name} T{tokens}: dense 8:8 {res['dense_8_8']['kernel_us']:.1f} us, dense 2:4 "
+            f"{res['dense_2_4']['kernel_us']:.1f} us, smfmac 2:4 {res['smfmac_2_4']['kernel_us']:.1f} us")
+    return out
+
+
 # --------------------------------------------------------------- CPU baseline
 def cpu_info():
     model = "unknown"
@@ -713,6 +772,8 @@ def main():
                 out["prefill_qwen15_6_8"] = prefill_step(torch, bl, 6, 8)
             elif sec == "train":
                 out["train_bitnet2b_6_8"] = train_step(torch, bl, 6, 8)
+            elif sec == "sp24":
+                out["sp24_prefill"] = sweep_sp24(torch, bl)
             elif sec == "sweep3b":
                 out["sweep_qwen3b"] = sweep_qwen3b(torch, bl)
             elif sec == "cpu":
@@ -815,6 +876,8 @@ def main():
         out["train_bitnet2b_6_8"] = train_step(torch, bl, 6, 8)
         log("qwen2.5-3b sweep ...")
         out["sweep_qwen3b"] = sweep_qwen3b(torch, bl)
+        log("2:4 on the sparse matrix instruction ...")
+        out["sp24_prefill"] = sweep_sp24(torch, bl)
     if not args.no_cpu_baseline:
         log("cpu baseline ...")
         out["cpu_baseline"] = cpu_baseline(6, 8)

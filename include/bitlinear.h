@@ -191,6 +191,53 @@ int bitlinear_contract(const int8_t *xq, const float *x_scale, int64_t tokens,
                        int m, const double *gamma, float *Y, int32_t *acc,
                        void *ws, size_t ws_bytes, void *stream);
 
+/* 2:4 on structured-sparse matrix hardware.  The Sparse-BitNet article
+ * (§七) ties N:M sparsity's speed-up to matrix units that skip the pruned
+ * half (2:4 sparse tensor cores); gfx950's counterpart is
+ * v_smfmac_i32_16x16x128_i8, whose sparse operand holds two values per four
+ * k plus a 2-bit position per value.  These calls store the 2:4 codes in
+ * that operand form and contract them at the sparse instruction's rate;
+ * the results are those of bitlinear_contract on the same codes.
+ *
+ * The sparse-operand + index layout (2 bits per weight): rows in strips of
+ * 64 (the last padded with zero codes), k in blocks of 128; superblock
+ * (strip p, block kb) at index p*(k/128) + kb holds 64 chunks of 32
+ * bytes; chunk c = r + 16q covers rows 64p + 16i + r (i = 0..3) over
+ * k = 128kb + 32q .. +31.  For row tile i, element e = 2u + s is slot s of
+ * quad u (k = 128kb + 32q + 4u .. +3): 32-bit word 2i of the chunk holds
+ * the slot's position in its quad at bits 2e..2e+1, word 2i+1 its code at
+ * bits 8(e%4) + 2(e/4) .. +1 (0 = 0, 1 = +1, 3 = -1).  A quad's two
+ * nonzero codes take the slots in position order; a single nonzero at
+ * position a takes slot 0 if a = 0 (slot 1: position 1, code 0), else
+ * slot 1 (slot 0: position 0, code 0); an all-zero quad has positions
+ * 0 and 1. */
+size_t bitlinear_sp24_packed_bytes(int64_t n_out, int64_t k);
+
+/* Workspace of bitlinear_contract_sp24 (split-k counters and int32 partial
+ * tiles for layers with few output tiles, as for the prefill kernel of
+ * bitlinear_contract); 0 means ws may be NULL. */
+size_t bitlinear_sp24_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out);
+
+/* Codes of a 2:4-masked layer in the sparse-operand layout.  W, mask and
+ * gamma as for bitlinear_pack with n:m = 2:4 (the codes are identical:
+ * kept by the mask and 2|W| > gamma); mask must be a 2:4 mask (a quad with
+ * more than two kept nonzero codes keeps only its first two).  packed_bytes
+ * must equal bitlinear_sp24_packed_bytes(n_out, k). */
+int bitlinear_pack_sp24(const uint16_t *W, const uint8_t *mask,
+                        const double *gamma, int64_t n_out, int64_t k,
+                        void *packed, size_t packed_bytes, void *stream);
+
+/* acc = x_q codes^T and Y = acc * gamma * s_t, as bitlinear_contract, for
+ * codes in the sparse-operand layout (any token count; one workgroup tile
+ * is 256 rows x 64 tokens).  ws: bitlinear_sp24_workspace_bytes() bytes,
+ * all zeros before its first use and returned to zero by every call (calls
+ * that overlap on one workspace race), or NULL when that is 0. */
+int bitlinear_contract_sp24(const int8_t *xq, const float *x_scale,
+                            int64_t tokens, int64_t k, const void *packed,
+                            int64_t n_out, const double *gamma, float *Y,
+                            int32_t *acc, void *ws, size_t ws_bytes,
+                            void *stream);
+
 /* Grouped decode: many BitLinear forwards with the same token count (1..16)
  * and N:M pattern in two launches (all activations, then all contractions),
  * e.g. the projections of several layers or of independent streams.  The

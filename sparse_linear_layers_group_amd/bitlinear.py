@@ -40,6 +40,10 @@ _SIGS = {
     "bitlinear_fwd": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_fwd_noalloc": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "bitlinear_sp24_packed_bytes": (_sz, [_i64, _i64]),
+    "bitlinear_sp24_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "bitlinear_pack_sp24": (_int, [_vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp]),
+    "bitlinear_contract_sp24": (_int, [_vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_act_quant": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "bitlinear_contract": (_int, [_vp, _vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_fwd_group_plan_bytes": (_sz, [_vp, _int, _i64]),
@@ -178,6 +182,34 @@ def bitlinear_fwd_noalloc(X, tokens, k, packed, n_out, n, m, gamma, Y, xq, x_sca
         _ptr(x_scale, (torch.float32,), tokens, "x_scale"),
         _ptr(acc, (torch.int32,), tokens * n_out, "acc", optional=True), _stream(stream))
     _check(st, "bitlinear_fwd_noalloc")
+
+
+def bitlinear_sp24_packed_bytes(n_out, k):
+    return int(lib().bitlinear_sp24_packed_bytes(int(n_out), int(k)))
+
+
+def bitlinear_sp24_workspace_bytes(tokens, k, n_out):
+    return int(lib().bitlinear_sp24_workspace_bytes(int(tokens), int(k), int(n_out)))
+
+
+def bitlinear_pack_sp24(W, mask, gamma, n_out, k, packed, packed_bytes=None, stream=None):
+    st = lib().bitlinear_pack_sp24(
+        _ptr(W, _BF16, n_out * k, "W"), _ptr(mask, (torch.uint8,), n_out * (k // 8), "mask"),
+        _ptr(gamma, (torch.float64,), 1, "gamma"), n_out, k, _ptr(packed, (torch.uint8,), None, "packed"),
+        packed.numel() if packed_bytes is None else int(packed_bytes), _stream(stream))
+    _check(st, "bitlinear_pack_sp24")
+
+
+def bitlinear_contract_sp24(xq, x_scale, tokens, k, packed, n_out, gamma, Y, acc=None, ws=None, ws_bytes=None,
+                            stream=None):
+    st = lib().bitlinear_contract_sp24(
+        _ptr(xq, (torch.int8,), tokens * k, "xq"), _ptr(x_scale, (torch.float32,), tokens, "x_scale"),
+        tokens, k, _ptr(packed, (torch.uint8,), None, "packed"), n_out, _ptr(gamma, (torch.float64,), 1, "gamma"),
+        _ptr(Y, (torch.float32,), tokens * n_out, "Y"),
+        _ptr(acc, (torch.int32,), tokens * n_out, "acc", optional=True),
+        _ptr(ws, (torch.uint8,), None, "ws", optional=True),
+        (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes), _stream(stream))
+    _check(st, "bitlinear_contract_sp24")
 
 
 def bitlinear_bwd_workspace_bytes(tokens, k, n_out):

@@ -316,6 +316,54 @@ int bitlinear_fwd_noalloc(const uint16_t* X, int64_t tokens, int64_t k, const vo
                        need ? kNoAllocScratchBytes : 0, stream);
 }
 
+size_t bitlinear_sp24_packed_bytes(int64_t n_out, int64_t k) {
+  if (n_out < 1 || k < 128 || k % 128 != 0 || n_out >= kLimit || k >= kLimit || n_out * k >= kLimit)
+    return 0;
+  return bl::sp24_packed_bytes(n_out, k);
+}
+
+size_t bitlinear_sp24_workspace_bytes(int64_t tokens, int64_t k, int64_t n_out) {
+  if (tokens < 1 || n_out < 1 || k < 128 || tokens >= kLimit || n_out >= kLimit) return 0;
+  return bl::gemm_ws_bytes(tokens, k, n_out);
+}
+
+int bitlinear_pack_sp24(const uint16_t* W, const uint8_t* mask, const double* gamma, int64_t n_out,
+                        int64_t k, void* packed, size_t packed_bytes, void* stream) {
+  TRY(check_layer(n_out, k));
+  TRY(check_ptr(W, 16, "W"));
+  TRY(check_ptr(mask, 16, "mask"));
+  TRY(check_ptr(gamma, 8, "gamma"));
+  TRY(check_ptr(packed, 16, "packed"));
+  const size_t need = bl::sp24_packed_bytes(n_out, k);
+  if (packed_bytes != need)
+    return fail(BL_ESHAPE, "packed_bytes must be %zu for this layer (got %zu)", need, packed_bytes);
+  hipError_t e = bl::launch_pack_sp24(W, mask, gamma, n_out, k, packed,
+                                      reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "sparse-operand pack launch");
+}
+
+int bitlinear_contract_sp24(const int8_t* xq, const float* x_scale, int64_t tokens, int64_t k,
+                            const void* packed, int64_t n_out, const double* gamma, float* Y,
+                            int32_t* acc, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_layer(n_out, k));
+  if (tokens < 0 || tokens >= kLimit || tokens * k >= kLimit || tokens * n_out >= kLimit)
+    return fail(BL_ESHAPE, "tokens must be >= 0 with tokens*k and tokens*n_out below 2^31");
+  if (tokens == 0) return ok();
+  TRY(check_ptr(xq, 16, "xq"));
+  TRY(check_ptr(x_scale, 4, "x_scale"));
+  TRY(check_ptr(packed, 16, "packed"));
+  TRY(check_ptr(gamma, 8, "gamma"));
+  TRY(check_ptr(Y, 16, "Y"));
+  TRY(check_opt_ptr(acc, 16, "acc"));
+  const size_t need = bl::gemm_ws_bytes(tokens, k, n_out);
+  if (need && (!ws || ws_bytes < need))
+    return fail(BL_EWORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws ? ws_bytes : (size_t)0);
+  if (need) TRY(check_ptr(ws, 16, "ws"));
+  hipError_t e = bl::launch_gemm_sp24(packed, xq, x_scale, gamma, Y, acc, ws, tokens, k, n_out,
+                                      reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "sparse contraction launch");
+}
+
 int bitlinear_act_quant(const uint16_t* X, int64_t tokens, int64_t k, int8_t* xq, float* x_scale,
                         void* stream) {
   if (k < 128 || k % 128 != 0)

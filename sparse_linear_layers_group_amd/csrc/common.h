@@ -66,6 +66,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 // MFMA operand types ---------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v8s __attribute__((ext_vector_type(8)));

@@ -47,6 +47,109 @@ __host__ __device__ constexpr int b_slot(int tt, int c) {
   return ((tt >> 4) * 2 + (c >> 2)) * 64 + (((tt & 15) ^ (2 * (c & 3) + 8 * (c >> 2))) + 16 * (c & 3));
 }
 
+// Split-k meeting and epilogue of one wavefront's 64-row x 16*kTT-token
+// tile (shared by the dense and the sparse-operand kernels): with several
+// parts, each part publishes its exact int32 tile (agent-scope stores: the
+// reader may sit on another XCD) and takes the (tile, wavefront) ticket;
+// the last part adds the others' tiles (agent-scope loads), writes Y and
+// returns the ticket to zero.  Lane l holds rows 64*strip + 16i +
+// 4*(l/16) + q of token t0 + 16j + l%16.
+template <int kTT>
+__device__ __forceinline__ void gemm_finish(v4i (&c)[kTT][4], bool live, int splits, int tile, int part,
+                                            int wave, int lane, int64_t strip, int64_t t0,
+                                            int64_t tokens, int64_t n_out,
+                                            const double* __restrict__ gamma,
+                                            const float* __restrict__ scale, float* __restrict__ Y,
+                                            int32_t* __restrict__ acc_out,
+                                            uint32_t* __restrict__ tickets,
+                                            v4i* __restrict__ partials) {
+  constexpr int BT = 16 * kTT;
+  if (!live) return;
+  if (splits > 1) {
+    // publish this part's tile (agent-scope stores: the reader may sit on
+    // another XCD), take the (tile, wavefront) ticket; the last part adds
+    // the others' tiles (agent-scope loads) and writes Y, then returns the
+    // ticket to zero
+    constexpr int kTileV4 = kTT * 4 * 64;  // v4i per wavefront tile
+    unsigned long long* own = reinterpret_cast<unsigned long long*>(
+        partials + ((size_t)(tile * splits + part) * kGStrips + wave) * kTileV4);
+#pragma unroll
+    for (int j = 0; j < kTT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const size_t e = 2 * ((size_t)(j * 4 + i) * 64 + lane);
+        st_agent_u64(own + e, (uint32_t)c[j][i][0] | ((unsigned long long)(uint32_t)c[j][i][1] << 32));
+        st_agent_u64(own + e + 1, (uint32_t)c[j][i][2] | ((unsigned long long)(uint32_t)c[j][i][3] << 32));
+      }
+    wait_memory_ops();
+    uint32_t t = 0;
+    if (lane == 0) t = atomic_fetch_add_global(&tickets[tile * kGStrips + wave], 1u);
+    t = __builtin_amdgcn_readfirstlane(t);
+    if (t != (uint32_t)splits - 1) return;
+    for (int z = 0; z < splits; ++z) {
+      if (z == part) continue;
+      const unsigned long long* other = reinterpret_cast<const unsigned long long*>(
+          partials + ((size_t)(tile * splits + z) * kGStrips + wave) * kTileV4);
+#pragma unroll
+      for (int j = 0; j < kTT; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const size_t e = 2 * ((size_t)(j * 4 + i) * 64 + lane);
+          const unsigned long long lo = ld_agent_u64(other + e), hi = ld_agent_u64(other + e + 1);
+          c[j][i] += v4i{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi,
+                         (int)(uint32_t)(hi >> 32)};
+        }
+    }
+    if (lane == 0) atomic_exchange_global(&tickets[tile * kGStrips + wave], 0u);
+  }
+  // epilogue: lane holds rows 64*strip + 16i + 4*(lane/16) + q of token
+  // t0 + 16j + lane%16
+  const double g = *gamma;
+  const int64_t r0 = strip * kStripRows + 4 * (lane >> 4);
+  if (t0 + BT <= tokens && strip * kStripRows + kStripRows <= n_out && (n_out & 3) == 0) {
+    // whole tile in range: 16-byte stores, no per-element checks; element
+    // offsets fit 32 bits (tokens * n_out < 2^31)
+    const uint32_t base = (uint32_t)(t0 + (lane & 15)) * (uint32_t)n_out + (uint32_t)r0;
+#pragma unroll
+    for (int j = 0; j < kTT; ++j) {
+      const float gs = out_scale(g, scale[t0 + 16 * j + (lane & 15)]);
+      const uint32_t o = base + (uint32_t)(16 * j) * (uint32_t)n_out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        st_stream(reinterpret_cast<v4f*>(Y + o + 16 * i),
+                  v4f{out_value(c[j][i][0], gs), out_value(c[j][i][1], gs),
+                      out_value(c[j][i][2], gs), out_value(c[j][i][3], gs)});
+        if (acc_out) st_global(reinterpret_cast<v4i*>(acc_out + o + 16 * i), c[j][i]);
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < kTT; ++j) {
+    const int64_t t = t0 + 16 * j + (lane & 15);
+    if (t >= tokens) continue;
+    const float gs = out_scale(g, scale[t]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r0 + 16 * i;
+      float* y = Y + t * n_out + r;
+      if (r + 4 <= n_out && (n_out & 3) == 0) {
+        st_global(reinterpret_cast<v4f*>(y),
+                  v4f{out_value(c[j][i][0], gs), out_value(c[j][i][1], gs),
+                      out_value(c[j][i][2], gs), out_value(c[j][i][3], gs)});
+        if (acc_out) st_global(reinterpret_cast<v4i*>(acc_out + t * n_out + r), c[j][i]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (r + q < n_out) {
+            st_global(y + q, out_value(c[j][i][q], gs));
+            if (acc_out) st_global(acc_out + t * n_out + r + q, (int32_t)c[j][i][q]);
+          }
+      }
+    }
+  }
+}
+
 template <int S, int BT>
 __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint32_t* __restrict__ packed,
                                                      const int8_t* __restrict__ xq,
@@ -274,90 +377,205 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
   if (kb + 3 < nkb) kblock(I1{}, I0{}, kb + 3);
   if (kb + 4 < nkb) kblock(I0{}, I1{}, kb + 4);
 
-  if (!live) return;
-  if (splits > 1) {
-    // publish this part's tile (agent-scope stores: the reader may sit on
-    // another XCD), take the (tile, wavefront) ticket; the last part adds
-    // the others' tiles (agent-scope loads) and writes Y, then returns the
-    // ticket to zero
-    constexpr int kTileV4 = kTT * 4 * 64;  // v4i per wavefront tile
-    unsigned long long* own = reinterpret_cast<unsigned long long*>(
-        partials + ((size_t)(tile * splits + part) * kGStrips + wave) * kTileV4);
+  gemm_finish<kTT>(c, live, splits, tile, part, wave, lane, strip, t0, tokens, n_out, gamma, scale, Y,
+                   acc_out, tickets, partials);
+}
+
+// ---------------------------------------------------------------------
+// 2:4 on the sparse int8 matrix instruction.  gfx950's
+// v_smfmac_i32_16x16x128_i8 multiplies a 16 x 128 operand that holds two
+// nonzeros per four k -- the structured sparsity the Sparse-BitNet article
+// (§七) points to in other vendors' sparse tensor cores -- stored as 16
+// values per lane plus a 2-bit position per value, at twice the dense
+// rate.  The weights come in the sparse-operand + index layout
+// (launch_pack_sp24): lane c of a (strip, k block) superblock loads its
+// 32-byte chunk, whose index words feed the instruction as they are and
+// whose value words (2-bit codes) become int8 operands with one v_perm per
+// four values.  Lane group q of an operand covers dense k [32q, 32q+32);
+// its partner in the B operand is k [16q, 16q+16) and [64+16q, 64+16q+16)
+// of the same lanes, i.e. the two B operands the dense kernel reads for its
+// two k halves, so the activation tile and its reads are the dense
+// kernel's.  Per k block a wavefront issues one sparse MFMA per (token
+// tile, row tile) -- half the dense kernel's count -- while it decodes the
+// next block's operands; chunks ride a four-slot register ring (the chunk
+// of block kb in slot kb % 4, loaded four blocks ahead).
+// ---------------------------------------------------------------------
+__device__ __forceinline__ v4i sp24_values(uint32_t val) {
+  // element e's code sits at bit 8(e%4) + 2(e/4): shifting by 2d brings the
+  // codes of elements 4d..4d+3 to the low bits of the four bytes, and each
+  // selects byte 0 (0x00), 1 (0x01) or 3 (0xff) of 0xff000100
+  v4i a;
 #pragma unroll
-    for (int j = 0; j < kTT; ++j)
+  for (int d = 0; d < 4; ++d)
+    a[d] = (int)__builtin_amdgcn_perm(0xff000100u, 0xff000100u, (val >> (2 * d)) & 0x03030303u);
+  return a;
+}
+
+template <int BT>
+__global__ __launch_bounds__(256, 2) void gemm_sp24_kernel(const uint32_t* __restrict__ packed,
+                                                          const int8_t* __restrict__ xq,
+                                                          const float* __restrict__ scale,
+                                                          const double* __restrict__ gamma,
+                                                          float* __restrict__ Y,
+                                                          int32_t* __restrict__ acc_out,
+                                                          int64_t tokens, int64_t k, int64_t n_out,
+                                                          int row_blocks, int token_blocks, int splits,
+                                                          uint32_t* __restrict__ tickets,
+                                                          v4i* __restrict__ partials) {
+  constexpr int kTT = BT / 16;
+  constexpr int kPieces = BT * 8 / 256;
+  constexpr int kChunk = 32;  // bytes per lane per k block
+  static_assert(kTT == 4, "one row tile of the next block is decoded per token-tile segment");
+  __shared__ __attribute__((aligned(16))) v4i Bs[2][kTT * 2 * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nblk = row_blocks * token_blocks;
+  const int nwork = nblk * splits;
+  const int per_xcd = (nwork + 7) / 8;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int full = nwork - (per_xcd - 1) * 8;
+  const int logical = xcd < full ? xcd * per_xcd + slot
+                                 : full * per_xcd + (xcd - full) * (per_xcd - 1) + slot;
+  if (slot >= (xcd < full ? per_xcd : per_xcd - 1)) return;
+  const int part = logical / nblk, tile = logical - part * nblk;
+  const int rb = tile % row_blocks, tb = tile / row_blocks;
+
+  const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
+  const int64_t strip = (int64_t)rb * kGStrips + wave;
+  const int64_t t0 = (int64_t)tb * BT;
+  const int nkb_all = (int)(k / kBlockK);
+  const int kb0 = (int)((int64_t)part * nkb_all / splits);
+  const int nkb = (int)((int64_t)(part + 1) * nkb_all / splits) - kb0;
+
+  const __amdgpu_buffer_rsrc_t xr = g_rsrc(xq, tokens * k);
+  uint32_t x_off[kPieces];
+  int x_slot[kPieces];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const size_t e = 2 * ((size_t)(j * 4 + i) * 64 + lane);
-        st_agent_u64(own + e, (uint32_t)c[j][i][0] | ((unsigned long long)(uint32_t)c[j][i][1] << 32));
-        st_agent_u64(own + e + 1, (uint32_t)c[j][i][2] | ((unsigned long long)(uint32_t)c[j][i][3] << 32));
-      }
-    wait_memory_ops();
-    uint32_t t = 0;
-    if (lane == 0) t = atomic_fetch_add_global(&tickets[tile * kGStrips + wave], 1u);
-    t = __builtin_amdgcn_readfirstlane(t);
-    if (t != (uint32_t)splits - 1) return;
-    for (int z = 0; z < splits; ++z) {
-      if (z == part) continue;
-      const unsigned long long* other = reinterpret_cast<const unsigned long long*>(
-          partials + ((size_t)(tile * splits + z) * kGStrips + wave) * kTileV4);
-#pragma unroll
-      for (int j = 0; j < kTT; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const size_t e = 2 * ((size_t)(j * 4 + i) * 64 + lane);
-          const unsigned long long lo = ld_agent_u64(other + e), hi = ld_agent_u64(other + e + 1);
-          c[j][i] += v4i{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi,
-                         (int)(uint32_t)(hi >> 32)};
-        }
-    }
-    if (lane == 0) atomic_exchange_global(&tickets[tile * kGStrips + wave], 0u);
+  for (int r = 0; r < kPieces; ++r) {
+    const int q = tid + 256 * r, tt = q >> 3, c = q & 7;
+    x_off[r] = t0 + tt < tokens ? (uint32_t)((t0 + tt) * k + 16 * c) : kGOOB;
+    x_slot[r] = b_slot(tt, c);
   }
-  // epilogue: lane holds rows 64*strip + 16i + 4*(lane/16) + q of token
-  // t0 + 16j + lane%16
-  const double g = *gamma;
-  const int64_t r0 = strip * kStripRows + 4 * (lane >> 4);
-  if (t0 + BT <= tokens && strip * kStripRows + kStripRows <= n_out && (n_out & 3) == 0) {
-    // whole tile in range: 16-byte stores, no per-element checks; element
-    // offsets fit 32 bits (tokens * n_out < 2^31)
-    const uint32_t base = (uint32_t)(t0 + (lane & 15)) * (uint32_t)n_out + (uint32_t)r0;
+  int b_rd[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) b_rd[h] = b_slot(lane & 15, (lane >> 4) + 4 * h);
+
+  // out-of-range loads (blocks past the last, strips past the layer) read
+  // zeros through the buffer range: no guards, no branches
+  const __amdgpu_buffer_rsrc_t pr = g_rsrc(packed, strips * nkb_all * kStripRows * kChunk);
+  const bool live = strip < strips;
+  const uint32_t c_base = live ? (uint32_t)((strip * nkb_all * kStripRows + lane) * kChunk) : kGOOB;
+
+  auto load_x = [&](int kb, u32x4* dst) {
+#pragma unroll
+    for (int r = 0; r < kPieces; ++r)
+      dst[r] = __builtin_amdgcn_raw_buffer_load_b128(xr, x_off[r] + (uint32_t)((kb0 + kb) * kBlockK),
+                                                     0, 0);
+  };
+  auto load_chunk = [&](int kb, uint32_t* dst) {
+    const uint32_t o = c_base + (uint32_t)(kb0 + kb) * (uint32_t)(kStripRows * kChunk);
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(pr, o, 0, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(pr, o + 16, 0, 0);
+    dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
+    dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
+  };
+
+  v4i c[kTT][4];
+#pragma unroll
+  for (int j = 0; j < kTT; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[j][i] = v4i{0, 0, 0, 0};
+
+  u32x4 xv[2][kPieces];
+  uint32_t w[4][8];       // chunk ring: block kb in w[kb % 4]
+  v4i a[2][4];            // operands of the current and the next block (set kb % 2)
+  int ix[2][4];           // their index words
+
+  load_x(0, xv[0]);
+  load_chunk(0, w[0]);
+  load_chunk(1, w[1]);
+  load_chunk(2, w[2]);
+  load_chunk(3, w[3]);
+  load_x(1, xv[1]);
+#pragma unroll
+  for (int r = 0; r < kPieces; ++r) Bs[0][x_slot[r]] = (v4i)xv[0][r];
+  load_x(2, xv[0]);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[0][i] = sp24_values(w[0][2 * i + 1]);
+    ix[0][i] = (int)w[0][2 * i];
+  }
+
+  // block kb: LDS stage and operand set P = kb % 2, chunk slot R = kb % 4
+  auto kblock = [&](auto parity, auto ring, int kb) {
+    constexpr int P = decltype(parity)::value;
+    constexpr int R = decltype(ring)::value;
+    load_chunk(kb + 4, w[R]);  // block kb's chunk was decoded during block kb-1
+    const uint32_t* wn = w[(R + 1) % 4];
+    v4i b0 = Bs[P][b_rd[0]], b1 = Bs[P][b_rd[1]];
 #pragma unroll
     for (int j = 0; j < kTT; ++j) {
-      const float gs = out_scale(g, scale[t0 + 16 * j + (lane & 15)]);
-      const uint32_t o = base + (uint32_t)(16 * j) * (uint32_t)n_out;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        st_stream(reinterpret_cast<v4f*>(Y + o + 16 * i),
-                  v4f{out_value(c[j][i][0], gs), out_value(c[j][i][1], gs),
-                      out_value(c[j][i][2], gs), out_value(c[j][i][3], gs)});
-        if (acc_out) st_global(reinterpret_cast<v4i*>(acc_out + o + 16 * i), c[j][i]);
+      v4i n0 = b0, n1 = b1;
+      if (j + 1 < kTT) {
+        n0 = Bs[P][b_rd[0] + 128 * (j + 1)];
+        n1 = Bs[P][b_rd[1] + 128 * (j + 1)];
       }
+      const v8i b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        c[j][i] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a[P][i], b, c[j][i], ix[P][i], 0, 0);
+      // side work: row tile j of the next block, this thread's activation
+      // pieces of the next block into the other stage, the loads of kb+3
+      a[P ^ 1][j] = sp24_values(wn[2 * j + 1]);
+      ix[P ^ 1][j] = (int)wn[2 * j];
+      if (j < kPieces) Bs[P ^ 1][x_slot[j]] = (v4i)xv[P ^ 1][j];
+      if (j == kTT / 2) load_x(kb + 3, xv[P ^ 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      b0 = n0;
+      b1 = n1;
     }
-    return;
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  int kb = 0;
+  for (; kb + 3 < nkb; kb += 4) {
+    kblock(I0{}, I0{}, kb);
+    kblock(I1{}, I1{}, kb + 1);
+    kblock(I0{}, I2{}, kb + 2);
+    kblock(I1{}, I3{}, kb + 3);
   }
-#pragma unroll
-  for (int j = 0; j < kTT; ++j) {
-    const int64_t t = t0 + 16 * j + (lane & 15);
-    if (t >= tokens) continue;
-    const float gs = out_scale(g, scale[t]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r = r0 + 16 * i;
-      float* y = Y + t * n_out + r;
-      if (r + 4 <= n_out && (n_out & 3) == 0) {
-        st_global(reinterpret_cast<v4f*>(y),
-                  v4f{out_value(c[j][i][0], gs), out_value(c[j][i][1], gs),
-                      out_value(c[j][i][2], gs), out_value(c[j][i][3], gs)});
-        if (acc_out) st_global(reinterpret_cast<v4i*>(acc_out + t * n_out + r), c[j][i]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (r + q < n_out) {
-            st_global(y + q, out_value(c[j][i][q], gs));
-            if (acc_out) st_global(acc_out + t * n_out + r + q, (int32_t)c[j][i][q]);
-          }
-      }
-    }
-  }
+  if (kb < nkb) kblock(I0{}, I0{}, kb);
+  if (kb + 1 < nkb) kblock(I1{}, I1{}, kb + 1);
+  if (kb + 2 < nkb) kblock(I0{}, I2{}, kb + 2);
+
+  gemm_finish<kTT>(c, live, splits, tile, part, wave, lane, strip, t0, tokens, n_out, gamma, scale, Y,
+                   acc_out, tickets, partials);
+}
+
+hipError_t launch_gemm_sp24(const void* packed, const int8_t* xq, const float* scale,
+                            const double* gamma, float* Y, int32_t* acc, void* ws, int64_t tokens,
+                            int64_t k, int64_t n_out, hipStream_t s) {
+  constexpr int BT = kGemmTileTokens;
+  static_assert(kGemmTileRows == kGStrips * kStripRows, "tile rows");
+  const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
+  const int row_blocks = (int)((strips + kGStrips - 1) / kGStrips);
+  const int token_blocks = (int)((tokens + BT - 1) / BT);
+  const int splits = gemm_splits(tokens, k, n_out);
+  if (splits > 1 && !ws) return hipErrorInvalidValue;
+  uint32_t* tickets = splits > 1 ? reinterpret_cast<uint32_t*>(ws) : nullptr;
+  v4i* partials = splits > 1 ? reinterpret_cast<v4i*>(reinterpret_cast<char*>(ws) +
+                                                      gemm_ticket_bytes(tokens, n_out))
+                             : nullptr;
+  const int nwork = row_blocks * token_blocks * splits;
+  gemm_sp24_kernel<BT><<<(unsigned)((nwork + 7) / 8 * 8), 256, 0, s>>>(
+      reinterpret_cast<const uint32_t*>(packed), xq, scale, gamma, Y, acc, tokens, k, n_out,
+      row_blocks, token_blocks, splits, tickets, partials);
+  return hipGetLastError();
 }
 
 template <int S>

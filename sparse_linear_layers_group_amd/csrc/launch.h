@@ -82,6 +82,14 @@ hipError_t launch_ternary_pack(const uint16_t* W, const uint8_t* mask, const dou
                                int64_t n_out, int64_t k, int S, void* packed, int8_t* wq,
                                hipStream_t s);
 
+// 2:4 codes in the sparse-operand + index layout: 32 bytes per chunk, one
+// chunk per (strip, 128-wide k block, lane)
+inline size_t sp24_packed_bytes(int64_t n_out, int64_t k) {
+  return (size_t)((n_out + 63) / 64) * 64 * (size_t)(k / 128) * 32;
+}
+hipError_t launch_pack_sp24(const uint16_t* W, const uint8_t* mask, const double* gamma,
+                            int64_t n_out, int64_t k, void* packed, hipStream_t s);
+
 // per-token int8 activations; also zero-fills zero_bytes of zero_ws
 // latent-weight update: Wm = RN32(Wm - lr * dW) (one fused rounding), W =
 // bf16 (nearest, ties to even) of the result; count a multiple of 8
@@ -258,6 +266,13 @@ inline size_t gemm_ws_bytes(int64_t tokens, int64_t k, int64_t n_out) {
 hipError_t launch_gemm(const void* packed, const int8_t* xq, const float* scale,
                        const double* gamma, float* Y, int32_t* acc, void* ws, int64_t tokens,
                        int64_t k, int64_t n_out, int S, hipStream_t s);
+
+// Prefill-shaped contraction of 2:4 codes in the sparse-operand + index
+// layout on the sparse int8 matrix instruction; same tiles, split-k and
+// workspace as launch_gemm
+hipError_t launch_gemm_sp24(const void* packed, const int8_t* xq, const float* scale,
+                            const double* gamma, float* Y, int32_t* acc, void* ws, int64_t tokens,
+                            int64_t k, int64_t n_out, hipStream_t s);
 
 // Backward.  Workspace (bf16 operands of the two products, each region
 // 256-byte aligned): (dY * s)^T [n_out x tp], x_q^T [k x tp] with tp the

@@ -623,6 +623,92 @@ __global__ __launch_bounds__(256) void ternary_pack_kernel(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------
+// 2:4 codes in the sparse-operand + index layout (the operand form of the
+// gfx950 sparse int8 matrix instruction).  One thread per 32-byte chunk:
+// chunk c = r + 16q of superblock (strip, kb) holds rows 16i + r of the
+// strip over k = 128kb + 32q .. +31, per row tile i an index word (2 bits
+// per element: the slot's position in its quad) and a value word (2 bits
+// per element at bit 8(e%4) + 2(e/4): 0, 1 = +1, 3 = -1), element e =
+// 2u + s for quad u, slot s.  A quad's slots: its two nonzero codes in
+// position order; one nonzero at a: (0, 1) if a = 0, else (0, a) with the
+// code in slot 1; none: (0, 1).  The codes are those of the dense format
+// (kept by the mask and 2|W| > gamma); a quad with more than two kept
+// nonzero codes (a mask that is not 2:4) keeps its first two.
+// ---------------------------------------------------------------------
+__device__ __forceinline__ void sp24_quad(uint32_t nz, uint32_t neg, int u, uint32_t& idx,
+                                          uint32_t& val) {
+  uint32_t p0 = 0, p1 = 1, c0 = 0, c1 = 0;
+  if (nz) {
+    const uint32_t a = __builtin_ctz(nz), rest = nz & (nz - 1);
+    const uint32_t ca = ((neg >> a) & 1u) ? 3u : 1u;
+    if (rest) {
+      const uint32_t b = __builtin_ctz(rest);
+      p0 = a; p1 = b; c0 = ca; c1 = ((neg >> b) & 1u) ? 3u : 1u;
+    } else if (a == 0) {
+      c0 = ca;
+    } else {
+      p1 = a; c1 = ca;
+    }
+  }
+  const int e0 = 2 * u, e1 = 2 * u + 1;
+  idx |= (p0 << (2 * e0)) | (p1 << (2 * e1));
+  val |= (c0 << (8 * (e0 & 3) + 2 * (e0 >> 2))) | (c1 << (8 * (e1 & 3) + 2 * (e1 >> 2)));
+}
+
+__global__ __launch_bounds__(256) void pack_sp24_kernel(const uint16_t* __restrict__ W,
+                                                       const uint8_t* __restrict__ mask,
+                                                       const double* __restrict__ gamma,
+                                                       int64_t n_out, int64_t k,
+                                                       uint32_t* __restrict__ packed) {
+  const int64_t chunk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nkb = k / kBlockK;
+  const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
+  if (chunk >= strips * nkb * kStripRows) return;
+  const int64_t sb = chunk / kStripRows;
+  const int c = (int)(chunk - sb * kStripRows);
+  const int64_t strip = sb / nkb, kb = sb - strip * nkb;
+  const int r = c & 15, q = c >> 4;
+  const uint32_t thr = code_threshold(*gamma);
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = strip * kStripRows + 16 * i + r;
+    uint32_t idx = 0, val = 0;
+    uint32_t nz = 0, neg = 0;  // 32 positions of the row's k slice
+    if (row < n_out) {
+      const uint16_t* w = W + row * k + kb * kBlockK + 32 * q;
+      const uint32_t keep = *reinterpret_cast<const uint32_t*>(mask + row * (k / 8) + kb * 16 + 4 * q);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint4 v = reinterpret_cast<const uint4*>(w)[g];
+        const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t h = (ws[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+          const uint32_t on = ((keep >> (8 * g + j)) & 1u) & ((h & 0x7fffu) >= thr ? 1u : 0u);
+          nz |= on << (8 * g + j);
+          neg |= (on & (h >> 15)) << (8 * g + j);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sp24_quad((nz >> (4 * u)) & 15u, (neg >> (4 * u)) & 15u, u, idx, val);
+    out[2 * i] = idx;
+    out[2 * i + 1] = val;
+  }
+  uint4* dst = reinterpret_cast<uint4*>(packed + chunk * 8);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
+hipError_t launch_pack_sp24(const uint16_t* W, const uint8_t* mask, const double* gamma,
+                            int64_t n_out, int64_t k, void* packed, hipStream_t s) {
+  const unsigned blocks = (unsigned)pack_blocks(n_out, k);
+  pack_sp24_kernel<<<blocks, 256, 0, s>>>(W, mask, gamma, n_out, k, reinterpret_cast<uint32_t*>(packed));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------
 // Grouped weight quantisation (several layers per launch).  Each launch
 // has a fixed grid; workgroup g takes the plan's workgroups g, g + grid, ...
 // and finds their layer in the plan's owner table.  Every workgroup of a

@@ -139,6 +139,27 @@ def test_fwd_noalloc_validation(L):
     assert "static scratch" in bl.bitlinear_last_error()
 
 
+@pytest.mark.parametrize("n_out,k", [(128, 256), (40, 384), (11008, 2048), (1, 128)])
+def test_sp24_sizes_match_layout_definition(L, n_out, k):
+    assert bl.bitlinear_sp24_packed_bytes(n_out, k) == oracle.sp24_packed_bytes(n_out, k)
+
+
+def test_sp24_validation(L):
+    assert bl.bitlinear_sp24_packed_bytes(128, 100) == 0
+    nb = bl.bitlinear_sp24_packed_bytes(128, 256)
+    p = L.bitlinear_pack_sp24
+    assert p(A, A, A, 128, 256, A, nb - 16, None) == bl.BL_ESHAPE
+    assert p(A, None, A, 128, 256, A, nb, None) == bl.BL_EINVAL
+    assert p(A, A, A, 128, 250, A, nb, None) == bl.BL_ESHAPE
+    c = L.bitlinear_contract_sp24
+    assert c(A, A, 4, 250, A, 128, A, A, None, None, 0, None) == bl.BL_ESHAPE
+    assert c(None, A, 4, 256, A, 128, A, A, None, None, 0, None) == bl.BL_EINVAL
+    assert c(None, None, 0, 256, None, 128, None, None, None, None, 0, None) == bl.BL_OK
+    need = bl.bitlinear_sp24_workspace_bytes(512, 1024, 1536)
+    assert need > 0
+    assert c(A, A, 512, 1024, A, 1536, A, A, None, None, 0, None) == bl.BL_EWORKSPACE
+
+
 def test_status_strings(L):
     for s in range(6):
         assert bl.bitlinear_status_string(s)
