@@ -673,8 +673,8 @@ int bitlinear_bwd(const uint16_t* dY, const int8_t* xq, const float* x_scale, co
   if (tokens == 0) {
     // no tokens: dX is empty and dW is all zeros (no workspace needed)
     if (dW) {
-      hipError_t e = bl::launch_bwd_dw(nullptr, nullptr, nullptr, dW, nullptr, 0, k, n_out,
-                                       reinterpret_cast<hipStream_t>(stream));
+      hipError_t e = bl::launch_bwd(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dW, nullptr,
+                                    0, k, n_out, bl::s_of(n, m), reinterpret_cast<hipStream_t>(stream));
       return hip_status(e, "dW clear");
     }
     return ok();
@@ -699,17 +699,9 @@ int bitlinear_bwd(const uint16_t* dY, const int8_t* xq, const float* x_scale, co
     TRY(check_ptr(xq, 16, "xq"));
     TRY(check_ptr(x_scale, 4, "x_scale"));
   }
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dX) {
-    hipError_t e =
-        bl::launch_bwd_dx(dY, packed, gamma, dX, ws, tokens, k, n_out, bl::s_of(n, m), s);
-    if (e != hipSuccess) return hip_status(e, "dX launch");
-  }
-  if (dW) {
-    hipError_t e = bl::launch_bwd_dw(dY, xq, x_scale, dW, ws, tokens, k, n_out, s);
-    if (e != hipSuccess) return hip_status(e, "dW launch");
-  }
-  return ok();
+  hipError_t e = bl::launch_bwd(dY, xq, x_scale, packed, gamma, dX, dW, ws, tokens, k, n_out,
+                                bl::s_of(n, m), reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "backward launch");
 }
 
 const char* bitlinear_status_string(int status) {

@@ -19,6 +19,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <utility>
+
 #include <type_traits>
 
 namespace bl {
@@ -169,24 +171,60 @@ __global__ __launch_bounds__(64) void prep_codes_t_kernel(const uint32_t* __rest
 constexpr int kBP = 80;
 constexpr int kGroupM = 8;
 
-__global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(
-    const uint16_t* __restrict__ A, int64_t lda, const uint16_t* __restrict__ B, int64_t ldb,
-    float* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-    const double* __restrict__ alpha, int64_t klen) {
+// One product of a launch: C[M][N] (row pitch ldc) = alpha * A B^T over a
+// k range of klen (split launches: plane blockIdx.y of C).
+struct NtProblem {
+  const uint16_t* A;
+  const uint16_t* B;
+  float* C;
+  const double* alpha;
+  int64_t lda, ldb, ldc, M, N, K, klen;
+};
+
+__host__ __device__ inline int64_t nt_tiles(const NtProblem& p) {
+  return ((p.M + 127) / 128) * ((p.N + 127) / 128);
+}
+
+// XCD share of a problem's tiles: XCD x runs tiles [start, start + cnt)
+__device__ __forceinline__ void xcd_share(int64_t T, int64_t x, int64_t& start, int64_t& cnt) {
+  const int64_t per = (T + 7) / 8, full = T - (per - 1) * 8;  // XCDs that get `per` tiles
+  cnt = T == 0 ? 0 : (x < full ? per : per - 1);
+  start = T == 0 ? 0 : (x < full ? x * per : full * per + (x - full) * (per - 1));
+}
+
+// A launch runs one or two independent products (the dX and dW of a
+// layer): the tiles of each are shared out over the 8 XCDs separately, so
+// every XCD runs the same mix of the two (tiles of different k depth cost
+// different times), the first problem's first within an XCD.  Two
+// products in one launch fill the partly used last round of each with
+// tiles of the other.
+__global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(NtProblem p0, NtProblem p1) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][128 * kBP];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][128 * kBP];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int64_t tiles_m = (M + 127) / 128, tiles_n = (N + 127) / 128;
-  int64_t m0, n0;
+  int64_t m0, n0, t;
+  bool second;
   {
-    const int64_t T = tiles_m * tiles_n, per = (T + 7) / 8;
     const int64_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int64_t full = T - (per - 1) * 8;  // XCDs that get `per` tiles
-    if (slot >= (xcd < full ? per : per - 1)) return;
-    const int64_t t = xcd < full ? xcd * per + slot : full * per + (xcd - full) * (per - 1) + slot;
+    int64_t s0, c0, s1, c1;
+    xcd_share(nt_tiles(p0), xcd, s0, c0);
+    xcd_share(nt_tiles(p1), xcd, s1, c1);
+    if (slot >= c0 + c1) return;
+    second = slot >= c0;
+    t = second ? s1 + slot - c0 : s0 + slot;
+  }
+  const NtProblem& pr = second ? p1 : p0;
+  const uint16_t* __restrict__ A = pr.A;
+  const uint16_t* __restrict__ B = pr.B;
+  float* __restrict__ C = pr.C;
+  const double* __restrict__ alpha = pr.alpha;
+  const int64_t lda = pr.lda, ldb = pr.ldb, ldc = pr.ldc, M = pr.M, N = pr.N, klen = pr.klen;
+  int64_t K = pr.K;
+  {
+    const int64_t tiles_m = (M + 127) / 128, tiles_n = (N + 127) / 128;
     const int64_t g = t / (kGroupM * tiles_n), r = t - g * kGroupM * tiles_n;
     const int64_t gm = tiles_m - g * kGroupM < kGroupM ? tiles_m - g * kGroupM : kGroupM;
     m0 = (g * kGroupM + r % gm) * 128;
@@ -344,30 +382,63 @@ __global__ void zero_f32_kernel(float* __restrict__ p, int64_t n) {
 }
 
 // ------------------------------------------------------------- launchers
-// C has row pitch ldc = N when the product is split (the partial planes in
-// `partials`, M * N floats each)
-static hipError_t gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
-                          int64_t ldc, int64_t M, int64_t N, int64_t K, const double* alpha,
-                          float* partials, hipStream_t s) {
-  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  const unsigned gx = (unsigned)((tiles + 7) / 8 * 8);
-  const int splits = bwd_splits(M, N, K);
-  if (splits == 1) {
-    gemm_nt_bf16_kernel<<<gx, 256, 0, s>>>(A, lda, B, ldb, C, ldc, M, N, K, alpha, K);
-    return hipGetLastError();
-  }
-  const int64_t klen = bwd_split_len(K, splits);
-  const int used = (int)((K + klen - 1) / klen);
-  gemm_nt_bf16_kernel<<<dim3(gx, (unsigned)used), 256, 0, s>>>(A, lda, B, ldb, partials, N, M, N, K,
-                                                               nullptr, klen);
-  const int64_t n4 = M * N / 4;
+// A product with few tiles and a deep k range runs split along k: its
+// planes go to `partials` (row pitch N, M * N floats each) and
+// split_sum_kernel adds them in order into C.
+static hipError_t gemm_nt_split(NtProblem p, float* partials, hipStream_t s) {
+  const int splits = bwd_splits(p.M, p.N, p.K);
+  const int64_t klen = bwd_split_len(p.K, splits);
+  const int used = (int)((p.K + klen - 1) / klen);
+  float* C = p.C;
+  const double* alpha = p.alpha;
+  p.C = partials;
+  p.ldc = p.N;
+  p.alpha = nullptr;
+  p.klen = klen;
+  NtProblem none = p;
+  none.M = 0;  // no tiles
+  const unsigned gx = (unsigned)((nt_tiles(p) + 7) / 8 * 8);
+  gemm_nt_bf16_kernel<<<dim3(gx, (unsigned)used), 256, 0, s>>>(p, none);
+  const int64_t n4 = p.M * p.N / 4;
   const int64_t blocks = (n4 + 255) / 256;
   split_sum_kernel<<<(unsigned)(blocks < 2048 ? blocks : 2048), 256, 0, s>>>(partials, used, n4, alpha, C);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dx(const uint16_t* dY, const void* packed, const double* gamma, float* dX,
-                         void* ws, int64_t tokens, int64_t k, int64_t n_out, int S, hipStream_t s) {
+// The products that are not split run in one launch (a null `b` is no
+// second product); split ones follow, one after the other (they share the
+// partial planes).
+static hipError_t gemm_nt_run(const NtProblem* a, const NtProblem* b, float* partials, hipStream_t s) {
+  const NtProblem* whole[2] = {nullptr, nullptr};
+  const NtProblem* split[2] = {nullptr, nullptr};
+  int nw = 0, ns = 0;
+  for (const NtProblem* p : {a, b}) {
+    if (!p) continue;
+    if (bwd_splits(p->M, p->N, p->K) > 1) split[ns++] = p;
+    else whole[nw++] = p;
+  }
+  if (nw) {
+    NtProblem p0 = *whole[0], p1 = p0;
+    if (nw == 2) {
+      p1 = *whole[1];
+      if (p1.K > p0.K) std::swap(p0, p1);  // the deeper product first within each XCD
+    } else {
+      p1.M = 0;  // no tiles
+    }
+    const int64_t per = (nt_tiles(p0) + 7) / 8 + (nt_tiles(p1) + 7) / 8;
+    gemm_nt_bf16_kernel<<<(unsigned)(8 * per), 256, 0, s>>>(p0, p1);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  for (int i = 0; i < ns; ++i) {
+    hipError_t e = gemm_nt_split(*split[i], partials, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
+
+static hipError_t prep_dx(const void* packed, void* ws, int64_t tokens, int64_t k, int64_t n_out, int S,
+                          hipStream_t s) {
   const int64_t nkb = k / kBlockK, strips = (n_out + kStripRows - 1) / kStripRows;
   const int64_t np = strips * kStripRows;
   uint16_t* codes_t = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + bwd_codes_offset(tokens, k, n_out));
@@ -377,19 +448,20 @@ hipError_t launch_bwd_dx(const uint16_t* dY, const void* packed, const double* g
   else if (S == 6) prep_codes_t_kernel<6><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
   else if (S == 2) prep_codes_t_kernel<2><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
   else prep_codes_t_kernel<4><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // dX [tokens x k] = gamma * dY [tokens x n_out] . codes^T [k x n_out]^T
-  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + bwd_partial_offset(tokens, k, n_out));
-  return gemm_nt(dY, n_out, codes_t, np, dX, k, tokens, k, n_out, gamma, partials, s);
+  return hipGetLastError();
 }
 
-hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* xq, const float* scale, float* dW,
-                         void* ws, int64_t tokens, int64_t k, int64_t n_out, hipStream_t s) {
-  if (tokens == 0) {
-    zero_f32_kernel<<<1024, 256, 0, s>>>(dW, n_out * k);
-    return hipGetLastError();
-  }
+// dX [tokens x k] = gamma * dY [tokens x n_out] . codes^T [k x n_out]^T
+static NtProblem dx_problem(const uint16_t* dY, const double* gamma, float* dX, void* ws, int64_t tokens,
+                            int64_t k, int64_t n_out) {
+  const int64_t np = (n_out + kStripRows - 1) / kStripRows * kStripRows;
+  const uint16_t* codes_t =
+      reinterpret_cast<const uint16_t*>(reinterpret_cast<char*>(ws) + bwd_codes_offset(tokens, k, n_out));
+  return NtProblem{dY, codes_t, dX, gamma, n_out, np, k, tokens, k, n_out, n_out};
+}
+
+static hipError_t prep_dw(const uint16_t* dY, const int8_t* xq, const float* scale, void* ws,
+                          int64_t tokens, int64_t k, int64_t n_out, hipStream_t s) {
   const int64_t tp = bwd_tokens_padded(tokens);
   char* w = reinterpret_cast<char*>(ws);
   uint16_t* dys_t = reinterpret_cast<uint16_t*>(w + bwd_dys_offset(tokens, k, n_out));
@@ -398,11 +470,34 @@ hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* xq, const float* scal
       dY, scale, tokens, n_out, tp, dys_t);
   prep_xq_t_kernel<<<dim3((unsigned)(tp / 64), (unsigned)(k / 64)), 256, 0, s>>>(xq, tokens, k, tp,
                                                                               xq_t);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+// dW [n_out x k] = (dY s)^T [n_out x tp] . x_q^T [k x tp]^T
+static NtProblem dw_problem(float* dW, void* ws, int64_t tokens, int64_t k, int64_t n_out) {
+  const int64_t tp = bwd_tokens_padded(tokens);
+  char* w = reinterpret_cast<char*>(ws);
+  return NtProblem{reinterpret_cast<const uint16_t*>(w + bwd_dys_offset(tokens, k, n_out)),
+                   reinterpret_cast<const uint16_t*>(w + bwd_xq_offset(tokens, k, n_out)),
+                   dW, nullptr, tp, tp, k, n_out, k, tp, tp};
+}
+
+hipError_t launch_bwd(const uint16_t* dY, const int8_t* xq, const float* scale, const void* packed,
+                      const double* gamma, float* dX, float* dW, void* ws, int64_t tokens, int64_t k,
+                      int64_t n_out, int S, hipStream_t s) {
+  if (tokens == 0) {  // dX is empty; dW is all zeros
+    if (dW) zero_f32_kernel<<<1024, 256, 0, s>>>(dW, n_out * k);
+    return hipGetLastError();
+  }
+  hipError_t e = hipSuccess;
+  if (dX) e = prep_dx(packed, ws, tokens, k, n_out, S, s);
+  if (e == hipSuccess && dW) e = prep_dw(dY, xq, scale, ws, tokens, k, n_out, s);
   if (e != hipSuccess) return e;
-  // dW [n_out x k] = (dY s)^T [n_out x tp] . x_q^T [k x tp]^T
-  float* partials = reinterpret_cast<float*>(w + bwd_partial_offset(tokens, k, n_out));
-  return gemm_nt(dys_t, tp, xq_t, tp, dW, k, n_out, k, tp, nullptr, partials, s);
+  NtProblem px{}, pw{};
+  if (dX) px = dx_problem(dY, gamma, dX, ws, tokens, k, n_out);
+  if (dW) pw = dw_problem(dW, ws, tokens, k, n_out);
+  float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + bwd_partial_offset(tokens, k, n_out));
+  return gemm_nt_run(dX ? &px : nullptr, dW ? &pw : nullptr, partials, s);
 }
 
 }  // namespace bl

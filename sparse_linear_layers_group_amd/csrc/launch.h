@@ -312,9 +312,11 @@ inline size_t bwd_ws_bytes(int64_t tokens, int64_t k, int64_t n_out) {
   const size_t pw = sw > 1 ? (size_t)sw * n_out * k * 4 : 0;
   return bwd_partial_offset(tokens, k, n_out) + bwd_align(px > pw ? px : pw);
 }
-hipError_t launch_bwd_dx(const uint16_t* dY, const void* packed, const double* gamma, float* dX,
-                         void* ws, int64_t tokens, int64_t k, int64_t n_out, int S, hipStream_t s);
-hipError_t launch_bwd_dw(const uint16_t* dY, const int8_t* xq, const float* scale, float* dW,
-                         void* ws, int64_t tokens, int64_t k, int64_t n_out, hipStream_t s);
+// dX (if non-null) and dW (if non-null) of one layer: operand preparation,
+// then the products that are not split along k in one launch, then the
+// split ones; tokens == 0 writes a zero dW
+hipError_t launch_bwd(const uint16_t* dY, const int8_t* xq, const float* scale, const void* packed,
+                      const double* gamma, float* dX, float* dW, void* ws, int64_t tokens, int64_t k,
+                      int64_t n_out, int S, hipStream_t s);
 
 }  // namespace bl
