@@ -55,8 +55,8 @@ DECODE_TRAFFIC = {
     "sources": ["sparse_linear_layers_group_amd/csrc/gemv.hip",
                 "sparse_linear_layers_group_amd/csrc/common.h",
                 "sparse_linear_layers_group_amd/csrc/launch.h"],
-    "sha256": "15dd177c999cbbe3ef9470b5e52b62aadb3a75990f1a7daba7ed02302f01b6f8",
-    "fetch_kib": 39918.6, "fetch_scale": 2.0,
+    "sha256": "b45fb952de7ad6807c6f875c3ea69918b8b8b998c04cf8260718a13b2e66db9d",
+    "fetch_kib": 39914.3, "fetch_scale": 2.0,
     "write_kib": 1188.0, "write_scale": 1.0,
 }
 
@@ -427,6 +427,39 @@ SWEEP_TOKENS = (1, 16, 512, 4096)
 SWEEP_PATTERNS = ((8, 8), (6, 8), (4, 8), (2, 4))
 
 
+def grouped_decode_point(torch, bl, lw, bufs, pool, tokens, n, m, iters, group=16):
+    """The same decode as one grouped launch over `group` distinct copies of
+    the matrix (as a decode step streams many matrices at once): the
+    per-launch start-up and tail are paid once for all of them.  Plans
+    rotate over the pool copies, so every launch reads HBM."""
+    k, n_out = lw.k, lw.n_out
+    ys = [torch.empty(tokens * n_out, dtype=torch.float32, device="cuda") for _ in range(group)]
+    plans = []
+    for c in range(max(2, len(pool) // group)):
+        entries = [dict(X=torch.zeros(tokens * k, dtype=torch.bfloat16, device="cuda"), packed=pool[(c * group + g) % len(pool)][0],
+                        gamma=lw.gamma, Y=ys[g], xq=pool[(c * group + g) % len(pool)][1], x_scale=bufs["x_scale"],
+                        k=k, n_out=n_out) for g in range(group)]
+        items = bl.make_fwd_items(entries, tokens)
+        plan = torch.empty(bl.bitlinear_fwd_group_plan_bytes(items, group, tokens), dtype=torch.uint8, device="cuda")
+        bl.bitlinear_fwd_group_plan(items, group, tokens, n, m, plan)
+        plans.append(plan)
+
+    def run(i):
+        bl.bitlinear_fwd_group(plans[i % len(plans)], n, m, 2)  # contraction of already-quantised x_q
+
+    for i in range(len(plans)):
+        run(i)
+    torch.cuda.synchronize()
+    with Timer(torch, ahead_ms=0.05 * (iters + 10), pre=lambda: [run(i) for i in range(10)]) as t:
+        for i in range(iters):
+            run(i)
+    us = 1000.0 * t.ms() / iters
+    byts = group * (lw.packed.numel() + tokens * k + 4 * tokens * n_out)
+    gbs = byts / (us * 1e-6) / 1e9
+    return {"kernel": "gemv_group_kernel", "matrices_per_launch": group, "kernel_us": round(us, 3),
+            "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "plans": len(plans)}
+
+
 def sweep_qwen3b(torch, bl, iters_decode=100, iters_prefill=20):
     """Qwen2.5-3B-shaped sweep: up 2048->11008 and down 11008->2048, token
     counts 1, 16 (decode kernel) and 512, 4096 (prefill kernel), patterns
@@ -479,6 +512,7 @@ def sweep_qwen3b(torch, bl, iters_decode=100, iters_prefill=20):
                     gbs = byts / (us * 1e-6) / 1e9
                     pt.update({"kernel": "gemv_kernel", "bound": "hbm", "gbs": round(gbs, 1),
                                "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+                    pt["grouped_16"] = grouped_decode_point(torch, bl, lw, bufs, pool, tokens, n, m, iters)
                 else:
                     ops = 2 * tokens * n_out * k
                     tops = ops / (us * 1e-6) / 1e12
