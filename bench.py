@@ -55,8 +55,8 @@ DECODE_TRAFFIC = {
     "sources": ["sparse_linear_layers_group_amd/csrc/gemv.hip",
                 "sparse_linear_layers_group_amd/csrc/common.h",
                 "sparse_linear_layers_group_amd/csrc/launch.h"],
-    "sha256": "b45fb952de7ad6807c6f875c3ea69918b8b8b998c04cf8260718a13b2e66db9d",
-    "fetch_kib": 39914.3, "fetch_scale": 2.0,
+    "sha256": "e8fac8f8b594082eb36f33058e193dc6845a6b01f0258680f1c0bace42c59e57",
+    "fetch_kib": 39913.0, "fetch_scale": 2.0,
     "write_kib": 1188.0, "write_scale": 1.0,
 }
 

@@ -271,6 +271,16 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item *items, int count,
                              size_t plan_bytes, void *stream);
 int bitlinear_fwd_group(const void *plan, int n, int m, int stages, void *stream);
 
+/* The bytes bitlinear_fwd_group_plan uploads, written to host memory
+ * instead (image: image_bytes >= bitlinear_fwd_group_plan_bytes(), any
+ * alignment of 16).  For callers that place the plan themselves (a copy of
+ * their own, pinned staging memory) and for host-side checks of a plan; no
+ * device call is made, and the item pointers are only stored.  Same
+ * validation and errors as bitlinear_fwd_group_plan. */
+int bitlinear_fwd_group_plan_host(const bitlinear_fwd_item *items, int count,
+                                  int64_t tokens, int n, int m, void *image,
+                                  size_t image_bytes);
+
 /* Grouped weight quantisation: steps 1-3 (mask, absmean scale, packing) of
  * many layers with the same N:M pattern in three launches (every mask and
  * partial sum, every gamma, every packed block), e.g. the per-step mask

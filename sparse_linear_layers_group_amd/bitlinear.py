@@ -11,6 +11,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +50,7 @@ _SIGS = {
     "bitlinear_contract": (_int, [_vp, _vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_fwd_group_plan_bytes": (_sz, [_vp, _int, _i64]),
     "bitlinear_fwd_group_plan": (_int, [_vp, _int, _i64, _int, _int, _vp, _sz, _vp]),
+    "bitlinear_fwd_group_plan_host": (_int, [_vp, _int, _i64, _int, _int, _vp, _sz]),
     "bitlinear_fwd_group": (_int, [_vp, _int, _int, _int, _vp]),
     "bitlinear_quant_group_workspace_bytes": (_sz, [_vp, _int]),
     "bitlinear_quant_group_plan_bytes": (_sz, [_vp, _int]),
@@ -302,6 +305,15 @@ def bitlinear_fwd_group_plan(items, count, tokens, n, m, plan, plan_bytes=None, 
                                         plan.numel() if plan_bytes is None else int(plan_bytes),
                                         _stream(stream))
     _check(st, "bitlinear_fwd_group_plan")
+
+
+def bitlinear_fwd_group_plan_host(items, count, tokens, n, m, image):
+    """The plan image into a host numpy uint8 array (no device call)."""
+    if not (isinstance(image, np.ndarray) and image.dtype == np.uint8 and image.flags["C_CONTIGUOUS"]):
+        raise TypeError("image must be a C-contiguous numpy uint8 array")
+    st = lib().bitlinear_fwd_group_plan_host(items, int(count), int(tokens), n, m,
+                                             image.ctypes.data_as(ctypes.c_void_p), image.nbytes)
+    _check(st, "bitlinear_fwd_group_plan_host")
 
 
 def bitlinear_fwd_group(plan, n, m, stages=3, stream=None):

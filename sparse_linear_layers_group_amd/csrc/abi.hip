@@ -457,8 +457,10 @@ size_t bitlinear_fwd_group_plan_bytes(const bitlinear_fwd_item* items, int count
   return bl::group_plan_bytes(strips, count, count * tokens);
 }
 
-int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t tokens, int n,
-                             int m, void* plan, size_t plan_bytes, void* stream) {
+namespace {
+// The plan image in host memory; uploading it is the only later step.
+int fwd_group_image(const bitlinear_fwd_item* items, int count, int64_t tokens, int n, int m,
+                    void* plan, size_t plan_bytes, std::vector<char>& img) {
   TRY(check_nm(n, m));
   int64_t steps = 0, nstrips = 0;
   TRY(group_shape(items, count, tokens, &steps, &nstrips));
@@ -476,7 +478,7 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t
   TRY(check_ptr(plan, 16, "plan"));
   if (plan_bytes < need) return fail(BL_EWORKSPACE, "plan needs %zu bytes (got %zu)", need, plan_bytes);
   const int S = bl::s_of(n, m);
-  std::vector<char> img(need, 0);
+  img.assign(need, 0);
   bl::GroupHeader* h = reinterpret_cast<bl::GroupHeader*>(img.data());
   h->count = count;
   h->tokens = (int32_t)tokens;
@@ -550,10 +552,26 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t
     }
     for (int32_t j : lst) descs[next++] = all[j];
   }
+  return BL_OK;
+}
+}  // namespace
+
+int bitlinear_fwd_group_plan(const bitlinear_fwd_item* items, int count, int64_t tokens, int n,
+                             int m, void* plan, size_t plan_bytes, void* stream) {
+  std::vector<char> img;
+  TRY(fwd_group_image(items, count, tokens, n, m, plan, plan_bytes, img));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(plan, img.data(), need, hipMemcpyHostToDevice, s);
+  hipError_t e = hipMemcpyAsync(plan, img.data(), img.size(), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   return hip_status(e, "plan upload");
+}
+
+int bitlinear_fwd_group_plan_host(const bitlinear_fwd_item* items, int count, int64_t tokens, int n,
+                                  int m, void* image, size_t image_bytes) {
+  std::vector<char> img;
+  TRY(fwd_group_image(items, count, tokens, n, m, image, image_bytes, img));
+  std::memcpy(image, img.data(), img.size());
+  return ok();
 }
 
 int bitlinear_fwd_group(const void* plan, int n, int m, int stages, void* stream) {

@@ -12,8 +12,8 @@
 //    A operands need -- so a wavefront's 64 loads are one contiguous span.
 //  * Each 8-group decodes from two 8-bit keys (low half: bitmap + first
 //    four signs; high half: last four signs + bitmap) through two 256-entry
-//    tables of int8x4 codes in LDS.  Lane l reads its own copy of the tables
-//    (64 copies, one per bank), so the lookups never conflict.
+//    tables of int8x4 codes in LDS.  Lane l reads copy l % 32 of the tables
+//    (32 copies), so the lookups of a half wavefront never conflict.
 //  * The codes go straight into v_mfma_i32_16x16x64_i8 as the A operand
 //    (row tile i, k half h); the B operand is the 16 activation bytes of
 //    token l%16 at k slice l/16 of that half -- two 16-byte loads per step
@@ -41,13 +41,15 @@ namespace bl {
 constexpr int kGemvThreads = 1024;  // 16 wavefronts, one workgroup per CU
 constexpr int kGemvWaves = kGemvThreads / 64;
 static_assert(kGemvWaves == kDecodeWavesPerBlock, "wavefronts per workgroup");
-constexpr int kLutCopies = 64;  // one table copy per LDS bank: lane l reads copy l
+constexpr int kLutCopies = kDecodeLutCopies;  // lane l reads copy l % 32
 constexpr int kDepth = 3;       // register ring: steps in flight + 1
 constexpr int kSlotDwords = 16 * kStripRows;  // one wavefront's cut-strip sums [token][row]
 
-// Tables in LDS: entry (key, half) of copy c at dword (key * 2 + half) * 64 + c
-// (128 KB).  Lane l always reads copy l, i.e. bank l % 32, so the lookups
-// of each half wavefront never collide whatever the keys.  The fill reads
+// Tables in LDS: entry (key, half) of copy c at dword (key * 2 + half) * 32 + c
+// (64 KB).  Lane l always reads copy l % 32, i.e. bank l % 32, so the
+// lookups of each half wavefront never collide whatever the keys (64 copies
+// measured no faster on MI355X and took twice the LDS and fill time).  The
+// fill reads
 // the 512 entries from the compile-time table in device memory and writes
 // the big one linearly (consecutive lanes, consecutive 16-byte chunks: no
 // conflicts).  The reads are issued before the first steps' loads: loads
@@ -258,7 +260,7 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut,
   const LutVals lv = load_lut();
   const int tokens = src.tokens;
   const int w = wave_id();
-  const uint32_t* lut_lane = lut + lane;
+  const uint32_t* lut_lane = lut + (lane & (kLutCopies - 1));
   const WaveRange wr = src.range(w);
   const int64_t count = wr.count;
   Cursor L = wr.first, C = wr.first;
@@ -475,6 +477,7 @@ template <int S>
 struct GroupSrc {
   const StripDesc* strips;
   const WaveStart* starts;
+  WaveStart mine;  // this wavefront's start record, read at entry
   int tokens;
   __device__ StripView view(const StripDesc& d) const {
     StripView v = make_strip<S>(d.packed, d.xq, tokens, d.k, d.n_out, d.row0);
@@ -491,8 +494,8 @@ struct GroupSrc {
       c.sv = strip(++c.sid);
     }
   }
-  __device__ WaveRange range(int w) const {
-    const WaveStart& ws = starts[(int64_t)blockIdx.x * kGemvWaves + w];
+  __device__ WaveRange range(int) const {
+    const WaveStart& ws = mine;
     WaveRange r;
     r.count = ws.count;
     r.first.sid = ws.rec;
@@ -534,22 +537,28 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_group_kernel(const char* __
   __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 2 * kLutCopies];
   GroupSrc<S> src;
   src.starts = reinterpret_cast<const WaveStart*>(plan + group_waves_offset());
-  // header and flag are read together (one round trip).  Each wavefront
-  // tests the flag in its own record, which its range comes from as well;
-  // all records of a workgroup carry the same flag, so the whole workgroup
-  // leaves or stays.
+  // The header fields and this wavefront's whole start record are read
+  // before the first branch, in one round trip (read after the header
+  // tests, each took a round trip of its own: ~0.5 us of a 20 us launch).
+  // Each wavefront tests the flag in its own record; all records of a
+  // workgroup carry the same flag, so the whole workgroup leaves or stays.
   const GroupHeader* hdr = reinterpret_cast<const GroupHeader*>(plan);
   const int64_t rows = hdr->rows;
+  const int32_t h_s = hdr->S;
   src.tokens = hdr->tokens;
-  if (hdr->S != S) {
+  src.mine = src.starts[(int64_t)blockIdx.x * kGemvWaves + wave_id()];
+  asm volatile("" : "+s"(src.mine.first.packed), "+s"(src.mine.first.xq), "+s"(src.mine.first.Y),
+               "+s"(src.mine.first.scale), "+s"(src.mine.first.gamma), "+s"(src.mine.first.n_out),
+               "+s"(src.mine.first.k), "+s"(src.mine.first.row0), "+s"(src.mine.rec), "+s"(src.mine.kb),
+               "+s"(src.mine.count), "+s"(src.mine.active) : "s"(h_s), "s"(rows), "s"(src.tokens));
+  if (h_s != S) {
     // a plan made for another sign-slot count: its strips are laid out for
     // that count, so no packed byte is read; every output becomes a quiet
     // NaN instead
     poison_outputs(plan, hdr);
     return;
   }
-  // (rows < 0 never holds; the test keeps the header read ahead of the branch)
-  if (!src.starts[(int64_t)blockIdx.x * kGemvWaves + wave_id()].active || rows < 0) return;
+  if (!src.mine.active) return;
   src.strips = reinterpret_cast<const StripDesc*>(plan + group_strips_offset(rows));
   run_block<S>(src, lut, threadIdx.x & 63);
 }

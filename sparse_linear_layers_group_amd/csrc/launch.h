@@ -117,6 +117,7 @@ hipError_t launch_act_quant(const uint16_t* X, int64_t tokens, int64_t k, int8_t
 // with few strips only) meets in an int32 workspace, and the last
 // workgroup to contribute writes it.
 constexpr int kDecodeBlocks = 256;     // one workgroup per CU
+constexpr int kDecodeLutCopies = 32;   // code table copies in the decode kernels' LDS
 constexpr int kDecodeWavesPerBlock = 16;
 constexpr int kMinStepsPerBlock = 16;  // at least ~1 step per wavefront
 __host__ __device__ inline int64_t decode_blocks(int64_t steps) {

@@ -243,6 +243,62 @@ def test_grouped_decode_matches_oracle(tokens, n, m):
             H.assert_y_close(e["Y"].cpu().numpy().reshape(Yref.shape).astype(np.float64), Yref)
 
 
+@pytest.mark.parametrize("tokens,shapes", [
+    # one strip per workgroup, ranges cut inside a 38-block strip, idle
+    # wavefronts (k = 128, 256)
+    (1, [(896, 4864), (64, 128), (128, 256), (200, 1152), (72, 640)]),
+    (16, [(896, 4864), (64, 128), (128, 256), (200, 1152), (72, 640)]),
+    # many strips per workgroup: the 0.5B feed-forward shapes
+    (1, [(4864, 896), (896, 4864), (4864, 896), (896, 896)]),
+    # ~31 one-block strips per workgroup at 16 tokens
+    (16, [(64000, 128)] * 8),
+])
+def test_grouped_decode_matches_single_calls(tokens, shapes):
+    """Grouped decode: every Y bit-identical to a single bitlinear_contract
+    call on the same int8 activations, and to the oracle within the decode
+    tolerance on a sample of rows."""
+    n, m = 6, 8
+    entries, singles = [], []
+    for i, (n_out, k) in enumerate(shapes):
+        W = synth.weights(n_out, k, seed=500 + i)
+        X = synth.activations(tokens, k, seed=600 + i)
+        lw = BitLinearWeight(n_out, k, n, m)
+        lw.quantize(bf16_tensor(W))
+        e = dict(X=bf16_tensor(X), packed=lw.packed, gamma=lw.gamma, k=k, n_out=n_out,
+                 Y=torch.full((tokens * n_out,), float("nan"), dtype=torch.float32, device="cuda"),
+                 xq=torch.empty(tokens * k, dtype=torch.int8, device="cuda"),
+                 x_scale=torch.empty(tokens, dtype=torch.float32, device="cuda"), lw=lw, W=W, Xb=X)
+        entries.append(e)
+    items = bl.make_fwd_items(entries, tokens)
+    plan = torch.empty(bl.bitlinear_fwd_group_plan_bytes(items, len(entries), tokens), dtype=torch.uint8,
+                       device="cuda")
+    bl.bitlinear_fwd_group_plan(items, len(entries), tokens, n, m, plan)
+    for rep in range(2):  # the plan is reused
+        for e in entries:
+            e["Y"].fill_(float("nan"))
+        bl.bitlinear_fwd_group(plan, n, m, 3)
+        torch.cuda.synchronize()
+        for i, e in enumerate(entries):
+            Ys = torch.empty_like(e["Y"])
+            nws = bl.bitlinear_fwd_workspace_bytes(tokens, e["k"], e["n_out"])
+            ws = torch.zeros(nws, dtype=torch.uint8, device="cuda") if nws else None
+            bl.bitlinear_contract(e["xq"], e["x_scale"], tokens, e["k"], e["lw"].packed, e["n_out"], n, m,
+                                  e["lw"].gamma, Ys, ws=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(e["Y"].cpu().numpy().view(np.uint32), Ys.cpu().numpy().view(np.uint32)), i
+    # the oracle on a sample of rows of the first item (gamma over all rows)
+    e = entries[0]
+    rows = np.arange(0, e["n_out"], max(1, e["n_out"] // 97))
+    xq, sc = oracle.act_quant(e["Xb"])
+    assert np.array_equal(e["xq"].cpu().numpy().reshape(xq.shape), xq)
+    g = oracle.gamma(e["W"])
+    Wr = np.ascontiguousarray(e["W"][rows])
+    T = oracle.ternary(Wr, oracle.mask(Wr, n, m), g)
+    acc_ref, Yref = oracle.fwd(xq, sc, T, g)
+    Y = e["Y"].cpu().numpy().reshape(tokens, e["n_out"])[:, rows]
+    H.assert_y_close(Y.astype(np.float64), Yref)
+
+
 @pytest.mark.parametrize("n_out,k,tokens", [(200, 2432, 300), (512, 1024, 17), (1536, 8960, 1024)])
 def test_prefill_split_k(n_out, k, tokens):
     """Layers with few output tiles split their k blocks over two

@@ -1,0 +1,155 @@
+"""Host-side checks of the grouped decode plan (no GPU): the image that
+bitlinear_fwd_group_plan uploads, built into host memory with stand-in
+device addresses (low words with bit 31 set, as real device addresses
+often have), is replayed against every read the contraction kernel makes:
+header, activation rows, items, each workgroup's strip list and the 16
+wavefront start records that cut it into ranges.  Every strip of every item
+must be covered exactly once, in whole k blocks, and the ranges must tile
+each workgroup's steps in the documented 19 : 17 : 15 : 13 proportions."""
+import numpy as np
+import pytest
+
+from sparse_linear_layers_group_amd import bitlinear as bl
+
+QWEN05 = [(896, 896), (128, 896), (128, 896), (896, 896), (4864, 896), (4864, 896), (896, 4864)]
+S_OF = {(8, 8): 8, (6, 8): 6, (4, 8): 4, (2, 4): 4, (3, 8): 4, (2, 8): 2}
+WEIGHTS = (19, 17, 15, 13)  # per group of four wavefronts (w // 4)
+
+# plan image: header 64 B | 256 x 16 wavefront starts (80 B) | row
+# descriptors (32 B, at least 1024) | strip descriptors (64 B) | items (64 B)
+HDR, WAVE, ROW, DESC, ITEM = 64, 80, 32, 64, 64
+
+
+def _wave_split(n, w):
+    c = sum(WEIGHTS[g] * min(max(w - 4 * g, 0), 4) for g in range(4))
+    return n * c // 256
+
+
+def _items(shapes):
+    arr = (bl.bitlinear_fwd_item * len(shapes))()
+    info = []
+    for i, (n_out, k) in enumerate(shapes):
+        base = 0x7f0000000000 + 0x100000000 * i + 0x80000000
+        p = dict(X=base, packed=base + 0x10000000, gamma=base + 0x20000000, Y=base + 0x30000000,
+                 xq=base + 0x40000000, x_scale=base + 0x50000000)
+        arr[i] = bl.bitlinear_fwd_item(p["X"], p["packed"], p["gamma"], p["Y"], p["xq"], p["x_scale"], k, n_out)
+        info.append(dict(p, k=k, n_out=n_out))
+    return arr, info
+
+
+class _Img:
+    def __init__(self, img):
+        self.b = img
+
+    def i32(self, o):
+        return int(self.b[o:o + 4].view(np.int32)[0])
+
+    def i64(self, o):
+        return int(self.b[o:o + 8].view(np.int64)[0])
+
+    def u64(self, o):
+        return int(self.b[o:o + 8].view(np.uint64)[0])
+
+    def desc(self, o):
+        return dict(packed=self.u64(o), xq=self.u64(o + 8), Y=self.u64(o + 16), scale=self.u64(o + 24),
+                    gamma=self.u64(o + 32), n_out=self.i64(o + 40), k=self.i32(o + 48), row0=self.i32(o + 52))
+
+
+def _replay(shapes, tokens, n=6, m=8):
+    items, info = _items(shapes)
+    nbytes = bl.bitlinear_fwd_group_plan_bytes(items, len(shapes), tokens)
+    img = np.zeros(nbytes, np.uint8)
+    bl.bitlinear_fwd_group_plan_host(items, len(shapes), tokens, n, m, img)
+    P = _Img(img)
+    bb = 2 * (8 + S_OF[(n, m)])
+    count, tok, s_hdr, blocks = P.i32(0), P.i32(4), P.i32(8), P.i32(12)
+    rows, steps, strips = P.i64(16), P.i64(24), P.i64(32)
+    assert (count, tok, s_hdr, rows) == (len(shapes), tokens, S_OF[(n, m)], len(shapes) * tokens)
+    assert steps == sum(-(-no // 64) * (k // 128) for no, k in shapes)
+    assert strips == sum(-(-no // 64) for no, _ in shapes)
+    assert 1 <= blocks <= 256
+    waves = HDR
+    rows_off = waves + 4096 * WAVE
+    strips_off = rows_off + max(rows, 1024) * ROW
+    items_off = strips_off + strips * DESC
+    assert items_off + count * ITEM == nbytes
+    r = 0
+    for it in info:
+        for t in range(tokens):
+            o = rows_off + r * ROW
+            assert (P.u64(o), P.u64(o + 8), P.u64(o + 16), P.i64(o + 24)) == (
+                it["X"] + 2 * t * it["k"], it["xq"] + t * it["k"], it["x_scale"] + 4 * t, it["k"])
+            r += 1
+    for i, it in enumerate(info):
+        o = items_off + i * ITEM
+        assert [P.u64(o + 8 * f) for f in range(6)] == [it[x] for x in ("X", "packed", "gamma", "Y", "xq", "x_scale")]
+        assert (P.i64(o + 48), P.i64(o + 56)) == (it["k"], it["n_out"])
+    want = {}
+    for it in info:
+        for st in range(-(-it["n_out"] // 64)):
+            want[it["packed"] + st * (it["k"] // 128) * 64 * bb] = (it, st)
+    owner = {}
+    next_desc = 0
+    for b in range(256):
+        first = waves + b * 16 * WAVE
+        if b >= blocks:
+            assert all(P.i32(first + w * WAVE + 76) == 0 for w in range(16))
+            continue
+        # the workgroup's strip list: contiguous descriptors from next_desc
+        rec0 = P.i32(first + 64)
+        assert rec0 == next_desc and P.i32(first + 68) == 0
+        n_b = sum(P.i32(first + w * WAVE + 72) for w in range(16))
+        steps_of = []
+        j, cum = rec0, 0
+        while cum < n_b:
+            d = P.desc(strips_off + j * DESC)
+            it, st = want[d["packed"]]
+            assert (d["xq"], d["Y"], d["scale"], d["gamma"]) == (it["xq"], it["Y"], it["x_scale"], it["gamma"])
+            assert (d["n_out"], d["k"], d["row0"]) == (it["n_out"], it["k"], 64 * st)
+            assert d["packed"] not in owner
+            owner[d["packed"]] = b
+            steps_of.append((j, cum, d["k"] // 128))
+            cum += d["k"] // 128
+            j += 1
+        assert cum == n_b
+        next_desc = j
+        # wavefront w: steps [split(w), split(w+1)) of the list, from its record
+        for w in range(16):
+            o = first + w * WAVE
+            rec, kb, cnt, act = P.i32(o + 64), P.i32(o + 68), P.i32(o + 72), P.i32(o + 76)
+            assert act == 1
+            s0, s1 = _wave_split(n_b, w), _wave_split(n_b, w + 1)
+            assert cnt == s1 - s0
+            jj, c0, nk = next((x for x in steps_of if x[1] <= s0 < x[1] + x[2]), steps_of[-1])
+            assert (rec, kb) == (jj, s0 - c0) or (cnt == 0 and s0 == n_b)
+            assert P.desc(o) == P.desc(strips_off + rec * DESC)
+    assert next_desc == strips and len(owner) == len(want)
+
+
+@pytest.mark.parametrize("shapes,tokens", [
+    (QWEN05 * 2, 1),
+    (QWEN05 * 24, 1),
+    (QWEN05 * 24, 16),
+    ([(48, 256), (128, 896), (40, 384), (896, 4864), (200, 1152)], 1),
+    ([(48, 256), (128, 896), (40, 384), (896, 4864), (200, 1152)], 16),
+    ([(64, 128), (128, 256)], 1),
+    ([(11008, 2048)] * 16, 1),
+    ([(2048, 11008)] * 16, 16),
+    ([(64000, 128)] * 8, 16),
+])
+def test_group_plan_replay(shapes, tokens):
+    _replay(shapes, tokens)
+
+
+@pytest.mark.parametrize("n,m", [(8, 8), (4, 8), (2, 4), (2, 8)])
+def test_group_plan_replay_patterns(n, m):
+    _replay(QWEN05 * 3, 2, n, m)
+
+
+def test_group_plan_host_rejects_short_image():
+    items, _ = _items(QWEN05)
+    nbytes = bl.bitlinear_fwd_group_plan_bytes(items, len(QWEN05), 1)
+    img = np.zeros(nbytes - 16, np.uint8)
+    with pytest.raises(bl.BitLinearError) as e:
+        bl.bitlinear_fwd_group_plan_host(items, len(QWEN05), 1, 6, 8, img)
+    assert e.value.status == bl.BL_EWORKSPACE
