@@ -398,11 +398,23 @@ def prefill_step(torch, bl, n, m, tokens=2048, iters=10):
             bl.bitlinear_contract(src["xq"], src["x_scale"], tokens, lw.k, packs[i], lw.n_out, n, m,
                                   lw.gamma, bufs[i]["Y"], ws=bufs[i]["ws"])
 
-    for f in (quant, act, gemm):
+    # the same GEMMs with the bf16 Y epilogue (half the output bytes)
+    ybf = [torch.empty(tokens * lw.n_out, dtype=torch.bfloat16, device="cuda") for lw in lws]
+
+    def gemm_bf16():
+        packs, b0, b2 = act_sets[state["g"] % len(act_sets)]
+        state["g"] += 1
+        for i, lw in enumerate(lws):
+            src = b2 if i == 2 else b0
+            bl.bitlinear_contract_bf16(src["xq"], src["x_scale"], tokens, lw.k, packs[i], lw.n_out, n, m,
+                                       lw.gamma, ybf[i], ws=bufs[i]["ws"])
+
+    for f in (quant, act, gemm, gemm_bf16):
         f()
     torch.cuda.synchronize()
     res = {}
-    for name, f in (("mask_pack_ms", quant), ("act_quant_ms", act), ("gemm_ms", gemm)):
+    for name, f in (("mask_pack_ms", quant), ("act_quant_ms", act), ("gemm_ms", gemm),
+                    ("gemm_bf16_y_ms", gemm_bf16)):
         with Timer(torch, ahead_ms=0.2 * (iters + 2), pre=lambda: [f(), f()]) as t:
             for _ in range(iters):
                 f()
@@ -416,6 +428,8 @@ def prefill_step(torch, bl, n, m, tokens=2048, iters=10):
     mp_bytes = wts * (2 + 2 + 0.125 + 0.125) + sum(packed_bytes(n_out, k, n, m) for _, n_out, k in QWEN15_PREFILL)
     res["mask_pack_gbs"] = mp_bytes / (res["mask_pack_ms"] * 1e-3) / 1e9
     res["step_ms"] = res["mask_pack_ms"] + res["act_quant_ms"] + res["gemm_ms"]
+    res["gemm_bf16_y_speedup"] = res["gemm_ms"] / res["gemm_bf16_y_ms"]
+    res["y_bytes_fp32"] = sum(4 * tokens * n_out for _, n_out, _ in QWEN15_PREFILL)
     out = {k2: round(v, 4) for k2, v in res.items()}
     out["inputs"] = (f"rotating over {len(qgs)} copies of the latent W, {len(x_sets)} of X and "
                      f"{len(act_sets)} of (packed codes, x_q): every pass reads HBM")

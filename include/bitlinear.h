@@ -191,6 +191,26 @@ int bitlinear_contract(const int8_t *xq, const float *x_scale, int64_t tokens,
                        int m, const double *gamma, float *Y, int32_t *acc,
                        void *ws, size_t ws_bytes, void *stream);
 
+/* bitlinear_fwd and bitlinear_contract with bf16 outputs: the optional bf16
+ * Y epilogue of the block glue, for a BitNet block whose next operation
+ * takes bf16 (the 2B4T article §二 describes a bf16 model around the
+ * BitLinears); it halves the bytes written at prefill sizes, where the
+ * binary32 Y is the largest stream.  Y is the binary32 Y of bitlinear_fwd,
+ * rounded once more to the nearest bf16 (ties to even), written as bf16 bit
+ * patterns: device uint16 [tokens x n_out], 16-byte aligned.  Every other
+ * argument, output, workspace rule and error is that of bitlinear_fwd /
+ * bitlinear_contract. */
+int bitlinear_fwd_bf16(const uint16_t *X, int64_t tokens, int64_t k,
+                       const void *packed, int64_t n_out, int n, int m,
+                       const double *gamma, uint16_t *Y, int8_t *xq,
+                       float *x_scale, int32_t *acc, void *ws, size_t ws_bytes,
+                       void *stream);
+int bitlinear_contract_bf16(const int8_t *xq, const float *x_scale,
+                            int64_t tokens, int64_t k, const void *packed,
+                            int64_t n_out, int n, int m, const double *gamma,
+                            uint16_t *Y, int32_t *acc, void *ws,
+                            size_t ws_bytes, void *stream);
+
 /* 2:4 on structured-sparse matrix hardware.  The Sparse-BitNet article
  * (§七) ties N:M sparsity's speed-up to matrix units that skip the pruned
  * half (2:4 sparse tensor cores); gfx950's counterpart is

@@ -42,6 +42,7 @@ def _load():
         "oracle_act_quant": (None, [_vp, _i64, _i64, _vp, _vp]),
         "oracle_fwd": (_int, [_vp, _vp, _vp, _dbl, _i64, _i64, _i64, _vp, _vp, _int]),
         "oracle_fwd_pairs": (None, [_vp, _vp, _vp, _dbl, _i64, _vp, _vp, _i64, _vp, _vp]),
+        "oracle_fwd_bf16": (_int, [_vp, _vp, _vp, _dbl, _i64, _i64, _i64, _vp]),
         "oracle_bwd_dx": (None, [_vp, _vp, _dbl, _i64, _i64, _i64, _vp, _int]),
         "oracle_bwd_dw": (None, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _int]),
         "oracle_bwd_dx_pairs": (None, [_vp, _vp, _dbl, _i64, _i64, _vp, _vp, _i64, _vp]),
@@ -126,6 +127,19 @@ def fwd(xq, scale, T, g, threads=1, want_acc=True, want_y=True):
     if ovf:
         raise OverflowError("an accumulator left the int32 range")
     return acc, Y
+
+
+def fwd_bf16(xq, scale, T, g):
+    """Contraction + epilogue with bf16 outputs -> uint16 [T, n] bf16 bits."""
+    xq = _c(xq, np.int8)
+    scale = _c(scale, np.float64)
+    T = _c(T, np.int8)
+    tokens, k = xq.shape
+    n_out = T.shape[0]
+    Y = np.zeros((tokens, n_out), dtype=np.uint16)
+    if _load().oracle_fwd_bf16(_p(xq), _p(scale), _p(T), float(g), tokens, k, n_out, _p(Y)):
+        raise OverflowError("an accumulator left the int32 range")
+    return Y
 
 
 def fwd_pairs(xq, scale, T, g, t_idx, n_idx):

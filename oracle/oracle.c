@@ -714,3 +714,35 @@ void oracle_relu2_gate_bwd(const float *dH, const float *G, const float *U, int6
         dG[i] = nearest_bf16(dg);
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* Step 6 with bf16 outputs: the optional bf16 Y epilogue of the block */
+/* glue ([2B4T] 二: the model around the BitLinears runs in bf16).     */
+/* No page fixes how a bf16 Y is rounded; the reading taken is the     */
+/* binary32 Y of the epilogue, rounded once more:                      */
+/*   s32 = the binary32 nearest to a_t / 127 (s_t as stored),          */
+/*   g32 = the binary32 nearest to gamma * s32 (binary64 product),     */
+/*   Y32 = the binary32 nearest to f(acc) * g32, where f(acc) is the   */
+/*         binary32 nearest to acc,                                    */
+/*   Y16 = the bf16 nearest to Y32 (ties to even).                     */
+/* Returns 0, or 1 if some accumulator left the int32 range.           */
+/* ------------------------------------------------------------------ */
+int oracle_fwd_bf16(const int8_t *xq, const double *scale, const int8_t *T, double gamma,
+                    int64_t tokens, int64_t k, int64_t n_out, uint16_t *Y)
+{
+    int overflow = 0;
+    for (int64_t t = 0; t < tokens; ++t) {
+        float s32 = (float)scale[t];
+        float g32 = (float)(gamma * (double)s32);
+        for (int64_t r = 0; r < n_out; ++r) {
+            int64_t s = 0;
+            for (int64_t c = 0; c < k; ++c)
+                s += (int64_t)xq[t * k + c] * (int64_t)T[r * k + c];
+            if (s > INT32_MAX || s < INT32_MIN) overflow = 1;
+            float a32 = (float)(int32_t)s;
+            float y32 = a32 * g32;
+            Y[t * n_out + r] = nearest_bf16(y32);
+        }
+    }
+    return overflow;
+}

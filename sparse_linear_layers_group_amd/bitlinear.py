@@ -48,6 +48,8 @@ _SIGS = {
     "bitlinear_contract_sp24": (_int, [_vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_act_quant": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "bitlinear_contract": (_int, [_vp, _vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "bitlinear_fwd_bf16": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "bitlinear_contract_bf16": (_int, [_vp, _vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_fwd_group_plan_bytes": (_sz, [_vp, _int, _i64]),
     "bitlinear_fwd_group_plan": (_int, [_vp, _int, _i64, _int, _int, _vp, _sz, _vp]),
     "bitlinear_fwd_group_plan_host": (_int, [_vp, _int, _i64, _int, _int, _vp, _sz]),
@@ -177,6 +179,21 @@ def bitlinear_fwd(X, tokens, k, packed, n_out, n, m, gamma, Y, xq, x_scale, acc=
     _check(st, "bitlinear_fwd")
 
 
+def bitlinear_fwd_bf16(X, tokens, k, packed, n_out, n, m, gamma, Y, xq, x_scale, acc=None, ws=None,
+                       ws_bytes=None, stream=None):
+    """bitlinear_fwd with bf16 Y (a bfloat16 tensor of tokens * n_out)."""
+    st = lib().bitlinear_fwd_bf16(
+        _ptr(X, _BF16, tokens * k, "X"), tokens, k, _ptr(packed, (torch.uint8,), None, "packed"),
+        n_out, n, m, _ptr(gamma, (torch.float64,), 1, "gamma"),
+        _ptr(Y, _BF16, tokens * n_out, "Y"), _ptr(xq, (torch.int8,), tokens * k, "xq"),
+        _ptr(x_scale, (torch.float32,), tokens, "x_scale"),
+        _ptr(acc, (torch.int32,), tokens * n_out, "acc", optional=True),
+        _ptr(ws, (torch.uint8,), None, "ws", optional=True),
+        (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes),
+        _stream(stream))
+    _check(st, "bitlinear_fwd_bf16")
+
+
 def bitlinear_fwd_noalloc(X, tokens, k, packed, n_out, n, m, gamma, Y, xq, x_scale, acc=None, stream=None):
     st = lib().bitlinear_fwd_noalloc(
         _ptr(X, _BF16, tokens * k, "X"), tokens, k, _ptr(packed, (torch.uint8,), None, "packed"),
@@ -274,6 +291,19 @@ def bitlinear_contract(xq, x_scale, tokens, k, packed, n_out, n, m, gamma, Y, ac
         _ptr(ws, (torch.uint8,), None, "ws", optional=True),
         (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes), _stream(stream))
     _check(st, "bitlinear_contract")
+
+
+def bitlinear_contract_bf16(xq, x_scale, tokens, k, packed, n_out, n, m, gamma, Y, acc=None, ws=None,
+                            ws_bytes=None, stream=None):
+    """bitlinear_contract with bf16 Y (a bfloat16 tensor of tokens * n_out)."""
+    st = lib().bitlinear_contract_bf16(
+        _ptr(xq, (torch.int8,), tokens * k, "xq"), _ptr(x_scale, (torch.float32,), tokens, "x_scale"),
+        tokens, k, _ptr(packed, (torch.uint8,), None, "packed"), n_out, n, m,
+        _ptr(gamma, (torch.float64,), 1, "gamma"), _ptr(Y, _BF16, tokens * n_out, "Y"),
+        _ptr(acc, (torch.int32,), tokens * n_out, "acc", optional=True),
+        _ptr(ws, (torch.uint8,), None, "ws", optional=True),
+        (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes), _stream(stream))
+    _check(st, "bitlinear_contract_bf16")
 
 
 class bitlinear_fwd_item(ctypes.Structure):

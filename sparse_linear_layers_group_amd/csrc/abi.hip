@@ -250,9 +250,11 @@ int bitlinear_pack(const uint16_t* W, const uint8_t* mask, const double* gamma, 
   return hip_status(e, "pack launch");
 }
 
-int bitlinear_fwd(const uint16_t* X, int64_t tokens, int64_t k, const void* packed, int64_t n_out,
-                  int n, int m, const double* gamma, float* Y, int8_t* xq, float* x_scale,
-                  int32_t* acc, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+// the forward with binary32 (Y) or bf16 (Yb) outputs: exactly one is given
+int fwd_impl(const uint16_t* X, int64_t tokens, int64_t k, const void* packed, int64_t n_out,
+             int n, int m, const double* gamma, float* Y, uint16_t* Yb, int8_t* xq, float* x_scale,
+             int32_t* acc, void* ws, size_t ws_bytes, void* stream) {
   TRY(check_nm(n, m));
   TRY(check_layer(n_out, k));
   if (tokens < 0) return fail(BL_ESHAPE, "tokens must be >= 0 (got %lld)", (long long)tokens);
@@ -262,7 +264,8 @@ int bitlinear_fwd(const uint16_t* X, int64_t tokens, int64_t k, const void* pack
   TRY(check_ptr(X, 16, "X"));
   TRY(check_ptr(packed, 16, "packed"));
   TRY(check_ptr(gamma, 8, "gamma"));
-  TRY(check_ptr(Y, 16, "Y"));
+  if (Yb) TRY(check_ptr(Yb, 16, "Y"));
+  else TRY(check_ptr(Y, 16, "Y"));
   TRY(check_ptr(xq, 16, "xq"));
   TRY(check_ptr(x_scale, 4, "x_scale"));
   TRY(check_opt_ptr(acc, 16, "acc"));
@@ -277,7 +280,7 @@ int bitlinear_fwd(const uint16_t* X, int64_t tokens, int64_t k, const void* pack
     hipError_t e = bl::launch_act_quant(X, tokens, k, xq, x_scale, need ? ws : nullptr,
                                         (int64_t)need, s);
     if (e != hipSuccess) return hip_status(e, "activation quant launch");
-    e = bl::launch_gemv(packed, xq, x_scale, gamma, Y, acc, ws, (int)tokens, k, n_out, S, s);
+    e = bl::launch_gemv(packed, xq, x_scale, gamma, Y, Yb, acc, ws, (int)tokens, k, n_out, S, s);
     return hip_status(e, "decode launch");
   }
   const size_t need = bitlinear_fwd_workspace_bytes(tokens, k, n_out);
@@ -289,8 +292,24 @@ int bitlinear_fwd(const uint16_t* X, int64_t tokens, int64_t k, const void* pack
   hipError_t e = bl::launch_act_quant(X, tokens, k, xq, x_scale, need ? ws : nullptr,
                                       need ? (int64_t)bl::gemm_ticket_bytes(tokens, n_out) : 0, s);
   if (e != hipSuccess) return hip_status(e, "activation quant launch");
-  e = bl::launch_gemm(packed, xq, x_scale, gamma, Y, acc, ws, tokens, k, n_out, S, s);
+  e = bl::launch_gemm(packed, xq, x_scale, gamma, Y, Yb, acc, ws, tokens, k, n_out, S, s);
   return hip_status(e, "prefill launch");
+}
+}  // namespace
+
+int bitlinear_fwd(const uint16_t* X, int64_t tokens, int64_t k, const void* packed, int64_t n_out,
+                  int n, int m, const double* gamma, float* Y, int8_t* xq, float* x_scale,
+                  int32_t* acc, void* ws, size_t ws_bytes, void* stream) {
+  return fwd_impl(X, tokens, k, packed, n_out, n, m, gamma, Y, nullptr, xq, x_scale, acc, ws, ws_bytes,
+                  stream);
+}
+
+int bitlinear_fwd_bf16(const uint16_t* X, int64_t tokens, int64_t k, const void* packed,
+                       int64_t n_out, int n, int m, const double* gamma, uint16_t* Y, int8_t* xq,
+                       float* x_scale, int32_t* acc, void* ws, size_t ws_bytes, void* stream) {
+  if (!Y) return fail(BL_EINVAL, "Y is NULL");
+  return fwd_impl(X, tokens, k, packed, n_out, n, m, gamma, nullptr, Y, xq, x_scale, acc, ws, ws_bytes,
+                  stream);
 }
 
 int bitlinear_fwd_noalloc(const uint16_t* X, int64_t tokens, int64_t k, const void* packed,
@@ -421,9 +440,10 @@ int bitlinear_latent_update(float* W_master, const float* dW, int64_t count, flo
   return hip_status(e, "latent update launch");
 }
 
-int bitlinear_contract(const int8_t* xq, const float* x_scale, int64_t tokens, int64_t k,
-                       const void* packed, int64_t n_out, int n, int m, const double* gamma,
-                       float* Y, int32_t* acc, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+int contract_impl(const int8_t* xq, const float* x_scale, int64_t tokens, int64_t k,
+                  const void* packed, int64_t n_out, int n, int m, const double* gamma, float* Y,
+                  uint16_t* Yb, int32_t* acc, void* ws, size_t ws_bytes, void* stream) {
   TRY(check_nm(n, m));
   TRY(check_layer(n_out, k));
   if (tokens < 0 || tokens >= kLimit || tokens * k >= kLimit || tokens * n_out >= kLimit)
@@ -433,7 +453,8 @@ int bitlinear_contract(const int8_t* xq, const float* x_scale, int64_t tokens, i
   TRY(check_ptr(x_scale, 4, "x_scale"));
   TRY(check_ptr(packed, 16, "packed"));
   TRY(check_ptr(gamma, 8, "gamma"));
-  TRY(check_ptr(Y, 16, "Y"));
+  if (Yb) TRY(check_ptr(Yb, 16, "Y"));
+  else TRY(check_ptr(Y, 16, "Y"));
   TRY(check_opt_ptr(acc, 16, "acc"));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int S = bl::s_of(n, m);
@@ -444,10 +465,26 @@ int bitlinear_contract(const int8_t* xq, const float* x_scale, int64_t tokens, i
   if (need) TRY(check_ptr(ws, 16, "ws"));
   hipError_t e;
   if (tokens <= 16)
-    e = bl::launch_gemv(packed, xq, x_scale, gamma, Y, acc, ws, (int)tokens, k, n_out, S, s);
+    e = bl::launch_gemv(packed, xq, x_scale, gamma, Y, Yb, acc, ws, (int)tokens, k, n_out, S, s);
   else
-    e = bl::launch_gemm(packed, xq, x_scale, gamma, Y, acc, ws, tokens, k, n_out, S, s);
+    e = bl::launch_gemm(packed, xq, x_scale, gamma, Y, Yb, acc, ws, tokens, k, n_out, S, s);
   return hip_status(e, "contraction launch");
+}
+}  // namespace
+
+int bitlinear_contract(const int8_t* xq, const float* x_scale, int64_t tokens, int64_t k,
+                       const void* packed, int64_t n_out, int n, int m, const double* gamma,
+                       float* Y, int32_t* acc, void* ws, size_t ws_bytes, void* stream) {
+  return contract_impl(xq, x_scale, tokens, k, packed, n_out, n, m, gamma, Y, nullptr, acc, ws, ws_bytes,
+                       stream);
+}
+
+int bitlinear_contract_bf16(const int8_t* xq, const float* x_scale, int64_t tokens, int64_t k,
+                            const void* packed, int64_t n_out, int n, int m, const double* gamma,
+                            uint16_t* Y, int32_t* acc, void* ws, size_t ws_bytes, void* stream) {
+  if (!Y) return fail(BL_EINVAL, "Y is NULL");
+  return contract_impl(xq, x_scale, tokens, k, packed, n_out, n, m, gamma, nullptr, Y, acc, ws,
+                       ws_bytes, stream);
 }
 
 

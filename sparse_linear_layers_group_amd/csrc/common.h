@@ -74,6 +74,13 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));
 
+// four binary32 outputs as bf16 (nearest, ties to even), packed for one
+// 8-byte store
+__device__ __forceinline__ u32x2 bf16x4(v4f y) {
+  return u32x2{(uint32_t)f32_to_bf16_rne(y[0]) | ((uint32_t)f32_to_bf16_rne(y[1]) << 16),
+               (uint32_t)f32_to_bf16_rne(y[2]) | ((uint32_t)f32_to_bf16_rne(y[3]) << 16)};
+}
+
 // explicit global-address-space accesses: pointers that arrive through
 // memory (e.g. from a plan) would otherwise become flat accesses, which also
 // count against the LDS counter and force extra waits

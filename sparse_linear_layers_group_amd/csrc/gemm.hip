@@ -60,7 +60,7 @@ __device__ __forceinline__ void gemm_finish(v4i (&c)[kTT][4], bool live, int spl
                                             int64_t tokens, int64_t n_out,
                                             const double* __restrict__ gamma,
                                             const float* __restrict__ scale, float* __restrict__ Y,
-                                            int32_t* __restrict__ acc_out,
+                                            uint16_t* __restrict__ Yb, int32_t* __restrict__ acc_out,
                                             uint32_t* __restrict__ tickets,
                                             v4i* __restrict__ partials) {
   constexpr int BT = 16 * kTT;
@@ -107,8 +107,8 @@ __device__ __forceinline__ void gemm_finish(v4i (&c)[kTT][4], bool live, int spl
   const double g = *gamma;
   const int64_t r0 = strip * kStripRows + 4 * (lane >> 4);
   if (t0 + BT <= tokens && strip * kStripRows + kStripRows <= n_out && (n_out & 3) == 0) {
-    // whole tile in range: 16-byte stores, no per-element checks; element
-    // offsets fit 32 bits (tokens * n_out < 2^31)
+    // whole tile in range: 16-byte (8-byte for bf16) stores, no per-element
+    // checks; element offsets fit 32 bits (tokens * n_out < 2^31)
     const uint32_t base = (uint32_t)(t0 + (lane & 15)) * (uint32_t)n_out + (uint32_t)r0;
 #pragma unroll
     for (int j = 0; j < kTT; ++j) {
@@ -116,9 +116,12 @@ __device__ __forceinline__ void gemm_finish(v4i (&c)[kTT][4], bool live, int spl
       const uint32_t o = base + (uint32_t)(16 * j) * (uint32_t)n_out;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        st_stream(reinterpret_cast<v4f*>(Y + o + 16 * i),
-                  v4f{out_value(c[j][i][0], gs), out_value(c[j][i][1], gs),
-                      out_value(c[j][i][2], gs), out_value(c[j][i][3], gs)});
+        const v4f y = v4f{out_value(c[j][i][0], gs), out_value(c[j][i][1], gs),
+                          out_value(c[j][i][2], gs), out_value(c[j][i][3], gs)};
+        if (Yb)
+          st_stream(reinterpret_cast<u32x2*>(Yb + o + 16 * i), bf16x4(y));
+        else
+          st_stream(reinterpret_cast<v4f*>(Y + o + 16 * i), y);
         if (acc_out) st_global(reinterpret_cast<v4i*>(acc_out + o + 16 * i), c[j][i]);
       }
     }
@@ -132,18 +135,25 @@ __device__ __forceinline__ void gemm_finish(v4i (&c)[kTT][4], bool live, int spl
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t r = r0 + 16 * i;
-      float* y = Y + t * n_out + r;
+      const int64_t e = t * n_out + r;
       if (r + 4 <= n_out && (n_out & 3) == 0) {
-        st_global(reinterpret_cast<v4f*>(y),
-                  v4f{out_value(c[j][i][0], gs), out_value(c[j][i][1], gs),
-                      out_value(c[j][i][2], gs), out_value(c[j][i][3], gs)});
-        if (acc_out) st_global(reinterpret_cast<v4i*>(acc_out + t * n_out + r), c[j][i]);
+        const v4f y = v4f{out_value(c[j][i][0], gs), out_value(c[j][i][1], gs),
+                          out_value(c[j][i][2], gs), out_value(c[j][i][3], gs)};
+        if (Yb)
+          st_global(reinterpret_cast<u32x2*>(Yb + e), bf16x4(y));
+        else
+          st_global(reinterpret_cast<v4f*>(Y + e), y);
+        if (acc_out) st_global(reinterpret_cast<v4i*>(acc_out + e), c[j][i]);
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (r + q < n_out) {
-            st_global(y + q, out_value(c[j][i][q], gs));
-            if (acc_out) st_global(acc_out + t * n_out + r + q, (int32_t)c[j][i][q]);
+            const float y = out_value(c[j][i][q], gs);
+            if (Yb)
+              st_global(Yb + e + q, f32_to_bf16_rne(y));
+            else
+              st_global(Y + e + q, y);
+            if (acc_out) st_global(acc_out + e + q, (int32_t)c[j][i][q]);
           }
       }
     }
@@ -155,7 +165,7 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
                                                      const int8_t* __restrict__ xq,
                                                      const float* __restrict__ scale,
                                                      const double* __restrict__ gamma,
-                                                     float* __restrict__ Y,
+                                                     float* __restrict__ Y, uint16_t* __restrict__ Yb,
                                                      int32_t* __restrict__ acc_out, int64_t tokens,
                                                      int64_t k, int64_t n_out, int row_blocks,
                                                      int token_blocks, int splits,
@@ -378,7 +388,7 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
   if (kb + 4 < nkb) kblock(I0{}, I1{}, kb + 4);
 
   gemm_finish<kTT>(c, live, splits, tile, part, wave, lane, strip, t0, tokens, n_out, gamma, scale, Y,
-                   acc_out, tickets, partials);
+                   Yb, acc_out, tickets, partials);
 }
 
 // ---------------------------------------------------------------------
@@ -417,6 +427,7 @@ __global__ __launch_bounds__(256, 2) void gemm_sp24_kernel(const uint32_t* __res
                                                           const float* __restrict__ scale,
                                                           const double* __restrict__ gamma,
                                                           float* __restrict__ Y,
+                                                          uint16_t* __restrict__ Yb,
                                                           int32_t* __restrict__ acc_out,
                                                           int64_t tokens, int64_t k, int64_t n_out,
                                                           int row_blocks, int token_blocks, int splits,
@@ -554,12 +565,13 @@ __global__ __launch_bounds__(256, 2) void gemm_sp24_kernel(const uint32_t* __res
   if (kb + 2 < nkb) kblock(I0{}, I2{}, kb + 2);
 
   gemm_finish<kTT>(c, live, splits, tile, part, wave, lane, strip, t0, tokens, n_out, gamma, scale, Y,
-                   acc_out, tickets, partials);
+                   Yb, acc_out, tickets, partials);
 }
 
 hipError_t launch_gemm_sp24(const void* packed, const int8_t* xq, const float* scale,
                             const double* gamma, float* Y, int32_t* acc, void* ws, int64_t tokens,
                             int64_t k, int64_t n_out, hipStream_t s) {
+  uint16_t* const Yb = nullptr;
   constexpr int BT = kGemmTileTokens;
   static_assert(kGemmTileRows == kGStrips * kStripRows, "tile rows");
   const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
@@ -573,14 +585,14 @@ hipError_t launch_gemm_sp24(const void* packed, const int8_t* xq, const float* s
                              : nullptr;
   const int nwork = row_blocks * token_blocks * splits;
   gemm_sp24_kernel<BT><<<(unsigned)((nwork + 7) / 8 * 8), 256, 0, s>>>(
-      reinterpret_cast<const uint32_t*>(packed), xq, scale, gamma, Y, acc, tokens, k, n_out,
+      reinterpret_cast<const uint32_t*>(packed), xq, scale, gamma, Y, Yb, acc, tokens, k, n_out,
       row_blocks, token_blocks, splits, tickets, partials);
   return hipGetLastError();
 }
 
 template <int S>
 static hipError_t launch_gemm_s(const void* packed, const int8_t* xq, const float* scale,
-                                const double* gamma, float* Y, int32_t* acc, void* ws,
+                                const double* gamma, float* Y, uint16_t* Yb, int32_t* acc, void* ws,
                                 int64_t tokens, int64_t k, int64_t n_out, hipStream_t s) {
   constexpr int BT = kGemmTileTokens;
   static_assert(kGemmTileRows == kGStrips * kStripRows, "tile rows");
@@ -596,18 +608,18 @@ static hipError_t launch_gemm_s(const void* packed, const int8_t* xq, const floa
                              : nullptr;
   const int nwork = row_blocks * token_blocks * splits;
   gemm_kernel<S, BT><<<(unsigned)((nwork + 7) / 8 * 8), 256, 0, s>>>(
-      reinterpret_cast<const uint32_t*>(packed), xq, scale, gamma, Y, acc, tokens, k, n_out,
+      reinterpret_cast<const uint32_t*>(packed), xq, scale, gamma, Y, Yb, acc, tokens, k, n_out,
       row_blocks, token_blocks, splits, tickets, partials);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const void* packed, const int8_t* xq, const float* scale,
-                       const double* gamma, float* Y, int32_t* acc, void* ws, int64_t tokens,
-                       int64_t k, int64_t n_out, int S, hipStream_t s) {
-  if (S == 8) return launch_gemm_s<8>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
-  if (S == 6) return launch_gemm_s<6>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
-  if (S == 2) return launch_gemm_s<2>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
-  return launch_gemm_s<4>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
+                       const double* gamma, float* Y, uint16_t* Yb, int32_t* acc, void* ws,
+                       int64_t tokens, int64_t k, int64_t n_out, int S, hipStream_t s) {
+  if (S == 8) return launch_gemm_s<8>(packed, xq, scale, gamma, Y, Yb, acc, ws, tokens, k, n_out, s);
+  if (S == 6) return launch_gemm_s<6>(packed, xq, scale, gamma, Y, Yb, acc, ws, tokens, k, n_out, s);
+  if (S == 2) return launch_gemm_s<2>(packed, xq, scale, gamma, Y, Yb, acc, ws, tokens, k, n_out, s);
+  return launch_gemm_s<4>(packed, xq, scale, gamma, Y, Yb, acc, ws, tokens, k, n_out, s);
 }
 
 }  // namespace bl

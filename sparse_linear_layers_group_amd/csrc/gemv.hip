@@ -94,6 +94,7 @@ struct StripView {
   int32_t k, nkb, row0;
   int64_t n_out;
   float* Y;
+  uint16_t* Yb;  // bf16 outputs instead of Y when not null
   int32_t* acc;  // optional int32 sums
   const float* scale;
   const double* gamma;
@@ -215,14 +216,16 @@ __device__ __forceinline__ void store_strip(const StripView& it, const v4i* c, i
   const int t = lane & 15, g = lane >> 4;
   if (t >= tokens) return;
   const int64_t o = (int64_t)t * it.n_out + row0 + 4 * g;
-  float* y = it.Y + o;
   const bool vec = row0 + kStripRows <= it.n_out && (tokens == 1 || (it.n_out & 3) == 0);
   if (vec) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      st_global(reinterpret_cast<v4f*>(y + 16 * i),
-                v4f{out_value(c[i][0], gs), out_value(c[i][1], gs), out_value(c[i][2], gs),
-                    out_value(c[i][3], gs)});
+      const v4f v = v4f{out_value(c[i][0], gs), out_value(c[i][1], gs), out_value(c[i][2], gs),
+                        out_value(c[i][3], gs)};
+      if (it.Yb)
+        st_global(reinterpret_cast<u32x2*>(it.Yb + o + 16 * i), bf16x4(v));
+      else
+        st_global(reinterpret_cast<v4f*>(it.Y + o + 16 * i), v);
       if (it.acc) st_global(reinterpret_cast<v4i*>(it.acc + o + 16 * i), c[i]);
     }
   } else {
@@ -231,7 +234,11 @@ __device__ __forceinline__ void store_strip(const StripView& it, const v4i* c, i
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (row0 + 16 * i + 4 * g + j < it.n_out) {
-          st_global(y + 16 * i + j, out_value(c[i][j], gs));
+          const float v = out_value(c[i][j], gs);
+          if (it.Yb)
+            st_global(it.Yb + o + 16 * i + j, f32_to_bf16_rne(v));
+          else
+            st_global(it.Y + o + 16 * i + j, v);
           if (it.acc) st_global(it.acc + o + 16 * i + j, (int32_t)c[i][j]);
         }
   }
@@ -392,6 +399,7 @@ struct SingleSrc {
   const char* packed;
   const int8_t* xq;
   float* Y;
+  uint16_t* Yb;
   int32_t* acc;
   const float* scale;
   const double* gamma;
@@ -404,6 +412,7 @@ struct SingleSrc {
     StripView v = make_strip<S>(packed + (int64_t)sid * nkb * kStripRows * block_bytes(S), xq,
                                 tokens, k, n_out, sid * kStripRows);
     v.Y = Y;
+    v.Yb = Yb;
     v.acc = acc;
     v.scale = scale;
     v.gamma = gamma;
@@ -482,6 +491,7 @@ struct GroupSrc {
   __device__ StripView view(const StripDesc& d) const {
     StripView v = make_strip<S>(d.packed, d.xq, tokens, d.k, d.n_out, d.row0);
     v.Y = d.Y;
+    v.Yb = nullptr;
     v.acc = nullptr;
     v.scale = d.scale;
     v.gamma = d.gamma;
@@ -565,12 +575,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_group_kernel(const char* __
 
 template <int S>
 static hipError_t launch_gemv_s(const void* packed, const int8_t* xq, const float* scale,
-                                const double* gamma, float* Y, int32_t* acc, void* ws,
+                                const double* gamma, float* Y, uint16_t* Yb, int32_t* acc, void* ws,
                                 int tokens, int64_t k, int64_t n_out, hipStream_t s) {
   SingleSrc<S> src;
   src.packed = reinterpret_cast<const char*>(packed);
   src.xq = xq;
   src.Y = Y;
+  src.Yb = Yb;
   src.acc = acc;
   src.scale = scale;
   src.gamma = gamma;
@@ -588,12 +599,12 @@ static hipError_t launch_gemv_s(const void* packed, const int8_t* xq, const floa
 }
 
 hipError_t launch_gemv(const void* packed, const int8_t* xq, const float* scale,
-                       const double* gamma, float* Y, int32_t* acc, void* ws, int tokens,
-                       int64_t k, int64_t n_out, int S, hipStream_t s) {
-  if (S == 8) return launch_gemv_s<8>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
-  if (S == 6) return launch_gemv_s<6>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
-  if (S == 2) return launch_gemv_s<2>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
-  return launch_gemv_s<4>(packed, xq, scale, gamma, Y, acc, ws, tokens, k, n_out, s);
+                       const double* gamma, float* Y, uint16_t* Yb, int32_t* acc, void* ws,
+                       int tokens, int64_t k, int64_t n_out, int S, hipStream_t s) {
+  if (S == 8) return launch_gemv_s<8>(packed, xq, scale, gamma, Y, Yb, acc, ws, tokens, k, n_out, s);
+  if (S == 6) return launch_gemv_s<6>(packed, xq, scale, gamma, Y, Yb, acc, ws, tokens, k, n_out, s);
+  if (S == 2) return launch_gemv_s<2>(packed, xq, scale, gamma, Y, Yb, acc, ws, tokens, k, n_out, s);
+  return launch_gemv_s<4>(packed, xq, scale, gamma, Y, Yb, acc, ws, tokens, k, n_out, s);
 }
 
 hipError_t launch_gemv_group(const void* plan, int S, hipStream_t s) {

@@ -154,9 +154,11 @@ inline size_t decode_ws_bytes(int64_t tokens, int64_t n_out) {
   const int64_t strips = (n_out + 63) / 64;
   return ((decode_partial_bytes(tokens, n_out) + 255) & ~(size_t)255) + (size_t)strips * 4;
 }
+// Y (binary32) or Yb (the same values rounded to bf16, ties to even): one of
+// the two is given, the other is null (as in the prefill launchers).
 hipError_t launch_gemv(const void* packed, const int8_t* xq, const float* scale,
-                       const double* gamma, float* Y, int32_t* acc, void* ws, int tokens,
-                       int64_t k, int64_t n_out, int S, hipStream_t s);
+                       const double* gamma, float* Y, uint16_t* Yb, int32_t* acc, void* ws,
+                       int tokens, int64_t k, int64_t n_out, int S, hipStream_t s);
 
 // Grouped decode: one plan in device memory describes many GEMVs that share
 // the token count and N:M pattern; kernels read it, so a run needs only the
@@ -265,8 +267,8 @@ inline size_t gemm_ws_bytes(int64_t tokens, int64_t k, int64_t n_out) {
          (size_t)gemm_tiles(tokens, n_out) * sp * kGemmTileRows * kGemmTileTokens * 4;
 }
 hipError_t launch_gemm(const void* packed, const int8_t* xq, const float* scale,
-                       const double* gamma, float* Y, int32_t* acc, void* ws, int64_t tokens,
-                       int64_t k, int64_t n_out, int S, hipStream_t s);
+                       const double* gamma, float* Y, uint16_t* Yb, int32_t* acc, void* ws,
+                       int64_t tokens, int64_t k, int64_t n_out, int S, hipStream_t s);
 
 // Prefill-shaped contraction of 2:4 codes in the sparse-operand + index
 // layout on the sparse int8 matrix instruction; same tiles, split-k and

@@ -252,3 +252,12 @@ def test_relu2_gate_validation(L):
     assert b(A, A, A, 12, A, A, None) == bl.BL_ESHAPE
     assert b(A, A, A, 16, None, A, None) == bl.BL_EINVAL
     assert b(None, None, None, 0, None, None, None) == bl.BL_OK
+
+
+def test_bf16_outputs_reject_null_y(L):
+    """The bf16-output calls check Y first, with every other pointer valid-looking."""
+    fake = ctypes.c_void_p(1 << 20)
+    st = L.bitlinear_contract_bf16(fake, fake, 1, 128, fake, 64, 6, 8, fake, None, None, None, 0, None)
+    assert st == bl.BL_EINVAL
+    st = L.bitlinear_fwd_bf16(fake, 1, 128, fake, 64, 6, 8, fake, None, fake, fake, None, None, 0, None)
+    assert st == bl.BL_EINVAL

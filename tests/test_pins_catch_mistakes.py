@@ -19,6 +19,7 @@ PIN_FILES = [
     "tests/test_oracle_gamma_ternary.py",
     "tests/test_oracle_actq_fwd.py",
     "tests/test_oracle_bwd_pack.py",
+    "tests/test_oracle_bf16_y.py",
 ]
 
 MUTANTS = {
@@ -44,6 +45,10 @@ MUTANTS = {
     "sp24_value_codes_linear": ("val |= code << (8 * (e % 4) + 2 * (e / 4));", "val |= code << (2 * e);"),
     "sp24_one_nonzero_slot": ("else { pos[1] = pos[0]; pos[0] = 0; }", "else { pos[1] = pos[0] == 3 ? 2 : 3; }"),
     "sp24_lane_groups_swapped": ("(strip * nkb + kb) * 64 + rr % 16 + 16 * q", "(strip * nkb + kb) * 64 + q + 4 * (rr % 16)"),
+    "bf16y_scale_product_in_binary32": ("float g32 = (float)(gamma * (double)s32);", "float g32 = (float)gamma * s32;"),
+    "bf16y_rounded_from_binary64": ("float y32 = a32 * g32;", "float y32 = (float)((double)(int32_t)s * gamma * scale[t]);"),
+    "bf16y_truncated": ("            Y[t * n_out + r] = nearest_bf16(y32);",
+                        "            { uint32_t u; memcpy(&u, &y32, 4); Y[t * n_out + r] = (uint16_t)(u >> 16); }"),
 }
 
 
