@@ -55,8 +55,8 @@ DECODE_TRAFFIC = {
     "sources": ["sparse_linear_layers_group_amd/csrc/gemv.hip",
                 "sparse_linear_layers_group_amd/csrc/common.h",
                 "sparse_linear_layers_group_amd/csrc/launch.h"],
-    "sha256": "e8fac8f8b594082eb36f33058e193dc6845a6b01f0258680f1c0bace42c59e57",
-    "fetch_kib": 39913.0, "fetch_scale": 2.0,
+    "sha256": "29d97cc88a8fcc7ec981c0f6138d4259297a2b517b25fbd5153af57c49c3498b",
+    "fetch_kib": 39919.3, "fetch_scale": 2.0,
     "write_kib": 1188.0, "write_scale": 1.0,
 }
 
@@ -231,31 +231,45 @@ def build_decode(torch, bl, n, m, tokens=1):
         plan = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         bl.bitlinear_fwd_group_plan(items, len(entries), tokens, n, m, plan)
         plans.append(plan)
+        if c == 0:
+            fused = bl.bitlinear_fwd_group_plan_fuses(items, len(entries), tokens, n, m)
     torch.cuda.synchronize()
     per_step = {
         "packed": QWEN05_LAYERS * sum(p.packed.numel() for p in packs),
         "x_bf16": QWEN05_LAYERS * sum(2 * tokens * k for _, _, k in QWEN05_LAYER),
         "x_int8": QWEN05_LAYERS * sum(tokens * k for _, _, k in QWEN05_LAYER),
         "y": QWEN05_LAYERS * sum(4 * tokens * n for _, n, _ in QWEN05_LAYER),
+        "scales": QWEN05_LAYERS * len(QWEN05_LAYER) * 4 * tokens,
     }
     return dict(packs=packs, plans=plans, keep=keep, copies=copies, per_step=per_step,
-                pool_bytes=copies * stack_bytes, ys=ys)
+                pool_bytes=copies * stack_bytes, ys=ys, fused=fused)
 
 
-def time_decode(torch, bl, d, n, m, steps, warmup):
+def time_decode(torch, bl, d, n, m, steps, warmup, one_launch=False):
+    """The decode step on the rotating pool: activation quantisation, then
+    the contraction (two launches).  Returns the step time and the
+    contraction's time (per launch with event pairs, and back to back);
+    with one_launch, also the one-launch step (stage 4) when the plan
+    allows it."""
     plans = d["plans"]
     for i in range(warmup):
         bl.bitlinear_fwd_group(plans[i % len(plans)], n, m, 3)
     torch.cuda.synchronize()
-    # whole steps, back to back
+
     def warm(stages):
         return lambda: [bl.bitlinear_fwd_group(plans[i % len(plans)], n, m, stages) for i in range(10)]
 
-    with Timer(torch, ahead_ms=0.05 * (steps + 10), pre=warm(3)) as t_all:
-        for i in range(steps):
-            bl.bitlinear_fwd_group(plans[i % len(plans)], n, m, 3)
-    ms_total = t_all.ms()
-    # the contraction kernel alone, per launch (events around each launch)
+    def back_to_back(stages, pre_stage=None):
+        if pre_stage:
+            for p in plans:
+                bl.bitlinear_fwd_group(p, n, m, pre_stage)
+        with Timer(torch, ahead_ms=0.05 * (steps + 10), pre=warm(stages)) as t:
+            for i in range(steps):
+                bl.bitlinear_fwd_group(plans[i % len(plans)], n, m, stages)
+        return t.ms() / steps
+
+    step_ms = back_to_back(3)
+    # the contraction alone, per launch (events around each launch)
     evs = []
     for i in range(steps):
         bl.bitlinear_fwd_group(plans[i % len(plans)], n, m, 1)
@@ -266,14 +280,13 @@ def time_decode(torch, bl, d, n, m, steps, warmup):
         b.record()
         evs.append((a, b))
     torch.cuda.synchronize()
-    gemv_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    kernel_pairs_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
     # the contraction alone, back to back (activations quantised once per plan)
-    for p in plans:
-        bl.bitlinear_fwd_group(p, n, m, 1)
-    with Timer(torch, ahead_ms=0.05 * (steps + 10), pre=warm(2)) as t_b2b:
-        for i in range(steps):
-            bl.bitlinear_fwd_group(plans[i % len(plans)], n, m, 2)
-    return ms_total / steps, gemv_ms, t_b2b.ms() / steps
+    kernel_ms = back_to_back(2, pre_stage=1)
+    out = dict(step_ms=step_ms, kernel_ms=kernel_ms, kernel_pairs_ms=kernel_pairs_ms)
+    if one_launch and d["fused"]:
+        out["one_launch_ms"] = back_to_back(4)
+    return out
 
 
 def single_call_latency(torch, bl, d, iters=200):
@@ -305,12 +318,15 @@ def single_call_latency(torch, bl, d, iters=200):
 
 
 def verify_decode_sample(torch, d, n, m):
-    """Sampled check of the grouped results against the oracle (one layer)."""
+    """Sampled check of the grouped results (the step as timed) against the
+    oracle (one layer)."""
     import numpy as np
     import oracle
     from sparse_linear_layers_group_amd import synth
     bl_plan = d["plans"][0]
     from sparse_linear_layers_group_amd import bitlinear as bl
+    for y in d["ys"]:
+        y.fill_(float("nan"))
     bl.bitlinear_fwd_group(bl_plan, n, m, 3)
     torch.cuda.synchronize()
     worst = 0.0
@@ -835,16 +851,18 @@ def main():
     d68 = build_decode(torch, bl, 6, 8)
     log(f"decode pool: {d68['copies']} copies, {d68['pool_bytes'] / 2**20:.0f} MiB ({time.perf_counter() - t_setup:.1f} s)")
     worst = verify_decode_sample(torch, d68, 6, 8)
-    step_ms, gemv_ms, gemv_b2b_ms = time_decode(torch, bl, d68, 6, 8, args.steps, args.warmup)
+    td = time_decode(torch, bl, d68, 6, 8, args.steps, args.warmup, one_launch=True)
+    step_ms, gemv_ms, gemv_b2b_ms = td["step_ms"], td["kernel_pairs_ms"], td["kernel_ms"]
     ps = d68["per_step"]
     step_bytes = ps["packed"] + ps["x_bf16"] + ps["y"]
     value = step_bytes / (step_ms * 1e-3) / 1e9
     gemv_bytes = ps["packed"] + ps["x_int8"] + ps["y"]
-    # kernel time: back-to-back contraction launches (events on the launch
-    # stream around the batch); per-launch event pairs add ~2-3 us of event
-    # overhead and are reported beside it
+    kname = "gemv_group_kernel<6, false> (grouped decode contraction)"
+    # kernel time: back-to-back launches (events on the launch stream around
+    # the batch); per-launch event pairs add ~2-3 us of event overhead and
+    # are reported beside it
     achieved = gemv_bytes / (gemv_b2b_ms * 1e-3) / 1e9
-    log(f"decode 6:8: step {step_ms * 1000:.1f} us, {value:.0f} GB/s; contraction {gemv_b2b_ms * 1000:.1f} us, {achieved:.0f} GB/s")
+    log(f"decode 6:8: step {step_ms * 1000:.1f} us, {value:.0f} GB/s; kernel {gemv_b2b_ms * 1000:.1f} us, {achieved:.0f} GB/s")
 
     out = {
         "metric": "6:8 BitLinear GB/s (decode) & int8 TOPS (prefill), % roofline, speedup vs 8:8",
@@ -863,6 +881,7 @@ def main():
             "workload": "Qwen2.5-0.5B-shaped decode, 1 token, 6:8: q 896->896, k/v 896->128, o 896->896, "
                         "gate/up 896->4864, down 4864->896 BitLinear GEMVs x 24 layers = 168 GEMVs per step, "
                         "grouped into one activation-quant launch + one contraction launch",
+            "launches_per_step": 2,
             "grouped": True,
             "layers_per_step": QWEN05_LAYERS,
             "tokens": 1,
@@ -871,7 +890,7 @@ def main():
             "bytes_per_step": step_bytes,
         },
         "roofline": {
-            "kernel": "gemv_group_kernel<6> (grouped decode contraction)",
+            "kernel": kname,
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
@@ -884,16 +903,24 @@ def main():
         },
         "check": {"decode_vs_oracle_max_rel_err": worst},
     }
+    if "one_launch_ms" in td:
+        # stage 4: every workgroup quantises its items' rows itself (slower:
+        # each row is quantised by every workgroup that contracts it)
+        out["one_launch_step"] = {
+            "step_us": round(td["one_launch_ms"] * 1000, 3),
+            "speedup_vs_two_launches": round(step_ms / td["one_launch_ms"], 4),
+        }
     if not args.quick:
         d88 = build_decode(torch, bl, 8, 8)
-        s88, _, g88 = time_decode(torch, bl, d88, 8, 8, args.steps, args.warmup)
+        t88 = time_decode(torch, bl, d88, 8, 8, args.steps, args.warmup)
+        s88, g88 = t88["step_ms"], t88["kernel_ms"]
         out["vs_8_8"] = {
             "step_speedup": round(s88 / step_ms, 4),
             "contraction_speedup": round(g88 / gemv_b2b_ms, 4),
             "bytes_ratio": round(d88["per_step"]["packed"] / ps["packed"], 4),
             "step_ms_8_8": round(s88, 5),
             "contraction_us_8_8": round(g88 * 1000, 3),
-            "contraction_gbs_8_8": round((d88["per_step"]["packed"] + ps["x_int8"] + ps["y"]) / (g88 * 1e-3) / 1e9, 2),
+            "kernel_gbs_8_8": round((gemv_bytes - ps["packed"] + d88["per_step"]["packed"]) / (g88 * 1e-3) / 1e9, 2),
         }
         log(f"decode 8:8: step {s88 * 1000:.1f} us, contraction {g88 * 1000:.1f} us")
         out["single_call_us"] = single_call_latency(torch, bl, d68)
@@ -904,7 +931,8 @@ def main():
         sweep = {}
         for n, m in ((4, 8), (3, 8), (2, 8), (2, 4)):
             dn = build_decode(torch, bl, n, m)
-            sn, _, gn = time_decode(torch, bl, dn, n, m, args.steps, args.warmup)
+            tn = time_decode(torch, bl, dn, n, m, args.steps, args.warmup)
+            sn, gn = tn["step_ms"], tn["kernel_ms"]
             pk = dn["per_step"]["packed"]
             sweep[f"{n}:{m}"] = {
                 "step_us": round(sn * 1000, 3),

@@ -268,7 +268,16 @@ int bitlinear_contract_sp24(const int8_t *xq, const float *x_scale,
  *          by bitlinear_fwd_group_plan (which synchronises `stream` once);
  *          it must stay allocated and unchanged while the plan is used.
  *   stages 1 = activation quantisation only, 2 = contraction only (x_q and
- *          x_scale already written), 3 = both.
+ *          x_scale already written), 3 = both (two launches), 4 = both in
+ *          one launch: each workgroup quantises the activation rows of the
+ *          items it contracts into its LDS (x_q and x_scale are still
+ *          written, once per item); results identical to 3.  Stage 4 needs
+ *          a plan whose workgroups' activation rows fit their LDS and
+ *          split into at most 64 segments of up to 1024 values (rows of
+ *          k values take ceil(k / 1024)) per workgroup
+ *          (bitlinear_fwd_group_plan_fuses() == 1, e.g. decode plans of
+ *          one token); run on any other plan it sets every Y to a quiet NaN
+ *          (status BL_OK: the host does not read the plan back).
  * n, m passed to bitlinear_fwd_group must be those the plan was made with;
  * the plan records its sign-slot count, and a contraction run whose n:m
  * has another count (4:8, 3:8 and 2:4 share one) reads no packed byte and
@@ -290,6 +299,14 @@ int bitlinear_fwd_group_plan(const bitlinear_fwd_item *items, int count,
                              int64_t tokens, int n, int m, void *plan,
                              size_t plan_bytes, void *stream);
 int bitlinear_fwd_group(const void *plan, int n, int m, int stages, void *stream);
+
+/* 1 when the plan bitlinear_fwd_group_plan would build for these items can
+ * run stage 4 (every workgroup's activation rows fit its LDS and its 64
+ * segment slots), 0 when not,
+ * minus the status (BL_EINVAL, BL_ESHAPE) for invalid items.  Host only: the plan is built in
+ * host memory and discarded. */
+int bitlinear_fwd_group_plan_fuses(const bitlinear_fwd_item *items, int count,
+                                   int64_t tokens, int n, int m);
 
 /* The bytes bitlinear_fwd_group_plan uploads, written to host memory
  * instead (image: image_bytes >= bitlinear_fwd_group_plan_bytes(), any

@@ -53,6 +53,7 @@ _SIGS = {
     "bitlinear_fwd_group_plan_bytes": (_sz, [_vp, _int, _i64]),
     "bitlinear_fwd_group_plan": (_int, [_vp, _int, _i64, _int, _int, _vp, _sz, _vp]),
     "bitlinear_fwd_group_plan_host": (_int, [_vp, _int, _i64, _int, _int, _vp, _sz]),
+    "bitlinear_fwd_group_plan_fuses": (_int, [_vp, _int, _i64, _int, _int]),
     "bitlinear_fwd_group": (_int, [_vp, _int, _int, _int, _vp]),
     "bitlinear_quant_group_workspace_bytes": (_sz, [_vp, _int]),
     "bitlinear_quant_group_plan_bytes": (_sz, [_vp, _int]),
@@ -344,6 +345,14 @@ def bitlinear_fwd_group_plan_host(items, count, tokens, n, m, image):
     st = lib().bitlinear_fwd_group_plan_host(items, int(count), int(tokens), n, m,
                                              image.ctypes.data_as(ctypes.c_void_p), image.nbytes)
     _check(st, "bitlinear_fwd_group_plan_host")
+
+
+def bitlinear_fwd_group_plan_fuses(items, count, tokens, n, m):
+    """True when the plan for these items can run stage 4 (one launch)."""
+    st = lib().bitlinear_fwd_group_plan_fuses(items, int(count), int(tokens), n, m)
+    if st < 0:
+        _check(-st, "bitlinear_fwd_group_plan_fuses")
+    return st == 1
 
 
 def bitlinear_fwd_group(plan, n, m, stages=3, stream=None):

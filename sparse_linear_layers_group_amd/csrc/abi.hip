@@ -529,7 +529,7 @@ int fwd_group_image(const bitlinear_fwd_item* items, int count, int64_t tokens, 
   int64_t r = 0;
   // every strip of every item: its descriptor and step count
   std::vector<bl::StripDesc> all;
-  std::vector<int32_t> nkb;
+  std::vector<int32_t> nkb, item_of;
   all.reserve((size_t)nstrips);
   for (int i = 0; i < count; ++i) {
     const bitlinear_fwd_item& it = items[i];
@@ -544,6 +544,7 @@ int fwd_group_image(const bitlinear_fwd_item* items, int count, int64_t tokens, 
                                   it.xq, it.Y, it.x_scale, it.gamma, it.n_out, (int32_t)it.k,
                                   (int32_t)(st * bl::kStripRows)});
       nkb.push_back((int32_t)(it.k / 128));
+      item_of.push_back(i);
     }
   }
   // whole strips to workgroups, longest first onto the least loaded (LPT);
@@ -565,6 +566,74 @@ int fwd_group_image(const bitlinear_fwd_item* items, int count, int64_t tokens, 
   }
   bl::WaveStart* wst = reinterpret_cast<bl::WaveStart*>(img.data() + bl::group_waves_offset());
   bl::StripDesc* descs = reinterpret_cast<bl::StripDesc*>(img.data() + bl::group_strips_offset(count * tokens));
+  // fused runs: each workgroup's items (in order of first use) get LDS room
+  // for their codes, then their scales, after the code tables; an item's
+  // first workgroup writes its x_q and x_scale.  Every (item, token) row is
+  // cut into segments of at most kFusedSegVals values, numbered in that
+  // order and dealt round-robin to the 16 wavefronts.  The plan fuses when
+  // every workgroup's room and segment count fit.
+  bl::FusedSeg* fseg = reinterpret_cast<bl::FusedSeg*>(img.data() + bl::group_fused_offset());
+  bool fused = true;
+  std::vector<char> written((size_t)count, 0);
+  for (int64_t b = 0; b < nb; ++b) {
+    std::vector<int32_t>& lst = lists[(size_t)b];
+    std::sort(lst.begin(), lst.end());  // (item, strip) order: an item's strips are adjacent
+    std::vector<int32_t> its;
+    for (int32_t j : lst)
+      if (its.empty() || its.back() != item_of[j]) its.push_back(item_of[j]);
+    std::vector<uint32_t> xo(its.size()), so(its.size());
+    uint64_t off = 0;
+    for (size_t q = 0; q < its.size(); ++q) {
+      xo[q] = (uint32_t)off;
+      off += ((uint64_t)tokens * (uint64_t)items[its[q]].k + 15) / 16 * 16;
+    }
+    for (size_t q = 0; q < its.size(); ++q) {
+      so[q] = (uint32_t)off;
+      off += ((uint64_t)tokens * 4 + 15) / 16 * 16;
+    }
+    if (off > (uint64_t)bl::kFusedCodeBytes) fused = false;
+    int64_t g = 0;  // segments of the workgroup so far
+    for (size_t q = 0; q < its.size(); ++q) {
+      const bitlinear_fwd_item& it = items[its[q]];
+      const bool writer = !written[(size_t)its[q]];
+      written[(size_t)its[q]] = 1;
+      const int64_t per_row = (it.k + bl::kFusedSegVals - 1) / bl::kFusedSegVals;
+      for (int64_t t = 0; t < tokens; ++t) {
+        const int64_t g_row = g;
+        for (int64_t v0 = 0; v0 < it.k; v0 += bl::kFusedSegVals, ++g) {
+          if (g >= bl::kFusedSegsPerBlock) {
+            fused = false;
+            continue;
+          }
+          bl::FusedSeg& f = fseg[(b * bl::kDecodeWavesPerBlock + g % bl::kDecodeWavesPerBlock) *
+                                     bl::kFusedSegsPerWave +
+                                 g / bl::kDecodeWavesPerBlock];
+          const int64_t o = t * it.k + v0;
+          f.x = it.X + o;
+          f.xq = writer ? it.xq + o : nullptr;
+          f.scale = writer && v0 == 0 ? it.x_scale + t : nullptr;
+          f.lds_q = xo[q] + (uint32_t)o;
+          f.lds_s = so[q] + 4 * (uint32_t)t;
+          f.nvals = (int32_t)std::min<int64_t>(bl::kFusedSegVals, it.k - v0);
+          f.slot = (int16_t)g;
+          f.row_slot = (int16_t)g_row;
+          f.row_slots = (int16_t)per_row;
+          f.first = v0 == 0 ? 1 : 0;
+        }
+      }
+    }
+    size_t q = 0;
+    for (int32_t j : lst) {
+      while (its[q] != item_of[j]) ++q;
+      all[j].pad[0] = (int32_t)xo[q];
+      all[j].pad[1] = (int32_t)so[q];
+    }
+  }
+  // a plan that does not fuse carries no segments (its fused runs write
+  // NaN outputs and read nothing else)
+  if (!fused)
+    std::memset(fseg, 0, (size_t)nb * bl::kFusedSegsPerBlock * sizeof(bl::FusedSeg));
+  h->fused = fused ? 1 : 0;
   int32_t next = 0;
   for (int64_t b = 0; b < nb; ++b) {
     std::vector<int32_t>& lst = lists[(size_t)b];
@@ -611,17 +680,34 @@ int bitlinear_fwd_group_plan_host(const bitlinear_fwd_item* items, int count, in
   return ok();
 }
 
+int bitlinear_fwd_group_plan_fuses(const bitlinear_fwd_item* items, int count, int64_t tokens, int n,
+                                   int m) {
+  // errors come back negated (1 and 0 are answers)
+  int64_t steps = 0, strips = 0;
+  int st = group_shape(items, count, tokens, &steps, &strips);
+  if (st != BL_OK) return -st;
+  std::vector<char> img;
+  st = fwd_group_image(items, count, tokens, n, m, reinterpret_cast<void*>(16),
+                       bl::group_plan_bytes(strips, count, count * tokens), img);
+  if (st != BL_OK) return -st;
+  return reinterpret_cast<const bl::GroupHeader*>(img.data())->fused ? 1 : 0;
+}
+
 int bitlinear_fwd_group(const void* plan, int n, int m, int stages, void* stream) {
   TRY(check_nm(n, m));
   TRY(check_ptr(plan, 16, "plan"));
-  if (stages < 1 || stages > 3) return fail(BL_EINVAL, "stages must be 1, 2 or 3 (got %d)", stages);
+  if (stages < 1 || stages > 4) return fail(BL_EINVAL, "stages must be 1, 2, 3 or 4 (got %d)", stages);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (stages == 4) {
+    hipError_t e = bl::launch_gemv_group(plan, bl::s_of(n, m), true, s);
+    return e != hipSuccess ? hip_status(e, "fused grouped decode launch") : ok();
+  }
   if (stages & 1) {
     hipError_t e = bl::launch_act_quant_group(plan, s);
     if (e != hipSuccess) return hip_status(e, "grouped activation launch");
   }
   if (stages & 2) {
-    hipError_t e = bl::launch_gemv_group(plan, bl::s_of(n, m), s);
+    hipError_t e = bl::launch_gemv_group(plan, bl::s_of(n, m), false, s);
     if (e != hipSuccess) return hip_status(e, "grouped decode launch");
   }
   return ok();

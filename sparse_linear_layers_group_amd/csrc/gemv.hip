@@ -33,6 +33,7 @@
 //  * The grouped kernel runs many GEMVs (same token count and pattern) from
 //    one device-resident plan in a single launch; the plan gives every
 //    workgroup whole strips, packed on the host for equal step counts.
+#include "actq.h"
 #include "common.h"
 #include "launch.h"
 
@@ -96,6 +97,7 @@ struct StripView {
   float* Y;
   uint16_t* Yb;  // bf16 outputs instead of Y when not null
   int32_t* acc;  // optional int32 sums
+  uint32_t x_lds, s_lds;  // fused runs: LDS byte offsets of the item's codes and scales
   const float* scale;
   const double* gamma;
 };
@@ -133,7 +135,10 @@ struct Stage {
   double gm;
 };
 
-template <int S>
+// kLdsX: the activations come from the workgroup's LDS copy (fused runs),
+// read when the step is decoded (lds_operands), not here: the first steps
+// are issued before the copy exists
+template <int S, bool kLdsX>
 __device__ __forceinline__ void issue(Stage<S>& st, const Cursor& cur, bool live, int lane,
                                       int tokens) {
   constexpr int kBytes = block_bytes(S);
@@ -162,20 +167,49 @@ __device__ __forceinline__ void issue(Stage<S>& st, const Cursor& cur, bool live
   }
   // B operand of k half h: token t = lane%16, k slice lane/16.  Columns
   // t >= tokens are never stored, so those lanes read token 0 (in range).
-  const int t = lane & 15, g = lane >> 4;
-  const uint32_t xo = (uint32_t)((t < tokens ? t : 0) * cur.sv.k + cur.kb * kBlockK + 16 * g);
+  if constexpr (!kLdsX) {
+    const int t = lane & 15, g = lane >> 4;
+    const uint32_t xo = (uint32_t)((t < tokens ? t : 0) * cur.sv.k + cur.kb * kBlockK + 16 * g);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(cur.sv.xr, xo + 64 * h, 0, 0);
-    st.b[h] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(cur.sv.xr, xo + 64 * h, 0, 0);
+      st.b[h] = v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    }
   }
 }
 
+// A zero the compiler cannot see through.  Each strip's first stage loads
+// its own copy of the strip's scales: merged with an earlier stage's
+// identical load, the stage's registers became a copy of that one, and the
+// copy waited for every load in flight.
+__device__ __forceinline__ uint32_t opaque_zero() {
+  uint32_t z;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  return z;
+}
+
+// Fused runs: the B operands of the step the compute cursor is at, and its
+// strip's token scale, from the LDS copy
 template <int S>
+__device__ __forceinline__ void lds_operands(Stage<S>& st, const Cursor& cur, int lane, int tokens,
+                                             const char* lds_x) {
+  typedef __attribute__((address_space(3))) char lds_char;
+  const int t = lane & 15, g = lane >> 4;
+  const int tt = t < tokens ? t : 0;
+  const uint32_t xo = cur.sv.x_lds + (uint32_t)(tt * cur.sv.k + cur.kb * kBlockK + 16 * g);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    st.b[h] = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>((const lds_char*)lds_x + xo + 64 * h);
+  st.sc = *reinterpret_cast<const __attribute__((address_space(3))) float*>(
+      (const lds_char*)lds_x + cur.sv.s_lds + 4 * tt + opaque_zero());
+}
+
+template <int S, bool kLdsX>
 __device__ __forceinline__ void issue_scale(Stage<S>& st, const Cursor& cur, int lane, int tokens) {
   const int t = lane & 15;
-  st.sc = ld_global(&cur.sv.scale[t < tokens ? t : 0]);
-  st.gm = ld_global(cur.sv.gamma);
+  const uint32_t z = opaque_zero();
+  if constexpr (!kLdsX) st.sc = ld_global(&cur.sv.scale[(t < tokens ? t : 0) + z]);
+  st.gm = ld_global(cur.sv.gamma + z);
 }
 
 // A operand of MFMA m = 2i + h: codes of fields 2m and 2m+1 of the chunk
@@ -265,6 +299,9 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut,
   // the table reads go first (they depend on nothing); the first steps'
   // loads are in flight while the workgroup builds the code tables
   const LutVals lv = load_lut();
+  // fused runs: the workgroup's activation segments, issued before the
+  // first weight loads so that they return first (loads complete in order)
+  const typename Src::Rows rows = src.load_rows(lane);
   const int tokens = src.tokens;
   const int w = wave_id();
   const uint32_t* lut_lane = lut + (lane & (kLutCopies - 1));
@@ -287,38 +324,49 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut,
   // once the load cursor has issued the last step it stops for good:
   // advance() may read the plan, and must never step past the range
   bool l_first = true, c_first = true;
-  float cur_sc = 0.f;
-  double cur_gm = 0.0;
-  float first_gs = 0.f;  // output scale of the wavefront's first strip
+  // output scale of the current strip, and of the wavefront's first strip.
+  // Formed from the stage's registers when the strip's first step is
+  // decoded: a plain copy of them let the compiler share the registers with
+  // the ring, and every back edge then copied the next stage's scales out
+  // of their load registers, waiting for all loads in flight.
+  float cur_gs = 0.f;
+  float first_gs = 0.f;
   auto load_step = [&](Stage<S>& st) {
-    issue<S>(st, L, live, lane, tokens);
-    if (L.kb == 0 || l_first) issue_scale<S>(st, L, lane, tokens);  // wave-uniform
+    issue<S, Src::kLdsX>(st, L, live, lane, tokens);
+    if (L.kb == 0 || l_first) issue_scale<S, Src::kLdsX>(st, L, lane, tokens);  // wave-uniform
     l_first = false;
     if (live) {
       if (--lleft == 0) live = false;
       else src.advance(L);
     }
   };
-  if (count > 0) {
+  // issued by idle wavefronts too (past-the-end offsets read zeros): the
+  // same loads on every path keep the compiler's completion counts exact,
+  // so the tables (loaded first) are written without waiting for the steps
 #pragma unroll
-    for (int s = 0; s < kDepth - 1; ++s) load_step(ring[s]);
-  }
+  for (int s = 0; s < kDepth - 1; ++s) load_step(ring[s]);
   // lane v < 16 holds wavefront v's (first strip, first k block, step
   // count) for the end phase (no loads there); read after the first steps'
   // loads so that nothing waits for it before then
   const v4i winfo = src.wave_info(lane & 15);
   write_lut(lut, lv);
+  if constexpr (Src::kLdsX) {
+    // fused runs: segment maxima, then the codes from registers
+    src.publish_max(rows, lane);
+    __syncthreads();
+    src.quantise(rows, lane);
+  }
   __syncthreads();
   if (count > 0) {
     while (cleft > 0) {
 #pragma unroll
       for (int s = 0; s < kDepth; ++s) {
         load_step(ring[(s + kDepth - 1) % kDepth]);
+        if constexpr (Src::kLdsX) lds_operands<S>(ring[s], C, lane, tokens, src.lds_x);
         decode_step<S>(ring[s], c, lut_lane);
         if (C.kb == 0 || c_first) {  // the strip's scales came with this step
-          cur_sc = ring[s].sc;
-          cur_gm = ring[s].gm;
-          if (c_first) first_gs = out_scale(cur_gm, cur_sc);
+          cur_gs = out_scale(ring[s].gm, ring[s].sc);
+          if (c_first) first_gs = cur_gs;
           c_first = false;
         }
         --cleft;
@@ -329,7 +377,7 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut,
             for (int i = 0; i < 4; ++i) cf[i] = c[i];
             first_open = false;
           } else {
-            store_strip(C.sv, c, lane, tokens, out_scale(cur_gm, cur_sc));
+            store_strip(C.sv, c, lane, tokens, cur_gs);
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) c[i] = v4i{0, 0, 0, 0};
@@ -387,7 +435,7 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut,
     else
       // the scales came with the strip's first step (no load here: one at
       // the end of the kernel would expose a full memory latency)
-      store_strip(sv, tot, lane, tokens, last ? out_scale(cur_gm, cur_sc) : first_gs);
+      store_strip(sv, tot, lane, tokens, last ? cur_gs : first_gs);
   }
 }
 
@@ -396,6 +444,8 @@ __device__ __forceinline__ void run_block(const Src& src, uint32_t* lut,
 // a workgroup boundary meets in the workspace.  sid = strip index.
 template <int S>
 struct SingleSrc {
+  static constexpr bool kLdsX = false;
+  const char* lds_x;  // unused
   const char* packed;
   const int8_t* xq;
   float* Y;
@@ -414,6 +464,8 @@ struct SingleSrc {
     v.Y = Y;
     v.Yb = Yb;
     v.acc = acc;
+    v.x_lds = 0;
+    v.s_lds = 0;
     v.scale = scale;
     v.gamma = gamma;
     return v;
@@ -443,6 +495,8 @@ struct SingleSrc {
     const int32_t sid = (int32_t)(s0 / nkb);
     return v4i{sid, (int32_t)(s0 - (int64_t)sid * nkb), (int32_t)(s1 - s0), 0};
   }
+  struct Rows {};
+  __device__ Rows load_rows(int) const { return Rows{}; }
   // does strip `sid` continue in another workgroup?
   __device__ bool cross(int32_t sid) const {
     const int64_t b = blockIdx.x;
@@ -481,18 +535,26 @@ struct SingleSrc {
 };
 
 // --------------------------------------------------------------- grouped
-// sid = index of the strip descriptor in the plan
-template <int S>
+// sid = index of the strip descriptor in the plan.  kFused: the workgroup
+// quantises the activation rows of its items into LDS first (segments of
+// them, the wavefront's own read with its start record), and its steps
+// read their B operands and scales there.
+template <int S, bool kFused>
 struct GroupSrc {
+  static constexpr bool kLdsX = kFused;
   const StripDesc* strips;
   const WaveStart* starts;
   WaveStart mine;  // this wavefront's start record, read at entry
   int tokens;
+  const char* lds_x;  // fused: LDS base of the activation codes
+  FusedSeg seg[kFused ? kFusedSegsPerWave : 1];  // fused: this wavefront's segments
   __device__ StripView view(const StripDesc& d) const {
     StripView v = make_strip<S>(d.packed, d.xq, tokens, d.k, d.n_out, d.row0);
     v.Y = d.Y;
     v.Yb = nullptr;
     v.acc = nullptr;
+    v.x_lds = (uint32_t)d.pad[0];
+    v.s_lds = (uint32_t)d.pad[1];
     v.scale = d.scale;
     v.gamma = d.gamma;
     return v;
@@ -513,14 +575,89 @@ struct GroupSrc {
     r.first.sv = view(ws.first);
     return r;
   }
-  // (first strip, first k block, step count) of wavefront v: the 16 bytes
-  // after the wave start's descriptor
+  // (first strip, first k block, step count) of wavefront v: the 12 bytes
+  // after the wave start's descriptor.  Only those three are loaded: with a
+  // fourth, unused word in the load, the compiler reused its register at
+  // once and waited for the load (the newest of all) before the tables.
   __device__ v4i wave_info(int v) const {
-    return ld_global(reinterpret_cast<const v4i*>(&starts[(int64_t)blockIdx.x * kGemvWaves + v].rec));
+    const u32x3 r = ld_global(reinterpret_cast<const u32x3*>(&starts[(int64_t)blockIdx.x * kGemvWaves + v].rec));
+    return v4i{(int)r.x, (int)r.y, (int)r.z, 0};
   }
   // the plan never cuts a strip between workgroups
   __device__ bool cross(int32_t) const { return false; }
   __device__ void cross_sum(const StripView&, int32_t, const v4i*, int) const {}
+
+  // Fused runs.  Lane l holds values [8l, 8l + 8) and [512 + 8l, ...) of
+  // each of the wavefront's segments.  Every load and store below is issued
+  // whatever the segment count: buffer accesses past a segment's end (or of
+  // a missing segment, an empty buffer) read zeros and store nothing, so
+  // the loads' completion counts stay exact and nothing waits early.
+  struct Rows {
+    u32x4 v[kFused ? kFusedSegsPerWave : 1][2];
+  };
+  __device__ Rows load_rows(int lane) const {
+    Rows r;
+    if constexpr (kFused) {
+#pragma unroll
+      for (int j = 0; j < kFusedSegsPerWave; ++j) {
+        const __amdgpu_buffer_rsrc_t x = rsrc(seg[j].x, 2 * (uint32_t)seg[j].nvals);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          r.v[j][h] = __builtin_amdgcn_raw_buffer_load_b128(x, 16 * lane + 1024 * h, 0, 0);
+      }
+    }
+    return r;
+  }
+  __device__ static float seg_absmax(const Rows& r, int j) {
+    return fmaxf(absmax8(make_uint4(r.v[j][0].x, r.v[j][0].y, r.v[j][0].z, r.v[j][0].w)),
+                 absmax8(make_uint4(r.v[j][1].x, r.v[j][1].y, r.v[j][1].z, r.v[j][1].w)));
+  }
+  typedef __attribute__((address_space(3))) float lds_float;
+  __device__ lds_float* max_slots() const {
+    typedef __attribute__((address_space(3))) char lds_char;
+    return reinterpret_cast<lds_float*>((lds_char*)lds_x + kFusedCodeBytes);
+  }
+  // each segment's absmax into its LDS slot
+  __device__ void publish_max(const Rows& r, int lane) const {
+    if constexpr (kFused) {
+      lds_float* slots = max_slots();
+#pragma unroll
+      for (int j = 0; j < kFusedSegsPerWave; ++j) {
+        const float a = wave_max(seg_absmax(r, j));
+        if (seg[j].nvals > 0 && lane == 0) slots[seg[j].slot] = a;
+      }
+    }
+  }
+  // the row's absmax (maximum over its segments' slots), then the codes
+  // into LDS and, in the writer, into x_q and x_scale -- exactly as the
+  // activation kernel forms them (quant8 / absmax8, s = a / 127)
+  __device__ void quantise(const Rows& r, int lane) const {
+    if constexpr (kFused) {
+      typedef __attribute__((address_space(3))) char lds_char;
+      const lds_float* slots = max_slots();
+#pragma unroll
+      for (int j = 0; j < kFusedSegsPerWave; ++j) {
+        const FusedSeg& f = seg[j];
+        const float a = wave_max(lane < f.row_slots ? slots[f.row_slot + lane] : 0.f);
+        const __amdgpu_buffer_rsrc_t xq = rsrc(f.xq, f.xq ? (uint32_t)f.nvals : 0u);
+        const __amdgpu_buffer_rsrc_t sc = rsrc(f.scale, f.scale ? 4u : 0u);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 x = r.v[j][h];
+          const uint2 q = quant8(make_uint4(x.x, x.y, x.z, x.w), a);
+          const int v = 512 * h + 8 * lane;
+          if (f.nvals > 0 && v < f.nvals)
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+                (lds_char*)lds_x + f.lds_q + (uint32_t)v) = u32x2{q.x, q.y};
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{q.x, q.y}, xq, (uint32_t)v, 0, 0);
+        }
+        const float s = a / 127.0f;
+        if (f.first && lane == 0)
+          *reinterpret_cast<__attribute__((address_space(3))) float*>((lds_char*)lds_x + f.lds_s) = s;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), sc, lane == 0 ? 0u : kOOB, 0, 0);
+      }
+    }
+  }
 };
 
 template <int S>
@@ -542,10 +679,11 @@ __device__ __noinline__ void poison_outputs(const char* plan, const GroupHeader*
   }
 }
 
-template <int S>
+template <int S, bool kFused>
 __global__ __launch_bounds__(kGemvThreads) void gemv_group_kernel(const char* __restrict__ plan) {
-  __shared__ __attribute__((aligned(16))) uint32_t lut[256 * 2 * kLutCopies];
-  GroupSrc<S> src;
+  // fused runs keep the workgroup's activation codes after the tables
+  __shared__ __attribute__((aligned(16))) uint32_t lut[kFused ? 160 * 1024 / 4 : 256 * 2 * kLutCopies];
+  GroupSrc<S, kFused> src;
   src.starts = reinterpret_cast<const WaveStart*>(plan + group_waves_offset());
   // The header fields and this wavefront's whole start record are read
   // before the first branch, in one round trip (read after the header
@@ -556,20 +694,39 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_group_kernel(const char* __
   const int64_t rows = hdr->rows;
   const int32_t h_s = hdr->S;
   src.tokens = hdr->tokens;
+  // fused runs: the plan's flag and this wavefront's segments, in the same
+  // round trip
+  int32_t h_fused = 1;
+  if constexpr (kFused) {
+    h_fused = hdr->fused;
+    const FusedSeg* fs = reinterpret_cast<const FusedSeg*>(plan + group_fused_offset()) +
+                         ((int64_t)blockIdx.x * kGemvWaves + wave_id()) * kFusedSegsPerWave;
+#pragma unroll
+    for (int j = 0; j < kFusedSegsPerWave; ++j) src.seg[j] = fs[j];
+  }
   src.mine = src.starts[(int64_t)blockIdx.x * kGemvWaves + wave_id()];
+  if constexpr (kFused) {
+    static_assert(kFusedSegsPerWave == 4, "one wait for all segment records");
+#define BL_SEG_OPS(j) "+s"(src.seg[j].x), "+s"(src.seg[j].xq), "+s"(src.seg[j].scale), \
+    "+s"(src.seg[j].lds_q), "+s"(src.seg[j].lds_s), "+s"(src.seg[j].nvals)
+    asm volatile("" : BL_SEG_OPS(0), BL_SEG_OPS(1), BL_SEG_OPS(2), BL_SEG_OPS(3), "+s"(h_fused));
+#undef BL_SEG_OPS
+  }
   asm volatile("" : "+s"(src.mine.first.packed), "+s"(src.mine.first.xq), "+s"(src.mine.first.Y),
                "+s"(src.mine.first.scale), "+s"(src.mine.first.gamma), "+s"(src.mine.first.n_out),
                "+s"(src.mine.first.k), "+s"(src.mine.first.row0), "+s"(src.mine.rec), "+s"(src.mine.kb),
                "+s"(src.mine.count), "+s"(src.mine.active) : "s"(h_s), "s"(rows), "s"(src.tokens));
-  if (h_s != S) {
-    // a plan made for another sign-slot count: its strips are laid out for
-    // that count, so no packed byte is read; every output becomes a quiet
-    // NaN instead
+  if (h_s != S || !h_fused) {
+    // a plan made for another sign-slot count (its strips are laid out for
+    // that count), or a fused run of a plan whose workgroups' activations
+    // do not fit LDS or the segment slots: no packed byte is read; every
+    // output becomes a quiet NaN instead
     poison_outputs(plan, hdr);
     return;
   }
   if (!src.mine.active) return;
   src.strips = reinterpret_cast<const StripDesc*>(plan + group_strips_offset(rows));
+  src.lds_x = reinterpret_cast<const char*>(lut + kDecodeLutBytes / 4);
   run_block<S>(src, lut, threadIdx.x & 63);
 }
 
@@ -578,6 +735,7 @@ static hipError_t launch_gemv_s(const void* packed, const int8_t* xq, const floa
                                 const double* gamma, float* Y, uint16_t* Yb, int32_t* acc, void* ws,
                                 int tokens, int64_t k, int64_t n_out, hipStream_t s) {
   SingleSrc<S> src;
+  src.lds_x = nullptr;
   src.packed = reinterpret_cast<const char*>(packed);
   src.xq = xq;
   src.Y = Y;
@@ -607,12 +765,18 @@ hipError_t launch_gemv(const void* packed, const int8_t* xq, const float* scale,
   return launch_gemv_s<4>(packed, xq, scale, gamma, Y, Yb, acc, ws, tokens, k, n_out, s);
 }
 
-hipError_t launch_gemv_group(const void* plan, int S, hipStream_t s) {
+template <bool kFused>
+static void launch_group_s(const char* p, int S, hipStream_t s) {
+  if (S == 8) gemv_group_kernel<8, kFused><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
+  else if (S == 6) gemv_group_kernel<6, kFused><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
+  else if (S == 2) gemv_group_kernel<2, kFused><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
+  else gemv_group_kernel<4, kFused><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
+}
+
+hipError_t launch_gemv_group(const void* plan, int S, bool fused, hipStream_t s) {
   const char* p = reinterpret_cast<const char*>(plan);
-  if (S == 8) gemv_group_kernel<8><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
-  else if (S == 6) gemv_group_kernel<6><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
-  else if (S == 2) gemv_group_kernel<2><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
-  else gemv_group_kernel<4><<<kDecodeBlocks, kGemvThreads, 0, s>>>(p);
+  if (fused) launch_group_s<true>(p, S, s);
+  else launch_group_s<false>(p, S, s);
   return hipGetLastError();
 }
 

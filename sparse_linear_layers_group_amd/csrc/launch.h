@@ -172,6 +172,8 @@ struct GroupHeader {
   int64_t rows;    // activation rows = count * tokens
   int64_t steps;   // superblocks over all items
   int64_t strips;  // strip descriptors
+  int32_t fused;   // 1: the contraction can quantise its own activations
+  int32_t pad;
 };
 struct GroupItem {
   const uint16_t* X;
@@ -202,6 +204,40 @@ struct WaveStart {            // a wavefront's range (80 bytes)
 };
 static_assert(sizeof(WaveStart) == 80, "wave start size");
 static_assert(offsetof(WaveStart, rec) == 64, "rec, kb, count, active: one 16-byte load");
+// Fused runs (activation quantisation inside the contraction launch): each
+// workgroup quantises the activation rows of the items its strips belong
+// to into its LDS, after the code tables, and reads its B operands and
+// token scales from there.  The rows are cut into segments of at most
+// kFusedSegVals values, dealt round-robin to the workgroup's 16 wavefronts
+// (at most kFusedSegsPerWave each, read with the wavefront's start record).
+// A wavefront loads its segments once, before its first weight loads,
+// publishes each segment's absmax in LDS, and after a barrier quantises
+// from registers with the row's absmax (the maximum over the row's
+// segments).  Each item's x_q and x_scale are written to memory by one
+// workgroup (its writer).  A strip descriptor's pad[0] and pad[1] hold the
+// LDS byte offsets of its item's codes and scales.
+constexpr int kFusedSegVals = 1024;     // values per segment (two 16-byte loads per lane)
+constexpr int kFusedSegsPerWave = 4;
+constexpr int kFusedSegsPerBlock = kFusedSegsPerWave * kDecodeWavesPerBlock;
+struct FusedSeg {          // one segment of one activation row (48 bytes)
+  const uint16_t* x;       // bf16, the segment's first value
+  int8_t* xq;              // x_q at the same place, or null (not the writer)
+  float* scale;            // the row's x_scale, or null (not the row's first
+                           // segment, or not the writer)
+  uint32_t lds_q;          // LDS byte offset of the segment's codes
+  uint32_t lds_s;          // LDS byte offset of the row's token scale
+  int32_t nvals;           // values (a multiple of 8); 0: no segment
+  int16_t slot;            // this segment's absmax slot in the workgroup
+  int16_t row_slot;        // first slot of the row
+  int16_t row_slots;       // slots of the row
+  int16_t first;           // 1: the segment that stores the row's scale
+  int32_t pad;
+};
+static_assert(sizeof(FusedSeg) == 48, "fused segment record");
+constexpr int kDecodeLutBytes = 512 * 4 * kDecodeLutCopies;
+constexpr int64_t kFusedLdsBytes = 160 * 1024 - kDecodeLutBytes;  // after the tables
+constexpr int64_t kFusedMaxBytes = 4 * kFusedSegsPerBlock;           // segment maxima, at the end
+constexpr int64_t kFusedCodeBytes = kFusedLdsBytes - kFusedMaxBytes;   // codes and scales
 // one activation row of the plan (self-contained: one 32-byte load)
 struct RowDesc {
   const uint16_t* X;  // bf16 [k]
@@ -211,6 +247,7 @@ struct RowDesc {
 };
 static_assert(sizeof(RowDesc) == 32, "row descriptor size");
 // plan image: header (64 bytes) | wave starts[kDecodeBlocks * 16] |
+//             fused segments[kDecodeBlocks * 16 * kFusedSegsPerWave] |
 //             row descriptors[rows] | strip descriptors | items[count]
 // (the row descriptors sit at a fixed offset, so the activation kernel
 // reads its row without waiting for the header; the region holds at least
@@ -219,8 +256,11 @@ constexpr size_t kGroupHeaderBytes = 64;
 constexpr int kActGroupBlocks = 1024;  // activation workgroups of a grouped run
 static_assert(sizeof(GroupHeader) <= kGroupHeaderBytes, "plan header size");
 __host__ __device__ inline size_t group_waves_offset() { return kGroupHeaderBytes; }
-__host__ __device__ inline size_t group_rows_offset() {
+__host__ __device__ inline size_t group_fused_offset() {
   return kGroupHeaderBytes + (size_t)kDecodeBlocks * kDecodeWavesPerBlock * sizeof(WaveStart);
+}
+__host__ __device__ inline size_t group_rows_offset() {
+  return group_fused_offset() + (size_t)kDecodeBlocks * kFusedSegsPerBlock * sizeof(FusedSeg);
 }
 __host__ __device__ inline size_t group_strips_offset(int64_t rows) {
   return group_rows_offset() + (size_t)(rows > kActGroupBlocks ? rows : kActGroupBlocks) * sizeof(RowDesc);
@@ -232,7 +272,9 @@ inline size_t group_plan_bytes(int64_t strips, int64_t count, int64_t rows) {
   return group_items_offset(rows, strips) + (size_t)count * sizeof(GroupItem);
 }
 hipError_t launch_act_quant_group(const void* plan, hipStream_t s);
-hipError_t launch_gemv_group(const void* plan, int S, hipStream_t s);
+// fused: the contraction quantises its activations itself (one launch for
+// both stages); a plan that does not fuse then gets NaN outputs
+hipError_t launch_gemv_group(const void* plan, int S, bool fused, hipStream_t s);
 
 // Prefill-shaped contraction (any token count).  Tiles are 256 rows x 64
 // tokens; when there are too few tiles to give every CU three workgroups,

@@ -11,6 +11,7 @@
 // Sparse-BitNet explainer article §三/§五/§六 (dynamic N:M mask from the
 // full-precision weights, quantise before sparsifying); BitNet b1.58 2B4T
 // article §一 (absmean ternary weights, 8-bit activations).
+#include "actq.h"
 #include "common.h"
 #include "launch.h"
 
@@ -772,36 +773,9 @@ __global__ __launch_bounds__(256) void ternary_pack_group_kernel(const char* __r
 }
 
 // ---------------------------------------------------------------------
-// Per-token absmax int8 activations.  One block per token.
-// x_q = rint(127 x / a) with a correctly rounded binary32 division: 127 x
-// is exact in binary32, and a quotient of two 8-bit-significand values that
-// is not a half-integer sits at least ~2^-16 (relative) away from one, far
-// beyond binary32 rounding, so rint(ties to even) of the rounded quotient
-// equals round-half-even of the exact quotient.  |x_q| <= 127, so the clip
-// to [-128, 127] never binds.  Optionally zeroes a workspace range.
+// Per-token absmax int8 activations (quant8 / absmax8 in actq.h).  One
+// block per token; optionally zeroes a workspace range.
 // ---------------------------------------------------------------------
-__device__ __forceinline__ uint2 quant8(const uint4& v, float a) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t q[2] = {0, 0};
-  if (a > 0.f) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float x = (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
-      const int qi = (int)rintf((127.0f * x) / a);
-      q[j >> 2] |= ((uint32_t)qi & 0xffu) << (8 * (j & 3));
-    }
-  }
-  return make_uint2(q[0], q[1]);
-}
-
-__device__ __forceinline__ float absmax8(const uint4& v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float a = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) a = fmaxf(a, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
-  return a;
-}
-
 // One row of k values by a 256-thread block.  Rows up to 256 * 8 * kHeld
 // values are read once and held in registers between the absmax and the
 // quantisation; longer rows take a second pass over memory.

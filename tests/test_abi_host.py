@@ -261,3 +261,9 @@ def test_bf16_outputs_reject_null_y(L):
     assert st == bl.BL_EINVAL
     st = L.bitlinear_fwd_bf16(fake, 1, 128, fake, 64, 6, 8, fake, None, fake, fake, None, None, 0, None)
     assert st == bl.BL_EINVAL
+
+
+def test_group_stages_validated(L):
+    fake = ctypes.c_void_p(1 << 20)
+    for stages in (0, 5, -1):
+        assert L.bitlinear_fwd_group(fake, 6, 8, stages, None) == bl.BL_EINVAL

@@ -621,3 +621,82 @@ def test_relu2_gate_bwd_matches_oracle(count):
     torch.cuda.synchronize()
     assert np.array_equal(bf16_bits(dG), dg_ref)
     assert np.array_equal(bf16_bits(dU), du_ref)
+
+
+def _group_entries(shapes, tokens, n, m, seed):
+    entries = []
+    for i, (n_out, k) in enumerate(shapes):
+        W = synth.weights(n_out, k, seed=seed + i)
+        X = synth.activations(tokens, k, seed=seed + 100 + i)
+        lw = BitLinearWeight(n_out, k, n, m)
+        lw.quantize(bf16_tensor(W))
+        entries.append(dict(X=bf16_tensor(X), packed=lw.packed, gamma=lw.gamma, k=k, n_out=n_out,
+                            Y=torch.full((tokens * n_out,), float("nan"), dtype=torch.float32, device="cuda"),
+                            xq=torch.zeros(tokens * k, dtype=torch.int8, device="cuda"),
+                            x_scale=torch.zeros(tokens, dtype=torch.float32, device="cuda"), lw=lw))
+    return entries
+
+
+@pytest.mark.parametrize("tokens,shapes", [
+    (1, [(896, 896), (128, 896), (128, 896), (896, 896), (4864, 896), (4864, 896), (896, 4864)] * 2),
+    (1, [(48, 256), (128, 896), (40, 384), (896, 4864), (200, 1152)]),
+    (5, [(48, 256), (128, 896), (40, 384), (896, 4864), (200, 1152)]),
+    (8, [(48, 256), (128, 896), (40, 384), (896, 4864), (200, 1152)]),
+    (1, [(11008, 2048)] * 4 + [(2048, 11008)] * 2),
+    # 5 rows of 11 segments (ten of 1024 values and one of 768): 55 of the
+    # workgroup's 64 absmax slots, each row's maximum over 11 of them
+    (5, [(128, 11008), (64, 256)]),
+])
+def test_grouped_decode_fused_matches_two_launches(tokens, shapes):
+    """Stage 4 (activation quantisation inside the contraction launch):
+    Y, x_q and x_scale bit-identical to stage 3 (two launches)."""
+    n, m = 6, 8
+    entries = _group_entries(shapes, tokens, n, m, seed=700)
+    items = bl.make_fwd_items(entries, tokens)
+    assert bl.bitlinear_fwd_group_plan_fuses(items, len(entries), tokens, n, m)
+    plan = torch.empty(bl.bitlinear_fwd_group_plan_bytes(items, len(entries), tokens), dtype=torch.uint8,
+                       device="cuda")
+    bl.bitlinear_fwd_group_plan(items, len(entries), tokens, n, m, plan)
+    bl.bitlinear_fwd_group(plan, n, m, 3)
+    torch.cuda.synchronize()
+    ref = [(e["Y"].cpu().numpy().copy(), e["xq"].cpu().numpy().copy(), e["x_scale"].cpu().numpy().copy())
+           for e in entries]
+    for rep in range(2):
+        for e in entries:
+            e["Y"].fill_(float("nan"))
+            e["xq"].zero_()
+            e["x_scale"].zero_()
+        bl.bitlinear_fwd_group(plan, n, m, 4)
+        torch.cuda.synchronize()
+        for i, (e, (Y, xq, sc)) in enumerate(zip(entries, ref)):
+            assert np.array_equal(e["Y"].cpu().numpy().view(np.uint32), Y.view(np.uint32)), i
+            assert np.array_equal(e["xq"].cpu().numpy(), xq), i
+            assert np.array_equal(e["x_scale"].cpu().numpy().view(np.uint32), sc.view(np.uint32)), i
+
+
+@pytest.mark.parametrize("tokens", [16, 6])
+def test_grouped_decode_fused_run_of_unfused_plan_is_nan(tokens):
+    """A plan whose workgroups' activation rows do not fit LDS (16 tokens of
+    an 11008-wide item) or need more than the 64 segment slots (6 tokens:
+    66 segments, 66 KB of codes) cannot run stage 4: every Y becomes NaN,
+    and the plan then still runs as two launches."""
+    n, m = 6, 8
+    entries = _group_entries([(128, 11008), (64, 256)], tokens, n, m, seed=900)
+    items = bl.make_fwd_items(entries, tokens)
+    assert not bl.bitlinear_fwd_group_plan_fuses(items, len(entries), tokens, n, m)
+    plan = torch.empty(bl.bitlinear_fwd_group_plan_bytes(items, len(entries), tokens), dtype=torch.uint8,
+                       device="cuda")
+    bl.bitlinear_fwd_group_plan(items, len(entries), tokens, n, m, plan)
+    for e in entries:
+        e["Y"].zero_()
+    bl.bitlinear_fwd_group(plan, n, m, 4)
+    torch.cuda.synchronize()
+    for e in entries:
+        assert torch.isnan(e["Y"]).all()
+    bl.bitlinear_fwd_group(plan, n, m, 3)
+    torch.cuda.synchronize()
+    for e in entries:
+        X = e["X"].view(torch.int16).cpu().numpy().view(np.uint16).reshape(tokens, e["k"])
+        xq, sc = oracle.act_quant(X)
+        assert np.array_equal(e["xq"].cpu().numpy().reshape(xq.shape), xq)
+        assert not torch.isnan(e["Y"]).any()

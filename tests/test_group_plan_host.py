@@ -5,7 +5,11 @@ often have), is replayed against every read the contraction kernel makes:
 header, activation rows, items, each workgroup's strip list and the 16
 wavefront start records that cut it into ranges.  Every strip of every item
 must be covered exactly once, in whole k blocks, and the ranges must tile
-each workgroup's steps in the documented 19 : 17 : 15 : 13 proportions."""
+each workgroup's steps in the documented 19 : 17 : 15 : 13 proportions.
+For one-launch runs, each wavefront's activation segments must cover every
+row of the workgroup's items exactly once, land in the LDS room the strips
+point at, and name the slots of their row's absmax; each item's x_q and
+x_scale must be written by exactly one workgroup."""
 import numpy as np
 import pytest
 
@@ -15,9 +19,12 @@ QWEN05 = [(896, 896), (128, 896), (128, 896), (896, 896), (4864, 896), (4864, 89
 S_OF = {(8, 8): 8, (6, 8): 6, (4, 8): 4, (2, 4): 4, (3, 8): 4, (2, 8): 2}
 WEIGHTS = (19, 17, 15, 13)  # per group of four wavefronts (w // 4)
 
-# plan image: header 64 B | 256 x 16 wavefront starts (80 B) | row
-# descriptors (32 B, at least 1024) | strip descriptors (64 B) | items (64 B)
-HDR, WAVE, ROW, DESC, ITEM = 64, 80, 32, 64, 64
+# plan image: header 64 B | 256 x 16 wavefront starts (80 B) | 256 x 16 x 4
+# fused segments (48 B) | row descriptors (32 B, at least 1024) | strip
+# descriptors (64 B) | items (64 B)
+HDR, WAVE, FSEG, ROW, DESC, ITEM = 64, 80, 48, 32, 64, 64
+SEGS_PER_WAVE, SEG_VALS = 4, 1024
+FUSED_CODES = 160 * 1024 - 512 * 4 * 32 - 4 * 64  # LDS after the code tables, before the 64 segment maxima
 
 
 def _wave_split(n, w):
@@ -52,7 +59,8 @@ class _Img:
 
     def desc(self, o):
         return dict(packed=self.u64(o), xq=self.u64(o + 8), Y=self.u64(o + 16), scale=self.u64(o + 24),
-                    gamma=self.u64(o + 32), n_out=self.i64(o + 40), k=self.i32(o + 48), row0=self.i32(o + 52))
+                    gamma=self.u64(o + 32), n_out=self.i64(o + 40), k=self.i32(o + 48), row0=self.i32(o + 52),
+                    lds_x=self.i32(o + 56), lds_s=self.i32(o + 60))
 
 
 def _replay(shapes, tokens, n=6, m=8):
@@ -63,13 +71,14 @@ def _replay(shapes, tokens, n=6, m=8):
     P = _Img(img)
     bb = 2 * (8 + S_OF[(n, m)])
     count, tok, s_hdr, blocks = P.i32(0), P.i32(4), P.i32(8), P.i32(12)
-    rows, steps, strips = P.i64(16), P.i64(24), P.i64(32)
+    rows, steps, strips, fused = P.i64(16), P.i64(24), P.i64(32), P.i32(40)
     assert (count, tok, s_hdr, rows) == (len(shapes), tokens, S_OF[(n, m)], len(shapes) * tokens)
     assert steps == sum(-(-no // 64) * (k // 128) for no, k in shapes)
     assert strips == sum(-(-no // 64) for no, _ in shapes)
     assert 1 <= blocks <= 256
     waves = HDR
-    rows_off = waves + 4096 * WAVE
+    fseg_off = waves + 4096 * WAVE
+    rows_off = fseg_off + 4096 * SEGS_PER_WAVE * FSEG
     strips_off = rows_off + max(rows, 1024) * ROW
     items_off = strips_off + strips * DESC
     assert items_off + count * ITEM == nbytes
@@ -90,6 +99,9 @@ def _replay(shapes, tokens, n=6, m=8):
             want[it["packed"] + st * (it["k"] // 128) * 64 * bb] = (it, st)
     owner = {}
     next_desc = 0
+    writers = {}
+    fits = True
+    item_of = {it["packed"]: i for i, it in enumerate(info)}
     for b in range(256):
         first = waves + b * 16 * WAVE
         if b >= blocks:
@@ -112,6 +124,75 @@ def _replay(shapes, tokens, n=6, m=8):
             cum += d["k"] // 128
             j += 1
         assert cum == n_b
+        # fused item list: the distinct items of the strips, in order, codes
+        # then scales in LDS; the strips carry their item's offsets
+        its = []
+        for jj in range(rec0, j):
+            d = P.desc(strips_off + jj * DESC)
+            i = item_of[want[d["packed"]][0]["packed"]]
+            if not its or its[-1] != i:
+                its.append(i)
+        off = 0
+        offs = {}
+        for i in its:
+            offs[i] = [off, None]
+            off += -(-tokens * info[i]["k"] // 16) * 16
+        for i in its:
+            offs[i][1] = off
+            off += -(-tokens * 4 // 16) * 16
+        room = off <= FUSED_CODES
+        for jj in range(rec0, j):
+            d = P.desc(strips_off + jj * DESC)
+            i = item_of[want[d["packed"]][0]["packed"]]
+            assert [d["lds_x"], d["lds_s"]] == offs[i]
+        # the segments as the wavefronts read them: slot j of wavefront w
+        segs = []
+        for w in range(16):
+            for sj in range(SEGS_PER_WAVE):
+                o = fseg_off + ((b * 16 + w) * SEGS_PER_WAVE + sj) * FSEG
+                f = dict(x=P.u64(o), xq=P.u64(o + 8), scale=P.u64(o + 16), lds_q=P.i32(o + 24),
+                         lds_s=P.i32(o + 28), nvals=P.i32(o + 32),
+                         slot=int(img[o + 36:o + 38].view(np.int16)[0]),
+                         row_slot=int(img[o + 38:o + 40].view(np.int16)[0]),
+                         row_slots=int(img[o + 40:o + 42].view(np.int16)[0]),
+                         first=int(img[o + 42:o + 44].view(np.int16)[0]))
+                if f["nvals"]:
+                    assert f["slot"] % 16 == w and f["slot"] // 16 == sj  # dealt round-robin
+                    segs.append(f)
+                else:
+                    assert f == dict.fromkeys(f, 0)
+        need = sum(tokens * -(-info[i]["k"] // SEG_VALS) for i in its)
+        fits = fits and room and need <= 16 * SEGS_PER_WAVE
+        if fused:
+            assert sorted(f["slot"] for f in segs) == list(range(need))
+            slot_of = {f["slot"]: f for f in segs}
+            for i in its:
+                it = info[i]
+                writer = i not in writers
+                if writer:
+                    writers[i] = b
+                for t in range(tokens):
+                    row = [f for f in segs if it["X"] + 2 * t * it["k"] <= f["x"] < it["X"] + 2 * (t + 1) * it["k"]]
+                    row.sort(key=lambda f: f["x"])
+                    # the row's values, each once, in segments of at most 1024
+                    v = 0
+                    for f in row:
+                        assert f["x"] == it["X"] + 2 * (t * it["k"] + v)
+                        assert f["nvals"] == min(SEG_VALS, it["k"] - v) and f["nvals"] % 8 == 0
+                        assert f["lds_q"] == offs[i][0] + t * it["k"] + v
+                        assert f["lds_s"] == offs[i][1] + 4 * t
+                        assert f["xq"] == (it["xq"] + t * it["k"] + v if writer else 0)
+                        assert f["scale"] == (it["x_scale"] + 4 * t if writer and v == 0 else 0)
+                        assert f["first"] == (1 if v == 0 else 0)
+                        v += f["nvals"]
+                    assert v == it["k"]
+                    # each segment names exactly its row's slots
+                    slots = sorted(f["slot"] for f in row)
+                    for f in row:
+                        assert list(range(f["row_slot"], f["row_slot"] + f["row_slots"])) == slots
+                        assert all(slot_of[q] in row for q in slots)
+        else:
+            assert not segs  # a plan that does not fuse carries no segments
         next_desc = j
         # wavefront w: steps [split(w), split(w+1)) of the list, from its record
         for w in range(16):
@@ -124,21 +205,31 @@ def _replay(shapes, tokens, n=6, m=8):
             assert (rec, kb) == (jj, s0 - c0) or (cnt == 0 and s0 == n_b)
             assert P.desc(o) == P.desc(strips_off + rec * DESC)
     assert next_desc == strips and len(owner) == len(want)
+    if fused:
+        assert sorted(writers) == list(range(count))  # every item written by exactly one workgroup
+    assert fused == (1 if fits else 0)
+    assert bl.bitlinear_fwd_group_plan_fuses(items, len(shapes), tokens, n, m) == bool(fused)
+    return fused
 
 
-@pytest.mark.parametrize("shapes,tokens", [
-    (QWEN05 * 2, 1),
-    (QWEN05 * 24, 1),
-    (QWEN05 * 24, 16),
-    ([(48, 256), (128, 896), (40, 384), (896, 4864), (200, 1152)], 1),
-    ([(48, 256), (128, 896), (40, 384), (896, 4864), (200, 1152)], 16),
-    ([(64, 128), (128, 256)], 1),
-    ([(11008, 2048)] * 16, 1),
-    ([(2048, 11008)] * 16, 16),
-    ([(64000, 128)] * 8, 16),
+@pytest.mark.parametrize("shapes,tokens,fuses", [
+    (QWEN05 * 2, 1, 1),
+    (QWEN05 * 24, 1, 1),
+    (QWEN05 * 24, 4, 0),  # codes fit LDS, but ~160 segments per workgroup (64 slots)
+    (QWEN05 * 24, 16, 0),  # up to ~150 KB of codes in some workgroups
+    ([(48, 256), (128, 896), (40, 384), (896, 4864), (200, 1152)], 1, 1),
+    ([(48, 256), (128, 896), (40, 384), (896, 4864), (200, 1152)], 16, 0),  # segments
+    ([(64, 128), (128, 256)], 1, 1),
+    ([(11008, 2048)] * 16, 1, 1),
+    ([(2048, 11008)] * 16, 16, 0),  # 176 KB of codes per item
+    ([(64000, 128)] * 8, 16, 0),  # 16 rows per item, one segment each: over 64 slots
+    ([(64000, 128)] * 3, 16, 1),
+    # ~40 distinct 2048-wide items per workgroup at 16 tokens: 1.3 MB of
+    # activation codes per workgroup, far past its LDS
+    ([(64, 2048)] * 10000, 16, 0),
 ])
-def test_group_plan_replay(shapes, tokens):
-    _replay(shapes, tokens)
+def test_group_plan_replay(shapes, tokens, fuses):
+    assert _replay(shapes, tokens) == fuses
 
 
 @pytest.mark.parametrize("n,m", [(8, 8), (4, 8), (2, 4), (2, 8)])
