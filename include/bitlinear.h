@@ -427,6 +427,13 @@ int bitlinear_bwd(const uint16_t *dY, const int8_t *xq, const float *x_scale,
                   int64_t k, int64_t n_out, int n, int m, float *dX,
                   float *dW, void *ws, size_t ws_bytes, void *stream);
 
+/* Output tiles of bitlinear_bwd's products, process-wide: 0 (the default)
+ * chooses per launch from the tile counts; 1, 2 or 3 fixes 128 x 128,
+ * 256 x 128 or 256 x 256.  Every choice contracts k in the same order
+ * through the same matrix instruction, so the results are identical bit
+ * for bit.  For tests and tuning; returns BL_EINVAL for any other value. */
+int bitlinear_bwd_tiles(int tiles);
+
 /* Static text for a status code. */
 const char *bitlinear_status_string(int status);
 

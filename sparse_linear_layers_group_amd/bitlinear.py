@@ -41,6 +41,7 @@ _SIGS = {
     "bitlinear_pack": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _vp, _sz, _vp]),
     "bitlinear_fwd": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _sz, _vp]),
+    "bitlinear_bwd_tiles": (_int, [_int]),
     "bitlinear_fwd_noalloc": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp]),
     "bitlinear_sp24_packed_bytes": (_sz, [_i64, _i64]),
     "bitlinear_sp24_workspace_bytes": (_sz, [_i64, _i64, _i64]),
@@ -250,6 +251,12 @@ def bitlinear_bwd(dY, xq, x_scale, packed, gamma, tokens, k, n_out, n, m, dX, dW
         (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes),
         _stream(stream))
     _check(st, "bitlinear_bwd")
+
+
+def bitlinear_bwd_tiles(tiles):
+    """Fix the backward products' tiles (0: chosen per launch, 1: 128 x 128,
+    2: 256 x 128, 3: 256 x 256)."""
+    _check(lib().bitlinear_bwd_tiles(int(tiles)), "bitlinear_bwd_tiles")
 
 
 def bitlinear_latent_update(W_master, dW, count, lr, W, stream=None):

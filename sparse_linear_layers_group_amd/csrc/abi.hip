@@ -798,6 +798,12 @@ int bitlinear_quant_group(const void* plan, int n, int m, int gamma_over, void* 
   return hip_status(e, "grouped quantisation launch");
 }
 
+int bitlinear_bwd_tiles(int tiles) {
+  if (bl::bwd_set_tiles(tiles) != 0)
+    return fail(BL_EINVAL, "bitlinear_bwd_tiles takes 0, 1, 2 or 3 (got %d)", tiles);
+  return ok();
+}
+
 int bitlinear_bwd(const uint16_t* dY, const int8_t* xq, const float* x_scale, const void* packed,
                   const double* gamma, int64_t tokens, int64_t k, int64_t n_out, int n, int m,
                   float* dX, float* dW, void* ws, size_t ws_bytes, void* stream) {

@@ -19,6 +19,7 @@
 #include "common.h"
 #include "launch.h"
 
+#include <atomic>
 #include <utility>
 
 #include <type_traits>
@@ -354,6 +355,248 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(NtProblem p0, NtPr
     }
 }
 
+// ------------------------------------------- 256 x 128 and 256 x 256 tiles
+// Large products run on 256-row tiles of wavefronts of 128 x 64 (8 x 4
+// MFMA tiles each): 256 x 128 (four wavefronts, two workgroups per CU) or
+// 256 x 256 (eight wavefronts, one per CU).  Each byte of an operand
+// fragment read from LDS feeds 1.33 times the MFMA work of the 64 x 64
+// wavefront tiles above, and each byte written into LDS 1.33 (256 x 128) or
+// 2 (256 x 256) times: those tiles' fragment reads and tile writes need
+// more LDS bandwidth than a CU has at the full MFMA rate.  (128 x 128
+// wavefront tiles would read less still, but 256 accumulators per lane made
+// the register allocator shuttle them between register files around every
+// MFMA.)  The tiles stream through three LDS stages of 32 k filled by LDS
+// DMA (buffer loads that write LDS directly, 16 bytes per lane, 1 KiB per
+// wavefront instruction), issued two stages ahead.  In a stage each
+// operand row's 64 bytes hold four 16-byte pieces, piece c of row r at
+// position c ^ ((r >> 1) & 3): the eight lanes that read one 128-byte bank
+// line at a time (rows r..r+7 of one k piece) then hit distinct banks, and
+// a DMA instruction's 64 lanes still write 1 KiB in order (lane l writes
+// row l / 4, position l % 4, and loads the piece that belongs there).
+constexpr int kBigM = 256;
+constexpr int kBigK = 32;                        // k per stage
+constexpr int kBigABytes = kBigM * kBigK * 2;    // 16 KiB
+template <int kWN>  // column wavefronts: tile N = 64 kWN, 2 kWN wavefronts
+struct BigTile {
+  static constexpr int N = 64 * kWN;
+  static constexpr int kWaves = 2 * kWN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kStageBytes = kBigABytes + N * kBigK * 2;
+  static constexpr int kAInstr = 16 / kWaves;    // A DMA instructions per wavefront and step
+  static constexpr int kPerStep = kAInstr + 2;   // + two of B
+};
+
+template <int kWN>
+__host__ __device__ inline int64_t nt_tiles_big(const NtProblem& p) {
+  return ((p.M + kBigM - 1) / kBigM) * ((p.N + BigTile<kWN>::N - 1) / BigTile<kWN>::N);
+}
+
+// gfx950-only builtins sit in plain (non-template) functions: used directly
+// in the kernel template, the host pass (which checks template bodies
+// against its own target) dropped the kernel's launch stub
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, __attribute__((address_space(3))) void* dst,
+                                          uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// wait until at most N vector memory operations of this wavefront are in
+// flight (the waits below count LDS DMA themselves)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// the three stages are separate arrays, each step's stage a compile-time
+// choice: the compiler then sees that a step's fragment reads and the DMA
+// in flight into the other stages touch different objects, and waits only
+// for the DMA of the stage being read (with one array it waited for every
+// DMA in flight before each read)
+// (namespace-scope arrays: a function-local __shared__ array in a template
+// made the host pass drop the kernel's launch stub)
+__shared__ __attribute__((aligned(1024))) char g_big2_st0[BigTile<2>::kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_big2_st1[BigTile<2>::kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_big2_st2[BigTile<2>::kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_big4_st0[BigTile<4>::kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_big4_st1[BigTile<4>::kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_big4_st2[BigTile<4>::kStageBytes];
+template <int kWN, int P>
+__device__ __forceinline__ char* big_stage() {
+  static_assert(kWN == 2 || kWN == 4, "tile widths");
+  if constexpr (kWN == 2) return P == 0 ? g_big2_st0 : P == 1 ? g_big2_st1 : g_big2_st2;
+  else return P == 0 ? g_big4_st0 : P == 1 ? g_big4_st1 : g_big4_st2;
+}
+
+// (512 threads at most: two wavefronts per SIMD either way, so the
+// register budget is the same; bounds that depend on kWN broke the host
+// side's template deduction)
+template <int kWN>
+__global__ __launch_bounds__(512) void gemm_nt_bf16_big_kernel(NtProblem p0, NtProblem p1) {
+  typedef BigTile<kWN> T;
+  typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int l16 = lane & 15, lg = lane >> 4;
+  int64_t m0, n0, t;
+  bool second;
+  {
+    const int64_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    int64_t s0, c0, s1, c1;
+    xcd_share(nt_tiles_big<kWN>(p0), xcd, s0, c0);
+    xcd_share(nt_tiles_big<kWN>(p1), xcd, s1, c1);
+    if (slot >= c0 + c1) return;
+    second = slot >= c0;
+    t = second ? s1 + slot - c0 : s0 + slot;
+  }
+  // the problem's fields, each selected on its own (a reference to one of
+  // the two argument structs put both in scratch memory)
+  const uint16_t* __restrict__ A = second ? p1.A : p0.A;
+  const uint16_t* __restrict__ B = second ? p1.B : p0.B;
+  float* __restrict__ C = second ? p1.C : p0.C;
+  const double* __restrict__ alpha = second ? p1.alpha : p0.alpha;
+  const int64_t lda = second ? p1.lda : p0.lda, ldb = second ? p1.ldb : p0.ldb;
+  const int64_t ldc = second ? p1.ldc : p0.ldc, M = second ? p1.M : p0.M, N = second ? p1.N : p0.N;
+  const int64_t klen = second ? p1.klen : p0.klen;
+  int64_t K = second ? p1.K : p0.K;
+  {
+    const int64_t tiles_m = (M + kBigM - 1) / kBigM, tiles_n = (N + T::N - 1) / T::N;
+    constexpr int64_t kG = 4;  // row tiles per group of the tile order
+    const int64_t g = t / (kG * tiles_n), r = t - g * kG * tiles_n;
+    const int64_t gm = tiles_m - g * kG < kG ? tiles_m - g * kG : kG;
+    m0 = (g * kG + r % gm) * kBigM;
+    n0 = (r / gm) * T::N;
+  }
+  const int64_t k0 = (int64_t)blockIdx.y * klen;
+  K = K - k0 < klen ? K - k0 : klen;
+  C += (int64_t)blockIdx.y * M * ldc;
+  const int64_t nks = (K + kBigK - 1) / kBigK;
+
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A), (short)0, (int)(M * lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(B), (short)0, (int)(N * ldb * 2), 0x00020000);
+  constexpr uint32_t kOOB = 0x80000000u;
+  // DMA: wavefront w fills A rows [16 kAInstr w, +16 kAInstr) and B rows
+  // [32w, 32w + 32), 16 rows per instruction; lane l covers row l / 4 of
+  // the instruction's 16 at position l % 4, i.e. logical piece kc / 8
+  // below (the same for every instruction)
+  const int kc = 8 * ((lane & 3) ^ ((lane >> 3) & 3));
+  uint32_t a_off[T::kAInstr], b_off[2];
+#pragma unroll
+  for (int q = 0; q < T::kAInstr; ++q) {
+    const int64_t row = 16 * (T::kAInstr * wave + q) + (lane >> 2);
+    a_off[q] = m0 + row < M ? (uint32_t)(((m0 + row) * lda + k0 + kc) * 2) : kOOB;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t row = 32 * wave + 16 * q + (lane >> 2);
+    b_off[q] = n0 + row < N ? (uint32_t)(((n0 + row) * ldb + k0 + kc) * 2) : kOOB;
+  }
+  // every step issues the same instructions per wavefront (past the last
+  // step they read zeros into a stage nobody reads), so the waits below
+  // can count them
+  auto dma = [&](auto stage, int64_t ks) {
+    constexpr int P = decltype(stage)::value;
+    const bool kv = ks * kBigK + kc < K;
+    const uint32_t ko = (uint32_t)(ks * kBigK * 2);
+    lds_char* st = (lds_char*)big_stage<kWN, P>();
+#pragma unroll
+    for (int q = 0; q < T::kAInstr; ++q)
+      lds_dma16(ar, (lds_void*)(st + 1024 * (T::kAInstr * wave + q)), kv ? a_off[q] + ko : kOOB);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      lds_dma16(br, (lds_void*)(st + kBigABytes + 1024 * (2 * wave + q)), kv ? b_off[q] + ko : kOOB);
+  };
+
+  v4f c[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // fragment of MFMA row tile i / column tile j: row (or column) 16i + l16
+  // of the wavefront's range, logical k piece lg
+  const uint32_t frag = (uint32_t)(l16 * 64 + 16 * (lg ^ ((l16 >> 1) & 3)));
+  const uint32_t a_base = (uint32_t)(wm * 128 * 64) + frag;
+  const uint32_t b_base = (uint32_t)kBigABytes + (uint32_t)(wn * 64 * 64) + frag;
+
+  typedef std::integral_constant<int, 0> S0;
+  typedef std::integral_constant<int, 1> S1;
+  typedef std::integral_constant<int, 2> S2;
+  // step ks reads stage ks % 3 and refills stage (ks + 2) % 3 (last read in
+  // step ks - 1) with step ks + 2
+  auto step = [&](auto stage, int64_t ks) {
+    constexpr int P = decltype(stage)::value;
+    // this wavefront's part of step ks has landed, then everyone's has and
+    // step ks - 1's reads are done.  A plain barrier with compiler-only
+    // fences: __syncthreads()'s workgroup release would wait for every LDS
+    // DMA in flight (they write LDS), draining the steps ahead
+    wait_vmcnt<T::kPerStep>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    dma(std::integral_constant<int, (P + 2) % 3>{}, ks + 2);
+    const lds_char* st = (const lds_char*)big_stage<kWN, P>();
+    v8bf a[8], b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b[j] = *reinterpret_cast<const __attribute__((address_space(3))) v8bf*>(st + b_base + j * 16 * 64);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      a[i] = *reinterpret_cast<const __attribute__((address_space(3))) v8bf*>(st + a_base + i * 16 * 64);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        c[i][j] = mfma_bf16(a[i], b[j], c[i][j]);
+  };
+
+  dma(S0{}, 0);
+  dma(S1{}, 1);
+  int64_t ks = 0;
+  for (; ks + 2 < nks; ks += 3) {
+    step(S0{}, ks);
+    step(S1{}, ks + 1);
+    step(S2{}, ks + 2);
+  }
+  if (ks < nks) step(S0{}, ks);
+  if (ks + 1 < nks) step(S1{}, ks + 1);
+  wait_vmcnt<0>();  // no LDS DMA outlives the workgroup
+
+  // lane holds C[m0 + 128wm + 16i + 4lg + q][n0 + 64wn + 16j + l16]
+  const double g = alpha ? *alpha : 1.0;
+  const bool scaled = alpha != nullptr;
+  if (m0 + kBigM <= M && n0 + T::N <= N) {
+    float* cb = C + (m0 + wm * 128 + 4 * lg) * ldc + n0 + wn * 64 + l16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float* cr = cb + (int64_t)(i * 16 + q) * ldc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          st_stream(cr + j * 16, scaled ? (float)((double)c[i][j][q] * g) : c[i][j][q]);
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t m = m0 + wm * 128 + i * 16 + 4 * lg + q;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = n0 + wn * 64 + j * 16 + l16;
+        if (n < N) C[m * ldc + n] = scaled ? (float)((double)c[i][j][q] * g) : c[i][j][q];
+      }
+    }
+}
+
 // C = alpha * (sum of the split planes, in order), binary32 sums
 __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ P, int splits,
                                                        int64_t n4, const double* __restrict__ alpha,
@@ -405,6 +648,24 @@ static hipError_t gemm_nt_split(NtProblem p, float* partials, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Tiles of the products that are not split: 0 chooses per launch by the
+// tile counts; 1, 2, 3 fix 128 x 128, 256 x 128 or 256 x 256
+// (bitlinear_bwd_tiles).
+static std::atomic<int> g_bwd_tiles{0};
+int bwd_set_tiles(int tiles) {
+  if (tiles < 0 || tiles > 3) return -1;
+  g_bwd_tiles.store(tiles, std::memory_order_relaxed);
+  return 0;
+}
+static int bwd_tile_kind(const NtProblem& p0, const NtProblem& p1) {
+  const int f = g_bwd_tiles.load(std::memory_order_relaxed);
+  if (f) return f;
+  // 256 x 256 when its tiles fill at least 1.5 rounds of the 256 CUs (the
+  // last round then at least half full), else 256 x 128
+  const int64_t t4 = nt_tiles_big<4>(p0) + nt_tiles_big<4>(p1);
+  return t4 >= 384 && t4 % 256 >= 128 ? 3 : 2;
+}
+
 // The products that are not split run in one launch (a null `b` is no
 // second product); split ones follow, one after the other (they share the
 // partial planes).
@@ -425,8 +686,17 @@ static hipError_t gemm_nt_run(const NtProblem* a, const NtProblem* b, float* par
     } else {
       p1.M = 0;  // no tiles
     }
-    const int64_t per = (nt_tiles(p0) + 7) / 8 + (nt_tiles(p1) + 7) / 8;
-    gemm_nt_bf16_kernel<<<(unsigned)(8 * per), 256, 0, s>>>(p0, p1);
+    const int kind = bwd_tile_kind(p0, p1);
+    if (kind == 3) {
+      const int64_t per = (nt_tiles_big<4>(p0) + 7) / 8 + (nt_tiles_big<4>(p1) + 7) / 8;
+      gemm_nt_bf16_big_kernel<4><<<(unsigned)(8 * per), BigTile<4>::kThreads, 0, s>>>(p0, p1);
+    } else if (kind == 2) {
+      const int64_t per = (nt_tiles_big<2>(p0) + 7) / 8 + (nt_tiles_big<2>(p1) + 7) / 8;
+      gemm_nt_bf16_big_kernel<2><<<(unsigned)(8 * per), BigTile<2>::kThreads, 0, s>>>(p0, p1);
+    } else {
+      const int64_t per = (nt_tiles(p0) + 7) / 8 + (nt_tiles(p1) + 7) / 8;
+      gemm_nt_bf16_kernel<<<(unsigned)(8 * per), 256, 0, s>>>(p0, p1);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

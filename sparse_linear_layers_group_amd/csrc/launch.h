@@ -363,5 +363,8 @@ inline size_t bwd_ws_bytes(int64_t tokens, int64_t k, int64_t n_out) {
 hipError_t launch_bwd(const uint16_t* dY, const int8_t* xq, const float* scale, const void* packed,
                       const double* gamma, float* dX, float* dW, void* ws, int64_t tokens, int64_t k,
                       int64_t n_out, int S, hipStream_t s);
+// fixes the backward products' tiles (0: by tile count, 1: 128 x 128,
+// 2: 256 x 128, 3: 256 x 256); -1 for another value
+int bwd_set_tiles(int tiles);
 
 }  // namespace bl
