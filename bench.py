@@ -55,8 +55,8 @@ DECODE_TRAFFIC = {
     "sources": ["sparse_linear_layers_group_amd/csrc/gemv.hip",
                 "sparse_linear_layers_group_amd/csrc/common.h",
                 "sparse_linear_layers_group_amd/csrc/launch.h"],
-    "sha256": "29d97cc88a8fcc7ec981c0f6138d4259297a2b517b25fbd5153af57c49c3498b",
-    "fetch_kib": 39919.3, "fetch_scale": 2.0,
+    "sha256": "0bafac59ff503e221422d2e3eafe50ad485b235155e4bf14d639824a7853967b",
+    "fetch_kib": 39919.8, "fetch_scale": 2.0,
     "write_kib": 1188.0, "write_scale": 1.0,
 }
 
