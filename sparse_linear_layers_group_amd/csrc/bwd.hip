@@ -403,11 +403,12 @@ __device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
 }
 
 // wait until at most N vector memory operations of this wavefront are in
-// flight (the waits below count LDS DMA themselves)
-template <int N>
+// flight (the waits below count LDS DMA themselves) and, with kLds, until
+// its LDS reads have returned
+template <int N, bool kLds = false>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | ((kLds ? 0 : 15) << 8));
 }
 
 // the three stages are separate arrays, each step's stage a compile-time
@@ -531,11 +532,11 @@ __global__ __launch_bounds__(512) void gemm_nt_bf16_big_kernel(NtProblem p0, NtP
   // step ks - 1) with step ks + 2
   auto step = [&](auto stage, int64_t ks) {
     constexpr int P = decltype(stage)::value;
-    // this wavefront's part of step ks has landed, then everyone's has and
-    // step ks - 1's reads are done.  A plain barrier with compiler-only
-    // fences: __syncthreads()'s workgroup release would wait for every LDS
-    // DMA in flight (they write LDS), draining the steps ahead
-    wait_vmcnt<T::kPerStep>();
+    // this wavefront's part of step ks has landed and its reads of step
+    // ks - 1 have returned, then everyone's has.  A plain barrier with
+    // compiler-only fences: __syncthreads()'s workgroup release would wait
+    // for every LDS DMA in flight (they write LDS), draining the steps ahead
+    wait_vmcnt<T::kPerStep, true>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
