@@ -647,10 +647,9 @@ def _group_entries(shapes, tokens, n, m, seed):
     # workgroup's 64 absmax slots, each row's maximum over 11 of them
     (5, [(128, 11008), (64, 256)]),
 ])
-def test_grouped_decode_fused_matches_two_launches(tokens, shapes):
+def test_grouped_decode_fused_matches_two_launches(tokens, shapes, n=6, m=8):
     """Stage 4 (activation quantisation inside the contraction launch):
     Y, x_q and x_scale bit-identical to stage 3 (two launches)."""
-    n, m = 6, 8
     entries = _group_entries(shapes, tokens, n, m, seed=700)
     items = bl.make_fwd_items(entries, tokens)
     assert bl.bitlinear_fwd_group_plan_fuses(items, len(entries), tokens, n, m)
@@ -672,6 +671,15 @@ def test_grouped_decode_fused_matches_two_launches(tokens, shapes):
             assert np.array_equal(e["Y"].cpu().numpy().view(np.uint32), Y.view(np.uint32)), i
             assert np.array_equal(e["xq"].cpu().numpy(), xq), i
             assert np.array_equal(e["x_scale"].cpu().numpy().view(np.uint32), sc.view(np.uint32)), i
+
+
+@pytest.mark.parametrize("n,m", [(8, 8), (2, 8), (2, 4)])
+def test_grouped_decode_fused_other_patterns(n, m):
+    """Stage 4 at the other sign-slot counts (S = 8, 2, 4): bit-identical to
+    stage 3 at 1 and 3 tokens."""
+    shapes = [(48, 256), (128, 896), (40, 384), (896, 4864), (200, 1152)]
+    for tokens in (1, 3):
+        test_grouped_decode_fused_matches_two_launches(tokens, shapes, n, m)
 
 
 @pytest.mark.parametrize("tokens", [16, 6])

@@ -244,3 +244,18 @@ def test_group_plan_host_rejects_short_image():
     with pytest.raises(bl.BitLinearError) as e:
         bl.bitlinear_fwd_group_plan_host(items, len(QWEN05), 1, 6, 8, img)
     assert e.value.status == bl.BL_EWORKSPACE
+
+
+def test_group_plan_fuses_reports_errors():
+    """bitlinear_fwd_group_plan_fuses answers 1 or 0, and turns invalid
+    items into the same errors the plan builder reports (negated on the C
+    side, raised by the binding)."""
+    items, _ = _items(QWEN05)
+    assert bl.bitlinear_fwd_group_plan_fuses(items, len(QWEN05), 1, 6, 8) is True
+    with pytest.raises(bl.BitLinearError) as e:
+        bl.bitlinear_fwd_group_plan_fuses(items, len(QWEN05), 1, 5, 8)
+    assert e.value.status == bl.BL_EUNSUPPORTED
+    bad, _ = _items([(64, 200)])  # k not a multiple of 128
+    with pytest.raises(bl.BitLinearError) as e:
+        bl.bitlinear_fwd_group_plan_fuses(bad, 1, 1, 6, 8)
+    assert e.value.status == bl.BL_ESHAPE
