@@ -610,20 +610,23 @@ def train_step(torch, bl, n, m, tokens=4096, iters=3):
         bl.bitlinear_relu2_gate(fb[4]["Y"], fb[5]["Y"], tokens, ffn, None, fb[6]["xq"], fb[6]["x_scale"])
         contract(6)
 
-    # one backward workspace, sized for the largest layer (calls run in order on one stream)
-    bws = torch.empty(max(bl.bitlinear_bwd_workspace_bytes(tokens, lw.k, lw.n_out) for lw in lws),
+    # down alone (its dX feeds the gating backward, which forms the dY of
+    # gate and up), then the other six layers in one grouped backward, whose
+    # products share launches (small layers fill what large ones leave)
+    group = (4, 5, 3, 0, 1, 2)
+    bitems = bl.make_bwd_items([dict(dY=dys[i], xq=fb[src[i]]["xq"], x_scale=fb[src[i]]["x_scale"],
+                                     packed=lws[i].packed, gamma=lws[i].gamma, dX=gx[i], dW=gw[i],
+                                     k=lws[i].k, n_out=lws[i].n_out) for i in group], tokens)
+    bws = torch.empty(max(bl.bitlinear_bwd_workspace_bytes(tokens, lws[6].k, lws[6].n_out),
+                          bl.bitlinear_bwd_group_workspace_bytes(bitems, len(group), tokens)),
                       dtype=torch.uint8, device="cuda")
 
-    def bwd_layer(i):
-        lw, a = lws[i], fb[src[i]]
-        bl.bitlinear_bwd(dys[i], a["xq"], a["x_scale"], lw.packed, lw.gamma, tokens, lw.k,
-                         lw.n_out, n, m, gx[i], gw[i], ws=bws)
-
     def bwd():
-        bwd_layer(6)  # down (synthetic dY), then the gating backward: dY of gate and up
+        lw, a = lws[6], fb[src[6]]
+        bl.bitlinear_bwd(dys[6], a["xq"], a["x_scale"], lw.packed, lw.gamma, tokens, lw.k,
+                         lw.n_out, n, m, gx[6], gw[6], ws=bws)
         bl.bitlinear_relu2_gate_bwd(gx[6], fb[4]["Y"], fb[5]["Y"], tokens * ffn, dys[4], dys[5])
-        for i in (4, 5, 3, 0, 1, 2):
-            bwd_layer(i)
+        bl.bitlinear_bwd_group(bitems, len(group), tokens, n, m, ws=bws)
 
     # binary32 latent weights; the update writes the bf16 W the plan reads
     lats = [LatentWeights(W) for W in Ws]

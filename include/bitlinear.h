@@ -427,6 +427,44 @@ int bitlinear_bwd(const uint16_t *dY, const int8_t *xq, const float *x_scale,
                   int64_t k, int64_t n_out, int n, int m, float *dX,
                   float *dW, void *ws, size_t ws_bytes, void *stream);
 
+/* Step 8-9 for several layers at once: the same dual straight-through
+ * backward (Sparse-BitNet article §三 and §六; formulas as for bitlinear_bwd)
+ * of independent layers, in shared launches.  Every item's operands are
+ * prepared first, then all their dX and dW products run in launches of up
+ * to 16 products (8 layers with both outputs), their tiles dealt over the
+ * CUs longest contraction first, so small layers fill what large ones
+ * leave instead of each leaving part of the chip idle.  Per item the
+ * results are those of bitlinear_bwd on the same arguments, bit for bit
+ * (every product contracts k in the same order through the same matrix
+ * instruction), except for products bitlinear_bwd splits along k (at most
+ * 128 tiles of 128 x 128 and k of 2048 or more): the grouped call sums
+ * those in one pass, so they agree to binary32 rounding.
+ *   items   host array of `count` (>= 1) descriptors; every pointer is a
+ *           device pointer with bitlinear_bwd's meaning, alignment and
+ *           rules; a NULL dX or dW skips that output; all items share
+ *           tokens and n:m.
+ *   ws      device workspace of at least bitlinear_bwd_group_workspace_bytes()
+ *           bytes, 256-byte aligned, clobbered (may be NULL when tokens is
+ *           0: every dW is then zeroed and nothing else runs).
+ * Every item is validated before anything is enqueued; an invalid one
+ * returns its bitlinear_bwd status and `bitlinear_last_error` names its
+ * index.  Calls that overlap on one workspace race. */
+typedef struct bitlinear_bwd_item {
+    const uint16_t *dY;     /* bf16 [tokens x n_out]          */
+    const int8_t *xq;       /* int8 [tokens x k] (for dW)     */
+    const float *x_scale;   /* float [tokens] (for dW)        */
+    const void *packed;     /* packed codes (for dX)          */
+    const double *gamma;    /* absmean scale (for dX)         */
+    float *dX;              /* float [tokens x k] or NULL     */
+    float *dW;              /* float [n_out x k] or NULL      */
+    int64_t k, n_out;
+} bitlinear_bwd_item;
+
+size_t bitlinear_bwd_group_workspace_bytes(const bitlinear_bwd_item *items, int count,
+                                           int64_t tokens);
+int bitlinear_bwd_group(const bitlinear_bwd_item *items, int count, int64_t tokens,
+                        int n, int m, void *ws, size_t ws_bytes, void *stream);
+
 /* Output tiles of bitlinear_bwd's products, process-wide: 0 (the default)
  * chooses per launch from the tile counts; 1, 2 or 3 fixes 128 x 128,
  * 256 x 128 or 256 x 256.  Every choice contracts k in the same order

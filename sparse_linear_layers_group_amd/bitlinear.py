@@ -42,6 +42,8 @@ _SIGS = {
     "bitlinear_fwd": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_bwd_tiles": (_int, [_int]),
+    "bitlinear_bwd_group_workspace_bytes": (_sz, [_vp, _int, _i64]),
+    "bitlinear_bwd_group": (_int, [_vp, _int, _i64, _int, _int, _vp, _sz, _vp]),
     "bitlinear_fwd_noalloc": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp]),
     "bitlinear_sp24_packed_bytes": (_sz, [_i64, _i64]),
     "bitlinear_sp24_workspace_bytes": (_sz, [_i64, _i64, _i64]),
@@ -251,6 +253,40 @@ def bitlinear_bwd(dY, xq, x_scale, packed, gamma, tokens, k, n_out, n, m, dX, dW
         (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes),
         _stream(stream))
     _check(st, "bitlinear_bwd")
+
+
+class bitlinear_bwd_item(ctypes.Structure):
+    """Mirror of the C struct bitlinear_bwd_item (device pointers as ints)."""
+    _fields_ = [("dY", _vp), ("xq", _vp), ("x_scale", _vp), ("packed", _vp), ("gamma", _vp),
+                ("dX", _vp), ("dW", _vp), ("k", _i64), ("n_out", _i64)]
+
+
+def make_bwd_items(entries, tokens):
+    """entries: dicts with tensors dY, xq, x_scale, packed, gamma, dX (or None),
+    dW (or None) and ints k, n_out."""
+    arr = (bitlinear_bwd_item * len(entries))()
+    for i, e in enumerate(entries):
+        k, n_out = int(e["k"]), int(e["n_out"])
+        arr[i] = bitlinear_bwd_item(
+            _ptr(e["dY"], _BF16, tokens * n_out, "dY"), _ptr(e.get("xq"), (torch.int8,), tokens * k, "xq", optional=True),
+            _ptr(e.get("x_scale"), (torch.float32,), tokens, "x_scale", optional=True),
+            _ptr(e.get("packed"), (torch.uint8,), None, "packed", optional=True),
+            _ptr(e.get("gamma"), (torch.float64,), 1, "gamma", optional=True),
+            _ptr(e.get("dX"), (torch.float32,), tokens * k, "dX", optional=True),
+            _ptr(e.get("dW"), (torch.float32,), n_out * k, "dW", optional=True), k, n_out)
+    return arr
+
+
+def bitlinear_bwd_group_workspace_bytes(items, count, tokens):
+    return int(lib().bitlinear_bwd_group_workspace_bytes(items, int(count), int(tokens)))
+
+
+def bitlinear_bwd_group(items, count, tokens, n, m, ws=None, ws_bytes=None, stream=None):
+    st = lib().bitlinear_bwd_group(items, int(count), int(tokens), n, m,
+                                   _ptr(ws, (torch.uint8,), None, "ws", optional=True),
+                                   (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes),
+                                   _stream(stream))
+    _check(st, "bitlinear_bwd_group")
 
 
 def bitlinear_bwd_tiles(tiles):

@@ -16,6 +16,7 @@
 
 #include "bitlinear.h"
 #include "common.h"
+#include "bwd_group.h"
 #include "launch.h"
 
 namespace {
@@ -796,6 +797,90 @@ int bitlinear_quant_group(const void* plan, int n, int m, int gamma_over, void* 
   TRY(check_ptr(plan, 16, "plan"));
   hipError_t e = bl::launch_quant_group(plan, n, m, gamma_over, reinterpret_cast<hipStream_t>(stream));
   return hip_status(e, "grouped quantisation launch");
+}
+
+namespace {
+// bitlinear_bwd's validation of one item of a grouped backward (everything
+// but the workspace)
+int check_bwd_item(const bitlinear_bwd_item& it, int64_t tokens) {
+  TRY(check_layer(it.n_out, it.k));
+  if (it.n_out % 16 != 0)
+    return fail(BL_ESHAPE, "the backward needs n_out to be a multiple of 16 (got %lld)", (long long)it.n_out);
+  if (tokens >= kLimit || tokens * it.k >= kLimit || tokens * it.n_out >= kLimit)
+    return fail(BL_ESHAPE, "tokens*k and tokens*n_out must stay below 2^31");
+  TRY(check_opt_ptr(it.dX, 16, "dX"));
+  TRY(check_opt_ptr(it.dW, 16, "dW"));
+  if (tokens == 0 || (!it.dX && !it.dW)) return BL_OK;
+  const int64_t tp = bl::bwd_tokens_padded(tokens), np = (it.n_out + 63) / 64 * 64;
+  if (tp * it.n_out >= kLimit / 2 || tp * it.k >= kLimit / 2 || it.k * np >= kLimit / 2)
+    return fail(BL_ESHAPE, "the backward needs tokens*n_out, tokens*k and n_out*k below 2^30");
+  TRY(check_ptr(it.dY, 16, "dY"));
+  if (it.dX) {
+    TRY(check_ptr(it.packed, 16, "packed"));
+    TRY(check_ptr(it.gamma, 8, "gamma"));
+  }
+  if (it.dW) {
+    TRY(check_ptr(it.xq, 16, "xq"));
+    TRY(check_ptr(it.x_scale, 4, "x_scale"));
+  }
+  return BL_OK;
+}
+}  // namespace
+
+size_t bitlinear_bwd_group_workspace_bytes(const bitlinear_bwd_item* items, int count, int64_t tokens) {
+  if (!items || count < 1 || tokens < 0 || tokens >= kLimit) return 0;
+  size_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    const bitlinear_bwd_item& it = items[i];
+    if (it.n_out < 1 || it.k < 128 || it.k % 128 != 0 || it.n_out % 16 != 0 || it.n_out >= kLimit ||
+        it.k >= kLimit)
+      return 0;
+    total += bl::bwd_group_item_bytes(tokens, it.k, it.n_out);
+  }
+  return total;
+}
+
+int bitlinear_bwd_group(const bitlinear_bwd_item* items, int count, int64_t tokens, int n, int m,
+                        void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_nm(n, m));
+  if (!items) return fail(BL_EINVAL, "items is NULL");
+  if (count < 1) return fail(BL_ESHAPE, "count must be >= 1 (got %d)", count);
+  if (tokens < 0) return fail(BL_ESHAPE, "tokens must be >= 0 (got %lld)", (long long)tokens);
+  for (int i = 0; i < count; ++i) {
+    const int st = check_bwd_item(items[i], tokens);
+    if (st != BL_OK) {
+      std::string detail = bitlinear_last_error();
+      return fail(st, "item %d: %s", i, detail.c_str());
+    }
+  }
+  bool any = false;
+  for (int i = 0; i < count; ++i) any = any || items[i].dX || items[i].dW;
+  if (!any) return ok();
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (tokens == 0) {
+    // no tokens: every dX is empty and every dW all zeros (no workspace)
+    for (int i = 0; i < count; ++i)
+      if (items[i].dW) {
+        hipError_t e = bl::launch_bwd(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, items[i].dW,
+                                      nullptr, 0, items[i].k, items[i].n_out, bl::s_of(n, m), s);
+        if (e != hipSuccess) return hip_status(e, "dW clear");
+      }
+    return ok();
+  }
+  const size_t need = bitlinear_bwd_group_workspace_bytes(items, count, tokens);
+  if (!ws || ws_bytes < need)
+    return fail(BL_EWORKSPACE, "grouped backward workspace needs %zu bytes (got %zu)", need,
+                ws ? ws_bytes : (size_t)0);
+  TRY(check_ptr(ws, 256, "ws"));
+  std::vector<bl::BwdItem> its;
+  for (int i = 0; i < count; ++i) {
+    const bitlinear_bwd_item& it = items[i];
+    if (!it.dX && !it.dW) continue;
+    its.push_back(bl::BwdItem{it.dY, it.xq, it.x_scale, it.packed, it.gamma, it.dX, it.dW, it.k, it.n_out});
+  }
+  if (its.empty()) return ok();
+  hipError_t e = bl::launch_bwd_group(its.data(), (int)its.size(), tokens, bl::s_of(n, m), ws, s);
+  return hip_status(e, "grouped backward launch");
 }
 
 int bitlinear_bwd_tiles(int tiles) {

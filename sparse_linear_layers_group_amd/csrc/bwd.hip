@@ -16,11 +16,14 @@
 // (exact in bf16), bf16(dY * s_t) transposed (rounded once), and x_q
 // transposed (exact).  Every conversion happens once per element, so the
 // product kernel is a plain copy-to-LDS and MFMA loop.
+#include "bwd_group.h"
 #include "common.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <atomic>
 #include <utility>
+#include <vector>
 
 #include <type_traits>
 
@@ -180,6 +183,14 @@ struct NtProblem {
   float* C;
   const double* alpha;
   int64_t lda, ldb, ldc, M, N, K, klen;
+};
+
+// the products of one launch of the 256-row kernel (its tiles dealt over
+// the XCDs problem by problem, in this order)
+constexpr int kMaxNt = 16;
+struct NtSet {
+  NtProblem p[kMaxNt];
+  int32_t n;
 };
 
 __host__ __device__ inline int64_t nt_tiles(const NtProblem& p) {
@@ -435,7 +446,7 @@ __device__ __forceinline__ char* big_stage() {
 // register budget is the same; bounds that depend on kWN broke the host
 // side's template deduction)
 template <int kWN>
-__global__ __launch_bounds__(512) void gemm_nt_bf16_big_kernel(NtProblem p0, NtProblem p1) {
+__global__ __launch_bounds__(512) void gemm_nt_bf16_big_kernel(NtSet set) {
   typedef BigTile<kWN> T;
   typedef __attribute__((address_space(3))) char lds_char;
   typedef __attribute__((address_space(3))) void lds_void;
@@ -443,27 +454,31 @@ __global__ __launch_bounds__(512) void gemm_nt_bf16_big_kernel(NtProblem p0, NtP
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / kWN, wn = wave % kWN;
   const int l16 = lane & 15, lg = lane >> 4;
-  int64_t m0, n0, t;
-  bool second;
+  int64_t m0, n0, t = 0;
+  int which = -1;
   {
+    // workgroup (XCD x, slot) takes the slot-th tile of XCD x's run: the XCD
+    // shares of the problems one after the other
     const int64_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    int64_t s0, c0, s1, c1;
-    xcd_share(nt_tiles_big<kWN>(p0), xcd, s0, c0);
-    xcd_share(nt_tiles_big<kWN>(p1), xcd, s1, c1);
-    if (slot >= c0 + c1) return;
-    second = slot >= c0;
-    t = second ? s1 + slot - c0 : s0 + slot;
+    int64_t before = 0;
+    for (int i = 0; i < set.n; ++i) {
+      int64_t s0, c0;
+      xcd_share(nt_tiles_big<kWN>(set.p[i]), xcd, s0, c0);
+      if (which < 0 && slot < before + c0) {
+        which = i;
+        t = s0 + slot - before;
+      }
+      before += c0;
+    }
+    if (which < 0) return;
   }
-  // the problem's fields, each selected on its own (a reference to one of
-  // the two argument structs put both in scratch memory)
-  const uint16_t* __restrict__ A = second ? p1.A : p0.A;
-  const uint16_t* __restrict__ B = second ? p1.B : p0.B;
-  float* __restrict__ C = second ? p1.C : p0.C;
-  const double* __restrict__ alpha = second ? p1.alpha : p0.alpha;
-  const int64_t lda = second ? p1.lda : p0.lda, ldb = second ? p1.ldb : p0.ldb;
-  const int64_t ldc = second ? p1.ldc : p0.ldc, M = second ? p1.M : p0.M, N = second ? p1.N : p0.N;
-  const int64_t klen = second ? p1.klen : p0.klen;
-  int64_t K = second ? p1.K : p0.K;
+  const NtProblem& pr = set.p[which];
+  const uint16_t* __restrict__ A = pr.A;
+  const uint16_t* __restrict__ B = pr.B;
+  float* __restrict__ C = pr.C;
+  const double* __restrict__ alpha = pr.alpha;
+  const int64_t lda = pr.lda, ldb = pr.ldb, ldc = pr.ldc, M = pr.M, N = pr.N, klen = pr.klen;
+  int64_t K = pr.K;
   {
     const int64_t tiles_m = (M + kBigM - 1) / kBigM, tiles_n = (N + T::N - 1) / T::N;
     constexpr int64_t kG = 4;  // row tiles per group of the tile order
@@ -658,13 +673,27 @@ int bwd_set_tiles(int tiles) {
   g_bwd_tiles.store(tiles, std::memory_order_relaxed);
   return 0;
 }
-static int bwd_tile_kind(const NtProblem& p0, const NtProblem& p1) {
-  const int f = g_bwd_tiles.load(std::memory_order_relaxed);
-  if (f) return f;
-  // 256 x 256 when its tiles fill at least 1.5 rounds of the 256 CUs (the
-  // last round then at least half full), else 256 x 128
-  const int64_t t4 = nt_tiles_big<4>(p0) + nt_tiles_big<4>(p1);
+// 256 x 256 when its tiles fill at least 1.5 rounds of the 256 CUs (the
+// last round then at least half full), else 256 x 128
+static int big_kind(const NtSet& set) {
+  int64_t t4 = 0;
+  for (int i = 0; i < set.n; ++i) t4 += nt_tiles_big<4>(set.p[i]);
   return t4 >= 384 && t4 % 256 >= 128 ? 3 : 2;
+}
+static int bwd_tile_kind(const NtSet& set) {
+  const int f = g_bwd_tiles.load(std::memory_order_relaxed);
+  return f ? f : big_kind(set);
+}
+static hipError_t launch_big(const NtSet& set, int kind, hipStream_t s) {
+  int64_t per = 0;
+  if (kind == 3) {
+    for (int i = 0; i < set.n; ++i) per += (nt_tiles_big<4>(set.p[i]) + 7) / 8;
+    gemm_nt_bf16_big_kernel<4><<<(unsigned)(8 * per), BigTile<4>::kThreads, 0, s>>>(set);
+  } else {
+    for (int i = 0; i < set.n; ++i) per += (nt_tiles_big<2>(set.p[i]) + 7) / 8;
+    gemm_nt_bf16_big_kernel<2><<<(unsigned)(8 * per), BigTile<2>::kThreads, 0, s>>>(set);
+  }
+  return hipGetLastError();
 }
 
 // The products that are not split run in one launch (a null `b` is no
@@ -687,13 +716,14 @@ static hipError_t gemm_nt_run(const NtProblem* a, const NtProblem* b, float* par
     } else {
       p1.M = 0;  // no tiles
     }
-    const int kind = bwd_tile_kind(p0, p1);
-    if (kind == 3) {
-      const int64_t per = (nt_tiles_big<4>(p0) + 7) / 8 + (nt_tiles_big<4>(p1) + 7) / 8;
-      gemm_nt_bf16_big_kernel<4><<<(unsigned)(8 * per), BigTile<4>::kThreads, 0, s>>>(p0, p1);
-    } else if (kind == 2) {
-      const int64_t per = (nt_tiles_big<2>(p0) + 7) / 8 + (nt_tiles_big<2>(p1) + 7) / 8;
-      gemm_nt_bf16_big_kernel<2><<<(unsigned)(8 * per), BigTile<2>::kThreads, 0, s>>>(p0, p1);
+    NtSet set{};
+    set.p[0] = p0;
+    set.p[1] = p1;
+    set.n = nw;
+    const int kind = bwd_tile_kind(set);
+    if (kind >= 2) {
+      hipError_t e = launch_big(set, kind, s);
+      if (e != hipSuccess) return e;
     } else {
       const int64_t per = (nt_tiles(p0) + 7) / 8 + (nt_tiles(p1) + 7) / 8;
       gemm_nt_bf16_kernel<<<(unsigned)(8 * per), 256, 0, s>>>(p0, p1);
@@ -769,6 +799,39 @@ hipError_t launch_bwd(const uint16_t* dY, const int8_t* xq, const float* scale, 
   if (dW) pw = dw_problem(dW, ws, tokens, k, n_out);
   float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + bwd_partial_offset(tokens, k, n_out));
   return gemm_nt_run(dX ? &px : nullptr, dW ? &pw : nullptr, partials, s);
+}
+
+hipError_t launch_bwd_group(const BwdItem* items, int count, int64_t tokens, int S, void* ws,
+                            hipStream_t s) {
+  std::vector<NtProblem> probs;
+  char* w = reinterpret_cast<char*>(ws);
+  for (int i = 0; i < count; ++i) {
+    const BwdItem& it = items[i];
+    hipError_t e = hipSuccess;
+    if (it.dX) {
+      e = prep_dx(it.packed, w, tokens, it.k, it.n_out, S, s);
+      probs.push_back(dx_problem(it.dY, it.gamma, it.dX, w, tokens, it.k, it.n_out));
+    }
+    if (e == hipSuccess && it.dW) {
+      e = prep_dw(it.dY, it.xq, it.scale, w, tokens, it.k, it.n_out, s);
+      probs.push_back(dw_problem(it.dW, w, tokens, it.k, it.n_out));
+    }
+    if (e != hipSuccess) return e;
+    w += bwd_group_item_bytes(tokens, it.k, it.n_out);
+  }
+  // deepest contraction first: within each XCD the longest tiles start
+  // first and the short ones fill the end (a longest-first schedule)
+  std::stable_sort(probs.begin(), probs.end(),
+                   [](const NtProblem& a, const NtProblem& b) { return a.K > b.K; });
+  for (size_t first = 0; first < probs.size(); first += kMaxNt) {
+    NtSet set{};
+    set.n = (int32_t)std::min<size_t>(kMaxNt, probs.size() - first);
+    for (int i = 0; i < set.n; ++i) set.p[i] = probs[first + (size_t)i];
+    const int f = g_bwd_tiles.load(std::memory_order_relaxed);
+    hipError_t e = launch_big(set, f >= 2 ? f : big_kind(set), s);  // 128 x 128 tiles take two products only
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace bl

@@ -267,3 +267,53 @@ def test_group_stages_validated(L):
     fake = ctypes.c_void_p(1 << 20)
     for stages in (0, 5, -1):
         assert L.bitlinear_fwd_group(fake, 6, 8, stages, None) == bl.BL_EINVAL
+
+
+def _bwd_items(specs):
+    """specs: (k, n_out, dX?, dW?) with stand-in aligned device addresses."""
+    arr = (bl.bitlinear_bwd_item * len(specs))()
+    for i, (k, n_out, want_dx, want_dw) in enumerate(specs):
+        arr[i] = bl.bitlinear_bwd_item(A, A, A, A, A, A if want_dx else None, A if want_dw else None, k, n_out)
+    return arr
+
+
+def test_bwd_group_sizes(L):
+    """The grouped workspace is the sum of every item's operand region (no
+    split partials), and 0 for an invalid item."""
+    items = _bwd_items([(256, 128, True, True), (2560, 640, True, True), (384, 272, False, True)])
+    total = bl.bitlinear_bwd_group_workspace_bytes(items, 3, 300)
+    parts = [bl.bitlinear_bwd_group_workspace_bytes(_bwd_items([s]), 1, 300)
+             for s in [(256, 128, True, True), (2560, 640, True, True), (384, 272, False, True)]]
+    assert total == sum(parts) > 0
+    assert all(p % 256 == 0 and p <= bl.bitlinear_bwd_workspace_bytes(300, k, n)
+               for p, (k, n, _, _) in zip(parts, [(256, 128, 0, 0), (2560, 640, 0, 0), (384, 272, 0, 0)]))
+    assert bl.bitlinear_bwd_group_workspace_bytes(_bwd_items([(256, 120, True, True)]), 1, 4) == 0
+    assert bl.bitlinear_bwd_group_workspace_bytes(items, 0, 4) == 0
+
+
+def test_bwd_group_validation(L):
+    """Every item is checked before anything is enqueued (on a host without
+    a GPU a launch would have returned BL_EHIP), and the error names the
+    item."""
+    g = L.bitlinear_bwd_group
+    good = _bwd_items([(256, 128, True, True), (384, 272, True, True)])
+    need = bl.bitlinear_bwd_group_workspace_bytes(good, 2, 4)
+    assert g(None, 1, 4, 6, 8, A, need, None) == bl.BL_EINVAL
+    assert g(good, 0, 4, 6, 8, A, need, None) == bl.BL_ESHAPE
+    assert g(good, 2, -1, 6, 8, A, need, None) == bl.BL_ESHAPE
+    assert g(good, 2, 4, 5, 8, A, need, None) == bl.BL_EUNSUPPORTED
+    assert g(good, 2, 4, 6, 8, A, need - 1, None) == bl.BL_EWORKSPACE
+    assert g(good, 2, 4, 6, 8, None, 0, None) == bl.BL_EWORKSPACE
+    assert g(good, 2, 4, 6, 8, A + 16, need, None) == bl.BL_EINVAL  # ws alignment
+    bad = _bwd_items([(256, 128, True, True), (384, 120, True, True)])  # n_out % 16
+    assert g(bad, 2, 4, 6, 8, A, need, None) == bl.BL_ESHAPE
+    assert "item 1" in bl.bitlinear_last_error()
+    bad = _bwd_items([(256, 128, True, True), (384, 272, False, True)])
+    bad[1].xq = None  # dW needs x_q
+    assert g(bad, 2, 4, 6, 8, A, need, None) == bl.BL_EINVAL
+    assert "item 1" in bl.bitlinear_last_error() and "xq" in bl.bitlinear_last_error()
+    bad = _bwd_items([(256, 128, True, True)])
+    bad[0].packed = None  # dX needs the packed codes
+    assert g(bad, 1, 4, 6, 8, A, need, None) == bl.BL_EINVAL
+    none = _bwd_items([(256, 128, False, False)])
+    assert g(none, 1, 4, 6, 8, None, 0, None) == bl.BL_OK  # nothing asked: nothing runs

@@ -60,3 +60,76 @@ def test_bwd_tiles_rejects_other_sizes():
     with pytest.raises(bl.BitLinearError):
         bl.bitlinear_bwd_tiles(4)
     bl.bitlinear_bwd_tiles(0)
+
+
+def _splits(M, N, K):
+    """bitlinear_bwd's split rule: at most 128 tiles of 128 x 128 and k >= 2048."""
+    tiles = -(-M // 128) * -(-N // 128)
+    return tiles <= 128 and K >= 2048
+
+
+def _group_case(shapes, tokens, outputs, seed):
+    """Layers with synthetic weights, activations and output gradients, their
+    per-layer bitlinear_bwd results, and the grouped call's."""
+    layers, entries = [], []
+    for i, (n_out, k) in enumerate(shapes):
+        W = synth.weights(n_out, k, seed=seed + i)
+        X = synth.activations(tokens, k, seed=seed + 50 + i)
+        dYb = synth.grad_output(tokens, n_out, seed=seed + 90 + i)
+        lw, _, _ = H.quantize_on_gpu(W, 6, 8, want_wq=False)
+        bufs = lw.fwd(bf16_tensor(X), tokens)
+        dY = bf16_tensor(dYb)
+        want_dx, want_dw = outputs[i]
+        ref = lw.bwd(dY, bufs["xq"], bufs["x_scale"], tokens, dX=want_dx, dW=want_dw)
+        e = dict(dY=dY, xq=bufs["xq"], x_scale=bufs["x_scale"], packed=lw.packed, gamma=lw.gamma, k=k, n_out=n_out,
+                 dX=torch.full((tokens * k,), float("nan"), device="cuda") if want_dx else None,
+                 dW=torch.full((n_out * k,), float("nan"), device="cuda") if want_dw else None)
+        layers.append((n_out, k, ref))
+        entries.append(e)
+    items = bl.make_bwd_items(entries, tokens)
+    ws = torch.empty(max(bl.bitlinear_bwd_group_workspace_bytes(items, len(entries), tokens), 256),
+                     dtype=torch.uint8, device="cuda")
+    bl.bitlinear_bwd_group(items, len(entries), tokens, 6, 8, ws)
+    torch.cuda.synchronize()
+    return layers, entries
+
+
+@pytest.mark.parametrize("shapes,tokens,outputs", [
+    # ragged layers, some outputs skipped
+    ([(272, 384), (48, 256), (512, 1024), (1040, 640)], 300,
+     [(True, True), (True, False), (False, True), (True, True)]),
+    # BitNet-2B4T q, k, v, o at 4096 tokens: the grouping the training step
+    # uses (the k and v dW are split along k by per-layer calls)
+    ([(2560, 2560), (640, 2560), (640, 2560), (2560, 2560)], 4096, [(True, True)] * 4),
+])
+def test_bwd_group_matches_per_layer_calls(shapes, tokens, outputs):
+    """bitlinear_bwd_group against bitlinear_bwd on each layer: bit for bit,
+    except products the per-layer call splits along k, which agree to
+    binary32 rounding (relative Frobenius difference below 1e-5)."""
+    layers, entries = _group_case(shapes, tokens, outputs, seed=tokens + len(shapes))
+    for (n_out, k, ref), e in zip(layers, entries):
+        for name, got, want, split in (("dX", e["dX"], ref[0], _splits(tokens, k, n_out)),
+                                       ("dW", e["dW"], ref[1], _splits(n_out, k, -(-tokens // 64) * 64))):
+            if got is None:
+                continue
+            g, w = got.cpu().numpy(), want.cpu().numpy()
+            if split:
+                d = np.linalg.norm((g - w).astype(np.float64)) / np.linalg.norm(w.astype(np.float64))
+                assert d < 1e-5, (name, n_out, k, d)
+            else:
+                assert np.array_equal(g.view(np.uint32), w.view(np.uint32)), (name, n_out, k)
+
+
+def test_bwd_group_no_tokens_zeroes_dw():
+    """No tokens: every requested dW becomes zeros, no workspace needed."""
+    entries = []
+    for n_out, k in ((128, 256), (64, 384)):
+        lw, _, _ = H.quantize_on_gpu(synth.weights(n_out, k, seed=n_out), 6, 8, want_wq=False)
+        entries.append(dict(dY=torch.empty(0, dtype=torch.bfloat16, device="cuda"), packed=lw.packed,
+                            gamma=lw.gamma, k=k, n_out=n_out,
+                            dW=torch.full((n_out * k,), float("nan"), device="cuda")))
+    items = bl.make_bwd_items(entries, 0)
+    bl.bitlinear_bwd_group(items, len(entries), 0, 6, 8)
+    torch.cuda.synchronize()
+    for e in entries:
+        assert torch.count_nonzero(e["dW"]).item() == 0
