@@ -610,23 +610,35 @@ def train_step(torch, bl, n, m, tokens=4096, iters=3):
         bl.bitlinear_relu2_gate(fb[4]["Y"], fb[5]["Y"], tokens, ffn, None, fb[6]["xq"], fb[6]["x_scale"])
         contract(6)
 
-    # down alone (its dX feeds the gating backward, which forms the dY of
-    # gate and up), then the other six layers in one grouped backward, whose
-    # products share launches (small layers fill what large ones leave)
-    group = (4, 5, 3, 0, 1, 2)
-    bitems = bl.make_bwd_items([dict(dY=dys[i], xq=fb[src[i]]["xq"], x_scale=fb[src[i]]["x_scale"],
-                                     packed=lws[i].packed, gamma=lws[i].gamma, dX=gx[i], dW=gw[i],
-                                     k=lws[i].k, n_out=lws[i].n_out) for i in group], tokens)
-    bws = torch.empty(max(bl.bitlinear_bwd_workspace_bytes(tokens, lws[6].k, lws[6].n_out),
-                          bl.bitlinear_bwd_group_workspace_bytes(bitems, len(group), tokens)),
+    # The backward in the order a block's data dependencies allow: down
+    # (its dX feeds the gating backward, which forms the dY of gate and
+    # up), then gate and up together, then o, then q, k and v together (in
+    # a model the attention backward sits between o and q/k/v, and o's dY
+    # comes from the feed-forward's input gradient).  Layers fed one input
+    # share a grouped call: their products share launches and their x_q is
+    # prepared once.
+    def item(i):
+        a = fb[src[i]]
+        return dict(dY=dys[i], xq=a["xq"], x_scale=a["x_scale"], packed=lws[i].packed,
+                    gamma=lws[i].gamma, dX=gx[i], dW=gw[i], k=lws[i].k, n_out=lws[i].n_out)
+    groups = [(4, 5), (0, 1, 2)]
+    gitems = [bl.make_bwd_items([item(i) for i in g], tokens) for g in groups]
+    bws = torch.empty(max([bl.bitlinear_bwd_workspace_bytes(tokens, lws[i].k, lws[i].n_out) for i in (6, 3)] +
+                          [bl.bitlinear_bwd_group_workspace_bytes(it, len(g), tokens)
+                           for it, g in zip(gitems, groups)]),
                       dtype=torch.uint8, device="cuda")
 
+    def bwd_layer(i):
+        lw, a = lws[i], fb[src[i]]
+        bl.bitlinear_bwd(dys[i], a["xq"], a["x_scale"], lw.packed, lw.gamma, tokens, lw.k,
+                         lw.n_out, n, m, gx[i], gw[i], ws=bws)
+
     def bwd():
-        lw, a = lws[6], fb[src[6]]
-        bl.bitlinear_bwd(dys[6], a["xq"], a["x_scale"], lw.packed, lw.gamma, tokens, lw.k,
-                         lw.n_out, n, m, gx[6], gw[6], ws=bws)
+        bwd_layer(6)
         bl.bitlinear_relu2_gate_bwd(gx[6], fb[4]["Y"], fb[5]["Y"], tokens * ffn, dys[4], dys[5])
-        bl.bitlinear_bwd_group(bitems, len(group), tokens, n, m, ws=bws)
+        bl.bitlinear_bwd_group(gitems[0], 2, tokens, n, m, ws=bws)
+        bwd_layer(3)
+        bl.bitlinear_bwd_group(gitems[1], 3, tokens, n, m, ws=bws)
 
     # binary32 latent weights; the update writes the bf16 W the plan reads
     lats = [LatentWeights(W) for W in Ws]

@@ -438,7 +438,9 @@ int bitlinear_bwd(const uint16_t *dY, const int8_t *xq, const float *x_scale,
  * (every product contracts k in the same order through the same matrix
  * instruction), except for products bitlinear_bwd splits along k (at most
  * 128 tiles of 128 x 128 and k of 2048 or more): the grouped call sums
- * those in one pass, so they agree to binary32 rounding.
+ * those in one pass, so they agree to binary32 rounding.  Items whose
+ * xq pointers and k are equal (layers fed the same input) share one
+ * prepared copy of x_q.
  *   items   host array of `count` (>= 1) descriptors; every pointer is a
  *           device pointer with bitlinear_bwd's meaning, alignment and
  *           rules; a NULL dX or dW skips that output; all items share

@@ -29,25 +29,66 @@
 
 namespace bl {
 
-__device__ __forceinline__ uint16_t code_bf16(uint32_t byte) {
-  // 0x01 -> +1.0, 0xff -> -1.0, 0 -> 0
-  return byte == 0u ? (uint16_t)0 : (byte == 1u ? (uint16_t)0x3f80 : (uint16_t)0xbf80);
-}
-
 // ------------------------------------------------------------- prep
+// All operand conversions of one backward call run in one launch: a list
+// of tasks (one matrix each), every workgroup of 256 threads takes one job
+// of one task.  Jobs of a dY or x_q task are 64 x 64 transposes through
+// LDS; jobs of a codes task are four packed superblocks, one per
+// wavefront, transposed in registers.
+
+// bf16 codes of one half-group from its 8-bit key: entry key * 2 + half
+// holds positions 0..3 as two bf16 pairs (the int8 codes of half_codes
+// with 0x01 -> +1.0 and 0xff -> -1.0, both exact)
+struct HalfBf16Table {
+  uint32_t v[1024];
+};
+constexpr uint32_t code_to_bf16(uint32_t byte) {
+  return byte == 0u ? 0u : (byte == 1u ? 0x3f80u : 0xbf80u);
+}
+constexpr HalfBf16Table make_half_bf16_table() {
+  HalfBf16Table t{};
+  for (uint32_t e = 0; e < 512; ++e) {
+    const uint32_t c = half_codes(e >> 1, e & 1u);
+    t.v[2 * e] = code_to_bf16(c & 0xffu) | (code_to_bf16((c >> 8) & 0xffu) << 16);
+    t.v[2 * e + 1] = code_to_bf16((c >> 16) & 0xffu) | (code_to_bf16(c >> 24) << 16);
+  }
+  return t;
+}
+__device__ constexpr HalfBf16Table kHalfBf16Table = make_half_bf16_table();
+static_assert(make_half_bf16_table().v[2 * (2 * 0x1f + 0)] == 0x3f80bf80u,
+              "low half, bitmap 1111, sign of nonzero 0: -1.0 then +1.0");
+
+enum PrepKind : int32_t { kPrepCodes = 0, kPrepDys = 1, kPrepXq = 2 };
+
+// One matrix of a prep launch.
+//   codes: src = packed codes, rows = k blocks per strip, cols = strips,
+//          pitch = np (rows of codes^T); jobs = ceil(superblocks / 4)
+//   dys:   src = dY, scale = s_t, rows = tokens, cols = n_out, pitch = tp
+//   xq:    src = x_q, rows = tokens, cols = k, pitch = tp
+// dY and x_q jobs are (64-token block fastest, 64-column block) tiles.
+struct PrepTask {
+  const void* src;
+  const float* scale;
+  uint16_t* out;
+  int64_t rows, cols, pitch;
+  int32_t kind, jobs;
+};
+constexpr int kMaxPrep = 16;
+struct PrepSet {
+  PrepTask t[kMaxPrep];
+  int32_t n;
+};
+
 // 64 x 64 transposes through LDS.  Source rows are the contraction index
 // of the product (tokens); each thread loads 16 bytes of a source row and
 // writes 16 bytes (8 consecutive source rows) of a destination row.
 constexpr int kTP = 66;  // LDS pitch (bf16) of the 64 x 64 transpose tile
 
 // dYsT[r][t] = bf16(dY[t][r] * s_t) for t < tokens, 0 for tokens <= t < tp
-__global__ __launch_bounds__(256) void prep_dys_t_kernel(const uint16_t* __restrict__ dY,
-                                                        const float* __restrict__ scale,
-                                                        int64_t tokens, int64_t n_out, int64_t tp,
-                                                        uint16_t* __restrict__ out) {
-  __shared__ uint16_t tile[64 * kTP];  // [t][r]
-  const int tid = threadIdx.x;
-  const int64_t t0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+__device__ __forceinline__ void prep_dys_tile(const uint16_t* __restrict__ dY,
+                                              const float* __restrict__ scale, int64_t tokens,
+                                              int64_t n_out, int64_t tp, uint16_t* __restrict__ out,
+                                              int64_t t0, int64_t r0, uint16_t* tile, int tid) {
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int q = tid + 256 * p, t = q >> 3, r8 = 8 * (q & 7);
@@ -79,12 +120,9 @@ __global__ __launch_bounds__(256) void prep_dys_t_kernel(const uint16_t* __restr
 }
 
 // xbT[c][t] = bf16(x_q[t][c]) (exact) for t < tokens, 0 up to tp
-__global__ __launch_bounds__(256) void prep_xq_t_kernel(const int8_t* __restrict__ xq,
-                                                       int64_t tokens, int64_t k, int64_t tp,
-                                                       uint16_t* __restrict__ out) {
-  __shared__ uint16_t tile[64 * kTP];  // [t][c]
-  const int tid = threadIdx.x;
-  const int64_t t0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+__device__ __forceinline__ void prep_xq_tile(const int8_t* __restrict__ xq, int64_t tokens, int64_t k,
+                                             int64_t tp, uint16_t* __restrict__ out, int64_t t0,
+                                             int64_t c0, uint16_t* tile, int tid) {
   {
     const int t = tid >> 2, c16 = 16 * (tid & 3);
     const int64_t tt = t0 + t;
@@ -109,50 +147,106 @@ __global__ __launch_bounds__(256) void prep_xq_t_kernel(const int8_t* __restrict
   }
 }
 
-// codesT[c][r] = bf16(code[r][c]) for the rows of one packed superblock
-// (64 rows x 128 columns) per workgroup of 64 threads; padding rows of
-// the last strip are zero fields, so rows up to the strip end are written
-// (the row pitch np = 64 * strips)
+// Lane exchanges inside groups of 8 lanes (data-parallel primitives: the
+// partner's register value, lane j reading lane j ^ 1, j ^ 2 or j ^ 4)
+__device__ __forceinline__ uint32_t lane_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xb1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ uint32_t lane_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4e, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ uint32_t lane_xor4(uint32_t v) {
+  // lanes 0-3 and 8-11 of each row of 16 read lane + 4 (row_shl:4), lanes
+  // 4-7 and 12-15 read lane - 4 (row_shr:4)
+  const int a = __builtin_amdgcn_update_dpp(0, (int)v, 0x104, 0xf, 0x5, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(a, (int)v, 0x114, 0xf, 0xa, false);
+}
+__device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// 8 x 8 transpose of bf16 values across the 8 lanes j = lane & 7 of a
+// group: in d[m], lane j holds elements 2m, 2m+1 of row j; out o[m], lane
+// j holds element j of rows 2m, 2m+1.  Three exchange stages, each with
+// the partner at lane distance 1, 2, 4.
+__device__ __forceinline__ void transpose8_bf16(const uint32_t (&d)[4], uint32_t (&o)[4], int lane) {
+  const int j = lane & 7;
+  // stage 1: lane j holds rows (j & ~1, +1) of elements 2m + (j & 1)
+  const uint32_t sel = (j & 1) ? 0x03020706u : 0x05040100u;
+  uint32_t x[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) x[m] = byte_perm(lane_xor1(d[m]), d[m], sel);
+  // stage 2: lane j holds rows (j & ~3) .. +3 of elements 2m + (j & 1),
+  // m = b and b + 2 with b = bit 1 of j
+  const bool b = (j >> 1) & 1;
+  const uint32_t r0 = lane_xor2(b ? x[0] : x[1]), r1 = lane_xor2(b ? x[2] : x[3]);
+  const uint32_t k0 = b ? x[1] : x[0], k1 = b ? x[3] : x[2];
+  const uint32_t y[4] = {b ? r0 : k0, b ? k0 : r0, b ? r1 : k1, b ? k1 : r1};
+  // stage 3: lane j holds rows 0..7 of element 2(2t + b) + (j & 1) = j,
+  // t = bit 2 of j
+  const bool t = (j >> 2) & 1;
+  const uint32_t q0 = lane_xor4(t ? y[0] : y[2]), q1 = lane_xor4(t ? y[1] : y[3]);
+  const uint32_t h0 = t ? y[2] : y[0], h1 = t ? y[3] : y[1];
+  o[0] = t ? q0 : h0;
+  o[1] = t ? q1 : h1;
+  o[2] = t ? h0 : q0;
+  o[3] = t ? h1 : q1;
+}
+
+// codesT[c][r] = bf16(code[r][c]) for one packed superblock (64 rows x 128
+// columns) per wavefront.  Lane c decodes chunk c: field f holds 8-group g
+// = field_group(c, f) of row field_row(c, f), so the 8 lanes of a group
+// hold 8 consecutive rows of one 8-group; after the transpose lane j holds
+// column 8g + j of those rows, one 16-byte store.  Padding rows of the last
+// strip are zero fields, so rows up to the strip end are written (the row
+// pitch np = 64 * strips).
 template <int S>
-__global__ __launch_bounds__(64) void prep_codes_t_kernel(const uint32_t* __restrict__ packed,
-                                                         int64_t nkb, int64_t np,
-                                                         uint16_t* __restrict__ out) {
+__device__ __forceinline__ void prep_codes_sb(const uint32_t* __restrict__ packed, int64_t sb,
+                                              int64_t nkb, int64_t np, uint16_t* __restrict__ out,
+                                              const u32x2* lut, int lane) {
   constexpr int kW = block_bytes(S) / 4;
-  __shared__ uint16_t tile[kBlockK * kTP];  // [c][r]
-  __shared__ uint32_t lut[512];
-  const int lane = threadIdx.x;
-  for (int idx = lane; idx < 512; idx += 64)  // lut[half * 256 + key]
-    lut[idx] = ld_global(&kHalfCodeTable.v[(idx & 255) * 2 + (idx >> 8)]);
-  const int64_t sb = blockIdx.x;  // superblock = strip * nkb + kb
   const int64_t strip = sb / nkb, kb = sb - strip * nkb;
   uint32_t w[kW + 1];
   const uint32_t* src = packed + (sb * kStripRows + lane) * kW;
 #pragma unroll
   for (int i = 0; i < kW; ++i) w[i] = ld_global(src + i);
   w[kW] = 0;
-  __syncthreads();
-  auto lk = [&](uint32_t key, int half) { return lut[half * 256 + key]; };
-  auto emit = [&](int f, uint32_t lo, uint32_t hi) {
-    const int rr = field_row(lane, f), gi = field_group(lane, f);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      tile[(gi * 8 + p) * kTP + rr] = code_bf16((lo >> (8 * p)) & 0xffu);
-      tile[(gi * 8 + 4 + p) * kTP + rr] = code_bf16((hi >> (8 * p)) & 0xffu);
-    }
+  uint16_t* dst = out + (kb * kBlockK + (lane & 7)) * np + strip * kStripRows + (lane & 8);
+  auto lk = [&](uint32_t key, int half) { return lut[key * 2 + half]; };
+  auto emit = [&](int f, u32x2 lo, u32x2 hi) {
+    const uint32_t d[4] = {lo.x, lo.y, hi.x, hi.y};
+    uint32_t o[4];
+    transpose8_bf16(d, o, lane);
+    st_global(reinterpret_cast<u32x4*>(dst + (int64_t)(8 * field_group(lane, f)) * np + 16 * (f >> 2)),
+              u32x4{o[0], o[1], o[2], o[3]});
   };
   decode_groups<S, 0, 16>(w, lk, emit);
-  __syncthreads();
-  // 128 columns x 64 rows: each thread writes 8 rows of 8 bf16 runs
-#pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    const int q = lane + 64 * p, c = q >> 3, r8 = 8 * (q & 7);
-    uint32_t o[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[e] = (uint32_t)tile[c * kTP + r8 + 2 * e] | ((uint32_t)tile[c * kTP + r8 + 2 * e + 1] << 16);
-    st_global(reinterpret_cast<u32x4*>(out + (kb * kBlockK + c) * np + strip * kStripRows + r8),
-              u32x4{o[0], o[1], o[2], o[3]});
+}
+
+template <int S>
+__global__ __launch_bounds__(256) void prep_group_kernel(PrepSet set) {
+  __shared__ uint16_t tile[64 * kTP];
+  __shared__ u32x2 lut[512];
+  const int tid = threadIdx.x;
+  int job = (int)blockIdx.x, ti = 0;
+  while (ti + 1 < set.n && job >= set.t[ti].jobs) job -= set.t[ti].jobs, ++ti;
+  const PrepTask& tk = set.t[ti];
+  if (tk.kind == kPrepCodes) {
+    reinterpret_cast<u32x4*>(lut)[tid] = ld_global(reinterpret_cast<const u32x4*>(kHalfBf16Table.v) + tid);
+    __syncthreads();
+    const int64_t sb = 4 * (int64_t)job + (tid >> 6);
+    if (sb < tk.rows * tk.cols)
+      prep_codes_sb<S>(reinterpret_cast<const uint32_t*>(tk.src), sb, tk.rows, tk.pitch, tk.out, lut,
+                       tid & 63);
+    return;
   }
+  const int64_t bx = tk.pitch / 64, t0 = 64 * (job % bx), c0 = 64 * (job / bx);
+  if (tk.kind == kPrepDys)
+    prep_dys_tile(reinterpret_cast<const uint16_t*>(tk.src), tk.scale, tk.rows, tk.cols, tk.pitch, tk.out,
+                  t0, c0, tile, tid);
+  else
+    prep_xq_tile(reinterpret_cast<const int8_t*>(tk.src), tk.rows, tk.cols, tk.pitch, tk.out, t0, c0,
+                 tile, tid);
 }
 
 // ------------------------------------------------------------- product
@@ -673,12 +767,25 @@ int bwd_set_tiles(int tiles) {
   g_bwd_tiles.store(tiles, std::memory_order_relaxed);
   return 0;
 }
-// 256 x 256 when its tiles fill at least 1.5 rounds of the 256 CUs (the
-// last round then at least half full), else 256 x 128
+// The tile size with the shorter estimated time, in rounds of one XCD's
+// 32 CUs (each XCD runs an eighth of every product).  256 x 256 tiles run
+// one per CU and a round costs 1, a partly filled last round too; 256 x 128
+// tiles run two per CU at ~1.18 per round (the same flops per CU at the
+// lower rate the narrower tiles reach), except a last round that leaves
+// every CU at most one tile, which costs ~0.6.  Ties (within 5%) go to
+// 256 x 256.  E.g. a 4096 x 2560 dX with its 2560 x 2560 dW (260 large
+// tiles: two rounds, the second nearly empty) takes 256 x 128; gate and up
+// of the BitNet-2B4T block together (860 large tiles) take 256 x 256.
 static int big_kind(const NtSet& set) {
-  int64_t t4 = 0;
-  for (int i = 0; i < set.n; ++i) t4 += nt_tiles_big<4>(set.p[i]);
-  return t4 >= 384 && t4 % 256 >= 128 ? 3 : 2;
+  int64_t n3 = 0, n2 = 0;
+  for (int i = 0; i < set.n; ++i) {
+    n3 += (nt_tiles_big<4>(set.p[i]) + 7) / 8;
+    n2 += (nt_tiles_big<2>(set.p[i]) + 7) / 8;
+  }
+  const double t3 = (double)((n3 + 31) / 32);
+  const int64_t rem2 = n2 % 64;
+  const double t2 = 1.18 * (double)(n2 / 64) + (rem2 == 0 ? 0.0 : rem2 <= 32 ? 0.6 : 1.18);
+  return t2 < 0.95 * t3 ? 2 : 3;
 }
 static int bwd_tile_kind(const NtSet& set) {
   const int f = g_bwd_tiles.load(std::memory_order_relaxed);
@@ -738,18 +845,36 @@ static hipError_t gemm_nt_run(const NtProblem* a, const NtProblem* b, float* par
   return hipGetLastError();
 }
 
-static hipError_t prep_dx(const void* packed, void* ws, int64_t tokens, int64_t k, int64_t n_out, int S,
-                          hipStream_t s) {
+// the prep tasks of one call, launched together (in chunks of kMaxPrep)
+struct PrepList {
+  std::vector<PrepTask> t;
+  hipError_t launch(int S, hipStream_t s) const {
+    for (size_t first = 0; first < t.size(); first += kMaxPrep) {
+      PrepSet set{};
+      set.n = (int32_t)std::min<size_t>(kMaxPrep, t.size() - first);
+      int64_t jobs = 0;
+      for (int i = 0; i < set.n; ++i) {
+        set.t[i] = t[first + (size_t)i];
+        jobs += set.t[i].jobs;
+      }
+      if (jobs == 0) continue;
+      if (S == 8) prep_group_kernel<8><<<(unsigned)jobs, 256, 0, s>>>(set);
+      else if (S == 6) prep_group_kernel<6><<<(unsigned)jobs, 256, 0, s>>>(set);
+      else if (S == 2) prep_group_kernel<2><<<(unsigned)jobs, 256, 0, s>>>(set);
+      else prep_group_kernel<4><<<(unsigned)jobs, 256, 0, s>>>(set);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+};
+
+// dX operand: the codes decoded and transposed (codes^T [k x np])
+static void prep_dx(PrepList& L, const void* packed, void* ws, int64_t tokens, int64_t k, int64_t n_out) {
   const int64_t nkb = k / kBlockK, strips = (n_out + kStripRows - 1) / kStripRows;
-  const int64_t np = strips * kStripRows;
   uint16_t* codes_t = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + bwd_codes_offset(tokens, k, n_out));
-  const uint32_t* p = reinterpret_cast<const uint32_t*>(packed);
-  const unsigned sbs = (unsigned)(strips * nkb);
-  if (S == 8) prep_codes_t_kernel<8><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
-  else if (S == 6) prep_codes_t_kernel<6><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
-  else if (S == 2) prep_codes_t_kernel<2><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
-  else prep_codes_t_kernel<4><<<sbs, 64, 0, s>>>(p, nkb, np, codes_t);
-  return hipGetLastError();
+  L.t.push_back(PrepTask{packed, nullptr, codes_t, nkb, strips, strips * kStripRows, kPrepCodes,
+                         (int32_t)((strips * nkb + 3) / 4)});
 }
 
 // dX [tokens x k] = gamma * dY [tokens x n_out] . codes^T [k x n_out]^T
@@ -761,17 +886,16 @@ static NtProblem dx_problem(const uint16_t* dY, const double* gamma, float* dX, 
   return NtProblem{dY, codes_t, dX, gamma, n_out, np, k, tokens, k, n_out, n_out};
 }
 
-static hipError_t prep_dw(const uint16_t* dY, const int8_t* xq, const float* scale, void* ws,
-                          int64_t tokens, int64_t k, int64_t n_out, hipStream_t s) {
+// dW operands: bf16(dY * s)^T always; x_q^T unless with_xq is false (the
+// grouped call reuses another item's x_q^T when two items share x_q)
+static void prep_dw(PrepList& L, const uint16_t* dY, const int8_t* xq, const float* scale, void* ws,
+                    int64_t tokens, int64_t k, int64_t n_out, bool with_xq = true) {
   const int64_t tp = bwd_tokens_padded(tokens);
   char* w = reinterpret_cast<char*>(ws);
   uint16_t* dys_t = reinterpret_cast<uint16_t*>(w + bwd_dys_offset(tokens, k, n_out));
   uint16_t* xq_t = reinterpret_cast<uint16_t*>(w + bwd_xq_offset(tokens, k, n_out));
-  prep_dys_t_kernel<<<dim3((unsigned)(tp / 64), (unsigned)((n_out + 63) / 64)), 256, 0, s>>>(
-      dY, scale, tokens, n_out, tp, dys_t);
-  prep_xq_t_kernel<<<dim3((unsigned)(tp / 64), (unsigned)(k / 64)), 256, 0, s>>>(xq, tokens, k, tp,
-                                                                              xq_t);
-  return hipGetLastError();
+  L.t.push_back(PrepTask{dY, scale, dys_t, tokens, n_out, tp, kPrepDys, (int32_t)((tp / 64) * ((n_out + 63) / 64))});
+  if (with_xq) L.t.push_back(PrepTask{xq, nullptr, xq_t, tokens, k, tp, kPrepXq, (int32_t)((tp / 64) * (k / 64))});
 }
 
 // dW [n_out x k] = (dY s)^T [n_out x tp] . x_q^T [k x tp]^T
@@ -790,9 +914,10 @@ hipError_t launch_bwd(const uint16_t* dY, const int8_t* xq, const float* scale, 
     if (dW) zero_f32_kernel<<<1024, 256, 0, s>>>(dW, n_out * k);
     return hipGetLastError();
   }
-  hipError_t e = hipSuccess;
-  if (dX) e = prep_dx(packed, ws, tokens, k, n_out, S, s);
-  if (e == hipSuccess && dW) e = prep_dw(dY, xq, scale, ws, tokens, k, n_out, s);
+  PrepList L;
+  if (dX) prep_dx(L, packed, ws, tokens, k, n_out);
+  if (dW) prep_dw(L, dY, xq, scale, ws, tokens, k, n_out);
+  hipError_t e = L.launch(S, s);
   if (e != hipSuccess) return e;
   NtProblem px{}, pw{};
   if (dX) px = dx_problem(dY, gamma, dX, ws, tokens, k, n_out);
@@ -804,21 +929,36 @@ hipError_t launch_bwd(const uint16_t* dY, const int8_t* xq, const float* scale, 
 hipError_t launch_bwd_group(const BwdItem* items, int count, int64_t tokens, int S, void* ws,
                             hipStream_t s) {
   std::vector<NtProblem> probs;
+  // x_q^T already prepared in this call, by x_q pointer and k: layers fed
+  // the same input (q, k, v; gate, up) share it
+  struct XqT {
+    const int8_t* xq;
+    int64_t k;
+    const uint16_t* t;
+  };
+  std::vector<XqT> done;
+  PrepList L;
   char* w = reinterpret_cast<char*>(ws);
   for (int i = 0; i < count; ++i) {
     const BwdItem& it = items[i];
-    hipError_t e = hipSuccess;
     if (it.dX) {
-      e = prep_dx(it.packed, w, tokens, it.k, it.n_out, S, s);
+      prep_dx(L, it.packed, w, tokens, it.k, it.n_out);
       probs.push_back(dx_problem(it.dY, it.gamma, it.dX, w, tokens, it.k, it.n_out));
     }
-    if (e == hipSuccess && it.dW) {
-      e = prep_dw(it.dY, it.xq, it.scale, w, tokens, it.k, it.n_out, s);
-      probs.push_back(dw_problem(it.dW, w, tokens, it.k, it.n_out));
+    if (it.dW) {
+      const XqT* seen = nullptr;
+      for (const XqT& d : done)
+        if (d.xq == it.xq && d.k == it.k) seen = &d;
+      prep_dw(L, it.dY, it.xq, it.scale, w, tokens, it.k, it.n_out, seen == nullptr);
+      NtProblem p = dw_problem(it.dW, w, tokens, it.k, it.n_out);
+      if (seen) p.B = seen->t;
+      else done.push_back(XqT{it.xq, it.k, p.B});
+      probs.push_back(p);
     }
-    if (e != hipSuccess) return e;
     w += bwd_group_item_bytes(tokens, it.k, it.n_out);
   }
+  hipError_t pe = L.launch(S, s);
+  if (pe != hipSuccess) return pe;
   // deepest contraction first: within each XCD the longest tiles start
   // first and the short ones fill the end (a longest-first schedule)
   std::stable_sort(probs.begin(), probs.end(),

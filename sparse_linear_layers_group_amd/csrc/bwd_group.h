@@ -25,8 +25,9 @@ inline size_t bwd_group_item_bytes(int64_t tokens, int64_t k, int64_t n_out) {
   return bwd_align(bwd_partial_offset(tokens, k, n_out));
 }
 
-// every item's operands prepared into its own workspace region, then all
-// products in launches of up to 16, deepest contraction first; tokens > 0
+// every item's operands prepared into its own workspace region (x_q^T once
+// per distinct x_q and k), then all products in launches of up to 16,
+// deepest contraction first; tokens > 0
 hipError_t launch_bwd_group(const BwdItem* items, int count, int64_t tokens, int S, void* ws,
                             hipStream_t s);
 

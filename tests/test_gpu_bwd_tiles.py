@@ -68,16 +68,20 @@ def _splits(M, N, K):
     return tiles <= 128 and K >= 2048
 
 
-def _group_case(shapes, tokens, outputs, seed):
+def _group_case(shapes, tokens, outputs, seed, inputs=None):
     """Layers with synthetic weights, activations and output gradients, their
-    per-layer bitlinear_bwd results, and the grouped call's."""
-    layers, entries = [], []
+    per-layer bitlinear_bwd results, and the grouped call's.  Layers with the
+    same entry in `inputs` take the same activations and pass the same x_q
+    and s_t tensors (as layers fed one input do)."""
+    layers, entries, fed = [], [], {}
     for i, (n_out, k) in enumerate(shapes):
         W = synth.weights(n_out, k, seed=seed + i)
-        X = synth.activations(tokens, k, seed=seed + 50 + i)
+        src = i if inputs is None else inputs[i]
         dYb = synth.grad_output(tokens, n_out, seed=seed + 90 + i)
         lw, _, _ = H.quantize_on_gpu(W, 6, 8, want_wq=False)
-        bufs = lw.fwd(bf16_tensor(X), tokens)
+        if src not in fed:
+            fed[src] = lw.fwd(bf16_tensor(synth.activations(tokens, k, seed=seed + 50 + src)), tokens)
+        bufs = fed[src]
         dY = bf16_tensor(dYb)
         want_dx, want_dw = outputs[i]
         ref = lw.bwd(dY, bufs["xq"], bufs["x_scale"], tokens, dX=want_dx, dW=want_dw)
@@ -94,19 +98,26 @@ def _group_case(shapes, tokens, outputs, seed):
     return layers, entries
 
 
-@pytest.mark.parametrize("shapes,tokens,outputs", [
+@pytest.mark.parametrize("shapes,tokens,outputs,inputs", [
     # ragged layers, some outputs skipped
     ([(272, 384), (48, 256), (512, 1024), (1040, 640)], 300,
-     [(True, True), (True, False), (False, True), (True, True)]),
-    # BitNet-2B4T q, k, v, o at 4096 tokens: the grouping the training step
-    # uses (the k and v dW are split along k by per-layer calls)
-    ([(2560, 2560), (640, 2560), (640, 2560), (2560, 2560)], 4096, [(True, True)] * 4),
+     [(True, True), (True, False), (False, True), (True, True)], None),
+    # ragged layers fed one input (one prepared x_q), one fed another
+    ([(272, 384), (48, 384), (512, 384), (1040, 640)], 300,
+     [(True, True), (False, True), (True, True), (True, True)], [0, 0, 0, 1]),
+    # BitNet-2B4T q, k, v (one input), o at 4096 tokens (the k and v dW are
+    # split along k by per-layer calls)
+    ([(2560, 2560), (640, 2560), (640, 2560), (2560, 2560)], 4096, [(True, True)] * 4, [0, 0, 0, 1]),
+    # BitNet-2B4T gate and up (one input) and down's dW alone, as the
+    # training step groups them after down's dX and the gating backward
+    ([(6912, 2560), (6912, 2560), (2560, 6912)], 4096, [(True, True), (True, True), (False, True)],
+     [0, 0, 1]),
 ])
-def test_bwd_group_matches_per_layer_calls(shapes, tokens, outputs):
+def test_bwd_group_matches_per_layer_calls(shapes, tokens, outputs, inputs):
     """bitlinear_bwd_group against bitlinear_bwd on each layer: bit for bit,
     except products the per-layer call splits along k, which agree to
     binary32 rounding (relative Frobenius difference below 1e-5)."""
-    layers, entries = _group_case(shapes, tokens, outputs, seed=tokens + len(shapes))
+    layers, entries = _group_case(shapes, tokens, outputs, seed=tokens + len(shapes), inputs=inputs)
     for (n_out, k, ref), e in zip(layers, entries):
         for name, got, want, split in (("dX", e["dX"], ref[0], _splits(tokens, k, n_out)),
                                        ("dW", e["dW"], ref[1], _splits(n_out, k, -(-tokens // 64) * 64))):
