@@ -448,9 +448,11 @@ int bitlinear_bwd(const uint16_t *dY, const int8_t *xq, const float *x_scale,
  *   ws      device workspace of at least bitlinear_bwd_group_workspace_bytes()
  *           bytes, 256-byte aligned, clobbered (may be NULL when tokens is
  *           0: every dW is then zeroed and nothing else runs).
- * Every item is validated before anything is enqueued; an invalid one
- * returns its bitlinear_bwd status and `bitlinear_last_error` names its
- * index.  Calls that overlap on one workspace race. */
+ * The layers must be independent: no item's dX or dW may overlap any
+ * item's inputs or another output (all conversions run before all
+ * products).  Every item is validated before anything is enqueued; an
+ * invalid one returns its bitlinear_bwd status and `bitlinear_last_error`
+ * names its index.  Calls that overlap on one workspace race. */
 typedef struct bitlinear_bwd_item {
     const uint16_t *dY;     /* bf16 [tokens x n_out]          */
     const int8_t *xq;       /* int8 [tokens x k] (for dW)     */
