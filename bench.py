@@ -406,24 +406,34 @@ def prefill_step(torch, bl, n, m, tokens=2048, iters=10):
         act_into(x1, x2, bufs[0], bufs[2])
         state["a"] += 1
 
-    def gemm():
-        packs, b0, b2 = act_sets[state["g"] % len(act_sets)]
-        state["g"] += 1
-        for i, lw in enumerate(lws):
-            src = b2 if i == 2 else b0
-            bl.bitlinear_contract(src["xq"], src["x_scale"], tokens, lw.k, packs[i], lw.n_out, n, m,
-                                  lw.gamma, bufs[i]["Y"], ws=bufs[i]["ws"])
-
-    # the same GEMMs with the bf16 Y epilogue (half the output bytes)
+    # gate and up read the same x_q: one grouped contraction, whose tiles
+    # share launches; down reads the gating output and runs alone
     ybf = [torch.empty(tokens * lw.n_out, dtype=torch.bfloat16, device="cuda") for lw in lws]
 
-    def gemm_bf16():
-        packs, b0, b2 = act_sets[state["g"] % len(act_sets)]
+    def gate_up_items(packs, out):
+        return bl.make_contract_items([dict(packed=packs[i], gamma=lws[i].gamma, n_out=lws[i].n_out, **out(i))
+                                       for i in (0, 1)], tokens)
+    gu32 = [gate_up_items(a[0], lambda i: dict(Y=bufs[i]["Y"])) for a in act_sets]
+    gu16 = [gate_up_items(a[0], lambda i: dict(Y_bf16=ybf[i])) for a in act_sets]
+
+    def gemm():
+        c = state["g"] % len(act_sets)
+        packs, b0, b2 = act_sets[c]
         state["g"] += 1
-        for i, lw in enumerate(lws):
-            src = b2 if i == 2 else b0
-            bl.bitlinear_contract_bf16(src["xq"], src["x_scale"], tokens, lw.k, packs[i], lw.n_out, n, m,
-                                       lw.gamma, ybf[i], ws=bufs[i]["ws"])
+        bl.bitlinear_contract_group(gu32[c], 2, b0["xq"], b0["x_scale"], tokens, 1536, n, m)
+        lw = lws[2]
+        bl.bitlinear_contract(b2["xq"], b2["x_scale"], tokens, lw.k, packs[2], lw.n_out, n, m,
+                              lw.gamma, bufs[2]["Y"], ws=bufs[2]["ws"])
+
+    # the same GEMMs with the bf16 Y epilogue (half the output bytes)
+    def gemm_bf16():
+        c = state["g"] % len(act_sets)
+        packs, b0, b2 = act_sets[c]
+        state["g"] += 1
+        bl.bitlinear_contract_group(gu16[c], 2, b0["xq"], b0["x_scale"], tokens, 1536, n, m)
+        lw = lws[2]
+        bl.bitlinear_contract_bf16(b2["xq"], b2["x_scale"], tokens, lw.k, packs[2], lw.n_out, n, m,
+                                   lw.gamma, ybf[2], ws=bufs[2]["ws"])
 
     for f in (quant, act, gemm, gemm_bf16):
         f()
@@ -449,6 +459,7 @@ def prefill_step(torch, bl, n, m, tokens=2048, iters=10):
     out = {k2: round(v, 4) for k2, v in res.items()}
     out["inputs"] = (f"rotating over {len(qgs)} copies of the latent W, {len(x_sets)} of X and "
                      f"{len(act_sets)} of (packed codes, x_q): every pass reads HBM")
+    out["gemm_launches"] = "gate + up in one grouped contraction (bitlinear_contract_group), down alone"
     return out
 
 
@@ -602,11 +613,17 @@ def train_step(torch, bl, n, m, tokens=4096, iters=3):
         bl.bitlinear_contract(a["xq"], a["x_scale"], tokens, lw.k, lw.packed, lw.n_out, n, m,
                               lw.gamma, fb[i]["Y"], ws=fb[i]["ws"])
 
+    # layers fed one input share a grouped contraction: q, k, v; gate, up
+    fgroups = [(0, 1, 2), (4, 5)]
+    fitems = [bl.make_contract_items([dict(packed=lws[i].packed, gamma=lws[i].gamma, Y=fb[i]["Y"],
+                                           n_out=lws[i].n_out) for i in g], tokens) for g in fgroups]
+
     def fwd():
         for i, x in ((0, X), (3, Xo)):
             bl.bitlinear_act_quant(x, tokens, lws[i].k, fb[i]["xq"], fb[i]["x_scale"])
-        for i in range(6):
-            contract(i)
+        bl.bitlinear_contract_group(fitems[0], 3, fb[0]["xq"], fb[0]["x_scale"], tokens, hid, n, m)
+        contract(3)
+        bl.bitlinear_contract_group(fitems[1], 2, fb[0]["xq"], fb[0]["x_scale"], tokens, hid, n, m)
         bl.bitlinear_relu2_gate(fb[4]["Y"], fb[5]["Y"], tokens, ffn, None, fb[6]["xq"], fb[6]["x_scale"])
         contract(6)
 

@@ -211,6 +211,39 @@ int bitlinear_contract_bf16(const int8_t *xq, const float *x_scale,
                             uint16_t *Y, int32_t *acc, void *ws,
                             size_t ws_bytes, void *stream);
 
+/* Steps 6-7 for several layers that read the same activations (a block's
+ * q, k and v, or gate and up): the contraction and epilogue of
+ * bitlinear_contract (BitNet b1.58 2B4T article §四) for every item, with
+ * the layers' tiles sharing launches at prefill sizes, so the short layers
+ * fill the partial rounds the others leave.  Per item the results (Y, or
+ * bf16 Y) are those of bitlinear_contract / bitlinear_contract_bf16 on the
+ * same arguments, bit for bit (the int32 sums are exact in any order).
+ *   items    host array of `count` (>= 1) descriptors: packed and gamma as
+ *            for bitlinear_contract, exactly one of Y (binary32) and Y_bf16
+ *            (bf16 bit patterns) non-NULL, both [tokens x n_out] device
+ *            arrays, 16-byte aligned; the outputs must not overlap each
+ *            other or the inputs.
+ *   xq, x_scale, tokens, k, n, m: as for bitlinear_contract, shared.
+ *   ws       bitlinear_contract_group_workspace_bytes() bytes (0 above 16
+ *            tokens; at most 16 tokens each item runs the decode-shaped
+ *            call in turn on this one workspace), zero-filled before the
+ *            first use, as for bitlinear_contract.
+ * Every item is validated before anything is enqueued; `bitlinear_last_error`
+ * names an invalid item's index. */
+typedef struct bitlinear_contract_item {
+    const void *packed;     /* packed codes [n_out x k]          */
+    const double *gamma;    /* absmean scale                     */
+    float *Y;               /* binary32 [tokens x n_out] or NULL */
+    uint16_t *Y_bf16;       /* bf16 [tokens x n_out] or NULL     */
+    int64_t n_out;
+} bitlinear_contract_item;
+
+size_t bitlinear_contract_group_workspace_bytes(const bitlinear_contract_item *items, int count,
+                                                int64_t tokens, int64_t k);
+int bitlinear_contract_group(const bitlinear_contract_item *items, int count, const int8_t *xq,
+                             const float *x_scale, int64_t tokens, int64_t k, int n, int m,
+                             void *ws, size_t ws_bytes, void *stream);
+
 /* 2:4 on structured-sparse matrix hardware.  The Sparse-BitNet article
  * (§七) ties N:M sparsity's speed-up to matrix units that skip the pruned
  * half (2:4 sparse tensor cores); gfx950's counterpart is

@@ -44,6 +44,8 @@ _SIGS = {
     "bitlinear_bwd_tiles": (_int, [_int]),
     "bitlinear_bwd_group_workspace_bytes": (_sz, [_vp, _int, _i64]),
     "bitlinear_bwd_group": (_int, [_vp, _int, _i64, _int, _int, _vp, _sz, _vp]),
+    "bitlinear_contract_group_workspace_bytes": (_sz, [_vp, _int, _i64, _i64]),
+    "bitlinear_contract_group": (_int, [_vp, _int, _vp, _vp, _i64, _i64, _int, _int, _vp, _sz, _vp]),
     "bitlinear_fwd_noalloc": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp]),
     "bitlinear_sp24_packed_bytes": (_sz, [_i64, _i64]),
     "bitlinear_sp24_workspace_bytes": (_sz, [_i64, _i64, _i64]),
@@ -335,6 +337,37 @@ def bitlinear_contract(xq, x_scale, tokens, k, packed, n_out, n, m, gamma, Y, ac
         _ptr(ws, (torch.uint8,), None, "ws", optional=True),
         (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes), _stream(stream))
     _check(st, "bitlinear_contract")
+
+
+class bitlinear_contract_item(ctypes.Structure):
+    """Mirror of the C struct bitlinear_contract_item (device pointers as ints)."""
+    _fields_ = [("packed", _vp), ("gamma", _vp), ("Y", _vp), ("Y_bf16", _vp), ("n_out", _i64)]
+
+
+def make_contract_items(entries, tokens):
+    """entries: dicts with tensors packed, gamma, Y (float32) or Y_bf16
+    (bfloat16), and int n_out."""
+    arr = (bitlinear_contract_item * len(entries))()
+    for i, e in enumerate(entries):
+        n_out = int(e["n_out"])
+        arr[i] = bitlinear_contract_item(
+            _ptr(e["packed"], (torch.uint8,), None, "packed"), _ptr(e["gamma"], (torch.float64,), 1, "gamma"),
+            _ptr(e.get("Y"), (torch.float32,), tokens * n_out, "Y", optional=True),
+            _ptr(e.get("Y_bf16"), _BF16, tokens * n_out, "Y_bf16", optional=True), n_out)
+    return arr
+
+
+def bitlinear_contract_group_workspace_bytes(items, count, tokens, k):
+    return int(lib().bitlinear_contract_group_workspace_bytes(items, int(count), int(tokens), int(k)))
+
+
+def bitlinear_contract_group(items, count, xq, x_scale, tokens, k, n, m, ws=None, ws_bytes=None, stream=None):
+    st = lib().bitlinear_contract_group(
+        items, int(count), _ptr(xq, (torch.int8,), tokens * k, "xq"),
+        _ptr(x_scale, (torch.float32,), tokens, "x_scale"), int(tokens), int(k), n, m,
+        _ptr(ws, (torch.uint8,), None, "ws", optional=True),
+        (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes), _stream(stream))
+    _check(st, "bitlinear_contract_group")
 
 
 def bitlinear_contract_bf16(xq, x_scale, tokens, k, packed, n_out, n, m, gamma, Y, acc=None, ws=None,

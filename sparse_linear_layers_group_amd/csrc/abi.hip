@@ -17,6 +17,7 @@
 #include "bitlinear.h"
 #include "common.h"
 #include "bwd_group.h"
+#include "gemm_group.h"
 #include "launch.h"
 
 namespace {
@@ -488,6 +489,66 @@ int bitlinear_contract_bf16(const int8_t* xq, const float* x_scale, int64_t toke
                        ws_bytes, stream);
 }
 
+
+size_t bitlinear_contract_group_workspace_bytes(const bitlinear_contract_item* items, int count,
+                                                int64_t tokens, int64_t k) {
+  if (!items || count < 1 || tokens < 0 || tokens >= kLimit || k < 128 || k % 128 != 0 || k >= kLimit) return 0;
+  size_t need = 0;
+  for (int i = 0; i < count; ++i) {
+    if (items[i].n_out < 1 || items[i].n_out >= kLimit) return 0;
+    if (tokens <= 16) need = std::max(need, bitlinear_fwd_workspace_bytes(tokens, k, items[i].n_out));
+  }
+  return need;
+}
+
+int bitlinear_contract_group(const bitlinear_contract_item* items, int count, const int8_t* xq,
+                             const float* x_scale, int64_t tokens, int64_t k, int n, int m, void* ws,
+                             size_t ws_bytes, void* stream) {
+  TRY(check_nm(n, m));
+  if (!items) return fail(BL_EINVAL, "items is NULL");
+  if (count < 1) return fail(BL_ESHAPE, "count must be >= 1 (got %d)", count);
+  for (int i = 0; i < count; ++i) {
+    const bitlinear_contract_item& it = items[i];
+    int st = check_layer(it.n_out, k);
+    if (st == BL_OK && (tokens < 0 || tokens >= kLimit || tokens * k >= kLimit || tokens * it.n_out >= kLimit))
+      st = fail(BL_ESHAPE, "tokens must be >= 0 with tokens*k and tokens*n_out below 2^31");
+    if (st == BL_OK && (it.Y != nullptr) == (it.Y_bf16 != nullptr))
+      st = fail(BL_EINVAL, "exactly one of Y and Y_bf16 must be given");
+    if (st == BL_OK && tokens > 0) {
+      st = check_ptr(it.packed, 16, "packed");
+      if (st == BL_OK) st = check_ptr(it.gamma, 8, "gamma");
+      if (st == BL_OK) st = it.Y ? check_ptr(it.Y, 16, "Y") : check_ptr(it.Y_bf16, 16, "Y_bf16");
+    }
+    if (st != BL_OK) {
+      std::string detail = bitlinear_last_error();
+      return fail(st, "item %d: %s", i, detail.c_str());
+    }
+  }
+  if (tokens == 0) return ok();
+  TRY(check_ptr(xq, 16, "xq"));
+  TRY(check_ptr(x_scale, 4, "x_scale"));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int S = bl::s_of(n, m);
+  if (tokens <= 16) {  // decode-shaped: each item in turn on the one workspace
+    const size_t need = bitlinear_contract_group_workspace_bytes(items, count, tokens, k);
+    if (need && (!ws || ws_bytes < need))
+      return fail(BL_EWORKSPACE, "decode workspace needs %zu bytes (got %zu)", need, ws ? ws_bytes : (size_t)0);
+    if (need) TRY(check_ptr(ws, 16, "ws"));
+    for (int i = 0; i < count; ++i) {
+      const bitlinear_contract_item& it = items[i];
+      hipError_t e = bl::launch_gemv(it.packed, xq, x_scale, it.gamma, it.Y, it.Y_bf16, nullptr, ws, (int)tokens,
+                                     k, it.n_out, S, s);
+      if (e != hipSuccess) return hip_status(e, "contraction launch");
+    }
+    return ok();
+  }
+  std::vector<bl::GemmGroupLayer> layers;
+  for (int i = 0; i < count; ++i)
+    layers.push_back(bl::GemmGroupLayer{items[i].packed, items[i].gamma, items[i].Y, items[i].Y_bf16, nullptr,
+                                        items[i].n_out});
+  hipError_t e = bl::launch_gemm_group(layers.data(), count, xq, x_scale, tokens, k, S, s);
+  return hip_status(e, "grouped contraction launch");
+}
 
 size_t bitlinear_fwd_group_plan_bytes(const bitlinear_fwd_item* items, int count, int64_t tokens) {
   int64_t steps = 0, strips = 0;

@@ -25,8 +25,10 @@
 // 128-token tiles at two per CU on every measured shape (more tiles for
 // layers with few rows, shorter store bursts at the end of a round).
 #include "common.h"
+#include "gemm_group.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace bl {
@@ -34,6 +36,7 @@ namespace bl {
 constexpr int kGStrips = 4;      // strips (wavefronts) per workgroup
 constexpr int kGLutCopies = 16;  // table copies: lane l reads copy l % 16
 constexpr uint32_t kGOOB = 0x80000000u;  // buffer offset past every range: loads give 0
+constexpr int kMaxGemmLayers = 8;       // layers of one grouped prefill launch
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t g_rsrc(const void* p, int64_t bytes) {
   const int64_t b = bytes < 0x7fffffff ? bytes : 0x7fffffff;
@@ -160,14 +163,31 @@ __device__ __forceinline__ void gemm_finish(v4i (&c)[kTT][4], bool live, int spl
   }
 }
 
+// One launch covers the layers of a GemmSet: layers that read the same
+// activations (x_q, s_t, tokens, k), each with its own codes, gamma and
+// output.  Tiles are numbered token block by token block, and within one
+// the row blocks of layer 0, then of layer 1, ..., so the workgroups an
+// XCD runs together share activations whatever layer they belong to.  A
+// single layer is a set of one (its tile order is then the plain one).
+struct GemmLayer {
+  const uint32_t* packed;
+  const double* gamma;
+  float* Y;
+  uint16_t* Yb;
+  int32_t* acc;
+  int64_t n_out;
+  int32_t row_blocks, first_rb;  // its row blocks; row blocks of the layers before it
+};
+struct GemmSet {
+  GemmLayer l[kMaxGemmLayers];
+  int32_t n, row_blocks;  // layers; row blocks of all layers (tiles per token block)
+};
+
 template <int S, int BT>
-__global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint32_t* __restrict__ packed,
+__global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(GemmSet set,
                                                      const int8_t* __restrict__ xq,
                                                      const float* __restrict__ scale,
-                                                     const double* __restrict__ gamma,
-                                                     float* __restrict__ Y, uint16_t* __restrict__ Yb,
-                                                     int32_t* __restrict__ acc_out, int64_t tokens,
-                                                     int64_t k, int64_t n_out, int row_blocks,
+                                                     int64_t tokens, int64_t k,
                                                      int token_blocks, int splits,
                                                      uint32_t* __restrict__ tickets,
                                                      v4i* __restrict__ partials) {
@@ -184,7 +204,7 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
   // each XCD a contiguous run of (part, tile) indices (row blocks fastest),
   // so tiles that share activations share that XCD's L2.  The grid is a
   // multiple of 8.
-  const int nblk = row_blocks * token_blocks;
+  const int nblk = set.row_blocks * token_blocks;
   const int nwork = nblk * splits;
   const int per_xcd = (nwork + 7) / 8;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -193,7 +213,17 @@ __global__ __launch_bounds__(256, BT == 128 ? 2 : 3) void gemm_kernel(const uint
                                  : full * per_xcd + (xcd - full) * (per_xcd - 1) + slot;
   if (slot >= (xcd < full ? per_xcd : per_xcd - 1)) return;
   const int part = logical / nblk, tile = logical - part * nblk;
-  const int rb = tile % row_blocks, tb = tile / row_blocks;
+  const int tb = tile / set.row_blocks, rball = tile - tb * set.row_blocks;
+  int li = 0;
+  while (li + 1 < set.n && rball >= set.l[li + 1].first_rb) ++li;
+  const GemmLayer& L = set.l[li];
+  const int rb = rball - L.first_rb;
+  const uint32_t* __restrict__ packed = L.packed;
+  const double* __restrict__ gamma = L.gamma;
+  float* __restrict__ Y = L.Y;
+  uint16_t* __restrict__ Yb = L.Yb;
+  int32_t* __restrict__ acc_out = L.acc;
+  const int64_t n_out = L.n_out;
 
   const int64_t strips = (n_out + kStripRows - 1) / kStripRows;
   const int64_t strip = (int64_t)rb * kGStrips + wave;
@@ -607,10 +637,50 @@ static hipError_t launch_gemm_s(const void* packed, const int8_t* xq, const floa
                                                       gemm_ticket_bytes(tokens, n_out))
                              : nullptr;
   const int nwork = row_blocks * token_blocks * splits;
-  gemm_kernel<S, BT><<<(unsigned)((nwork + 7) / 8 * 8), 256, 0, s>>>(
-      reinterpret_cast<const uint32_t*>(packed), xq, scale, gamma, Y, Yb, acc, tokens, k, n_out,
-      row_blocks, token_blocks, splits, tickets, partials);
+  GemmSet set{};
+  set.l[0] = GemmLayer{reinterpret_cast<const uint32_t*>(packed), gamma, Y, Yb, acc, n_out, row_blocks, 0};
+  set.n = 1;
+  set.row_blocks = row_blocks;
+  gemm_kernel<S, BT><<<(unsigned)((nwork + 7) / 8 * 8), 256, 0, s>>>(set, xq, scale, tokens, k, token_blocks,
+                                                                    splits, tickets, partials);
   return hipGetLastError();
+}
+
+// Layers that read the same activations, in launches of up to
+// kMaxGemmLayers layers each, never split along k
+template <int S>
+static hipError_t launch_gemm_group_s(const GemmGroupLayer* layers, int count, const int8_t* xq,
+                                      const float* scale, int64_t tokens, int64_t k, hipStream_t s) {
+  constexpr int BT = kGemmTileTokens;
+  const int token_blocks = (int)((tokens + BT - 1) / BT);
+  for (int first = 0; first < count; first += kMaxGemmLayers) {
+    GemmSet set{};
+    set.n = std::min(kMaxGemmLayers, count - first);
+    int rbs = 0;
+    for (int i = 0; i < set.n; ++i) {
+      const GemmGroupLayer& g = layers[first + i];
+      const int64_t strips = (g.n_out + kStripRows - 1) / kStripRows;
+      const int row_blocks = (int)((strips + kGStrips - 1) / kGStrips);
+      set.l[i] = GemmLayer{reinterpret_cast<const uint32_t*>(g.packed), g.gamma, g.Y, g.Yb, g.acc, g.n_out,
+                           row_blocks, rbs};
+      rbs += row_blocks;
+    }
+    set.row_blocks = rbs;
+    const int nwork = rbs * token_blocks;
+    gemm_kernel<S, BT><<<(unsigned)((nwork + 7) / 8 * 8), 256, 0, s>>>(set, xq, scale, tokens, k, token_blocks,
+                                                                      1, nullptr, nullptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_gemm_group(const GemmGroupLayer* layers, int count, const int8_t* xq, const float* scale,
+                             int64_t tokens, int64_t k, int S, hipStream_t s) {
+  if (S == 8) return launch_gemm_group_s<8>(layers, count, xq, scale, tokens, k, s);
+  if (S == 6) return launch_gemm_group_s<6>(layers, count, xq, scale, tokens, k, s);
+  if (S == 2) return launch_gemm_group_s<2>(layers, count, xq, scale, tokens, k, s);
+  return launch_gemm_group_s<4>(layers, count, xq, scale, tokens, k, s);
 }
 
 hipError_t launch_gemm(const void* packed, const int8_t* xq, const float* scale,

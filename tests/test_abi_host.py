@@ -317,3 +317,51 @@ def test_bwd_group_validation(L):
     assert g(bad, 1, 4, 6, 8, A, need, None) == bl.BL_EINVAL
     none = _bwd_items([(256, 128, False, False)])
     assert g(none, 1, 4, 6, 8, None, 0, None) == bl.BL_OK  # nothing asked: nothing runs
+
+
+def _contract_items(specs):
+    """specs: (n_out, Y?, Y_bf16?) with stand-in aligned device addresses."""
+    arr = (bl.bitlinear_contract_item * len(specs))()
+    for i, (n_out, y, yb) in enumerate(specs):
+        arr[i] = bl.bitlinear_contract_item(A, A, A if y else None, A if yb else None, n_out)
+    return arr
+
+
+def test_contract_group_sizes(L):
+    """No workspace above 16 tokens; at most 16 tokens the largest of the
+    items' decode workspaces (they run in turn on one); 0 for a bad shape."""
+    items = _contract_items([(896, True, False), (128, True, False), (4864, False, True)])
+    assert bl.bitlinear_contract_group_workspace_bytes(items, 3, 64, 896) == 0
+    for tokens in (1, 16):
+        want = max(bl.bitlinear_fwd_workspace_bytes(tokens, 896, n) for n in (896, 128, 4864))
+        assert bl.bitlinear_contract_group_workspace_bytes(items, 3, tokens, 896) == want
+    assert bl.bitlinear_contract_group_workspace_bytes(items, 3, 64, 100) == 0  # k % 128
+    assert bl.bitlinear_contract_group_workspace_bytes(items, 0, 64, 896) == 0
+
+
+def test_contract_group_validation(L):
+    """Every item is checked before anything is enqueued, and the error
+    names the item."""
+    g = L.bitlinear_contract_group
+    good = _contract_items([(896, True, False), (128, False, True)])
+    assert g(None, 1, A, A, 64, 896, 6, 8, None, 0, None) == bl.BL_EINVAL
+    assert g(good, 0, A, A, 64, 896, 6, 8, None, 0, None) == bl.BL_ESHAPE
+    assert g(good, 2, A, A, 64, 896, 5, 8, None, 0, None) == bl.BL_EUNSUPPORTED
+    assert g(good, 2, A, A, 64, 100, 6, 8, None, 0, None) == bl.BL_ESHAPE
+    assert g(good, 2, A, A, -1, 896, 6, 8, None, 0, None) == bl.BL_ESHAPE
+    both = _contract_items([(896, True, False), (128, True, True)])
+    assert g(both, 2, A, A, 64, 896, 6, 8, None, 0, None) == bl.BL_EINVAL
+    assert "item 1" in bl.bitlinear_last_error()
+    neither = _contract_items([(896, False, False)])
+    assert g(neither, 1, A, A, 64, 896, 6, 8, None, 0, None) == bl.BL_EINVAL
+    bad = _contract_items([(896, True, False), (0, True, False)])
+    assert g(bad, 2, A, A, 64, 896, 6, 8, None, 0, None) == bl.BL_ESHAPE
+    assert "item 1" in bl.bitlinear_last_error()
+    bad = _contract_items([(896, True, False)])
+    bad[0].gamma = A + 4  # gamma needs 8-byte alignment
+    assert g(bad, 1, A, A, 64, 896, 6, 8, None, 0, None) == bl.BL_EINVAL
+    assert g(good, 2, None, A, 64, 896, 6, 8, None, 0, None) == bl.BL_EINVAL  # xq
+    need = bl.bitlinear_contract_group_workspace_bytes(good, 2, 4, 896)
+    assert need > 0
+    assert g(good, 2, A, A, 4, 896, 6, 8, None, 0, None) == bl.BL_EWORKSPACE
+    assert g(good, 2, A, A, 0, 896, 6, 8, None, 0, None) == bl.BL_OK  # no tokens: nothing runs
