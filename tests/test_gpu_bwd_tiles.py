@@ -131,6 +131,30 @@ def test_bwd_group_matches_per_layer_calls(shapes, tokens, outputs, inputs):
                 assert np.array_equal(g.view(np.uint32), w.view(np.uint32)), (name, n_out, k)
 
 
+def test_bwd_group_many_items():
+    """Nine layers: 22 conversion tasks (two conversion launches of at most
+    16 tasks) and 17 products (two product launches of at most 16), four of
+    the layers sharing one input; bit-identical to per-layer calls except
+    split products."""
+    shapes = [(64, 256), (128, 384), (48, 256), (256, 640), (192, 256), (80, 512), (320, 256), (64, 384),
+              (112, 768)]  # (n_out, k); the layers fed input 0 share k = 256
+    outputs = [(True, True)] * 8 + [(True, False)]
+    inputs = [0, 1, 0, 2, 0, 3, 0, 4, 5]
+    tokens = 200
+    layers, entries = _group_case(shapes, tokens, outputs, seed=91, inputs=inputs)
+    for (n_out, k, ref), e in zip(layers, entries):
+        for name, got, want, split in (("dX", e["dX"], ref[0], _splits(tokens, k, n_out)),
+                                       ("dW", e["dW"], ref[1], _splits(n_out, k, -(-tokens // 64) * 64))):
+            if got is None:
+                continue
+            g, w = got.cpu().numpy(), want.cpu().numpy()
+            if split:
+                d = np.linalg.norm((g - w).astype(np.float64)) / np.linalg.norm(w.astype(np.float64))
+                assert d < 1e-5, (name, n_out, k, d)
+            else:
+                assert np.array_equal(g.view(np.uint32), w.view(np.uint32)), (name, n_out, k)
+
+
 def test_bwd_group_no_tokens_zeroes_dw():
     """No tokens: every requested dW becomes zeros, no workspace needed."""
     entries = []
