@@ -155,6 +155,22 @@ def test_bwd_group_many_items():
                 assert np.array_equal(g.view(np.uint32), w.view(np.uint32)), (name, n_out, k)
 
 
+def test_bwd_group_reruns_bit_identical():
+    """A second grouped call on the same inputs (the same workspace reused)
+    gives the same bits."""
+    shapes, tokens = [(272, 384), (48, 384), (512, 384)], 300
+    layers, entries = _group_case(shapes, tokens, [(True, True)] * 3, seed=23, inputs=[0, 0, 0])
+    first = [(e["dX"].cpu().numpy().copy(), e["dW"].cpu().numpy().copy()) for e in entries]
+    items = bl.make_bwd_items(entries, tokens)
+    ws = torch.empty(max(bl.bitlinear_bwd_group_workspace_bytes(items, len(entries), tokens), 256),
+                     dtype=torch.uint8, device="cuda")
+    bl.bitlinear_bwd_group(items, len(entries), tokens, 6, 8, ws)
+    torch.cuda.synchronize()
+    for (dx, dw), e in zip(first, entries):
+        assert np.array_equal(dx.view(np.uint32), e["dX"].cpu().numpy().view(np.uint32))
+        assert np.array_equal(dw.view(np.uint32), e["dW"].cpu().numpy().view(np.uint32))
+
+
 def test_bwd_group_no_tokens_zeroes_dw():
     """No tokens: every requested dW becomes zeros, no workspace needed."""
     entries = []

@@ -106,3 +106,17 @@ def test_contract_group_more_layers_than_one_launch():
     for (lw, _, _), e in zip(layers, entries):
         got = e.get("Y", e.get("Y_bf16"))
         assert np.array_equal(_bits(got), _bits(_own_call(lw, e, xq, sc, tokens, k, 6, 8)))
+
+
+def test_contract_group_reruns_bit_identical():
+    """Two calls on the same inputs give the same bits (no order-dependent
+    sums anywhere in the grouped launches)."""
+    tokens, k = 520, 512
+    shapes = [1040, 320, 64]
+    X, xq, sc, layers, entries = _case(shapes, [False, True, False], tokens, k, 6, 8, seed=17, with_oracle=False)
+    first = [_bits(e.get("Y", e.get("Y_bf16"))).copy() for e in entries]
+    items = bl.make_contract_items(entries, tokens)
+    bl.bitlinear_contract_group(items, len(entries), xq, sc, tokens, k, 6, 8)
+    torch.cuda.synchronize()
+    for f, e in zip(first, entries):
+        assert np.array_equal(f, _bits(e.get("Y", e.get("Y_bf16"))))
