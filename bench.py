@@ -652,8 +652,11 @@ def train_step(torch, bl, n, m, tokens=4096, iters=3):
                          lw.n_out, n, m, gx[i], gw[i], ws=bws)
 
     def bwd():
-        bwd_layer(6)
-        bl.bitlinear_relu2_gate_bwd(gx[6], fb[4]["Y"], fb[5]["Y"], tokens * ffn, dys[4], dys[5])
+        # down's backward with the gating backward fused into its dX
+        # epilogue: down's dX (h's gradient) never reaches memory
+        lw, a = lws[6], fb[src[6]]
+        bl.bitlinear_bwd_relu2_gate(dys[6], a["xq"], a["x_scale"], lw.packed, lw.gamma, tokens, lw.k, lw.n_out,
+                                    n, m, fb[4]["Y"], fb[5]["Y"], dys[4], dys[5], gw[6], ws=bws)
         bl.bitlinear_bwd_group(gitems[0], 2, tokens, n, m, ws=bws)
         bwd_layer(3)
         bl.bitlinear_bwd_group(gitems[1], 3, tokens, n, m, ws=bws)

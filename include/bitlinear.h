@@ -502,6 +502,27 @@ size_t bitlinear_bwd_group_workspace_bytes(const bitlinear_bwd_item *items, int 
 int bitlinear_bwd_group(const bitlinear_bwd_item *items, int count, int64_t tokens,
                         int n, int m, void *ws, size_t ws_bytes, void *stream);
 
+/* Steps 8-9 of the down projection of the BitNet b1.58 2B4T feed-forward
+ * with the squared-ReLU gating backward (2B4T article §一) fused into its dX
+ * product: the dual straight-through backward of bitlinear_bwd (Sparse-BitNet
+ * article §三 and §六) whose dX, h's gradient dH, never reaches memory;
+ * the product's epilogue forms dG and dU as bitlinear_relu2_gate_bwd forms
+ * them from dH.  Results are those of bitlinear_bwd (with the same dW)
+ * followed by bitlinear_relu2_gate_bwd, bit for bit.
+ *   dY, xq, x_scale, packed, gamma, tokens, k, n_out, n, m, dW, ws:
+ *            as for bitlinear_bwd (k is the gate and up layers' n_out).
+ *   G, U     device float [tokens x k]: the gate and up outputs, read.
+ *   dG, dU   device bf16 [tokens x k]: their output gradients, written.
+ * All 16-byte aligned; outputs must not overlap the inputs.  Errors as for
+ * bitlinear_bwd.  The products always run on 256-row tiles: a fixed
+ * 128 x 128 choice of bitlinear_bwd_tiles falls back to the per-launch
+ * choice here, which changes no bit. */
+int bitlinear_bwd_relu2_gate(const uint16_t *dY, const int8_t *xq, const float *x_scale,
+                             const void *packed, const double *gamma, int64_t tokens,
+                             int64_t k, int64_t n_out, int n, int m, const float *G,
+                             const float *U, uint16_t *dG, uint16_t *dU, float *dW,
+                             void *ws, size_t ws_bytes, void *stream);
+
 /* Output tiles of bitlinear_bwd's products, process-wide: 0 (the default)
  * chooses per launch from the tile counts; 1, 2 or 3 fixes 128 x 128,
  * 256 x 128 or 256 x 256.  Every choice contracts k in the same order

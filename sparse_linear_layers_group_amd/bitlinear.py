@@ -42,6 +42,8 @@ _SIGS = {
     "bitlinear_fwd": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _sz, _vp]),
     "bitlinear_bwd_tiles": (_int, [_int]),
+    "bitlinear_bwd_relu2_gate": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp,
+                                         _vp, _vp, _sz, _vp]),
     "bitlinear_bwd_group_workspace_bytes": (_sz, [_vp, _int, _i64]),
     "bitlinear_bwd_group": (_int, [_vp, _int, _i64, _int, _int, _vp, _sz, _vp]),
     "bitlinear_contract_group_workspace_bytes": (_sz, [_vp, _int, _i64, _i64]),
@@ -289,6 +291,21 @@ def bitlinear_bwd_group(items, count, tokens, n, m, ws=None, ws_bytes=None, stre
                                    (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes),
                                    _stream(stream))
     _check(st, "bitlinear_bwd_group")
+
+
+def bitlinear_bwd_relu2_gate(dY, xq, x_scale, packed, gamma, tokens, k, n_out, n, m, G, U, dG, dU, dW=None,
+                             ws=None, ws_bytes=None, stream=None):
+    """The down projection's backward with the squared-ReLU gating backward
+    fused into its dX epilogue: dG, dU (bfloat16, tokens * k) and dW."""
+    st = lib().bitlinear_bwd_relu2_gate(
+        _ptr(dY, _BF16, tokens * n_out, "dY"), _ptr(xq, (torch.int8,), tokens * k, "xq", optional=True),
+        _ptr(x_scale, (torch.float32,), tokens, "x_scale", optional=True),
+        _ptr(packed, (torch.uint8,), None, "packed"), _ptr(gamma, (torch.float64,), 1, "gamma"),
+        tokens, k, n_out, n, m, _ptr(G, (torch.float32,), tokens * k, "G"), _ptr(U, (torch.float32,), tokens * k, "U"),
+        _ptr(dG, _BF16, tokens * k, "dG"), _ptr(dU, _BF16, tokens * k, "dU"),
+        _ptr(dW, (torch.float32,), n_out * k, "dW", optional=True), _ptr(ws, (torch.uint8,), None, "ws", optional=True),
+        (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes), _stream(stream))
+    _check(st, "bitlinear_bwd_relu2_gate")
 
 
 def bitlinear_bwd_tiles(tiles):

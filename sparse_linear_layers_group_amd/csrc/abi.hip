@@ -944,6 +944,52 @@ int bitlinear_bwd_group(const bitlinear_bwd_item* items, int count, int64_t toke
   return hip_status(e, "grouped backward launch");
 }
 
+int bitlinear_bwd_relu2_gate(const uint16_t* dY, const int8_t* xq, const float* x_scale, const void* packed,
+                             const double* gamma, int64_t tokens, int64_t k, int64_t n_out, int n, int m,
+                             const float* G, const float* U, uint16_t* dG, uint16_t* dU, float* dW, void* ws,
+                             size_t ws_bytes, void* stream) {
+  TRY(check_nm(n, m));
+  TRY(check_layer(n_out, k));
+  if (n_out % 16 != 0)
+    return fail(BL_ESHAPE, "the backward needs n_out to be a multiple of 16 (got %lld)", (long long)n_out);
+  if (tokens < 0) return fail(BL_ESHAPE, "tokens must be >= 0 (got %lld)", (long long)tokens);
+  if (tokens >= kLimit || tokens * k >= kLimit || tokens * n_out >= kLimit)
+    return fail(BL_ESHAPE, "tokens*k and tokens*n_out must stay below 2^31");
+  TRY(check_opt_ptr(dW, 16, "dW"));
+  if (tokens == 0) {
+    // no tokens: dG and dU are empty and dW is all zeros
+    if (dW) {
+      hipError_t e = bl::launch_bwd(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dW, nullptr, 0, k, n_out,
+                                    bl::s_of(n, m), reinterpret_cast<hipStream_t>(stream));
+      return hip_status(e, "dW clear");
+    }
+    return ok();
+  }
+  {
+    const int64_t tp = bl::bwd_tokens_padded(tokens), np = (n_out + 63) / 64 * 64;
+    if (tp * n_out >= kLimit / 2 || tp * k >= kLimit / 2 || k * np >= kLimit / 2)
+      return fail(BL_ESHAPE, "the backward needs tokens*n_out, tokens*k and n_out*k below 2^30");
+  }
+  const size_t need = bl::bwd_ws_bytes(tokens, k, n_out);
+  if (!ws || ws_bytes < need)
+    return fail(BL_EWORKSPACE, "backward workspace needs %zu bytes (got %zu)", need, ws ? ws_bytes : (size_t)0);
+  TRY(check_ptr(ws, 256, "ws"));
+  TRY(check_ptr(dY, 16, "dY"));
+  TRY(check_ptr(packed, 16, "packed"));
+  TRY(check_ptr(gamma, 8, "gamma"));
+  TRY(check_ptr(G, 16, "G"));
+  TRY(check_ptr(U, 16, "U"));
+  TRY(check_ptr(dG, 16, "dG"));
+  TRY(check_ptr(dU, 16, "dU"));
+  if (dW) {
+    TRY(check_ptr(xq, 16, "xq"));
+    TRY(check_ptr(x_scale, 4, "x_scale"));
+  }
+  hipError_t e = bl::launch_bwd_gate(dY, xq, x_scale, packed, gamma, G, U, dG, dU, dW, ws, tokens, k, n_out,
+                                     bl::s_of(n, m), reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e, "backward launch");
+}
+
 int bitlinear_bwd_tiles(int tiles) {
   if (bl::bwd_set_tiles(tiles) != 0)
     return fail(BL_EINVAL, "bitlinear_bwd_tiles takes 0, 1, 2 or 3 (got %d)", tiles);

@@ -277,6 +277,14 @@ struct NtProblem {
   float* C;
   const double* alpha;
   int64_t lda, ldb, ldc, M, N, K, klen;
+  // gated epilogue (256-row kernel only): with G set, C is not written;
+  // the squared-ReLU gating backward of C (as relu2_gate_bwd_kernel
+  // computes it from a stored C) goes to dG and dU instead, G, U, dG, dU
+  // laid out like C
+  const float* G = nullptr;
+  const float* U = nullptr;
+  uint16_t* dG = nullptr;
+  uint16_t* dU = nullptr;
 };
 
 // the products of one launch of the 256-row kernel (its tiles dealt over
@@ -680,6 +688,51 @@ __global__ __launch_bounds__(512) void gemm_nt_bf16_big_kernel(NtSet set) {
   // lane holds C[m0 + 128wm + 16i + 4lg + q][n0 + 64wn + 16j + l16]
   const double g = alpha ? *alpha : 1.0;
   const bool scaled = alpha != nullptr;
+  if (pr.G) {
+    const float* __restrict__ G = pr.G;
+    const float* __restrict__ U = pr.U;
+    uint16_t* __restrict__ dG = pr.dG;
+    uint16_t* __restrict__ dU = pr.dU;
+    // software-pipelined over the MFMA row tiles: row tile i + 1's 32
+    // loads issue before row tile i's stores (stores could alias them as
+    // far as the compiler knows, so a load written after a store waits)
+    float gv[2][4][4], uv[2][4][4];
+    auto load = [&](int i, float (&gb)[4][4], float (&ub)[4][4]) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t m = m0 + wm * 128 + i * 16 + 4 * lg + q;
+          const int64_t n = n0 + wn * 64 + j * 16 + l16;
+          const bool in = m < M && n < N;
+          const int64_t e = in ? m * ldc + n : 0;
+          gb[q][j] = in ? ld_global(G + e) : 0.f;
+          ub[q][j] = in ? ld_global(U + e) : 0.f;
+        }
+    };
+    load(0, gv[0], uv[0]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i + 1 < 8) load(i + 1, gv[(i + 1) & 1], uv[(i + 1) & 1]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t m = m0 + wm * 128 + i * 16 + 4 * lg + q;
+          const int64_t n = n0 + wn * 64 + j * 16 + l16;
+          if (m >= M || n >= N) continue;
+          const int64_t e = m * ldc + n;
+          const float dh = scaled ? (float)((double)c[i][j][q] * g) : c[i][j][q];
+          const float gq = gv[i & 1][q][j];
+          const float r = gq > 0.f ? gq : 0.f;
+          const float r2 = r * r;
+          const float du = dh * uv[i & 1][q][j];
+          st_global(dU + e, f32_to_bf16_rne(dh * r2));
+          st_global(dG + e, f32_to_bf16_rne(du * (2.f * r)));
+        }
+    }
+    return;
+  }
   if (m0 + kBigM <= M && n0 + T::N <= N) {
     float* cb = C + (m0 + wm * 128 + 4 * lg) * ldc + n0 + wn * 64 + l16;
 #pragma unroll
@@ -924,6 +977,51 @@ hipError_t launch_bwd(const uint16_t* dY, const int8_t* xq, const float* scale, 
   if (dW) pw = dw_problem(dW, ws, tokens, k, n_out);
   float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + bwd_partial_offset(tokens, k, n_out));
   return gemm_nt_run(dX ? &px : nullptr, dW ? &pw : nullptr, partials, s);
+}
+
+// The down projection's backward with the gating backward fused into its
+// dX product: the dX tiles never reach memory; their epilogue forms dG and
+// dU (the squared-ReLU gating backward of dX, as relu2_gate_bwd_kernel
+// computes it), so results equal bitlinear_bwd followed by the gating
+// backward bit for bit.  dX runs unsplit on the 256-row kernel (its
+// epilogue holds the gating); dW as in launch_bwd.  tokens > 0.
+hipError_t launch_bwd_gate(const uint16_t* dY, const int8_t* xq, const float* scale, const void* packed,
+                           const double* gamma, const float* G, const float* U, uint16_t* dG, uint16_t* dU,
+                           float* dW, void* ws, int64_t tokens, int64_t k, int64_t n_out, int S,
+                           hipStream_t s) {
+  PrepList L;
+  prep_dx(L, packed, ws, tokens, k, n_out);
+  if (dW) prep_dw(L, dY, xq, scale, ws, tokens, k, n_out);
+  hipError_t e = L.launch(S, s);
+  if (e != hipSuccess) return e;
+  NtProblem px = dx_problem(dY, gamma, nullptr, ws, tokens, k, n_out);
+  px.G = G;
+  px.U = U;
+  px.dG = dG;
+  px.dU = dU;
+  NtSet set{};
+  set.p[0] = px;
+  set.n = 1;
+  NtProblem pw{};
+  bool dw_split = false;
+  if (dW) {
+    pw = dw_problem(dW, ws, tokens, k, n_out);
+    dw_split = bwd_splits(pw.M, pw.N, pw.K) > 1;
+    if (!dw_split) {
+      set.p[1] = pw;
+      set.n = 2;
+      if (pw.K > px.K) std::swap(set.p[0], set.p[1]);  // the deeper product first within each XCD
+    }
+  }
+  const int f = g_bwd_tiles.load(std::memory_order_relaxed);
+  e = launch_big(set, f >= 2 ? f : big_kind(set), s);  // 128 x 128 tiles have no gated epilogue
+  if (e != hipSuccess) return e;
+  if (dw_split) {
+    float* partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + bwd_partial_offset(tokens, k, n_out));
+    e = gemm_nt_split(pw, partials, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_group(const BwdItem* items, int count, int64_t tokens, int S, void* ws,

@@ -31,4 +31,11 @@ inline size_t bwd_group_item_bytes(int64_t tokens, int64_t k, int64_t n_out) {
 hipError_t launch_bwd_group(const BwdItem* items, int count, int64_t tokens, int S, void* ws,
                             hipStream_t s);
 
+// the down projection's backward with the gating backward fused into its
+// dX epilogue (dG, dU bf16 [tokens x k]; dW optional); tokens > 0
+hipError_t launch_bwd_gate(const uint16_t* dY, const int8_t* xq, const float* scale, const void* packed,
+                           const double* gamma, const float* G, const float* U, uint16_t* dG, uint16_t* dU,
+                           float* dW, void* ws, int64_t tokens, int64_t k, int64_t n_out, int S,
+                           hipStream_t s);
+
 }  // namespace bl

@@ -184,3 +184,42 @@ def test_bwd_group_no_tokens_zeroes_dw():
     torch.cuda.synchronize()
     for e in entries:
         assert torch.count_nonzero(e["dW"]).item() == 0
+
+
+@pytest.mark.parametrize("n_out,k,tokens,want_dw", [
+    (272, 384, 300, True), (48, 256, 70, False),     # ragged
+    (2560, 6912, 4096, True),                          # BitNet-2B4T down at 4096 tokens
+])
+def test_bwd_relu2_gate_matches_separate_calls(n_out, k, tokens, want_dw):
+    """The down projection's backward with the gating backward fused into
+    its dX epilogue: dG, dU and dW bit-identical to bitlinear_bwd followed
+    by bitlinear_relu2_gate_bwd, on every tile choice."""
+    lw, _, _ = H.quantize_on_gpu(synth.weights(n_out, k, seed=k + tokens), 6, 8, want_wq=False)
+    bufs = lw.fwd(bf16_tensor(synth.activations(tokens, k, seed=tokens)), tokens)
+    dY = bf16_tensor(synth.grad_output(tokens, n_out, seed=n_out))
+    gen = torch.Generator(device="cuda").manual_seed(tokens)
+    G = torch.randn(tokens * k, device="cuda", generator=gen)
+    U = torch.randn(tokens * k, device="cuda", generator=gen)
+    ws = torch.empty(bl.bitlinear_bwd_workspace_bytes(tokens, k, n_out), dtype=torch.uint8, device="cuda")
+    dX = torch.empty(tokens * k, dtype=torch.float32, device="cuda")
+    dW_ref = torch.empty(n_out * k, dtype=torch.float32, device="cuda")
+    bl.bitlinear_bwd(dY, bufs["xq"], bufs["x_scale"], lw.packed, lw.gamma, tokens, k, n_out, 6, 8, dX, dW_ref, ws=ws)
+    dG_ref = torch.empty(tokens * k, dtype=torch.bfloat16, device="cuda")
+    dU_ref = torch.empty(tokens * k, dtype=torch.bfloat16, device="cuda")
+    bl.bitlinear_relu2_gate_bwd(dX, G, U, tokens * k, dG_ref, dU_ref)
+    torch.cuda.synchronize()
+    for tiles in (0, 1, 2, 3):
+        bl.bitlinear_bwd_tiles(tiles)
+        try:
+            dG = torch.full((tokens * k,), 0x7fc0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+            dU = torch.full((tokens * k,), 0x7fc0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+            dW = torch.full((n_out * k,), float("nan"), device="cuda") if want_dw else None
+            bl.bitlinear_bwd_relu2_gate(dY, bufs["xq"], bufs["x_scale"], lw.packed, lw.gamma, tokens, k, n_out, 6, 8,
+                                        G, U, dG, dU, dW, ws=ws)
+            torch.cuda.synchronize()
+        finally:
+            bl.bitlinear_bwd_tiles(0)
+        assert torch.equal(dG.view(torch.int16), dG_ref.view(torch.int16)), tiles
+        assert torch.equal(dU.view(torch.int16), dU_ref.view(torch.int16)), tiles
+        if want_dw:
+            assert np.array_equal(dW.cpu().numpy().view(np.uint32), dW_ref.cpu().numpy().view(np.uint32)), tiles
