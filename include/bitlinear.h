@@ -502,6 +502,27 @@ size_t bitlinear_bwd_group_workspace_bytes(const bitlinear_bwd_item *items, int 
 int bitlinear_bwd_group(const bitlinear_bwd_item *items, int count, int64_t tokens,
                         int n, int m, void *ws, size_t ws_bytes, void *stream);
 
+/* bitlinear_bwd_group in two halves, so that the half that does not wait
+ * for dY can run on another stream while earlier work runs (the same
+ * method and sections as bitlinear_bwd_group):
+ *   BL_BWD_PREPARE  converts what reads only packed codes and x_q (the
+ *                   codes for dX, x_q^T for dW) into ws; no product runs
+ *                   and nothing but ws is written.
+ *   BL_BWD_FINISH   converts dY, then runs every product, reading what a
+ *                   BL_BWD_PREPARE call with the same items, tokens, n:m
+ *                   and ws left in ws.
+ *   both            exactly bitlinear_bwd_group.
+ * PREPARE then FINISH gives bitlinear_bwd_group's results bit for bit,
+ * provided packed, x_q and ws are not changed in between and FINISH is
+ * ordered after PREPARE (same stream, or an event).  With tokens == 0
+ * PREPARE does nothing and FINISH zeroes every dW.  Other arguments and
+ * errors as for bitlinear_bwd_group; any other phase is BL_EINVAL. */
+#define BL_BWD_PREPARE 1
+#define BL_BWD_FINISH 2
+int bitlinear_bwd_group_phase(const bitlinear_bwd_item *items, int count, int64_t tokens,
+                              int n, int m, int phase, void *ws, size_t ws_bytes,
+                              void *stream);
+
 /* Steps 8-9 of the down projection of the BitNet b1.58 2B4T feed-forward
  * with the squared-ReLU gating backward (2B4T article §一) fused into its dX
  * product: the dual straight-through backward of bitlinear_bwd (Sparse-BitNet

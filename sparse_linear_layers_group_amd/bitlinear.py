@@ -46,6 +46,7 @@ _SIGS = {
                                          _vp, _vp, _sz, _vp]),
     "bitlinear_bwd_group_workspace_bytes": (_sz, [_vp, _int, _i64]),
     "bitlinear_bwd_group": (_int, [_vp, _int, _i64, _int, _int, _vp, _sz, _vp]),
+    "bitlinear_bwd_group_phase": (_int, [_vp, _int, _i64, _int, _int, _int, _vp, _sz, _vp]),
     "bitlinear_contract_group_workspace_bytes": (_sz, [_vp, _int, _i64, _i64]),
     "bitlinear_contract_group": (_int, [_vp, _int, _vp, _vp, _i64, _i64, _int, _int, _vp, _sz, _vp]),
     "bitlinear_fwd_noalloc": (_int, [_vp, _i64, _i64, _vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -291,6 +292,20 @@ def bitlinear_bwd_group(items, count, tokens, n, m, ws=None, ws_bytes=None, stre
                                    (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes),
                                    _stream(stream))
     _check(st, "bitlinear_bwd_group")
+
+
+BL_BWD_PREPARE = 1
+BL_BWD_FINISH = 2
+
+
+def bitlinear_bwd_group_phase(items, count, tokens, n, m, phase, ws=None, ws_bytes=None, stream=None):
+    """One half of bitlinear_bwd_group: BL_BWD_PREPARE converts the codes and
+    x_q into ws, BL_BWD_FINISH converts dY and runs the products."""
+    st = lib().bitlinear_bwd_group_phase(items, int(count), int(tokens), n, m, int(phase),
+                                         _ptr(ws, (torch.uint8,), None, "ws", optional=True),
+                                         (ws.numel() if ws is not None else 0) if ws_bytes is None else int(ws_bytes),
+                                         _stream(stream))
+    _check(st, "bitlinear_bwd_group_phase")
 
 
 def bitlinear_bwd_relu2_gate(dY, xq, x_scale, packed, gamma, tokens, k, n_out, n, m, G, U, dG, dU, dW=None,

@@ -901,8 +901,8 @@ size_t bitlinear_bwd_group_workspace_bytes(const bitlinear_bwd_item* items, int 
   return total;
 }
 
-int bitlinear_bwd_group(const bitlinear_bwd_item* items, int count, int64_t tokens, int n, int m,
-                        void* ws, size_t ws_bytes, void* stream) {
+static int bwd_group_run(const bitlinear_bwd_item* items, int count, int64_t tokens, int n, int m, int phase,
+                         void* ws, size_t ws_bytes, void* stream) {
   TRY(check_nm(n, m));
   if (!items) return fail(BL_EINVAL, "items is NULL");
   if (count < 1) return fail(BL_ESHAPE, "count must be >= 1 (got %d)", count);
@@ -919,7 +919,9 @@ int bitlinear_bwd_group(const bitlinear_bwd_item* items, int count, int64_t toke
   if (!any) return ok();
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (tokens == 0) {
-    // no tokens: every dX is empty and every dW all zeros (no workspace)
+    // no tokens: every dX is empty and every dW all zeros (no workspace);
+    // the zeros belong to the second phase
+    if (!(phase & 2)) return ok();
     for (int i = 0; i < count; ++i)
       if (items[i].dW) {
         hipError_t e = bl::launch_bwd(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, items[i].dW,
@@ -940,8 +942,20 @@ int bitlinear_bwd_group(const bitlinear_bwd_item* items, int count, int64_t toke
     its.push_back(bl::BwdItem{it.dY, it.xq, it.x_scale, it.packed, it.gamma, it.dX, it.dW, it.k, it.n_out});
   }
   if (its.empty()) return ok();
-  hipError_t e = bl::launch_bwd_group(its.data(), (int)its.size(), tokens, bl::s_of(n, m), ws, s);
+  hipError_t e = bl::launch_bwd_group(its.data(), (int)its.size(), tokens, bl::s_of(n, m), ws, phase, s);
   return hip_status(e, "grouped backward launch");
+}
+
+int bitlinear_bwd_group(const bitlinear_bwd_item* items, int count, int64_t tokens, int n, int m,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return bwd_group_run(items, count, tokens, n, m, BL_BWD_PREPARE | BL_BWD_FINISH, ws, ws_bytes, stream);
+}
+
+int bitlinear_bwd_group_phase(const bitlinear_bwd_item* items, int count, int64_t tokens, int n, int m,
+                              int phase, void* ws, size_t ws_bytes, void* stream) {
+  if (phase < 1 || phase > (BL_BWD_PREPARE | BL_BWD_FINISH))
+    return fail(BL_EINVAL, "phase must be BL_BWD_PREPARE, BL_BWD_FINISH or both (got %d)", phase);
+  return bwd_group_run(items, count, tokens, n, m, phase, ws, ws_bytes, stream);
 }
 
 int bitlinear_bwd_relu2_gate(const uint16_t* dY, const int8_t* xq, const float* x_scale, const void* packed,

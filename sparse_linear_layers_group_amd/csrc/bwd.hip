@@ -939,15 +939,17 @@ static NtProblem dx_problem(const uint16_t* dY, const double* gamma, float* dX, 
   return NtProblem{dY, codes_t, dX, gamma, n_out, np, k, tokens, k, n_out, n_out};
 }
 
-// dW operands: bf16(dY * s)^T always; x_q^T unless with_xq is false (the
-// grouped call reuses another item's x_q^T when two items share x_q)
+// dW operands: bf16(dY * s)^T unless with_dys is false, x_q^T unless
+// with_xq is false (the grouped call reuses another item's x_q^T when two
+// items share x_q, and its phases split the two)
 static void prep_dw(PrepList& L, const uint16_t* dY, const int8_t* xq, const float* scale, void* ws,
-                    int64_t tokens, int64_t k, int64_t n_out, bool with_xq = true) {
+                    int64_t tokens, int64_t k, int64_t n_out, bool with_xq = true, bool with_dys = true) {
   const int64_t tp = bwd_tokens_padded(tokens);
   char* w = reinterpret_cast<char*>(ws);
   uint16_t* dys_t = reinterpret_cast<uint16_t*>(w + bwd_dys_offset(tokens, k, n_out));
   uint16_t* xq_t = reinterpret_cast<uint16_t*>(w + bwd_xq_offset(tokens, k, n_out));
-  L.t.push_back(PrepTask{dY, scale, dys_t, tokens, n_out, tp, kPrepDys, (int32_t)((tp / 64) * ((n_out + 63) / 64))});
+  if (with_dys)
+    L.t.push_back(PrepTask{dY, scale, dys_t, tokens, n_out, tp, kPrepDys, (int32_t)((tp / 64) * ((n_out + 63) / 64))});
   if (with_xq) L.t.push_back(PrepTask{xq, nullptr, xq_t, tokens, k, tp, kPrepXq, (int32_t)((tp / 64) * (k / 64))});
 }
 
@@ -1024,8 +1026,12 @@ hipError_t launch_bwd_gate(const uint16_t* dY, const int8_t* xq, const float* sc
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_group(const BwdItem* items, int count, int64_t tokens, int S, void* ws,
+hipError_t launch_bwd_group(const BwdItem* items, int count, int64_t tokens, int S, void* ws, int phase,
                             hipStream_t s) {
+  // phase bit 0: the conversions that read only packed codes and x_q;
+  // bit 1: the dY conversions and the products.  Both walk the items in
+  // the same order, so every operand lands at the same place either way
+  const bool first = (phase & 1) != 0, second = (phase & 2) != 0;
   std::vector<NtProblem> probs;
   // x_q^T already prepared in this call, by x_q pointer and k: layers fed
   // the same input (q, k, v; gate, up) share it
@@ -1040,14 +1046,14 @@ hipError_t launch_bwd_group(const BwdItem* items, int count, int64_t tokens, int
   for (int i = 0; i < count; ++i) {
     const BwdItem& it = items[i];
     if (it.dX) {
-      prep_dx(L, it.packed, w, tokens, it.k, it.n_out);
+      if (first) prep_dx(L, it.packed, w, tokens, it.k, it.n_out);
       probs.push_back(dx_problem(it.dY, it.gamma, it.dX, w, tokens, it.k, it.n_out));
     }
     if (it.dW) {
       const XqT* seen = nullptr;
       for (const XqT& d : done)
         if (d.xq == it.xq && d.k == it.k) seen = &d;
-      prep_dw(L, it.dY, it.xq, it.scale, w, tokens, it.k, it.n_out, seen == nullptr);
+      prep_dw(L, it.dY, it.xq, it.scale, w, tokens, it.k, it.n_out, first && seen == nullptr, second);
       NtProblem p = dw_problem(it.dW, w, tokens, it.k, it.n_out);
       if (seen) p.B = seen->t;
       else done.push_back(XqT{it.xq, it.k, p.B});
@@ -1056,7 +1062,7 @@ hipError_t launch_bwd_group(const BwdItem* items, int count, int64_t tokens, int
     w += bwd_group_item_bytes(tokens, it.k, it.n_out);
   }
   hipError_t pe = L.launch(S, s);
-  if (pe != hipSuccess) return pe;
+  if (pe != hipSuccess || !second) return pe;
   // deepest contraction first: within each XCD the longest tiles start
   // first and the short ones fill the end (a longest-first schedule)
   std::stable_sort(probs.begin(), probs.end(),

@@ -27,8 +27,10 @@ inline size_t bwd_group_item_bytes(int64_t tokens, int64_t k, int64_t n_out) {
 
 // every item's operands prepared into its own workspace region (x_q^T once
 // per distinct x_q and k), then all products in launches of up to 16,
-// deepest contraction first; tokens > 0
-hipError_t launch_bwd_group(const BwdItem* items, int count, int64_t tokens, int S, void* ws,
+// deepest contraction first; tokens > 0.  phase 1 runs only the
+// conversions of packed codes and x_q, phase 2 the rest (on what phase 1
+// left in ws), phase 3 both
+hipError_t launch_bwd_group(const BwdItem* items, int count, int64_t tokens, int S, void* ws, int phase,
                             hipStream_t s);
 
 // the down projection's backward with the gating backward fused into its

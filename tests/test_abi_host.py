@@ -365,3 +365,22 @@ def test_contract_group_validation(L):
     assert need > 0
     assert g(good, 2, A, A, 4, 896, 6, 8, None, 0, None) == bl.BL_EWORKSPACE
     assert g(good, 2, A, A, 0, 896, 6, 8, None, 0, None) == bl.BL_OK  # no tokens: nothing runs
+
+
+def test_bwd_group_phase_validation(L):
+    """The phased grouped backward takes BL_BWD_PREPARE, BL_BWD_FINISH or both,
+    validates like the one-call form, and with no tokens the preparing half
+    enqueues nothing."""
+    g = L.bitlinear_bwd_group_phase
+    good = _bwd_items([(256, 128, True, True), (384, 272, True, True)])
+    need = bl.bitlinear_bwd_group_workspace_bytes(good, 2, 4)
+    for phase in (0, 4, -1):
+        assert g(good, 2, 4, 6, 8, phase, A, need, None) == bl.BL_EINVAL
+        assert "phase" in bl.bitlinear_last_error()
+    for phase in (bl.BL_BWD_PREPARE, bl.BL_BWD_FINISH, bl.BL_BWD_PREPARE | bl.BL_BWD_FINISH):
+        assert g(good, 2, 4, 6, 8, phase, A, need - 1, None) == bl.BL_EWORKSPACE
+        assert g(good, 2, 4, 5, 8, phase, A, need, None) == bl.BL_EUNSUPPORTED
+        bad = _bwd_items([(256, 128, True, True), (384, 120, True, True)])
+        assert g(bad, 2, 4, 6, 8, phase, A, need, None) == bl.BL_ESHAPE
+        assert "item 1" in bl.bitlinear_last_error()
+    assert g(good, 2, 0, 6, 8, bl.BL_BWD_PREPARE, None, 0, None) == bl.BL_OK

@@ -223,3 +223,36 @@ def test_bwd_relu2_gate_matches_separate_calls(n_out, k, tokens, want_dw):
         assert torch.equal(dU.view(torch.int16), dU_ref.view(torch.int16)), tiles
         if want_dw:
             assert np.array_equal(dW.cpu().numpy().view(np.uint32), dW_ref.cpu().numpy().view(np.uint32)), tiles
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shapes,tokens,outputs,inputs", [
+    ([(272, 384), (48, 384), (512, 384), (1040, 640)], 300,
+     [(True, True), (False, True), (True, True), (True, True)], [0, 0, 0, 1]),
+    ([(2560, 2560), (640, 2560), (640, 2560)], 4096, [(True, True)] * 3, [0, 0, 0]),
+])
+def test_bwd_group_phases_match_one_call(shapes, tokens, outputs, inputs):
+    """BL_BWD_PREPARE on a second stream, then BL_BWD_FINISH on the current
+    one after an event, on a workspace that starts as garbage: dX and dW
+    equal the one-call grouped backward's bit for bit."""
+    layers, entries = _group_case(shapes, tokens, outputs, seed=7 * tokens + len(shapes), inputs=inputs)
+    fresh = [dict(e, dX=None if e["dX"] is None else torch.full_like(e["dX"], float("nan")),
+                  dW=None if e["dW"] is None else torch.full_like(e["dW"], float("nan"))) for e in entries]
+    items = bl.make_bwd_items(fresh, tokens)
+    need = bl.bitlinear_bwd_group_workspace_bytes(items, len(fresh), tokens)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bl.bitlinear_bwd_group_phase(items, len(fresh), tokens, 6, 8, bl.BL_BWD_PREPARE, ws,
+                                     stream=side.cuda_stream)
+    done = torch.cuda.Event()
+    done.record(side)
+    torch.cuda.current_stream().wait_event(done)
+    bl.bitlinear_bwd_group_phase(items, len(fresh), tokens, 6, 8, bl.BL_BWD_FINISH, ws)
+    torch.cuda.synchronize()
+    for e, f in zip(entries, fresh):
+        for name in ("dX", "dW"):
+            if e[name] is None:
+                continue
+            assert np.array_equal(f[name].cpu().numpy().view(np.uint32), e[name].cpu().numpy().view(np.uint32)), name
