@@ -714,22 +714,46 @@ __global__ __launch_bounds__(512) void gemm_nt_bf16_big_kernel(NtSet set) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i + 1 < 8) load(i + 1, gv[(i + 1) & 1], uv[(i + 1) & 1]);
+      // lanes l16 and l16 ^ 1 hold neighbouring columns of the same four
+      // rows: after one exchange the even lane stores rows 0 and 2 and the
+      // odd lane rows 1 and 3, each as a 4-byte pair of columns (k is a
+      // multiple of 128, so both columns of a pair are in range together)
+      const bool odd = (l16 & 1) != 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int j = 0; j < 4; ++j) {
+        uint32_t hu[4], hg[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t m = m0 + wm * 128 + i * 16 + 4 * lg + q;
-          const int64_t n = n0 + wn * 64 + j * 16 + l16;
-          if (m >= M || n >= N) continue;
-          const int64_t e = m * ldc + n;
+        for (int q = 0; q < 4; ++q) {
           const float dh = scaled ? (float)((double)c[i][j][q] * g) : c[i][j][q];
           const float gq = gv[i & 1][q][j];
           const float r = gq > 0.f ? gq : 0.f;
           const float r2 = r * r;
           const float du = dh * uv[i & 1][q][j];
-          st_global(dU + e, f32_to_bf16_rne(dh * r2));
-          st_global(dG + e, f32_to_bf16_rne(du * (2.f * r)));
+          hu[q] = f32_to_bf16_rne(dh * r2);
+          hg[q] = f32_to_bf16_rne(du * (2.f * r));
         }
+        const uint32_t pu0 = hu[0] | hu[1] << 16, pu1 = hu[2] | hu[3] << 16;
+        const uint32_t pg0 = hg[0] | hg[1] << 16, pg1 = hg[2] | hg[3] << 16;
+        const uint32_t xu0 = lane_xor1(pu0), xu1 = lane_xor1(pu1);
+        const uint32_t xg0 = lane_xor1(pg0), xg1 = lane_xor1(pg1);
+        const int64_t col = n0 + wn * 64 + j * 16 + (l16 & ~1);
+        if (col >= N) continue;
+        const int64_t ra = m0 + wm * 128 + i * 16 + 4 * lg + (odd ? 1 : 0);
+        if (ra < M) {
+          const int64_t e = ra * ldc + col;
+          st_global(reinterpret_cast<uint32_t*>(dU + e),
+                    odd ? (xu0 >> 16) | (pu0 & 0xffff0000u) : (pu0 & 0xffffu) | (xu0 << 16));
+          st_global(reinterpret_cast<uint32_t*>(dG + e),
+                    odd ? (xg0 >> 16) | (pg0 & 0xffff0000u) : (pg0 & 0xffffu) | (xg0 << 16));
+        }
+        if (ra + 2 < M) {
+          const int64_t e = (ra + 2) * ldc + col;
+          st_global(reinterpret_cast<uint32_t*>(dU + e),
+                    odd ? (xu1 >> 16) | (pu1 & 0xffff0000u) : (pu1 & 0xffffu) | (xu1 << 16));
+          st_global(reinterpret_cast<uint32_t*>(dG + e),
+                    odd ? (xg1 >> 16) | (pg1 & 0xffff0000u) : (pg1 & 0xffffu) | (xg1 << 16));
+        }
+      }
     }
     return;
   }
